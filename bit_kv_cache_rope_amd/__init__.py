@@ -1,0 +1,237 @@
+"""bit_kv_cache_rope_amd — Python binding of libwushkv (WUSH-KV cache path on MI355X).
+
+Argument marshalling only: every step of the write and read path runs in the
+HIP kernels of libwushkv.so.  PyTorch supplies device memory and the stream.
+The functions keep the C names:
+
+    wushkv_quantize_keys(K, pos, rope, T_k, bits, quantizer, out)
+    wushkv_quantize_values(V, bits, quantizer, out)
+    wushkv_dequantize(packed, n_tokens, n_heads, bits, quantizer, T_k_inv=None, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch  # imported first: the library binds to the HIP runtime torch has loaded
+
+from . import _lib
+from ._lib import WushKVError, F32, BF16, Q_SYM_RMS, Q_AFFINE_PCT  # noqa: F401
+
+__all__ = [
+    "WushKVError", "Quantizer", "sym", "affine", "Transform", "Rope", "PackedCache", "alloc_packed",
+    "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize", "wushkv_debug_rope_transform",
+    "wushkv_debug_rope_cos_sin", "wushkv_rope_frequencies", "library",
+]
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libwushkv.so (raises ImportError if it is not built)."""
+    L = _lib.load()
+    maps = _lib.hip_runtimes_mapped()
+    if len(maps) > 1:
+        raise RuntimeError(f"more than one HIP runtime mapped into this process: {maps}")
+    return L
+
+
+@dataclass(frozen=True)
+class Quantizer:
+    kind: int = Q_SYM_RMS
+    clip_alpha: float = 2.0
+    group: int = 128
+    p_lo: float = 1.0
+    p_hi: float = 99.0
+
+    def c(self) -> _lib.Quantizer:
+        return _lib.Quantizer(self.kind, self.clip_alpha, self.group, self.p_lo, self.p_hi)
+
+    @property
+    def scales_per_head(self) -> int:
+        return 1 if self.kind == Q_SYM_RMS else 4
+
+
+def sym(clip_alpha: float = 2.0) -> Quantizer:
+    return Quantizer(Q_SYM_RMS, clip_alpha, 128, 0.0, 100.0)
+
+
+def affine(p_lo: float = 1.0, p_hi: float = 99.0) -> Quantizer:
+    return Quantizer(Q_AFFINE_PCT, 0.0, 32, p_lo, p_hi)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Transform:
+    """Key transform handle (T_k, or T_k^-1 for reads); T: [H][128][128] fp32, y = T x."""
+
+    def __init__(self, T):
+        T = torch.as_tensor(T).detach().to("cpu", torch.float32).contiguous()
+        if T.dim() != 3 or T.shape[1:] != (128, 128):
+            raise ValueError("T must be [n_heads][128][128]")
+        self.n_heads = int(T.shape[0])
+        h = ctypes.c_void_p()
+        _lib.check(library().wushkv_transform_create(ctypes.c_void_p(T.data_ptr()), self.n_heads, ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            library().wushkv_transform_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Rope:
+    """RoPE handle: base theta, positions in [0, max_pos)."""
+
+    def __init__(self, theta: float = 1e6, max_pos: int = 1 << 17):
+        self.theta, self.max_pos = float(theta), int(max_pos)
+        h = ctypes.c_void_p()
+        _lib.check(library().wushkv_rope_create(ctypes.c_float(self.theta), self.max_pos, ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            library().wushkv_rope_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+@dataclass
+class PackedCache:
+    """Caller-owned packed cache: codes uint8 [rows][H][16*bits], scales fp16
+    [rows][H] (sym) or [rows][H][4] (affine), zeros fp16 [rows][H][4] (affine)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    zeros: torch.Tensor | None = None
+    slots: torch.Tensor | None = None
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    def c(self) -> _lib.Packed:
+        return _lib.Packed(self.codes.data_ptr(), self.scales.data_ptr(),
+                           None if self.zeros is None else self.zeros.data_ptr(),
+                           None if self.slots is None else self.slots.data_ptr(), self.n_rows)
+
+    def with_slots(self, slots: torch.Tensor | None) -> "PackedCache":
+        return PackedCache(self.codes, self.scales, self.zeros, slots)
+
+
+def alloc_packed(rows: int, n_heads: int, bits: int, quantizer: Quantizer, device="cuda",
+                 slots: torch.Tensor | None = None) -> PackedCache:
+    codes = torch.zeros((rows, n_heads, 16 * bits), dtype=torch.uint8, device=device)
+    if quantizer.kind == Q_SYM_RMS:
+        scales = torch.zeros((rows, n_heads), dtype=torch.float16, device=device)
+        zeros = None
+    else:
+        scales = torch.zeros((rows, n_heads, 4), dtype=torch.float16, device=device)
+        zeros = torch.zeros((rows, n_heads, 4), dtype=torch.float16, device=device)
+    return PackedCache(codes, scales, zeros, slots)
+
+
+def _kv_args(X: torch.Tensor):
+    if not X.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if X.dtype == torch.bfloat16:
+        dt = BF16
+    elif X.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError("K/V must be bfloat16 or float32")
+    if X.dim() != 3 or X.shape[2] != 128 or X.stride(2) != 1 or X.stride(1) != 128:
+        raise ValueError("K/V must be [n_tokens][n_heads][128] with contiguous heads")
+    stride = X.stride(0) if X.shape[0] > 1 else X.shape[1] * 128
+    return dt, int(X.shape[0]), int(X.shape[1]), int(stride)
+
+
+def _check_device_tensor(t: torch.Tensor | None, name: str, dtype):
+    if t is None:
+        return
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor")
+
+
+def wushkv_quantize_keys(K: torch.Tensor, pos: torch.Tensor, rope: Rope, T_k: Transform, bits: int,
+                         quantizer: Quantizer, out: PackedCache, stream=None) -> None:
+    dt, n, h, stride = _kv_args(K)
+    _check_device_tensor(pos, "pos", torch.int32)
+    _check_device_tensor(out.slots, "slots", torch.int64)
+    q = quantizer.c()
+    p = out.c()
+    _lib.check(library().wushkv_quantize_keys(
+        ctypes.c_void_p(K.data_ptr()), dt, n, h, stride, ctypes.c_void_p(pos.data_ptr()), rope.handle,
+        T_k.handle, bits, ctypes.byref(q), ctypes.byref(p), _stream(stream)))
+
+
+def wushkv_quantize_values(V: torch.Tensor, bits: int, quantizer: Quantizer, out: PackedCache,
+                           stream=None) -> None:
+    dt, n, h, stride = _kv_args(V)
+    _check_device_tensor(out.slots, "slots", torch.int64)
+    q = quantizer.c()
+    p = out.c()
+    _lib.check(library().wushkv_quantize_values(
+        ctypes.c_void_p(V.data_ptr()), dt, n, h, stride, bits, ctypes.byref(q), ctypes.byref(p),
+        _stream(stream)))
+
+
+def wushkv_dequantize(packed: PackedCache, n_tokens: int, n_heads: int, bits: int, quantizer: Quantizer,
+                      T_k_inv: Transform | None = None, out: torch.Tensor | None = None,
+                      out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((n_tokens, n_heads, 128), dtype=out_dtype, device=packed.codes.device)
+    if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 or bfloat16 tensor")
+    _check_device_tensor(packed.slots, "slots", torch.int64)
+    q = quantizer.c()
+    p = packed.c()
+    _lib.check(library().wushkv_dequantize(
+        ctypes.byref(p), n_tokens, n_heads, bits, ctypes.byref(q), None if T_k_inv is None else T_k_inv.handle,
+        ctypes.c_void_p(out.data_ptr()), F32 if out.dtype == torch.float32 else BF16, _stream(stream)))
+    return out
+
+
+def wushkv_debug_rope_transform(K: torch.Tensor, pos: torch.Tensor, rope: Rope, T_k: Transform,
+                                stream=None) -> torch.Tensor:
+    dt, n, h, stride = _kv_args(K)
+    _check_device_tensor(pos, "pos", torch.int32)
+    y = torch.empty((n, h, 128), dtype=torch.float32, device=K.device)
+    _lib.check(library().wushkv_debug_rope_transform(
+        ctypes.c_void_p(K.data_ptr()), dt, n, h, stride, ctypes.c_void_p(pos.data_ptr()), rope.handle,
+        T_k.handle, ctypes.c_void_p(y.data_ptr()), _stream(stream)))
+    return y
+
+
+def wushkv_debug_rope_cos_sin(rope: Rope, pos: torch.Tensor, stream=None) -> torch.Tensor:
+    _check_device_tensor(pos, "pos", torch.int32)
+    cs = torch.empty((pos.numel(), 64, 2), dtype=torch.float32, device=pos.device)
+    _lib.check(library().wushkv_debug_rope_cos_sin(rope.handle, ctypes.c_void_p(pos.data_ptr()), pos.numel(),
+                                                   ctypes.c_void_p(cs.data_ptr()), _stream(stream)))
+    return cs
+
+
+def wushkv_rope_frequencies(theta: float):
+    out = (ctypes.c_float * 64)()
+    _lib.check(library().wushkv_rope_frequencies(ctypes.c_float(theta), out))
+    return list(out)

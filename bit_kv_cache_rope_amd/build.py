@@ -1,0 +1,73 @@
+"""Build libwushkv.so for gfx950 with hipcc (in-tree, no JIT cache).
+
+    python -m bit_kv_cache_rope_amd.build [--jobs N]
+
+Each HIP source compiles to its own object (in parallel), then one shared
+library is linked next to this file.  Flags: -O3, fp contraction off (the
+kernels spell out every fma they mean), packed-fp32 instructions off.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build", "wushkv")
+LIB_PATH = os.path.join(HERE, "libwushkv.so")
+SOURCES = ["api.hip", "keys.hip", "values.hip", "dequant.hip"]
+HEADERS = ["device_common.h", "internal.h"]
+ARCH = os.environ.get("WUSHKV_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def compile_flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+            "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Always recompiles (the build check must compile every time)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    args = ap.parse_args()
+    build(args.jobs, verbose=True)
+    sys.exit(0)

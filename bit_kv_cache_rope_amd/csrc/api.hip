@@ -1,0 +1,463 @@
+// libwushkv C ABI: argument validation, handles and launch dispatch.
+//
+// Every entry point validates on the host before anything is launched and
+// reports failures as status codes with a thread-local detail string.  Handle
+// creation allocates device memory; the quantize / dequantize calls do not.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+wushkv_status fail(wushkv_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+wushkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(WUSHKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// bf16 bit pattern of an fp32 value, round-to-nearest-even (finite inputs).
+uint16_t host_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float host_bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+wushkv_status current_device(int* dev) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return fail(WUSHKV_ERR_NO_DEVICE, "no HIP device visible");
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return WUSHKV_OK;
+}
+
+// Quantizer description -> kernel arguments.  The percentile interpolation
+// follows h = 31 p / 100, i = floor(h), g = RN32(h - i); the kernels provide
+// order statistics 0, 1 (low end) and 30, 31 (high end).
+wushkv_status make_quant(const wushkv_quantizer* q, wushkv::QuantArgs* out) {
+  if (!q) return fail(WUSHKV_ERR_INVALID_ARG, "quantizer is NULL");
+  std::memset(out, 0, sizeof(*out));
+  if (q->kind == WUSHKV_Q_SYM_RMS) {
+    if (q->group != WUSHKV_HEAD_DIM) return fail(WUSHKV_ERR_UNSUPPORTED, "symmetric quantizer needs group 128");
+    if (!(q->clip_alpha > 0.0f) || !std::isfinite(q->clip_alpha))
+      return fail(WUSHKV_ERR_INVALID_ARG, "clip_alpha must be finite and > 0");
+    out->kind = 0;
+    out->alpha = q->clip_alpha;
+    return WUSHKV_OK;
+  }
+  if (q->kind == WUSHKV_Q_AFFINE_PCT) {
+    if (q->group != 32) return fail(WUSHKV_ERR_UNSUPPORTED, "affine quantizer needs group 32");
+    if (!(q->p_lo >= 0.0f) || !(q->p_hi <= 100.0f) || !(q->p_lo <= q->p_hi))
+      return fail(WUSHKV_ERR_INVALID_ARG, "need 0 <= p_lo <= p_hi <= 100");
+    out->kind = 1;
+    const double hl = 31.0 * (double)q->p_lo / 100.0;
+    if (hl >= 1.0) return fail(WUSHKV_ERR_UNSUPPORTED, "p_lo must be below 100/31 (order statistics 0 and 1)");
+    out->g_lo = (float)hl;
+    out->lo_mode = out->g_lo == 0.0f ? 1 : 0;
+    const double hh = 31.0 * (double)q->p_hi / 100.0;
+    if (hh >= 31.0) {
+      out->hi_mode = 2;
+    } else {
+      const double fl = std::floor(hh);
+      if (fl != 30.0) return fail(WUSHKV_ERR_UNSUPPORTED, "p_hi must be at least 3000/31 (order statistics 30 and 31)");
+      out->g_hi = (float)(hh - fl);
+      out->hi_mode = out->g_hi == 0.0f ? 1 : 0;
+    }
+    return WUSHKV_OK;
+  }
+  return fail(WUSHKV_ERR_INVALID_ARG, "unknown quantizer kind");
+}
+
+wushkv_status check_packed(const wushkv_packed* p, int kind, int64_t n_tokens, bool writer) {
+  if (!p) return fail(WUSHKV_ERR_INVALID_ARG, "packed cache view is NULL");
+  if (!p->codes || !p->scales) return fail(WUSHKV_ERR_INVALID_ARG, "codes and scales must be set");
+  if (kind == 1 && !p->zeros) return fail(WUSHKV_ERR_INVALID_ARG, "affine quantizer needs zeros");
+  if (!aligned(p->codes, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "codes must be 16-byte aligned");
+  if (!aligned(p->scales, kind == 1 ? 8 : 2)) return fail(WUSHKV_ERR_ALIGNMENT, "scales misaligned");
+  if (kind == 1 && !aligned(p->zeros, 8)) return fail(WUSHKV_ERR_ALIGNMENT, "zeros must be 8-byte aligned");
+  if (p->n_rows < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_rows < 0");
+  if (!p->slots && p->n_rows < n_tokens)
+    return fail(WUSHKV_ERR_INVALID_ARG, writer ? "cache has fewer rows than tokens" : "cache has fewer rows than requested");
+  return WUSHKV_OK;
+}
+
+wushkv_status check_tensor(const void* X, wushkv_dtype dt, int64_t n_tokens, int n_heads, int64_t stride) {
+  if (dt != WUSHKV_F32 && dt != WUSHKV_BF16) return fail(WUSHKV_ERR_INVALID_ARG, "dtype must be F32 or BF16");
+  if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
+  if (n_tokens < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (stride < (int64_t)n_heads * WUSHKV_HEAD_DIM) return fail(WUSHKV_ERR_INVALID_ARG, "token_stride < n_heads*128");
+  const int64_t esz = dt == WUSHKV_F32 ? 4 : 2;
+  if ((stride * esz) % 16) return fail(WUSHKV_ERR_ALIGNMENT, "token_stride must span a multiple of 16 bytes");
+  if (n_tokens > 0) {
+    if (!X) return fail(WUSHKV_ERR_INVALID_ARG, "input tensor is NULL");
+    if (!aligned(X, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "input tensor must be 16-byte aligned");
+  }
+  return WUSHKV_OK;
+}
+
+int choose_hg(int64_t n_tiles, int n_heads, int cus, int max_hg) {
+  int hg = (n_tiles * n_heads >= 2LL * cus) ? 4 : 1;
+  if (hg > max_hg) hg = max_hg;
+  while (hg > 1 && n_heads % hg) hg /= 2;
+  return hg;
+}
+
+int blocks_per_group(int64_t n_tiles, int n_groups, int hg, int cus) {
+  const int per_cu = 4 / hg;  // 8 waves per CU: blocks of 2*hg waves
+  int64_t b = ((int64_t)cus * per_cu) / n_groups;
+  if (b < 1) b = 1;
+  if (b > n_tiles) b = n_tiles;
+  return (int)b;
+}
+
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+std::mutex g_cus_mu;
+
+}  // namespace
+
+namespace wushkv {
+
+int device_cu_count(int device) {
+  if (device < 0 || device >= kMaxDevices) return 256;
+  std::lock_guard<std::mutex> lk(g_cus_mu);
+  if (!g_cus[device]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) n = 256;
+    g_cus[device] = n;
+  }
+  return g_cus[device];
+}
+
+}  // namespace wushkv
+
+extern "C" {
+
+int wushkv_version(void) { return 1; }
+
+const char* wushkv_last_error(void) { return g_err.c_str(); }
+
+const char* wushkv_status_string(wushkv_status s) {
+  switch (s) {
+    case WUSHKV_OK: return "ok";
+    case WUSHKV_ERR_INVALID_ARG: return "invalid argument";
+    case WUSHKV_ERR_UNSUPPORTED: return "unsupported";
+    case WUSHKV_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case WUSHKV_ERR_NO_DEVICE: return "no HIP device";
+    case WUSHKV_ERR_HIP: return "HIP runtime error";
+    case WUSHKV_ERR_OOM: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+wushkv_status wushkv_rope_frequencies(float theta, float* omega_out) {
+  if (!omega_out) return fail(WUSHKV_ERR_INVALID_ARG, "omega_out is NULL");
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(WUSHKV_ERR_INVALID_ARG, "theta must be finite and > 1");
+  for (int i = 0; i < 64; ++i) omega_out[i] = (float)std::pow((double)theta, -(double)(2 * i) / 128.0);
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_transform_create(const float* T, int n_heads, wushkv_transform** out) {
+  if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!T) return fail(WUSHKV_ERR_INVALID_ARG, "T is NULL");
+  if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
+  int dev;
+  wushkv_status st = current_device(&dev);
+  if (st) return st;
+  const size_t H = (size_t)n_heads, D = WUSHKV_HEAD_DIM;
+  for (size_t i = 0; i < H * D * D; ++i)
+    if (!std::isfinite(T[i])) return fail(WUSHKV_ERR_INVALID_ARG, "T has a non-finite entry");
+  // A-operand order: chunk (h, mt, s), lane l, element e <- T~[h][32 mt + l%32][16 s + 8 (l/32) + e]
+  std::vector<uint16_t> swz(H * D * D);
+  for (size_t h = 0; h < H; ++h)
+    for (int mt = 0; mt < 4; ++mt)
+      for (int s = 0; s < 8; ++s)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e) {
+            const size_t r = 32 * mt + (l % 32), c = 16 * s + 8 * (l / 32) + e;
+            swz[((((h * 4 + mt) * 8 + s) * 64 + l) * 8) + e] = host_bf16(T[(h * D + r) * D + c]);
+          }
+  std::vector<float> gsum(H * 4 * D);
+  for (size_t h = 0; h < H; ++h)
+    for (int g = 0; g < 4; ++g)
+      for (size_t r = 0; r < D; ++r) {
+        double acc = 0.0;
+        for (int j = 32 * g; j < 32 * g + 32; ++j) acc += (double)host_bf16_value(host_bf16(T[(h * D + r) * D + j]));
+        gsum[(h * 4 + g) * D + r] = (float)acc;
+      }
+  auto* t = new (std::nothrow) wushkv_transform();
+  if (!t) return fail(WUSHKV_ERR_OOM, "host allocation failed");
+  t->n_heads = n_heads;
+  t->device = dev;
+  hipError_t e = hipMalloc(&t->d_swz, swz.size() * 2);
+  if (e != hipSuccess) { delete t; return fail(WUSHKV_ERR_OOM, "hipMalloc for the transform failed"); }
+  e = hipMalloc((void**)&t->d_gsum, gsum.size() * 4);
+  if (e != hipSuccess) { (void)hipFree(t->d_swz); delete t; return fail(WUSHKV_ERR_OOM, "hipMalloc for the transform failed"); }
+  e = hipMemcpy(t->d_swz, swz.data(), swz.size() * 2, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(t->d_gsum, gsum.data(), gsum.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(t->d_swz); (void)hipFree(t->d_gsum); delete t;
+    return hip_fail(e, "hipMemcpy (transform)");
+  }
+  *out = t;
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_transform_destroy(wushkv_transform* t) {
+  if (!t) return WUSHKV_OK;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(t->device);
+  (void)hipFree(t->d_swz);
+  (void)hipFree(t->d_gsum);
+  if (prev >= 0) (void)hipSetDevice(prev);
+  delete t;
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out) {
+  if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (max_pos < 1 || max_pos > WUSHKV_MAX_POS) return fail(WUSHKV_ERR_INVALID_ARG, "max_pos must be in [1, 2^24]");
+  float om[64];
+  wushkv_status st = wushkv_rope_frequencies(theta, om);
+  if (st) return st;
+  int dev;
+  st = current_device(&dev);
+  if (st) return st;
+  const int hi_rows = (max_pos + 1023) / 1024;
+  const size_t lo_n = (size_t)1024 * 64, hi_n = (size_t)hi_rows * 64;
+  // [lo | lo_t | hi | hi_t], each entry (cos, sin) as two doubles
+  std::vector<double> buf(2 * (2 * lo_n + 2 * hi_n));
+  double* lo = buf.data();
+  double* lo_t = lo + 2 * lo_n;
+  double* hi = lo_t + 2 * lo_n;
+  double* hi_t = hi + 2 * hi_n;
+  auto fill = [&](double* head, double* tail, size_t row, double mult, int i) {
+    const double ang = mult * (double)om[i];  // exact: < 2^24 times a 24-bit significand
+    const long double c = cosl((long double)ang), s = sinl((long double)ang);
+    const double ch = (double)c, sh = (double)s;
+    const size_t k = 2 * (row * 64 + i);
+    head[k] = ch;
+    head[k + 1] = sh;
+    tail[k] = (double)(c - (long double)ch);
+    tail[k + 1] = (double)(s - (long double)sh);
+  };
+  for (size_t r = 0; r < 1024; ++r)
+    for (int i = 0; i < 64; ++i) fill(lo, lo_t, r, (double)r, i);
+  for (size_t r = 0; r < (size_t)hi_rows; ++r)
+    for (int i = 0; i < 64; ++i) fill(hi, hi_t, r, (double)(r * 1024), i);
+  auto* rp = new (std::nothrow) wushkv_rope();
+  if (!rp) return fail(WUSHKV_ERR_OOM, "host allocation failed");
+  rp->theta = theta;
+  rp->max_pos = max_pos;
+  rp->device = dev;
+  rp->hi_rows = hi_rows;
+  hipError_t e = hipMalloc(&rp->d_block, buf.size() * sizeof(double));
+  if (e != hipSuccess) { delete rp; return fail(WUSHKV_ERR_OOM, "hipMalloc for the RoPE tables failed"); }
+  e = hipMemcpy(rp->d_block, buf.data(), buf.size() * sizeof(double), hipMemcpyHostToDevice);
+  if (e != hipSuccess) { (void)hipFree(rp->d_block); delete rp; return hip_fail(e, "hipMemcpy (RoPE tables)"); }
+  const double2* base = (const double2*)rp->d_block;
+  rp->d_lo = base;
+  rp->d_lo_t = base + lo_n;
+  rp->d_hi = base + 2 * lo_n;
+  rp->d_hi_t = base + 2 * lo_n + hi_n;
+  *out = rp;
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_rope_destroy(wushkv_rope* r) {
+  if (!r) return WUSHKV_OK;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(r->device);
+  (void)hipFree(r->d_block);
+  if (prev >= 0) (void)hipSetDevice(prev);
+  delete r;
+  return WUSHKV_OK;
+}
+
+static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_tokens, int n_heads,
+                                 int64_t token_stride, const int32_t* pos, const wushkv_rope* rope,
+                                 const wushkv_transform* T_k, int bits, const wushkv_quantizer* quantizer,
+                                 const wushkv_packed* out, float* y_out, void* stream) {
+  wushkv_status st = check_tensor(K, k_dtype, n_tokens, n_heads, token_stride);
+  if (st) return st;
+  if (!rope) return fail(WUSHKV_ERR_INVALID_ARG, "rope handle is NULL");
+  if (!T_k) return fail(WUSHKV_ERR_INVALID_ARG, "transform handle is NULL");
+  if (T_k->n_heads != n_heads) return fail(WUSHKV_ERR_INVALID_ARG, "transform has a different head count");
+  wushkv::QuantArgs qa{};
+  if (!y_out) {
+    if (bits < 2 || bits > 4) return fail(WUSHKV_ERR_INVALID_ARG, "bits must be 2, 3 or 4");
+    st = make_quant(quantizer, &qa);
+    if (st) return st;
+    st = check_packed(out, qa.kind, n_tokens, true);
+    if (st) return st;
+  } else if (!aligned(y_out, 16)) {
+    return fail(WUSHKV_ERR_ALIGNMENT, "y_out must be 16-byte aligned");
+  }
+  if (n_tokens == 0) return WUSHKV_OK;
+  if (!pos) return fail(WUSHKV_ERR_INVALID_ARG, "pos is NULL");
+  int dev;
+  st = current_device(&dev);
+  if (st) return st;
+  if (dev != T_k->device || dev != rope->device)
+    return fail(WUSHKV_ERR_INVALID_ARG, "handles belong to another device than the current one");
+  const int cus = wushkv::device_cu_count(dev);
+  const int64_t n_tiles = (n_tokens + 31) / 32;
+  const int hg = choose_hg(n_tiles, n_heads, cus, k_dtype == WUSHKV_F32 ? 2 : 4);
+  wushkv::KeysArgs a{};
+  a.K = K;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.stride = token_stride;
+  a.pos = pos;
+  a.max_pos = rope->max_pos;
+  a.T = T_k->d_swz;
+  a.rope_lo = rope->d_lo;
+  a.rope_hi = rope->d_hi;
+  a.rope_lo_t = rope->d_lo_t;
+  a.rope_hi_t = rope->d_hi_t;
+  if (out && !y_out) {
+    a.codes = (uint8_t*)out->codes;
+    a.scales = (uint16_t*)out->scales;
+    a.zeros = (uint16_t*)out->zeros;
+    a.slots = out->slots;
+    a.n_rows = out->n_rows;
+  }
+  a.q = qa;
+  a.y_out = y_out;
+  a.n_groups = n_heads / hg;
+  a.blocks_per_group = blocks_per_group(n_tiles, a.n_groups, hg, cus);
+  hipError_t e = wushkv::launch_keys(a, bits, k_dtype == WUSHKV_F32, hg, y_out != nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "key kernel launch");
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_quantize_keys(const void* K, wushkv_dtype k_dtype, int64_t n_tokens, int n_heads,
+                                   int64_t token_stride, const int32_t* pos, const wushkv_rope* rope,
+                                   const wushkv_transform* T_k, int bits, const wushkv_quantizer* quantizer,
+                                   const wushkv_packed* out, void* stream) {
+  return keys_common(K, k_dtype, n_tokens, n_heads, token_stride, pos, rope, T_k, bits, quantizer, out,
+                     nullptr, stream);
+}
+
+wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, int64_t n_tokens, int n_heads,
+                                          int64_t token_stride, const int32_t* pos, const wushkv_rope* rope,
+                                          const wushkv_transform* T_k, float* y_out, void* stream) {
+  if (!y_out) return fail(WUSHKV_ERR_INVALID_ARG, "y_out is NULL");
+  return keys_common(K, k_dtype, n_tokens, n_heads, token_stride, pos, rope, T_k, 2, nullptr, nullptr, y_out,
+                     stream);
+}
+
+wushkv_status wushkv_quantize_values(const void* V, wushkv_dtype v_dtype, int64_t n_tokens, int n_heads,
+                                     int64_t token_stride, int bits, const wushkv_quantizer* quantizer,
+                                     const wushkv_packed* out, void* stream) {
+  wushkv_status st = check_tensor(V, v_dtype, n_tokens, n_heads, token_stride);
+  if (st) return st;
+  if (bits < 2 || bits > 4) return fail(WUSHKV_ERR_INVALID_ARG, "bits must be 2, 3 or 4");
+  wushkv::QuantArgs qa{};
+  st = make_quant(quantizer, &qa);
+  if (st) return st;
+  st = check_packed(out, qa.kind, n_tokens, true);
+  if (st) return st;
+  if (n_tokens == 0) return WUSHKV_OK;
+  int dev;
+  st = current_device(&dev);
+  if (st) return st;
+  wushkv::ValuesArgs a{};
+  a.V = V;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.stride = token_stride;
+  a.codes = (uint8_t*)out->codes;
+  a.scales = (uint16_t*)out->scales;
+  a.zeros = (uint16_t*)out->zeros;
+  a.slots = out->slots;
+  a.n_rows = out->n_rows;
+  a.q = qa;
+  hipError_t e = wushkv::launch_values(a, bits, v_dtype == WUSHKV_F32, 4 * wushkv::device_cu_count(dev),
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "value kernel launch");
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n_heads, int bits,
+                                const wushkv_quantizer* quantizer, const wushkv_transform* T_k_inv, void* out,
+                                wushkv_dtype out_dtype, void* stream) {
+  if (bits < 2 || bits > 4) return fail(WUSHKV_ERR_INVALID_ARG, "bits must be 2, 3 or 4");
+  if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
+  if (n_tokens < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (out_dtype != WUSHKV_F32 && out_dtype != WUSHKV_BF16) return fail(WUSHKV_ERR_INVALID_ARG, "bad out_dtype");
+  wushkv::QuantArgs qa{};
+  wushkv_status st = make_quant(quantizer, &qa);
+  if (st) return st;
+  st = check_packed(in, qa.kind, n_tokens, false);
+  if (st) return st;
+  if (T_k_inv && T_k_inv->n_heads != n_heads) return fail(WUSHKV_ERR_INVALID_ARG, "T_k_inv has a different head count");
+  if (n_tokens == 0) return WUSHKV_OK;
+  if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned(out, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "out must be 16-byte aligned");
+  int dev;
+  st = current_device(&dev);
+  if (st) return st;
+  if (T_k_inv && T_k_inv->device != dev) return fail(WUSHKV_ERR_INVALID_ARG, "T_k_inv belongs to another device");
+  const int cus = wushkv::device_cu_count(dev);
+  wushkv::DequantArgs a{};
+  a.codes = (const uint8_t*)in->codes;
+  a.scales = (const uint16_t*)in->scales;
+  a.zeros = (const uint16_t*)in->zeros;
+  a.slots = in->slots;
+  a.n_rows = in->n_rows;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.kind = qa.kind;
+  a.out = out;
+  a.out_bf16 = out_dtype == WUSHKV_BF16;
+  int hg = 1;
+  if (T_k_inv) {
+    a.Tinv = T_k_inv->d_swz;
+    a.gsum = T_k_inv->d_gsum;
+    const int64_t n_tiles = (n_tokens + 31) / 32;
+    hg = choose_hg(n_tiles, n_heads, cus, 4);
+    a.n_groups = n_heads / hg;
+    a.blocks_per_group = blocks_per_group(n_tiles, a.n_groups, hg, cus);
+  }
+  hipError_t e = wushkv::launch_dequant(a, bits, hg, 4 * cus, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dequantize kernel launch");
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos, int64_t n, float* cs_out,
+                                        void* stream) {
+  if (!rope) return fail(WUSHKV_ERR_INVALID_ARG, "rope handle is NULL");
+  if (n < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return WUSHKV_OK;
+  if (!pos || !cs_out) return fail(WUSHKV_ERR_INVALID_ARG, "pos and cs_out must be set");
+  hipError_t e = wushkv::launch_rope_cos_sin(rope, pos, n, cs_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cos/sin kernel launch");
+  return WUSHKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal interfaces of libwushkv: handle layouts and kernel launch arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wushkv.h"
+
+// Key-transform handle: T~ = bf16(T) in the order the MFMA A operand is read.
+// Chunk (h, mt, s) holds, for lane l, the 8 bf16 values
+//   T~[h][32*mt + (l % 32)][16*s + 8*(l / 32) + e], e = 0..7,
+// so each wave reads one contiguous 1 KiB chunk per (row tile, k step).
+struct wushkv_transform {
+  int n_heads;
+  int device;
+  void* d_swz;     // bf16 [H][4][8][64][8]
+  float* d_gsum;   // [H][4][128]: sum over j in group g of T~[h][r][j], for affine reads
+};
+
+// RoPE handle: cos/sin split tables (see rope_cos_sin in device_common.h).
+struct wushkv_rope {
+  float theta;
+  int32_t max_pos;
+  int device;
+  int hi_rows;
+  void* d_block;          // one allocation holding the four tables
+  const double2* d_lo;    // [1024][64]
+  const double2* d_hi;    // [hi_rows][64]
+  const double2* d_lo_t;  // tails
+  const double2* d_hi_t;
+};
+
+namespace wushkv {
+
+struct QuantArgs {
+  int kind;       // 0 sym, 1 affine
+  float alpha;    // sym clip factor
+  float g_lo;     // affine: interpolation weight of the low percentile (order statistics 0, 1)
+  int lo_mode;    // 0: fma(g_lo, s1 - s0, s0); 1: s0
+  float g_hi;     // affine: weight of the high percentile (order statistics 30, 31)
+  int hi_mode;    // 0: fma(g_hi, s31 - s30, s30); 1: s30; 2: s31
+};
+
+struct KeysArgs {
+  const void* K;
+  int64_t n_tokens;
+  int n_heads;
+  int64_t stride;  // elements between tokens
+  const int32_t* pos;
+  int32_t max_pos;
+  const void* T;   // swizzled bf16
+  const double2* rope_lo;
+  const double2* rope_hi;
+  const double2* rope_lo_t;
+  const double2* rope_hi_t;
+  uint8_t* codes;
+  uint16_t* scales;
+  uint16_t* zeros;
+  const int64_t* slots;
+  int64_t n_rows;
+  QuantArgs q;
+  float* y_out;    // debug: fp32 transformed keys instead of codes
+  int n_groups;    // head groups (heads per group = the kernel's HG)
+  int blocks_per_group;
+};
+
+struct ValuesArgs {
+  const void* V;
+  int64_t n_tokens;
+  int n_heads;
+  int64_t stride;
+  uint8_t* codes;
+  uint16_t* scales;
+  uint16_t* zeros;
+  const int64_t* slots;
+  int64_t n_rows;
+  QuantArgs q;
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  const int64_t* slots;
+  int64_t n_rows;
+  int64_t n_tokens;
+  int n_heads;
+  int kind;
+  const void* Tinv;       // swizzled bf16 (NULL: no transform)
+  const float* gsum;      // [H][4][128] (affine with Tinv)
+  void* out;
+  int out_bf16;
+  int n_groups;
+  int blocks_per_group;
+};
+
+int device_cu_count(int device);
+
+hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_group, int y_out,
+                       hipStream_t stream);
+hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int n_blocks, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int n_blocks,
+                          hipStream_t stream);
+hipError_t launch_rope_cos_sin(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs,
+                               hipStream_t stream);
+
+}  // namespace wushkv

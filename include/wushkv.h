@@ -1,0 +1,180 @@
+/*
+ * libwushkv — WUSH-KV KV-cache write/read path on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, and where the pages about WUSH-KV (arXiv
+ * 2609.38121) state it:
+ *   - Keys are rotated with RoPE, then multiplied by their KV head's key
+ *     transform T_k, a general invertible 128x128 matrix (not only an
+ *     orthogonal one), online, because the transform is applied after RoPE
+ *     (ai4snews summary "WUSH-KV cuts 2-bit KV-cache perplexity ...", method and
+ *     deployment paragraphs; arXiv abstract; cere-bro post "WUSH-KV: 2-bit
+ *     KV-Cache Quantization with Data-Adaptive Transforms", Gaps: "adds a
+ *     matmul per decode step").
+ *   - Values need no online transform (it is folded into the weights) and are
+ *     only quantized (same sources; cere-bro flowchart "Folded into weights").
+ *   - Both go through a clipped b-bit scalar quantizer: an RMS-clipped
+ *     symmetric INT grid (the QuEST-style quantizer of the theory) or a
+ *     percentile-clipped affine grid (the OSCAR-style quantizer of the
+ *     end-to-end evaluation), per token, and are bit-packed into a paged /
+ *     slot-addressed cache (ai4snews deployment and end-to-end paragraphs).
+ *   - A read path unpacks and dequantizes, for keys optionally through T_k^-1.
+ *
+ * Numerical contract (what the GPU kernels reproduce):
+ *   RoPE     rotate-half on channel pairs (i, i+64); w_i = RN32(theta^(-2i/128));
+ *            c, s = cos, sin of the exact angle pos*w_i, each rounded once to
+ *            fp32; x_i = fma(k_i, c, -(k_{i+64} s)), x_{i+64} = fma(k_{i+64}, c, k_i s).
+ *   operands x~ = bf16(x) and T~ = bf16(T_k) (round-to-nearest-even);
+ *            y = T~ x~ accumulated in fp32 (MFMA).
+ *   sym      S = contiguous pairwise fp32 sum of y_j^2; rms = sqrt(S/128)
+ *            (correctly rounded); C = alpha*rms; step = RN16sat(2C/(2^b-1));
+ *            levels (q - (2^b-1)/2)*step.
+ *   affine   per 32-channel group: lo, hi = p_lo / p_hi percentiles by linear
+ *            interpolation between order statistics (IEEE totalOrder);
+ *            step = RN16sat((hi-lo)/(2^b-1)), zero = RN16sat(lo); levels zero + q*step.
+ *   codes    index of the nearest level in exact arithmetic, ties to the even
+ *            code; step 0 gives code 2^(b-1) (sym) or 0 (affine).
+ *   packing  code j of a 128-vector at bits [b*j, b*j+b) of an LSB-first bit
+ *            stream (stream bit 8k+t = bit t of byte k): 16*b bytes per record.
+ *
+ * Memory layout (all device memory, caller-owned; the library never allocates
+ * on the hot path):
+ *   K, V     [n_tokens][n_heads][128], element (n,h,c) at base + n*token_stride
+ *            + h*128 + c; bf16 or fp32; 16-byte aligned rows.
+ *   codes    [n_rows][n_heads][16*bits] bytes.
+ *   scales   fp16; sym: [n_rows][n_heads]; affine: [n_rows][n_heads][4].
+ *   zeros    fp16, affine only: [n_rows][n_heads][4].
+ *   row      slots[n] when slots != NULL, else n.
+ *
+ * Every call validates its arguments on the host before any launch and
+ * returns a status; nothing is thrown.  Launches are asynchronous on the
+ * given HIP stream (a hipStream_t passed as void*; NULL = the null stream).
+ * Non-finite inputs are not supported (results unspecified, memory-safe).
+ */
+#ifndef WUSHKV_H_
+#define WUSHKV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WUSHKV_HEAD_DIM 128
+#define WUSHKV_MAX_POS (1 << 24)
+
+typedef enum {
+  WUSHKV_OK = 0,
+  WUSHKV_ERR_INVALID_ARG = 1,  /* NULL pointer, bad size, bad enum value        */
+  WUSHKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. percentiles) */
+  WUSHKV_ERR_ALIGNMENT = 3,    /* pointer or stride not aligned as required    */
+  WUSHKV_ERR_NO_DEVICE = 4,    /* no HIP device visible                        */
+  WUSHKV_ERR_HIP = 5,          /* a HIP runtime call failed                    */
+  WUSHKV_ERR_OOM = 6           /* device allocation failed (handles only)      */
+} wushkv_status;
+
+typedef enum { WUSHKV_F32 = 0, WUSHKV_BF16 = 1 } wushkv_dtype;
+
+typedef enum {
+  WUSHKV_Q_SYM_RMS = 0,    /* symmetric grid, clip = clip_alpha * RMS over the 128-vector */
+  WUSHKV_Q_AFFINE_PCT = 1  /* affine grid per 32-channel group, percentile clip          */
+} wushkv_qkind;
+
+/* Scalar quantizer description.
+ *   WUSHKV_Q_SYM_RMS:    group must be 128; clip_alpha > 0 (2.0 in the workloads).
+ *   WUSHKV_Q_AFFINE_PCT: group must be 32; 0 <= p_lo <= p_hi <= 100.  The GPU
+ *     kernels select the two extreme order statistics at each end, so they need
+ *     p_lo < 100/31 and p_hi >= 3000/31 (the 1st/99th percentiles qualify);
+ *     other percentiles return WUSHKV_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t kind;       /* wushkv_qkind */
+  float clip_alpha;
+  int32_t group;
+  float p_lo, p_hi;
+} wushkv_quantizer;
+
+/* Packed cache view (device pointers, caller-owned).
+ *   codes:  [n_rows][n_heads][16*bits] bytes, 16-byte aligned.
+ *   scales: fp16 bits, 2-byte aligned (8-byte aligned for affine).
+ *   zeros:  fp16 bits for affine, NULL for symmetric.
+ *   slots:  int64 row per token, or NULL (row = token index).  Rows outside
+ *           [0, n_rows) are skipped by writers and read as zero-filled by the
+ *           reader; callers must not rely on that.
+ *   n_rows: capacity of the cache in rows. */
+typedef struct {
+  void* codes;
+  void* scales;
+  void* zeros;
+  const int64_t* slots;
+  int64_t n_rows;
+} wushkv_packed;
+
+typedef struct wushkv_transform wushkv_transform; /* opaque, library-owned */
+typedef struct wushkv_rope wushkv_rope;           /* opaque, library-owned */
+
+/* Key transform handle: rounds T (host, fp32, [n_heads][128][128] row-major,
+ * y = T x) to bf16 once and stores it on the current device in the MFMA
+ * operand order the kernels read.  The same call prepares T_k^-1 for reads.
+ * Allocates device memory (not a hot-path call). */
+wushkv_status wushkv_transform_create(const float* T_host, int n_heads, wushkv_transform** out);
+wushkv_status wushkv_transform_destroy(wushkv_transform* t);
+
+/* RoPE handle for base theta and positions [0, max_pos), max_pos <= 2^24.
+ * Builds cos/sin split tables (fp64 with extended-precision tails) on the
+ * current device.  Allocates device memory (not a hot-path call). */
+wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out);
+wushkv_status wushkv_rope_destroy(wushkv_rope* r);
+
+/* Host-only: the 64 RoPE frequencies w_i = RN32(theta^(-2i/128)) the library
+ * uses.  Touches no device. */
+wushkv_status wushkv_rope_frequencies(float theta, float* omega_out /* [64] */);
+
+/* Keys: RoPE -> bf16 -> T_k -> quantize -> pack into `out`.
+ *   K: device, bf16 or fp32, layout above; token_stride in elements (>= n_heads*128,
+ *      a multiple of 8 for bf16 and 4 for fp32).
+ *   pos: device int32 [n_tokens]; positions are clamped to [0, max_pos).
+ *   T_k: handle with n_heads heads; rope: handle for theta.
+ *   bits: 2, 3 or 4.  n_tokens == 0 is a no-op. */
+wushkv_status wushkv_quantize_keys(const void* K, wushkv_dtype k_dtype, int64_t n_tokens,
+                                   int n_heads, int64_t token_stride, const int32_t* pos,
+                                   const wushkv_rope* rope, const wushkv_transform* T_k, int bits,
+                                   const wushkv_quantizer* quantizer, const wushkv_packed* out,
+                                   void* stream);
+
+/* Values: quantize -> pack (no RoPE, no transform).  Same layouts as keys. */
+wushkv_status wushkv_quantize_values(const void* V, wushkv_dtype v_dtype, int64_t n_tokens,
+                                     int n_heads, int64_t token_stride, int bits,
+                                     const wushkv_quantizer* quantizer, const wushkv_packed* out,
+                                     void* stream);
+
+/* Read path: rows in->slots[n] (or n) for n < n_tokens are unpacked and
+ * dequantized into out[n_tokens][n_heads][128] (fp32 or bf16, contiguous,
+ * 16-byte aligned).  T_k_inv: NULL for values (or for keys kept in the
+ * transformed basis); otherwise a transform handle holding T_k^-1, applied as
+ * k^ = T~inv y^ with bf16 T~inv and fp32 accumulation. */
+wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n_heads, int bits,
+                                const wushkv_quantizer* quantizer,
+                                const wushkv_transform* T_k_inv, void* out,
+                                wushkv_dtype out_dtype, void* stream);
+
+/* Test support: the fp32 transformed keys y = T~ bf16(RoPE(K)) as the key
+ * kernel computes them, written to y_out [n_tokens][n_heads][128] (device). */
+wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, int64_t n_tokens,
+                                          int n_heads, int64_t token_stride, const int32_t* pos,
+                                          const wushkv_rope* rope, const wushkv_transform* T_k,
+                                          float* y_out, void* stream);
+
+/* Test support: the (cos, sin) pairs the key kernel uses, cs_out[n][64][2]
+ * fp32 (device), for device positions pos[n]. */
+wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
+                                        int64_t n, float* cs_out, void* stream);
+
+const char* wushkv_status_string(wushkv_status s);
+/* Detail message of the last failed call on this thread ("" if none). */
+const char* wushkv_last_error(void);
+int wushkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WUSHKV_H_ */

@@ -1,0 +1,446 @@
+"""GPU parity: libwushkv (through the C ABI) against the CPU oracle on the same
+seeded inputs.
+
+Bars (the numerical contract of the write/read path):
+  * cos/sin, RoPE operands, the quantizer fed a given fp32 tensor, packing,
+    values end to end, plain dequantization: bit-exact;
+  * transform y = T~ bf16(RoPE(k)): max |y_gpu - y_ref| <= 1e-5 * max |y_ref| per
+    128-vector (fp32 accumulation on MFMA against an fp64 sum);
+  * keys end to end: codes may differ only where the GPU's and the oracle's y
+    fall on different sides of a decision midpoint, or where the step / zero
+    crosses an fp16 rounding boundary; mismatches <= 1e-5 of elements;
+  * dequantization through T_k^-1: within 1e-5 * max |k^_ref| per vector.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TRANSFORM_TOL = 1e-5
+MISMATCH_RATE = 1e-5
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env(oracle_mod, synth_mod):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import bit_kv_cache_rope_amd as bk
+    bk.library()
+    os.environ.setdefault("WUSHKV_ORACLE_THREADS", "all")
+    return dict(torch=torch, bk=bk, oracle=oracle_mod, synth=synth_mod)
+
+
+def to_dev(env, a):
+    torch = env["torch"]
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host_u16(t):
+    return t.detach().cpu().view(dtype=__import__("torch").int16).numpy().view(np.uint16)
+
+
+def oracle_q(env, q):
+    o = env["oracle"]
+    return o.sym(q.clip_alpha) if q.kind == 0 else o.affine(q.p_lo, q.p_hi)
+
+
+def run_keys(env, K, pos, T, bits, q, theta=1e6, max_pos=1 << 17, slots=None, rows=None):
+    bk = env["bk"]
+    torch = env["torch"]
+    N, H = K.shape[0], K.shape[1]
+    rows = rows if rows is not None else N
+    rope = bk.Rope(theta, max_pos)
+    tk = bk.Transform(T)
+    out = bk.alloc_packed(rows, H, bits, q)
+    if slots is not None:
+        out = out.with_slots(to_dev(env, slots))
+    bk.wushkv_quantize_keys(to_dev(env, K), to_dev(env, pos), rope, tk, bits, q, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_values(env, V, bits, q, slots=None, rows=None):
+    bk = env["bk"]
+    N, H = V.shape[0], V.shape[1]
+    rows = rows if rows is not None else N
+    out = bk.alloc_packed(rows, H, bits, q)
+    if slots is not None:
+        out = out.with_slots(to_dev(env, slots))
+    bk.wushkv_quantize_values(to_dev(env, V), bits, q, out)
+    env["torch"].cuda.synchronize()
+    return out
+
+
+def packed_host(p):
+    return dict(codes=p.codes.cpu().numpy(), scales=host_u16(p.scales),
+                zeros=None if p.zeros is None else host_u16(p.zeros))
+
+
+def assert_same_packed(g, r, what):
+    for k in ("codes", "scales", "zeros"):
+        if r[k] is None:
+            continue
+        bad = np.argwhere(g[k] != r[k])
+        assert bad.size == 0, f"{what}: {k} differ at {bad[:5].tolist()} (total {len(bad)})"
+
+
+def f16(bits_u16):
+    return bits_u16.view(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------------- cos / sin
+
+def test_cos_sin_exhaustive(env):
+    bk, torch, o = env["bk"], env["torch"], env["oracle"]
+    n = 1 << 17
+    say(f"cos/sin exhaustive theta=1e6 pos < {n}")
+    rope = bk.Rope(1e6, n)
+    pos = np.arange(n, dtype=np.int32)
+    cs = bk.wushkv_debug_rope_cos_sin(rope, to_dev(env, pos)).cpu().numpy()
+    ref = o.cos_sin(1e6, pos)
+    bad = np.argwhere(cs.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, f"cos/sin differ at {bad[:5].tolist()} ({len(bad)})"
+    say("cos/sin sampled theta=1e6 pos < 2^24 and theta=1e4")
+    rng = np.random.default_rng(7)
+    for theta, mp in ((1e6, 1 << 24), (1e4, 1 << 20)):
+        rope = bk.Rope(theta, mp)
+        pos = np.concatenate([[0, mp - 1], rng.integers(0, mp, 40000)]).astype(np.int32)
+        cs = bk.wushkv_debug_rope_cos_sin(rope, to_dev(env, pos)).cpu().numpy()
+        ref = o.cos_sin(theta, pos)
+        assert np.array_equal(cs.view(np.uint32), ref.view(np.uint32)), theta
+
+
+# ---------------------------------------------------------------------------------- transform
+
+def _y_gpu(env, K, pos, T, theta=1e6):
+    bk = env["bk"]
+    rope = bk.Rope(theta, 1 << 17)
+    tk = bk.Transform(T)
+    y = bk.wushkv_debug_rope_transform(to_dev(env, K), to_dev(env, pos), rope, tk)
+    env["torch"].cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _y_ref(env, K, pos, T, theta=1e6):
+    return env["oracle"].quantize_keys(K, pos, T, theta, 2, env["oracle"].sym(), want_y=True)["y"]
+
+
+@pytest.mark.parametrize("name,n", [("tiny", 256), ("qwen3_8b_prefill", 4096), ("qwen3_8b_prefill", 1000),
+                                    ("affine_pct", 33)])
+def test_transform_within_tolerance(env, name, n):
+    s = env["synth"]
+    w = s.WORKLOADS[name]
+    say(f"transform {name} n={n}")
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, _ = s.transform(w, 0)
+    yg, yr = _y_gpu(env, K, pos, T), _y_ref(env, K, pos, T)
+    err = np.abs(yg - yr).max(axis=2)
+    ref = np.abs(yr).max(axis=2)
+    rel = err / np.maximum(ref, 1e-30)
+    say(f"  max rel err {rel.max():.3e}")
+    assert np.all(err <= TRANSFORM_TOL * ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_transform_exact_special_cases(env, dtype):
+    """Identity, permutation and signed powers of two are exact in fp32, so the
+    GPU's y must equal the oracle's bit for bit -- which also pins RoPE and the
+    bf16 operand rounding exactly."""
+    s = env["synth"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    n = 2048
+    K = s.kv(w, 0, "K", 5000, n, dtype=dtype)
+    pos = np.random.default_rng(3).integers(0, 1 << 17, n).astype(np.int32)
+    rng = np.random.default_rng(11)
+    H = K.shape[1]
+    Ts = {"identity": np.stack([np.eye(128, dtype=np.float32)] * H)}
+    P = np.zeros((H, 128, 128), np.float32)
+    for h in range(H):
+        P[h, np.arange(128), rng.permutation(128)] = 1.0
+    Ts["permutation"] = P
+    Ts["diag"] = np.stack([np.diag((2.0 ** rng.integers(-3, 4, 128) * rng.choice([-1, 1], 128)).astype(np.float32))
+                           for _ in range(H)])
+    for tn, T in Ts.items():
+        say(f"exact transform {tn} {dtype}")
+        yg, yr = _y_gpu(env, K, pos, T), _y_ref(env, K, pos, T)
+        bad = np.argwhere(yg.view(np.uint32) != yr.view(np.uint32))
+        assert bad.size == 0, f"{tn}: differ at {bad[:5].tolist()} ({len(bad)})"
+
+
+# ---------------------------------------------------------------------------------- quantizer + packing
+
+QUANTS = [("sym", 2), ("sym", 3), ("sym", 4), ("affine", 2), ("affine", 3), ("affine", 4)]
+
+
+def _bkq(env, kind):
+    return env["bk"].sym(2.0) if kind == "sym" else env["bk"].affine(1.0, 99.0)
+
+
+@pytest.mark.parametrize("kind,bits", QUANTS)
+def test_quantizer_bit_exact_on_same_fp32_tensor(env, kind, bits):
+    """Both sides quantize the oracle's fp32 transformed keys."""
+    s, o = env["synth"], env["oracle"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    n = 3000
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, _ = s.transform(w, 0)
+    y = _y_ref(env, K, pos, T)
+    q = _bkq(env, kind)
+    say(f"quantizer on oracle y: {kind} {bits}-bit n={n}")
+    g = packed_host(run_values(env, y, bits, q))
+    r = o.quantize_values(y, bits, oracle_q(env, q))
+    assert_same_packed(g, r, f"{kind}{bits}")
+
+
+@pytest.mark.parametrize("name,n,kind,bits", [
+    ("tiny", 256, "sym", 2), ("qwen3_8b_prefill", 32768, "sym", 2), ("qwen3_8b_prefill", 777, "sym", 3),
+    ("qwen3_32b_full", 8192, "sym", 3), ("qwen3_32b_full", 8192, "sym", 4), ("affine_pct", 8192, "affine", 2),
+    ("affine_pct", 1001, "affine", 3), ("affine_pct", 513, "affine", 4), ("decode_append", 64, "sym", 2)])
+def test_values_bit_exact(env, name, n, kind, bits):
+    s, o = env["synth"], env["oracle"]
+    w = s.WORKLOADS[name]
+    V = s.kv(w, 0, "V", 0, n)
+    q = _bkq(env, kind)
+    say(f"values {name} n={n} {kind} {bits}-bit")
+    g = packed_host(run_values(env, V, bits, q))
+    r = o.quantize_values(V, bits, oracle_q(env, q))
+    assert_same_packed(g, r, f"values {name}")
+
+
+def test_values_strided_and_slots(env):
+    """A token stride larger than H*128 (a slice of a fused tensor) and slot-addressed rows."""
+    s, o, torch, bk = env["synth"], env["oracle"], env["torch"], env["bk"]
+    w = s.WORKLOADS["decode_append"]
+    V = s.kv(w, 0, "V")
+    slots = s.slots(w)
+    rows = int(slots.max()) + 1
+    q = bk.sym(2.0)
+    say("values strided + slots")
+    big = torch.zeros((V.shape[0], 3, 8, 128), dtype=torch.bfloat16, device="cuda")
+    big[:, 1] = to_dev(env, V)
+    view = big[:, 1]
+    out = bk.alloc_packed(rows, 8, 2, q).with_slots(to_dev(env, slots))
+    bk.wushkv_quantize_values(view, 2, q, out)
+    torch.cuda.synchronize()
+    r = o.quantize_values(V, 2, oracle_q(env, q))
+    sl = torch.from_numpy(slots).cuda()
+    assert np.array_equal(out.codes[sl].cpu().numpy(), r["codes"])
+    assert np.array_equal(host_u16(out.scales[sl]), r["scales"])
+    mask = torch.ones(rows, dtype=torch.bool, device="cuda")
+    mask[sl] = False
+    assert int(out.codes[mask].count_nonzero()) == 0
+
+
+# ---------------------------------------------------------------------------------- keys end to end
+
+def fp16_boundary_dist(x):
+    """Relative distance of x (fp64) to the nearest fp16 rounding midpoint."""
+    x = np.abs(np.asarray(x, np.float64))
+    h = x.astype(np.float16).astype(np.float64)
+    up = np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(h.astype(np.float16), np.float16(0)).astype(np.float64)
+    mids = np.stack([(h + up) / 2, (h + dn) / 2])
+    return np.min(np.abs(mids - x), axis=0) / np.maximum(x, 1e-30)
+
+
+def unpack_codes(codes, bits):
+    """[..., 16*bits] LSB-first records -> [..., 128] codes (numpy.unpackbits)."""
+    b = np.unpackbits(codes, axis=-1, bitorder="little").reshape(codes.shape[:-1] + (128, bits))
+    return (b.astype(np.uint8) << np.arange(bits, dtype=np.uint8)).sum(axis=-1).astype(np.uint8)
+
+
+def account_keys(env, K, pos, T, bits, q, what):
+    """Compare GPU keys with the oracle and attribute every mismatch."""
+    o = env["oracle"]
+    N, H = K.shape[0], K.shape[1]
+    g = packed_host(run_keys(env, K, pos, T, bits, q))
+    r = o.quantize_keys(K, pos, T, 1e6, bits, oracle_q(env, q), want_y=True)
+    yr = r["y"].astype(np.float64)
+    yg = _y_gpu(env, K, pos, T).astype(np.float64)
+    gq, rq = unpack_codes(g["codes"], bits), unpack_codes(r["codes"], bits)
+    mism = gq != rq
+    L = 1 << bits
+    unexplained = 0
+    if q.kind == 0:
+        sc_diff = g["scales"] != r["scales"]
+        # a differing step must come from an fp16 rounding boundary of 2*alpha*rms/(L-1)
+        exact = 2 * q.clip_alpha * np.sqrt((yr ** 2).mean(axis=2)) / (L - 1)
+        near = fp16_boundary_dist(exact) <= 1e-6
+        assert np.all(near[sc_diff]), f"{what}: step differs away from an fp16 boundary"
+        d = f16(r["scales"])[..., None]
+        same = ~sc_diff[..., None] & mism
+        # with equal steps, a code may only differ if a midpoint lies between y_gpu and y_ref
+        for n, h, j in np.argwhere(same):
+            dd = d[n, h, 0]
+            mids = (np.arange(L - 1) + 1 - L // 2) * dd
+            lo, hi = sorted((yg[n, h, j], yr[n, h, j]))
+            if not np.any((mids >= lo) & (mids <= hi)):
+                unexplained += 1
+    else:
+        gs = g["scales"] != r["scales"]
+        gz = g["zeros"] != r["zeros"]
+        diff = gs | gz
+        same = np.repeat(~diff, 32, axis=2) & mism
+        s_, z_ = f16(r["scales"]), f16(r["zeros"])
+        for n, h, j in np.argwhere(same):
+            gi = j // 32
+            mids = z_[n, h, gi] + (np.arange(L - 1) + 0.5) * s_[n, h, gi]
+            lo, hi = sorted((yg[n, h, j], yr[n, h, j]))
+            if not np.any((mids >= lo) & (mids <= hi)):
+                unexplained += 1
+        sc_diff = diff
+    rate = mism.mean()
+    say(f"  {what}: code mismatches {int(mism.sum())}/{mism.size} (rate {rate:.2e}), "
+        f"scale diffs {int(sc_diff.sum())}, unexplained {unexplained}")
+    assert unexplained == 0
+    return int(mism.sum()), mism.size
+
+
+@pytest.mark.parametrize("name,n,kind,bits", [
+    ("tiny", 256, "sym", 2), ("qwen3_8b_prefill", 32768, "sym", 2), ("qwen3_32b_full", 8192, "sym", 3),
+    ("qwen3_32b_full", 8192, "sym", 4), ("affine_pct", 16384, "affine", 2), ("affine_pct", 999, "affine", 3)])
+def test_keys_end_to_end(env, name, n, kind, bits):
+    s = env["synth"]
+    w = s.WORKLOADS[name]
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, _ = s.transform(w, 0)
+    say(f"keys {name} n={n} {kind} {bits}-bit")
+    m, tot = account_keys(env, K, pos, T, bits, _bkq(env, kind), f"keys {name}")
+    if tot >= 1_000_000:
+        assert m <= MISMATCH_RATE * tot
+
+
+def test_keys_identity_equals_values_of_rope(env):
+    """With T = I the key path reduces to the plain quantizer on bf16(RoPE(K)) -- bit-exact."""
+    s, o = env["synth"], env["oracle"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    n = 4096
+    K = s.kv(w, 0, "K", 100, n)
+    pos = s.positions(w, 100, n)
+    eye = np.stack([np.eye(128, dtype=np.float32)] * 8)
+    for kind, bits in (("sym", 2), ("affine", 2), ("sym", 4)):
+        q = _bkq(env, kind)
+        say(f"keys identity {kind} {bits}")
+        g = packed_host(run_keys(env, K, pos, eye, bits, q))
+        r = o.quantize_keys(K, pos, eye, 1e6, bits, oracle_q(env, q))
+        assert_same_packed(g, r, "identity keys")
+
+
+def test_decode_append_slots(env):
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["decode_append"]
+    slots = s.slots(w)
+    rows = 64 * 32768
+    pos = s.positions(w)
+    q = bk.sym(2.0)
+    for layer in (0, 17, 35):
+        say(f"decode append layer {layer}")
+        K = s.kv(w, layer, "K")
+        V = s.kv(w, layer, "V")
+        T, _ = s.transform(w, layer)
+        pk = run_keys(env, K, pos, T, 2, q, slots=slots, rows=rows)
+        pv = run_values(env, V, 2, q, slots=slots, rows=rows)
+        sl = torch.from_numpy(slots).cuda()
+        rk = o.quantize_keys(K, pos, T, 1e6, 2, o.sym(), want_y=True)
+        rv = o.quantize_values(V, 2, o.sym())
+        assert np.array_equal(pv.codes[sl].cpu().numpy(), rv["codes"])
+        gk = pk.codes[sl].cpu().numpy()
+        frac = (gk != rk["codes"]).mean()
+        say(f"  key record bytes differing: {frac:.2e}")
+        assert frac <= 1e-3  # a flipped code changes one byte of a 32-byte record
+        assert int(pk.codes.count_nonzero()) <= 64 * 8 * 32
+
+
+# ---------------------------------------------------------------------------------- read path
+
+@pytest.mark.parametrize("kind,bits", QUANTS)
+def test_dequant_plain_bit_exact(env, kind, bits):
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["affine_pct" if kind == "affine" else "qwen3_32b_full"]
+    n = 2049
+    V = s.kv(w, 0, "V", 0, n)
+    q = _bkq(env, kind)
+    say(f"dequant plain {kind} {bits}")
+    p = run_values(env, V, bits, q)
+    h = packed_host(p)
+    ref = o.dequantize(h["codes"], h["scales"], h["zeros"], n, V.shape[1], bits, oracle_q(env, q))
+    out32 = bk.wushkv_dequantize(p, n, V.shape[1], bits, q, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(out32.view(np.uint32), ref.view(np.uint32))
+    out16 = bk.wushkv_dequantize(p, n, V.shape[1], bits, q, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(out16.view(np.uint32), o.round_bf16(ref).view(np.uint32))
+
+
+@pytest.mark.parametrize("kind,bits", QUANTS)
+def test_dequant_inverse_transform(env, kind, bits):
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["affine_pct" if kind == "affine" else "qwen3_32b_full"]
+    n = 1025
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, Ti = s.transform(w, 0)
+    q = _bkq(env, kind)
+    say(f"dequant through T^-1 {kind} {bits}")
+    p = run_keys(env, K, pos, T, bits, q)
+    h = packed_host(p)
+    ref = o.dequantize(h["codes"], h["scales"], h["zeros"], n, K.shape[1], bits, oracle_q(env, q), Tinv=Ti)
+    g = bk.wushkv_dequantize(p, n, K.shape[1], bits, q, T_k_inv=bk.Transform(Ti), out_dtype=torch.float32)
+    g = g.cpu().numpy()
+    err = np.abs(g - ref).max(axis=2)
+    mag = np.abs(ref).max(axis=2)
+    say(f"  max rel err {(err / np.maximum(mag, 1e-30)).max():.3e}")
+    assert np.all(err <= TRANSFORM_TOL * mag)
+    g16 = bk.wushkv_dequantize(p, n, K.shape[1], bits, q, T_k_inv=bk.Transform(Ti), out_dtype=torch.bfloat16)
+    g16 = g16.float().cpu().numpy()
+    assert np.all(np.abs(g16 - ref) <= np.abs(ref) * 2.0 ** -8 + TRANSFORM_TOL * mag[..., None])
+
+
+# ---------------------------------------------------------------------------------- edges
+
+@pytest.mark.parametrize("n", [0, 1, 31, 33, 65])
+def test_ragged_and_empty(env, n):
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    K = s.kv(w, 0, "K", 0, max(n, 1))[:n]
+    V = s.kv(w, 0, "V", 0, max(n, 1))[:n]
+    pos = s.positions(w, 0, max(n, 1))[:n]
+    T, _ = s.transform(w, 0)
+    q = bk.sym(2.0)
+    say(f"ragged n={n}")
+    pk = run_keys(env, K, pos, T, 2, q, rows=max(n, 1))
+    pv = run_values(env, V, 2, q, rows=max(n, 1))
+    if n == 0:
+        assert int(pk.codes.count_nonzero()) == 0 and int(pv.codes.count_nonzero()) == 0
+        return
+    rv = o.quantize_values(V, 2, o.sym())
+    assert np.array_equal(pv.codes.cpu().numpy(), rv["codes"])
+    rk = o.quantize_keys(K, pos, T, 1e6, 2, o.sym())
+    assert (pk.codes.cpu().numpy() != rk["codes"]).mean() <= 1e-3
+
+
+def test_deterministic(env):
+    s, bk = env["synth"], env["bk"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    n = 8192
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, _ = s.transform(w, 0)
+    say("determinism")
+    a = packed_host(run_keys(env, K, pos, T, 2, bk.sym()))
+    b = packed_host(run_keys(env, K, pos, T, 2, bk.sym()))
+    c = packed_host(run_keys(env, K, pos, T, 2, bk.sym()))
+    assert_same_packed(a, b, "run 2")
+    assert_same_packed(a, c, "run 3")
