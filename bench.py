@@ -1,0 +1,245 @@
+"""Benchmark: WUSH-KV cache write path (K+V into the 2-bit cache) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the Qwen3-8B-shaped single-layer prefill -- 32768 tokens x 8 KV
+heads x 128, bf16 keys and values (seeded synthetic: per-channel LogNormal(0,1)
+scales times Student-t(3) noise), per-head general invertible T_k, RoPE theta
+1e6, 2-bit RMS-clipped symmetric codes with one fp16 step per (token, head).
+
+One step = wushkv_quantize_keys (RoPE -> bf16 -> T_k on MFMA -> quantize ->
+pack) + wushkv_quantize_values (quantize -> pack) over the whole layer.  Inputs
+are resident in HBM before timing; the step cycles through enough input/output
+sets (> 2x the 256 MB MALL) that no set is re-read from the MALL.
+
+Prints one JSON line.  `value` is K+V tokens/s of the whole step; `roofline`
+is for the key kernel (algorithmic bytes per launch / its mean duration, from
+HIP events on the launch stream); `cpu_baseline` is the CPU oracle as it
+stands, single-threaded, on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "K+V tokens/s into 2-bit cache; achieved HBM GB/s and MFMA % of peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MALL_BYTES = 256 << 20
+D = 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "keys_qwen3_8b_prefill_traffic.md")
+KEY_KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_rope_amd", "csrc", f)
+                      for f in ("keys.hip", "device_common.h")]
+
+
+def key_bytes_per_token(H: int, bits: int) -> int:
+    """Algorithmic bytes of the key kernel per token: bf16 K in, int32 position,
+    packed codes and fp16 steps out."""
+    return H * D * 2 + 4 + H * 16 * bits + H * 2
+
+
+def value_bytes_per_token(H: int, bits: int) -> int:
+    return H * D * 2 + H * 16 * bits + H * 2
+
+
+def key_kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KEY_KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per key-kernel launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    m = re.search(r"^bench-traffic: (\{.*\})\s*$", open(TRAFFIC_FILE).read(), re.M)
+    if not m:
+        return None
+    t = json.loads(m.group(1))
+    if t.get("source_sha") != key_kernel_sha():
+        return None
+    return t
+
+
+def cpu_baseline(w, synth, seconds_hint: float = 20.0) -> dict:
+    import oracle
+    oracle.build()
+    n = w.tokens
+    K = synth.kv(w, 0, "K", 0, n)
+    V = synth.kv(w, 0, "V", 0, n)
+    pos = synth.positions(w, 0, n)
+    T, _ = synth.transform(w, 0)
+    t0 = time.perf_counter()
+    oracle.quantize_keys(K, pos, T, w.theta, 2, oracle.sym(w.clip_alpha), threads=1)
+    oracle.quantize_values(V, 2, oracle.sym(w.clip_alpha), threads=1)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full layer of the workload ({n} tokens x {w.heads} heads, K and V), "
+                      f"single-threaded, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the cache write path shards by KV head, token range or layer "
+              "with no exchange between GPUs, so this build times a single MI355X only.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import bit_kv_cache_rope_amd as bk
+
+    w = synth.WORKLOADS["qwen3_8b_prefill"]
+    N, H, bits = w.tokens, w.heads, 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = bk.sym(w.clip_alpha)
+
+    K = synth.kv(w, 0, "K")
+    V = synth.kv(w, 0, "V")
+    pos = synth.positions(w)
+    T, _ = synth.transform(w, 0)
+    rope = bk.Rope(w.theta, 1 << 17)
+    tk = bk.Transform(T)
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    set_bytes = N * (key_bytes_per_token(H, bits) + value_bytes_per_token(H, bits))
+    n_sets = max(2, -(-2 * MALL_BYTES // set_bytes) + 1)
+    Kd, Vd = dev_bf16(K), dev_bf16(V)
+    sets = []
+    for i in range(n_sets):
+        sets.append(dict(K=Kd.clone(), V=Vd.clone(), pos=torch.from_numpy(pos).to(dev),
+                         ko=bk.alloc_packed(N, H, bits, q, dev), vo=bk.alloc_packed(N, H, bits, q, dev)))
+    del Kd, Vd
+    stream = torch.cuda.current_stream()
+    # launches with their arguments marshalled once, so the host stays ahead of the GPU
+    calls = [(bk.prepare_quantize_keys(s["K"], s["pos"], rope, tk, bits, q, s["ko"], stream=stream),
+              bk.prepare_quantize_values(s["V"], bits, q, s["vo"], stream=stream)) for s in sets]
+
+    def step(i, evs=None):
+        kcall, vcall = calls[i % n_sets]
+        if evs is not None:
+            evs[0].record(stream)
+        kcall()
+        if evs is not None:
+            evs[1].record(stream)
+        vcall()
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    key_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    val_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- read path on the same data (keys back through T_k^-1, values plain), reported alongside
+    _, Ti = synth.transform(w, 0)
+    tki = bk.Transform(Ti)
+    outk = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+    outv = torch.empty_like(outk)
+    rcalls = [(bk.prepare_dequantize(s["ko"], N, H, bits, q, outk, T_k_inv=tki, stream=stream),
+               bk.prepare_dequantize(s["vo"], N, H, bits, q, outv, stream=stream)) for s in sets]
+    rd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
+    for i in range(25):
+        kc, vc = rcalls[i % n_sets]
+        e = rd[i - 5] if i >= 5 else None
+        if e:
+            e[0].record(stream)
+        kc()
+        if e:
+            e[1].record(stream)
+        vc()
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    rk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in rd]))
+    rv_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in rd]))
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = N * args.steps / elapsed
+    kb = N * key_bytes_per_token(H, bits) + H * D * D * 2  # + T~ read once per launch
+    vb = N * value_bytes_per_token(H, bits)
+    key_us = float(key_ms.mean()) * 1e3
+    val_us = float(val_ms.mean()) * 1e3
+    achieved = kb / (key_us * 1e-6) / 1e9
+    key_flops = 2.0 * N * H * D * D
+    traffic = read_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(
+                    (traffic["fetch_bytes_per_launch"] + traffic["write_bytes_per_launch"]) / 1e6, 3)}
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_prefill_layer", "tokens": N, "kv_heads": H, "head_dim": D,
+                   "bits": bits, "quantizer": "symmetric, clip 2.0 x RMS, fp16 step per token-head",
+                   "kv_dtype": "bf16", "rope_theta": w.theta, "buffer_sets": n_sets},
+        "roofline": roofline,
+        "kernels": {
+            "keys_us": round(key_us, 2), "values_us": round(val_us, 2),
+            "keys_algorithmic_bytes": kb, "values_algorithmic_bytes": vb,
+            "values_gbs": round(vb / (val_us * 1e-6) / 1e9, 1),
+            "step_gbs": round((kb + vb) / (ms_per_step * 1e-3) / 1e9, 1),
+            "keys_mfma_tflops": round(key_flops / (key_us * 1e-6) / 1e12, 2),
+            "keys_mfma_frac": round(key_flops / (key_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic_note": None if traffic is None else "roofline.traffic in MB per key launch (FETCH+WRITE)",
+        },
+        "read_path": {
+            "keys_through_T_inv_us": round(rk_ms * 1e3, 2), "values_us": round(rv_ms * 1e3, 2),
+            "tokens_per_s": round(N / ((rk_ms + rv_ms) * 1e-3), 1),
+            "keys_gbs": round((N * (H * 16 * bits + H * 2 + H * D * 2) + H * D * D * 2) / (rk_ms * 1e-3) / 1e9, 1),
+            "out_dtype": "bf16",
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle (single thread, one layer)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, synth)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

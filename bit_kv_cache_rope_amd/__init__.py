@@ -21,16 +21,25 @@ from ._lib import WushKVError, F32, BF16, Q_SYM_RMS, Q_AFFINE_PCT  # noqa: F401
 __all__ = [
     "WushKVError", "Quantizer", "sym", "affine", "Transform", "Rope", "PackedCache", "alloc_packed",
     "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize", "wushkv_debug_rope_transform",
-    "wushkv_debug_rope_cos_sin", "wushkv_rope_frequencies", "library",
+    "wushkv_debug_rope_cos_sin", "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
+    "prepare_quantize_values", "prepare_dequantize",
 ]
 
 
+_checked = False
+
+
 def library() -> ctypes.CDLL:
-    """The loaded libwushkv.so (raises ImportError if it is not built)."""
+    """The loaded libwushkv.so (raises ImportError if it is not built).  The
+    first call also checks that a single HIP runtime is mapped (the one torch
+    loaded)."""
+    global _checked
     L = _lib.load()
-    maps = _lib.hip_runtimes_mapped()
-    if len(maps) > 1:
-        raise RuntimeError(f"more than one HIP runtime mapped into this process: {maps}")
+    if not _checked:
+        maps = _lib.hip_runtimes_mapped()
+        if len(maps) > 1:
+            raise RuntimeError(f"more than one HIP runtime mapped into this process: {maps}")
+        _checked = True
     return L
 
 
@@ -229,6 +238,45 @@ def wushkv_debug_rope_cos_sin(rope: Rope, pos: torch.Tensor, stream=None) -> tor
     _lib.check(library().wushkv_debug_rope_cos_sin(rope.handle, ctypes.c_void_p(pos.data_ptr()), pos.numel(),
                                                    ctypes.c_void_p(cs.data_ptr()), _stream(stream)))
     return cs
+
+
+class PreparedCall:
+    """A libwushkv call with its arguments marshalled once; calling it launches
+    again with the same tensors and stream (for tight loops and benchmarks)."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st:
+            _lib.check(st)
+
+
+def prepare_quantize_keys(K, pos, rope: Rope, T_k: Transform, bits: int, quantizer: Quantizer,
+                          out: PackedCache, stream=None) -> PreparedCall:
+    dt, n, h, stride = _kv_args(K)
+    _check_device_tensor(pos, "pos", torch.int32)
+    q, p = quantizer.c(), out.c()
+    args = (ctypes.c_void_p(K.data_ptr()), dt, n, h, stride, ctypes.c_void_p(pos.data_ptr()), rope.handle,
+            T_k.handle, bits, ctypes.byref(q), ctypes.byref(p), _stream(stream))
+    return PreparedCall(library().wushkv_quantize_keys, args, (K, pos, rope, T_k, q, p, out))
+
+
+def prepare_quantize_values(V, bits: int, quantizer: Quantizer, out: PackedCache, stream=None) -> PreparedCall:
+    dt, n, h, stride = _kv_args(V)
+    q, p = quantizer.c(), out.c()
+    args = (ctypes.c_void_p(V.data_ptr()), dt, n, h, stride, bits, ctypes.byref(q), ctypes.byref(p),
+            _stream(stream))
+    return PreparedCall(library().wushkv_quantize_values, args, (V, q, p, out))
+
+
+def prepare_dequantize(packed: PackedCache, n_tokens: int, n_heads: int, bits: int, quantizer: Quantizer,
+                       out: torch.Tensor, T_k_inv: Transform | None = None, stream=None) -> PreparedCall:
+    q, p = quantizer.c(), packed.c()
+    args = (ctypes.byref(p), n_tokens, n_heads, bits, ctypes.byref(q), None if T_k_inv is None else T_k_inv.handle,
+            ctypes.c_void_p(out.data_ptr()), F32 if out.dtype == torch.float32 else BF16, _stream(stream))
+    return PreparedCall(library().wushkv_dequantize, args, (packed, q, p, out, T_k_inv))
 
 
 def wushkv_rope_frequencies(theta: float):

@@ -93,8 +93,8 @@ wushkv_status check_packed(const wushkv_packed* p, int kind, int64_t n_tokens, b
   if (!p->codes || !p->scales) return fail(WUSHKV_ERR_INVALID_ARG, "codes and scales must be set");
   if (kind == 1 && !p->zeros) return fail(WUSHKV_ERR_INVALID_ARG, "affine quantizer needs zeros");
   if (!aligned(p->codes, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "codes must be 16-byte aligned");
-  if (!aligned(p->scales, kind == 1 ? 8 : 2)) return fail(WUSHKV_ERR_ALIGNMENT, "scales misaligned");
-  if (kind == 1 && !aligned(p->zeros, 8)) return fail(WUSHKV_ERR_ALIGNMENT, "zeros must be 8-byte aligned");
+  if (!aligned(p->scales, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "scales must be 16-byte aligned");
+  if (kind == 1 && !aligned(p->zeros, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "zeros must be 16-byte aligned");
   if (p->n_rows < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_rows < 0");
   if (!p->slots && p->n_rows < n_tokens)
     return fail(WUSHKV_ERR_INVALID_ARG, writer ? "cache has fewer rows than tokens" : "cache has fewer rows than requested");
@@ -113,6 +113,16 @@ wushkv_status check_tensor(const void* X, wushkv_dtype dt, int64_t n_tokens, int
     if (!aligned(X, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "input tensor must be 16-byte aligned");
   }
   return WUSHKV_OK;
+}
+
+// Round-up multiplier for division by d (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, v / d == (umulhi(v, m) + v) >> l for v < 2^31.
+void div_magic(uint32_t d, uint32_t* m, uint32_t* l) {
+  uint32_t k = 0;
+  while ((1ull << k) < d) ++k;
+  *l = k;
+  *m = (uint32_t)(((1ull << 32) * ((1ull << k) - d)) / d + 1);
 }
 
 int choose_hg(int64_t n_tiles, int n_heads, int cus, int max_hg) {
@@ -247,27 +257,30 @@ wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out
   st = current_device(&dev);
   if (st) return st;
   const int hi_rows = (max_pos + 1023) / 1024;
-  const size_t lo_n = (size_t)1024 * 64, hi_n = (size_t)hi_rows * 64;
-  // [lo | lo_t | hi | hi_t], each entry (cos, sin) as two doubles
-  std::vector<double> buf(2 * (2 * lo_n + 2 * hi_n));
-  double* lo = buf.data();
-  double* lo_t = lo + 2 * lo_n;
-  double* hi = lo_t + 2 * lo_n;
-  double* hi_t = hi + 2 * hi_n;
-  auto fill = [&](double* head, double* tail, size_t row, double mult, int i) {
+  const size_t n0 = (size_t)32 * 64, n2 = (size_t)hi_rows * 64;
+  // [t0 | t1 | t2 | t0t | t1t | t2t], each entry (cos, sin) as two doubles
+  const size_t heads = 2 * n0 + n2;
+  std::vector<double> buf(4 * heads);
+  double* head = buf.data();
+  double* tail = head + 2 * heads;
+  // entry e of a table starting at entry offset `off`: angle = mult * w_i
+  auto fill = [&](size_t off, size_t row, double mult, int i) {
     const double ang = mult * (double)om[i];  // exact: < 2^24 times a 24-bit significand
     const long double c = cosl((long double)ang), s = sinl((long double)ang);
     const double ch = (double)c, sh = (double)s;
-    const size_t k = 2 * (row * 64 + i);
+    const size_t k = 2 * (off + row * 64 + i);
     head[k] = ch;
     head[k + 1] = sh;
     tail[k] = (double)(c - (long double)ch);
     tail[k + 1] = (double)(s - (long double)sh);
   };
-  for (size_t r = 0; r < 1024; ++r)
-    for (int i = 0; i < 64; ++i) fill(lo, lo_t, r, (double)r, i);
+  for (size_t r = 0; r < 32; ++r)
+    for (int i = 0; i < 64; ++i) {
+      fill(0, r, (double)r, i);
+      fill(n0, r, (double)(r * 32), i);
+    }
   for (size_t r = 0; r < (size_t)hi_rows; ++r)
-    for (int i = 0; i < 64; ++i) fill(hi, hi_t, r, (double)(r * 1024), i);
+    for (int i = 0; i < 64; ++i) fill(2 * n0, r, (double)(r * 1024), i);
   auto* rp = new (std::nothrow) wushkv_rope();
   if (!rp) return fail(WUSHKV_ERR_OOM, "host allocation failed");
   rp->theta = theta;
@@ -279,10 +292,12 @@ wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out
   e = hipMemcpy(rp->d_block, buf.data(), buf.size() * sizeof(double), hipMemcpyHostToDevice);
   if (e != hipSuccess) { (void)hipFree(rp->d_block); delete rp; return hip_fail(e, "hipMemcpy (RoPE tables)"); }
   const double2* base = (const double2*)rp->d_block;
-  rp->d_lo = base;
-  rp->d_lo_t = base + lo_n;
-  rp->d_hi = base + 2 * lo_n;
-  rp->d_hi_t = base + 2 * lo_n + hi_n;
+  rp->t0 = base;
+  rp->t1 = base + n0;
+  rp->t2 = base + 2 * n0;
+  rp->t0t = base + heads;
+  rp->t1t = base + heads + n0;
+  rp->t2t = base + heads + 2 * n0;
   *out = rp;
   return WUSHKV_OK;
 }
@@ -335,10 +350,12 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
   a.pos = pos;
   a.max_pos = rope->max_pos;
   a.T = T_k->d_swz;
-  a.rope_lo = rope->d_lo;
-  a.rope_hi = rope->d_hi;
-  a.rope_lo_t = rope->d_lo_t;
-  a.rope_hi_t = rope->d_hi_t;
+  a.t0 = rope->t0;
+  a.t1 = rope->t1;
+  a.t2 = rope->t2;
+  a.t0t = rope->t0t;
+  a.t1t = rope->t1t;
+  a.t2t = rope->t2t;
   if (out && !y_out) {
     a.codes = (uint8_t*)out->codes;
     a.scales = (uint16_t*)out->scales;
@@ -349,8 +366,7 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
   a.q = qa;
   a.y_out = y_out;
   a.n_groups = n_heads / hg;
-  a.blocks_per_group = blocks_per_group(n_tiles, a.n_groups, hg, cus);
-  hipError_t e = wushkv::launch_keys(a, bits, k_dtype == WUSHKV_F32, hg, y_out != nullptr, (hipStream_t)stream);
+  hipError_t e = wushkv::launch_keys(a, bits, k_dtype == WUSHKV_F32, hg, y_out != nullptr, cus, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "key kernel launch");
   return WUSHKV_OK;
 }
@@ -386,18 +402,21 @@ wushkv_status wushkv_quantize_values(const void* V, wushkv_dtype v_dtype, int64_
   int dev;
   st = current_device(&dev);
   if (st) return st;
+  if (n_tokens * n_heads >= (1LL << 31))
+    return fail(WUSHKV_ERR_UNSUPPORTED, "values need n_tokens * n_heads < 2^31");
   wushkv::ValuesArgs a{};
   a.V = V;
   a.n_tokens = n_tokens;
   a.n_heads = n_heads;
   a.stride = token_stride;
+  div_magic((uint32_t)n_heads, &a.div_m, &a.div_l);
   a.codes = (uint8_t*)out->codes;
   a.scales = (uint16_t*)out->scales;
   a.zeros = (uint16_t*)out->zeros;
   a.slots = out->slots;
   a.n_rows = out->n_rows;
   a.q = qa;
-  hipError_t e = wushkv::launch_values(a, bits, v_dtype == WUSHKV_F32, 4 * wushkv::device_cu_count(dev),
+  hipError_t e = wushkv::launch_values(a, bits, v_dtype == WUSHKV_F32, wushkv::device_cu_count(dev),
                                        (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "value kernel launch");
   return WUSHKV_OK;

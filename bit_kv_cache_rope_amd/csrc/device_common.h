@@ -81,6 +81,33 @@ __device__ __forceinline__ uint32_t sym_code(float y, float delta, float rdelta)
   }
 }
 
+// 2-bit symmetric code of y placed at bit `sh`, from per-vector thresholds.
+// With tp = delta and tz = 0 the three midpoint tests are A = [y > -delta],
+// B = [y >= 0], C = [y > delta] (ties as in the nearest-level rule) and the
+// code is A + B + C; since A >= B >= C its bits are bit1 = B and
+// bit0 = C | (A & !B).  A zero step uses tp = +inf, tz = -inf: code 2.
+__device__ __forceinline__ uint32_t sym2_bits(float y, float tp, float tz, int sh) {
+  const bool A = y > -tp, B = y >= tz, C = y > tp;
+  const bool b0 = C | (A & !B);
+  return (b0 ? (1u << sh) : 0u) | (B ? (2u << sh) : 0u);
+}
+
+// Sum over aligned groups of 2, 4, 8 and 16 lanes by DPP moves: after step k a
+// lane holds the sum of its 2^k-lane block, each step adding the two halves'
+// sums (commutative, so both halves hold the same value).  Equal to xor
+// butterflies with offsets 1, 2, 4, 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_sum16(float v) {
+  v = v + dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = v + dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = v + dpp_f32<0x141>(v);  // row_half_mirror
+  v = v + dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Affine grid z + q*s, q in [0, L).  The midpoints z + (k + 1/2) s are exact in
 // fp64 for fp16 z and s, so comparing the fp32 input against them in fp64 is exact.
 template <int BITS>
@@ -99,14 +126,19 @@ __device__ __forceinline__ uint32_t affine_code(float x, double z, double s) {
 // ---------------------------------------------------------------------------------------------
 // RoPE cos/sin of the exact angle pos * w_i, rounded once to fp32.
 //
-// pos = ph * 1024 + pl.  Tables (built on the host in extended precision):
-//   lo[pl][i]  = (cos, sin)(pl * w_i)            as fp64, tails in lo_t
-//   hi[ph][i]  = (cos, sin)(ph * 1024 * w_i)     as fp64, tails in hi_t
-// Fast path: angle addition in fp64 (absolute error below 2^-51).  If every
+// pos = p2 * 1024 + p1 * 32 + p0 with p0, p1 < 32.  Tables (built on the host in
+// extended precision, heads as fp64 with their tails in separate arrays):
+//   t0[p0][i] = (cos, sin)(p0 * w_i)          32 rows  (kept in LDS by the key kernel)
+//   t1[p1][i] = (cos, sin)(p1 * 32 * w_i)     32 rows  (kept in LDS by the key kernel)
+//   t2[p2][i] = (cos, sin)(p2 * 1024 * w_i)   ceil(max_pos / 1024) rows (global)
+// Fast path: two angle additions in fp64 (absolute error below 2^-50).  If every
 // value within 2^-49 of that estimate rounds to the same fp32, that float is
-// the answer; otherwise a slow path rounds a double-double evaluation from the
-// tables and their tails (error near 2^-100 plus the tables' own ~2^-64).
+// the answer; otherwise a slow path redoes both additions in double-double from
+// the heads and tails (error near 2^-100 plus the tables' own ~2^-64) and
+// rounds that.
 constexpr double kRopeFastErr = 0x1p-49;
+constexpr int kRopeLoRows = 32;
+constexpr int kRopeMidRows = 32;
 
 __device__ __forceinline__ void two_prod(double a, double b, double& p, double& e) {
   p = a * b;
@@ -126,12 +158,10 @@ __device__ __forceinline__ float float_next_up(float f) {
 }
 __device__ __forceinline__ float float_next_down(float f) { return -float_next_up(-f); }
 
-// Correctly rounds v = a1*b1 + sg*a2*b2 to fp32, where each factor is given as
-// an fp64 head plus tail (a1 + a1t, ...).  v is formed as a double-double
-// (vh + vl, error near 2^-100 absolute), RN32(vh) is taken, and the residual
-// (vh - f) + vl decides whether the neighbouring float is nearer.
-__device__ __noinline__ float rope_round_slow(double a1, double a1t, double b1, double b1t,
-                                              double a2, double a2t, double b2, double b2t, double sg) {
+// Double-double v = a1*b1 + sg*a2*b2 from head+tail factors (error ~2^-100 for
+// |factors| <= 1); sg is +1 or -1.
+__device__ __forceinline__ void dd_pair(double a1, double a1t, double b1, double b1t, double a2, double a2t,
+                                        double b2, double b2t, double sg, double& vh, double& vl) {
   double p1, e1, p2, e2;
   two_prod(a1, b1, p1, e1);
   two_prod(a2, b2, p2, e2);
@@ -139,55 +169,71 @@ __device__ __noinline__ float rope_round_slow(double a1, double a1t, double b1, 
   e2 *= sg;
   double t, e3;
   two_sum(p1, p2, t, e3);
-  double cross = (a1 * b1t + a1t * b1) + sg * (a2 * b2t + a2t * b2);
-  double rest = ((e1 + e2) + e3) + cross;
-  double vh, vl;
+  const double cross = (a1 * b1t + a1t * b1) + sg * (a2 * b2t + a2t * b2);
+  const double rest = ((e1 + e2) + e3) + cross;
   two_sum(t, rest, vh, vl);
+}
+
+// RN32 of the double-double vh + vl: RN32(vh), then the residual (vh - f) + vl
+// decides whether a neighbouring float is nearer (ties to even).
+__device__ __forceinline__ float dd_round_f32(double vh, double vl) {
   float f = (float)vh;
-  double d = (vh - (double)f) + vl;  // vh - f is exact (f is the fp32 rounding of vh)
+  const double d = (vh - (double)f) + vl;  // vh - f is exact
   if (d > 0.0) {
-    float u = float_next_up(f);
-    double halfgap = 0.5 * ((double)u - (double)f);
+    const float u = float_next_up(f);
+    const double halfgap = 0.5 * ((double)u - (double)f);
     if (d > halfgap || (d == halfgap && (__float_as_uint(u) & 1u) == 0u)) f = u;
   } else if (d < 0.0) {
-    float w = float_next_down(f);
-    double halfgap = 0.5 * ((double)f - (double)w);
+    const float w = float_next_down(f);
+    const double halfgap = 0.5 * ((double)f - (double)w);
     if (-d > halfgap || (-d == halfgap && (__float_as_uint(w) & 1u) == 0u)) f = w;
   }
   return f;
 }
 
-// (cos, sin)(pos * w_i) as fp32.
-__device__ __forceinline__ float2 rope_cos_sin(int pos, int i, const double2* __restrict__ lo,
-                                               const double2* __restrict__ hi,
-                                               const double2* __restrict__ lo_t,
-                                               const double2* __restrict__ hi_t) {
-  const int pl = pos & 1023, ph = pos >> 10;
-  const double2 B = lo[pl * kPairs + i];  // (cos, sin) of the low part
-  const double2 A = hi[ph * kPairs + i];  // (cos, sin) of the high part
-  // cos(A+B) = cA cB - sA sB ;  sin(A+B) = sA cB + cA sB
-  const double c = __builtin_fma(A.x, B.x, -(A.y * B.y));
-  const double s = __builtin_fma(A.y, B.x, A.x * B.y);
-  float fc, fs;
-  {
-    float f1 = (float)(c - kRopeFastErr), f2 = (float)(c + kRopeFastErr);
-    if (__builtin_expect(f1 == f2, 1)) {
-      fc = f1;
-    } else {
-      const double2 Bt = lo_t[pl * kPairs + i], At = hi_t[ph * kPairs + i];
-      fc = rope_round_slow(A.x, At.x, B.x, Bt.x, A.y, At.y, B.y, Bt.y, -1.0);
-    }
-  }
-  {
-    float f1 = (float)(s - kRopeFastErr), f2 = (float)(s + kRopeFastErr);
-    if (__builtin_expect(f1 == f2, 1)) {
-      fs = f1;
-    } else {
-      const double2 Bt = lo_t[pl * kPairs + i], At = hi_t[ph * kPairs + i];
-      fs = rope_round_slow(A.y, At.y, B.x, Bt.x, A.x, At.x, B.y, Bt.y, 1.0);
-    }
-  }
-  return make_float2(fc, fs);
+// Slow path: (cos, sin)(a + m + b) correctly rounded, from the three table
+// entries (head, tail) of the angle parts.
+__device__ __forceinline__ float2 rope_cos_sin_slow(double2 A, double2 At, double2 M, double2 Mt, double2 B,
+                                                 double2 Bt) {
+  double ch, cl, sh, sl;
+  dd_pair(A.x, At.x, M.x, Mt.x, A.y, At.y, M.y, Mt.y, -1.0, ch, cl);  // cos(a+m)
+  dd_pair(A.y, At.y, M.x, Mt.x, A.x, At.x, M.y, Mt.y, 1.0, sh, sl);   // sin(a+m)
+  double c2h, c2l, s2h, s2l;
+  dd_pair(ch, cl, B.x, Bt.x, sh, sl, B.y, Bt.y, -1.0, c2h, c2l);      // cos(a+m+b)
+  dd_pair(sh, sl, B.x, Bt.x, ch, cl, B.y, Bt.y, 1.0, s2h, s2l);       // sin(a+m+b)
+  return make_float2(dd_round_f32(c2h, c2l), dd_round_f32(s2h, s2l));
+}
+
+// Fast path from the three heads; `exact` is false when the slow path is needed.
+__device__ __forceinline__ float2 rope_cos_sin_fast(double2 A, double2 M, double2 B, bool& exact) {
+  const double c1 = __builtin_fma(A.x, M.x, -(A.y * M.y));
+  const double s1 = __builtin_fma(A.y, M.x, A.x * M.y);
+  const double c = __builtin_fma(c1, B.x, -(s1 * B.y));
+  const double s = __builtin_fma(s1, B.x, c1 * B.y);
+  const float fc1 = (float)(c - kRopeFastErr), fc2 = (float)(c + kRopeFastErr);
+  const float fs1 = (float)(s - kRopeFastErr), fs2 = (float)(s + kRopeFastErr);
+  exact = (fc1 == fc2) && (fs1 == fs2);
+  return make_float2(fc1, fs1);
+}
+
+struct RopeTables {
+  const double2* t0;    // [32][64]
+  const double2* t1;    // [32][64]
+  const double2* t2;    // [hi_rows][64]
+  const double2* t0t;   // tails
+  const double2* t1t;
+  const double2* t2t;
+};
+
+// (cos, sin)(pos * w_i) with every table read from global memory.
+__device__ __forceinline__ float2 rope_cos_sin(int pos, int i, const RopeTables& t) {
+  const int p0 = pos & 31, p1 = (pos >> 5) & 31, p2 = pos >> 10;
+  const double2 A = t.t2[p2 * kPairs + i], M = t.t1[p1 * kPairs + i], B = t.t0[p0 * kPairs + i];
+  bool exact;
+  float2 v = rope_cos_sin_fast(A, M, B, exact);
+  if (__builtin_expect(!exact, 0))
+    v = rope_cos_sin_slow(A, t.t2t[p2 * kPairs + i], M, t.t1t[p1 * kPairs + i], B, t.t0t[p0 * kPairs + i]);
+  return v;
 }
 
 }  // namespace wushkv

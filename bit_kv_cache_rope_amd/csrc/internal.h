@@ -23,11 +23,13 @@ struct wushkv_rope {
   int32_t max_pos;
   int device;
   int hi_rows;
-  void* d_block;          // one allocation holding the four tables
-  const double2* d_lo;    // [1024][64]
-  const double2* d_hi;    // [hi_rows][64]
-  const double2* d_lo_t;  // tails
-  const double2* d_hi_t;
+  void* d_block;          // one allocation holding the six tables
+  const double2* t0;      // [32][64]       (cos, sin)(p0 * w)
+  const double2* t1;      // [32][64]       (cos, sin)(p1 * 32 * w)
+  const double2* t2;      // [hi_rows][64]  (cos, sin)(p2 * 1024 * w)
+  const double2* t0t;     // tails of the three
+  const double2* t1t;
+  const double2* t2t;
 };
 
 namespace wushkv {
@@ -49,10 +51,12 @@ struct KeysArgs {
   const int32_t* pos;
   int32_t max_pos;
   const void* T;   // swizzled bf16
-  const double2* rope_lo;
-  const double2* rope_hi;
-  const double2* rope_lo_t;
-  const double2* rope_hi_t;
+  const double2* t0;
+  const double2* t1;
+  const double2* t2;
+  const double2* t0t;
+  const double2* t1t;
+  const double2* t2t;
   uint8_t* codes;
   uint16_t* scales;
   uint16_t* zeros;
@@ -61,7 +65,7 @@ struct KeysArgs {
   QuantArgs q;
   float* y_out;    // debug: fp32 transformed keys instead of codes
   int n_groups;    // head groups (heads per group = the kernel's HG)
-  int blocks_per_group;
+  int blocks_per_group;  // set by the launcher
 };
 
 struct ValuesArgs {
@@ -69,6 +73,8 @@ struct ValuesArgs {
   int64_t n_tokens;
   int n_heads;
   int64_t stride;
+  uint32_t div_m;  // v / n_heads == (umulhi(v, div_m) + v) >> div_l for v < 2^31
+  uint32_t div_l;
   uint8_t* codes;
   uint16_t* scales;
   uint16_t* zeros;
@@ -96,9 +102,11 @@ struct DequantArgs {
 
 int device_cu_count(int device);
 
-hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_group, int y_out,
+// Launchers size their persistent grids from the device's CU count and the
+// kernel's occupancy.
+hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_group, int y_out, int cus,
                        hipStream_t stream);
-hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int n_blocks, hipStream_t stream);
+hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int n_blocks,
                           hipStream_t stream);
 hipError_t launch_rope_cos_sin(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs,

@@ -6,12 +6,16 @@
 //
 // Layout: a 128-channel (token, head) vector is spread over 16 lanes, 8
 // contiguous channels per lane, so one wave load instruction covers 4 vectors
-// (1 KiB contiguous for a dense tensor).  Each wave handles 16 vectors per
-// iteration (4 loads per lane, the next iteration's loads in flight while the
-// current one is quantized).  Reductions are xor butterflies inside the 16-lane
-// group, which realise the contiguous pairwise tree exactly (offsets 1, 2, 4, 8
-// combine 16-, 32-, 64-, 128-channel halves).  Records are staged in LDS and
-// written back as 16-byte chunks.
+// (1 KiB contiguous for a dense tensor).  A wave handles 32 vectors per
+// iteration (8 loads of 16 bytes per lane); the next iteration's loads are in
+// flight while the current one is quantized.  Reductions are xor butterflies
+// inside the 16-lane group, which realise the contiguous pairwise tree exactly
+// (offsets 1, 2, 4, 8 combine 16-, 32-, 64-, 128-channel halves).  Records and
+// scales are staged in LDS and written back as 16-byte chunks.
+//
+// Loads are unconditional (indices are clamped to the last vector) and the
+// loop is unrolled by two over two register sets, so the only wait on the
+// prefetch is the explicit one before each iteration's stores.
 #include "device_common.h"
 #include "internal.h"
 
@@ -22,74 +26,80 @@ namespace wushkv {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kPerWave = 16;              // vectors per wave per iteration
+constexpr int kU = 8;                     // loads per lane per iteration
+constexpr int kPerWave = 4 * kU;          // vectors per wave per iteration
 constexpr int kVecs = kWaves * kPerWave;  // vectors per block per iteration
 
 template <bool F32IN>
 struct RawVals;
 template <>
 struct RawVals<false> {
-  uint4 v[4];
+  uint4 v[kU];
 };
 template <>
 struct RawVals<true> {
-  float4 v[8];
+  float4 v[2 * kU];
 };
 
-template <bool F32IN>
-__device__ __forceinline__ void load_vals(RawVals<F32IN>& r, const ValuesArgs& a, int64_t vbase, int l16) {
+// (token, head) of a flattened vector index v < 2^31: n = v / H by a multiply-high.
+__device__ __forceinline__ uint32_t div_heads(uint32_t v, const ValuesArgs& a) {
+  return (__umulhi(v, a.div_m) + v) >> a.div_l;
+}
+
+// Vector indices are 32-bit: a bf16 tensor with 2^31 vectors of 256 bytes
+// would not fit one GPU.
+template <bool F32IN, bool DENSE>
+__device__ __forceinline__ void load_vals(RawVals<F32IN>& r, int64_t* rows, const ValuesArgs& a,
+                                          uint32_t vbase, int l16, uint32_t last) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t v = vbase + 4 * u;
-    const int64_t nv = a.n_tokens * a.n_heads;
-    if (v < nv) {
-      const int64_t n = v / a.n_heads;
-      const int h = (int)(v - n * a.n_heads);
-      if constexpr (F32IN) {
-        const float* p = (const float*)a.V + n * a.stride + (int64_t)h * kD + 8 * l16;
-        r.v[2 * u] = *(const float4*)p;
-        r.v[2 * u + 1] = *(const float4*)(p + 4);
-      } else {
-        const uint16_t* p = (const uint16_t*)a.V + n * a.stride + (int64_t)h * kD + 8 * l16;
-        r.v[u] = *(const uint4*)p;
-      }
+  for (int u = 0; u < kU; ++u) {
+    const uint32_t v = min(vbase + 4u * u, last);
+    uint64_t off;  // element offset of the vector
+    if constexpr (DENSE) {
+      off = (uint64_t)v * kD;
     } else {
-      if constexpr (F32IN) {
-        r.v[2 * u] = {};
-        r.v[2 * u + 1] = {};
-      } else {
-        r.v[u] = {};
-      }
+      const uint32_t n = div_heads(v, a);
+      const uint32_t h = v - n * (uint32_t)a.n_heads;
+      off = (uint64_t)n * (uint64_t)a.stride + h * kD;
+      rows[u] = a.slots ? a.slots[n] : (int64_t)n;
+    }
+    if constexpr (F32IN) {
+      const float* p = (const float*)a.V + off + 8 * l16;
+      r.v[2 * u] = *(const float4*)p;
+      r.v[2 * u + 1] = *(const float4*)(p + 4);
+    } else {
+      r.v[u] = *(const uint4*)((const uint16_t*)a.V + off + 8 * l16);
     }
   }
 }
 
-template <int BITS, int QK, bool F32IN>
+template <int BITS, int QK, bool F32IN, bool DENSE>
 __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a) {
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
+  constexpr int NSC = QK ? 4 : 1;
   __shared__ __align__(16) uint8_t rec_lds[kVecs * REC];
+  __shared__ __align__(16) uint16_t sc_lds[kVecs * NSC];
+  __shared__ __align__(16) uint16_t zr_lds[QK ? kVecs * 4 : 8];
+  __shared__ int64_t row_lds[DENSE ? 1 : kVecs];
+  __shared__ float ss_lds[kWaves][kPerWave];          // sum of squares per vector
+  __shared__ __align__(16) float tp_lds[kWaves][4][kU];  // threshold per (sub, u)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane >> 4, l16 = lane & 15;
   const int64_t nv = a.n_tokens * a.n_heads;
+  const uint32_t last = (uint32_t)(nv - 1);
   const int64_t n_iter = (nv + kVecs - 1) / kVecs;
   int64_t it = blockIdx.x;
   if (it >= n_iter) return;
 
-  RawVals<F32IN> cur, nxt;
-  load_vals<F32IN>(cur, a, it * kVecs + wave * kPerWave + sub, l16);
-
-  while (true) {
+  auto step = [&](RawVals<F32IN>& cur, int64_t* rcur, RawVals<F32IN>& nxt, int64_t* rnxt)
+      __attribute__((always_inline)) -> bool {
     const int64_t it_next = it + gridDim.x;
     const bool has_next = it_next < n_iter;
-    if (has_next) load_vals<F32IN>(nxt, a, it_next * kVecs + wave * kPerWave + sub, l16);
+    if (has_next) load_vals<F32IN, DENSE>(nxt, rnxt, a, (uint32_t)(it_next * kVecs) + wave * kPerWave + sub, l16, last);
 
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int vloc = wave * kPerWave + 4 * u + sub;  // vector index within the block iteration
-      const int64_t v = it * kVecs + vloc;
-      float x[8];
+    auto unpack = [&](int u, float* x) __attribute__((always_inline)) {
       if constexpr (F32IN) {
         const float4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
         x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w; x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
@@ -100,31 +110,87 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
         x[4] = bf16lo_to_f32(p.z); x[5] = bf16hi_to_f32(p.z);
         x[6] = bf16lo_to_f32(p.w); x[7] = bf16hi_to_f32(p.w);
       }
-      uint32_t packed = 0;
-      uint16_t sc = 0, sh = 0, zh = 0;
-      if constexpr (QK == 0) {
-        float q[8];
+    };
+    auto store_codes = [&](int vloc, uint32_t packed) __attribute__((always_inline)) {
+      // this lane's 8 codes: BITS bytes at record offset BITS * l16
+      uint8_t* dst = &rec_lds[vloc * REC + BITS * l16];
+      if constexpr (BITS == 2) {
+        *(uint16_t*)dst = (uint16_t)packed;
+      } else if constexpr (BITS == 4) {
+        *(uint32_t*)dst = packed;
+      } else {
+        dst[0] = (uint8_t)packed;
+        dst[1] = (uint8_t)(packed >> 8);
+        dst[2] = (uint8_t)(packed >> 16);
+      }
+    };
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (l16 == 0) row_lds[wave * kPerWave + 4 * u + sub] = rcur[u];
+    }
+
+    if constexpr (QK == 0) {
+      // (1) sum of squares of each vector: in-lane pairwise over 8 channels, then
+      //     across the 16 lanes of the vector.
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        float x[8], q[8];
+        unpack(u, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = x[e] * x[e];
         float P = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-        P = P + __shfl_xor(P, 1);
-        P = P + __shfl_xor(P, 2);
-        P = P + __shfl_xor(P, 4);
-        P = P + __shfl_xor(P, 8);
+        P = dpp_sum16(P);
+        if (l16 == 0) ss_lds[wave][4 * u + sub] = P;
+      }
+      // (2) one lane per vector: step, fp16 scale and threshold
+      if (lane < kPerWave) {
+        const float P = ss_lds[wave][lane];
         const float ms = P * 0.0078125f;
         const float rms = __builtin_sqrtf(ms);
         const float C = a.q.alpha * rms;
         const float twoC = 2.0f * C;
         const float d32 = twoC / (float)(L - 1);
-        sc = f16_sat_bits(d32);
+        const uint16_t sc = f16_sat_bits(d32);
         const float delta = f16_bits_to_f32(sc);
-        const float rdelta = __builtin_amdgcn_rcpf(delta);
+        sc_lds[wave * kPerWave + lane] = sc;
+        // BITS == 2: the threshold tp (+inf for a zero step); otherwise the step
+        // itself (+inf for a zero step, whose reciprocal 0 then yields code L/2)
+        tp_lds[wave][lane & 3][lane >> 2] = delta == 0.0f ? __builtin_inff() : delta;
+      }
+      // (3) codes
+      float tp[kU];
+      {
+        const float4 t0 = *(const float4*)&tp_lds[wave][sub][0];
+        const float4 t1 = *(const float4*)&tp_lds[wave][sub][4];
+        tp[0] = t0.x; tp[1] = t0.y; tp[2] = t0.z; tp[3] = t0.w;
+        tp[4] = t1.x; tp[5] = t1.y; tp[6] = t1.z; tp[7] = t1.w;
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t c = delta == 0.0f ? (uint32_t)(L / 2) : sym_code<BITS>(x[e], delta, rdelta);
-          packed |= c << (BITS * e);
+      for (int u = 0; u < kU; ++u) {
+        float x[8];
+        unpack(u, x);
+        uint32_t packed = 0;
+        if constexpr (BITS == 2) {
+          const float tz = tp[u] == __builtin_inff() ? -__builtin_inff() : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) packed |= sym2_bits(x[e], tp[u], tz, 2 * e);
+        } else {
+          const float rd = tp[u] == __builtin_inff() ? 0.0f : __builtin_amdgcn_rcpf(tp[u]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], tp[u], rd) << (BITS * e);
         }
-      } else {
+        // keep the word 32 bits wide so code counts compile to compare + add-with-carry
+        asm("" : "+v"(packed));
+        store_codes(wave * kPerWave + 4 * u + sub, packed);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int vloc = wave * kPerWave + 4 * u + sub;
+        float x[8];
+        unpack(u, x);
+        uint32_t packed = 0;
         // group of 32 channels = 4 lanes: two extremes at each end, merged by xor 1, 2
         int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
 #pragma unroll
@@ -150,88 +216,126 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
         const float hi = a.q.hi_mode == 0 ? __builtin_fmaf(a.q.g_hi, s31 - s30, s30)
                                           : (a.q.hi_mode == 1 ? s30 : s31);
         const float s32 = (hi - lo) / (float)(L - 1);
-        sh = f16_sat_bits(s32);
-        zh = f16_sat_bits(lo);
+        const uint16_t sh = f16_sat_bits(s32), zh = f16_sat_bits(lo);
         const double sd = (double)f16_bits_to_f32(sh), zd = (double)f16_bits_to_f32(zh);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(x[e], zd, sd);
           packed |= c << (BITS * e);
         }
+        if ((l16 & 3) == 0) {
+          sc_lds[vloc * 4 + (l16 >> 2)] = sh;
+          zr_lds[vloc * 4 + (l16 >> 2)] = zh;
+        }
+        store_codes(vloc, packed);
       }
-      // this lane's 8 codes: BITS bytes at record offset BITS * l16
-      uint8_t* dst = &rec_lds[vloc * REC + BITS * l16];
-      if constexpr (BITS == 2) {
-        *(uint16_t*)dst = (uint16_t)packed;
-      } else if constexpr (BITS == 4) {
-        *(uint32_t*)dst = packed;
-      } else {
-        dst[0] = (uint8_t)packed;
-        dst[1] = (uint8_t)(packed >> 8);
-        dst[2] = (uint8_t)(packed >> 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the prefetch has landed
+    __syncthreads();
+
+    // write back: records (BITS 16-byte chunks each) and scales (+ zeros)
+    const int64_t vb = it * kVecs;
+    if constexpr (DENSE) {
+      const int64_t nvalid = nv - vb < kVecs ? nv - vb : kVecs;
+      for (int c = tid; c < kVecs * BITS; c += 64 * kWaves)
+        if (c < nvalid * BITS) *(uint4*)(a.codes + vb * REC + 16 * c) = *(const uint4*)&rec_lds[16 * c];
+      constexpr int SCB = kVecs * NSC * 2 / 16;  // 16-byte chunks of scales
+      for (int c = tid; c < SCB; c += 64 * kWaves) {
+        const int64_t first = (int64_t)c * 8 / NSC;  // first vector of the chunk
+        if (first + 8 / NSC <= nvalid) {
+          *(uint4*)(a.scales + vb * NSC + 8 * c) = *(const uint4*)&sc_lds[8 * c];
+          if constexpr (QK != 0) *(uint4*)(a.zeros + vb * NSC + 8 * c) = *(const uint4*)&zr_lds[8 * c];
+        } else {
+          for (int k = 0; k < 8; ++k)
+            if ((int64_t)(8 * c + k) < nvalid * NSC) {
+              a.scales[vb * NSC + 8 * c + k] = sc_lds[8 * c + k];
+              if constexpr (QK != 0) a.zeros[vb * NSC + 8 * c + k] = zr_lds[8 * c + k];
+            }
+        }
       }
-      if (v < nv) {
-        const int64_t n = v / a.n_heads;
-        const int h = (int)(v - n * a.n_heads);
-        const int64_t row = a.slots ? a.slots[n] : n;
-        if (row >= 0 && row < a.n_rows) {
+    } else {
+      for (int c = tid; c < kVecs * BITS; c += 64 * kWaves) {
+        const int vloc = c / BITS, k = c - vloc * BITS;
+        const int64_t v = vb + vloc;
+        const int64_t row = row_lds[vloc];
+        if (v < nv && row >= 0 && row < a.n_rows) {
+          const uint32_t n = div_heads((uint32_t)v, a);
+          const int h = (int)((uint32_t)v - n * (uint32_t)a.n_heads);
+          *(uint4*)(a.codes + (row * a.n_heads + h) * REC + 16 * k) = *(const uint4*)&rec_lds[vloc * REC + 16 * k];
+        }
+      }
+      for (int vloc = tid; vloc < kVecs; vloc += 64 * kWaves) {
+        const int64_t v = vb + vloc;
+        const int64_t row = row_lds[vloc];
+        if (v < nv && row >= 0 && row < a.n_rows) {
+          const uint32_t n = div_heads((uint32_t)v, a);
+          const int h = (int)((uint32_t)v - n * (uint32_t)a.n_heads);
           const int64_t slot = row * a.n_heads + h;
           if constexpr (QK == 0) {
-            if (l16 == 0) a.scales[slot] = sc;
+            a.scales[slot] = sc_lds[vloc];
           } else {
-            if ((l16 & 3) == 0) {
-              a.scales[slot * 4 + (l16 >> 2)] = sh;
-              a.zeros[slot * 4 + (l16 >> 2)] = zh;
-            }
+            const uint16_t* s = &sc_lds[vloc * 4];
+            const uint16_t* z = &zr_lds[vloc * 4];
+            *(uint2*)(a.scales + slot * 4) = make_uint2(s[0] | ((uint32_t)s[1] << 16), s[2] | ((uint32_t)s[3] << 16));
+            *(uint2*)(a.zeros + slot * 4) = make_uint2(z[0] | ((uint32_t)z[1] << 16), z[2] | ((uint32_t)z[3] << 16));
           }
         }
       }
     }
     __syncthreads();
-    // write back the block's records as 16-byte chunks
-    for (int c = tid; c < kVecs * BITS; c += 64 * kWaves) {
-      const int vloc = c / BITS, k = c - vloc * BITS;
-      const int64_t v = it * kVecs + vloc;
-      if (v < nv) {
-        const int64_t n = v / a.n_heads;
-        const int h = (int)(v - n * a.n_heads);
-        const int64_t row = a.slots ? a.slots[n] : n;
-        if (row >= 0 && row < a.n_rows)
-          *(uint4*)(a.codes + (row * a.n_heads + h) * REC + 16 * k) = *(const uint4*)&rec_lds[vloc * REC + 16 * k];
-      }
-    }
-    __syncthreads();
-    if (!has_next) break;
-    it = it_next;
-    cur = nxt;
+    if (has_next) it = it_next;
+    return has_next;
+  };
+
+  RawVals<F32IN> ra, rb;
+  int64_t rowa[kU], rowb[kU];
+  load_vals<F32IN, DENSE>(ra, rowa, a, (uint32_t)(it * kVecs) + wave * kPerWave + sub, l16, last);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  while (true) {
+    if (!step(ra, rowa, rb, rowb)) break;
+    if (!step(rb, rowb, ra, rowa)) break;
   }
 }
 
-template <int BITS, int QK>
-hipError_t launch_v(const ValuesArgs& a, int f32_in, int blocks, hipStream_t st) {
-  if (f32_in) values_kernel<BITS, QK, true><<<blocks, 64 * kWaves, 0, st>>>(a);
-  else values_kernel<BITS, QK, false><<<blocks, 64 * kWaves, 0, st>>>(a);
+template <int BITS, int QK, bool F32IN, bool DENSE>
+hipError_t launch_v(const ValuesArgs& a, int cus, hipStream_t st) {
+  auto k = values_kernel<BITS, QK, F32IN, DENSE>;
+  static int occ = 0;  // resident blocks per CU, one value per instantiation
+  if (!occ) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * kWaves, 0) != hipSuccess || n < 1) n = 1;
+    occ = n;
+  }
+  const int64_t nv = a.n_tokens * a.n_heads;
+  const int64_t n_iter = (nv + kVecs - 1) / kVecs;
+  const int64_t cap = (int64_t)cus * occ;
+  const int blocks = (int)(n_iter < cap ? n_iter : cap);
+  if (blocks <= 0) return hipSuccess;
+  k<<<blocks, 64 * kWaves, 0, st>>>(a);
   return hipGetLastError();
+}
+
+template <int BITS, int QK>
+hipError_t launch_vd(const ValuesArgs& a, int f32_in, int cus, hipStream_t st) {
+  const bool dense = a.slots == nullptr && a.stride == (int64_t)a.n_heads * kD;
+  if (f32_in) return dense ? launch_v<BITS, QK, true, true>(a, cus, st) : launch_v<BITS, QK, true, false>(a, cus, st);
+  return dense ? launch_v<BITS, QK, false, true>(a, cus, st) : launch_v<BITS, QK, false, false>(a, cus, st);
 }
 
 }  // namespace
 
-hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int max_blocks, hipStream_t st) {
-  const int64_t nv = a.n_tokens * a.n_heads;
-  const int64_t n_iter = (nv + kVecs - 1) / kVecs;
-  const int blocks = (int)(n_iter < max_blocks ? n_iter : max_blocks);
-  if (blocks <= 0) return hipSuccess;
+hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t st) {
   if (a.q.kind == 0) {
     switch (bits) {
-      case 2: return launch_v<2, 0>(a, f32_in, blocks, st);
-      case 3: return launch_v<3, 0>(a, f32_in, blocks, st);
-      case 4: return launch_v<4, 0>(a, f32_in, blocks, st);
+      case 2: return launch_vd<2, 0>(a, f32_in, cus, st);
+      case 3: return launch_vd<3, 0>(a, f32_in, cus, st);
+      case 4: return launch_vd<4, 0>(a, f32_in, cus, st);
     }
   } else {
     switch (bits) {
-      case 2: return launch_v<2, 1>(a, f32_in, blocks, st);
-      case 3: return launch_v<3, 1>(a, f32_in, blocks, st);
-      case 4: return launch_v<4, 1>(a, f32_in, blocks, st);
+      case 2: return launch_vd<2, 1>(a, f32_in, cus, st);
+      case 3: return launch_vd<3, 1>(a, f32_in, cus, st);
+      case 4: return launch_vd<4, 1>(a, f32_in, cus, st);
     }
   }
   return hipErrorInvalidValue;

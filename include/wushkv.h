@@ -94,8 +94,8 @@ typedef struct {
 
 /* Packed cache view (device pointers, caller-owned).
  *   codes:  [n_rows][n_heads][16*bits] bytes, 16-byte aligned.
- *   scales: fp16 bits, 2-byte aligned (8-byte aligned for affine).
- *   zeros:  fp16 bits for affine, NULL for symmetric.
+ *   scales: fp16 bits, 16-byte aligned.
+ *   zeros:  fp16 bits for affine (16-byte aligned), NULL for symmetric.
  *   slots:  int64 row per token, or NULL (row = token index).  Rows outside
  *           [0, n_rows) are skipped by writers and read as zero-filled by the
  *           reader; callers must not rely on that.
@@ -140,7 +140,8 @@ wushkv_status wushkv_quantize_keys(const void* K, wushkv_dtype k_dtype, int64_t 
                                    const wushkv_quantizer* quantizer, const wushkv_packed* out,
                                    void* stream);
 
-/* Values: quantize -> pack (no RoPE, no transform).  Same layouts as keys. */
+/* Values: quantize -> pack (no RoPE, no transform).  Same layouts as keys.
+ * n_tokens*n_heads must stay below 2^31 (WUSHKV_ERR_UNSUPPORTED otherwise). */
 wushkv_status wushkv_quantize_values(const void* V, wushkv_dtype v_dtype, int64_t n_tokens,
                                      int n_heads, int64_t token_stride, int bits,
                                      const wushkv_quantizer* quantizer, const wushkv_packed* out,

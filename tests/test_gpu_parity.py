@@ -444,3 +444,37 @@ def test_deterministic(env):
     c = packed_host(run_keys(env, K, pos, T, 2, bk.sym()))
     assert_same_packed(a, b, "run 2")
     assert_same_packed(a, c, "run 3")
+
+
+@pytest.mark.parametrize("H", [3, 5])
+def test_odd_head_count_strided_slots(env, H):
+    """Head counts that are not powers of two (exact division by H on the GPU),
+    a token stride larger than H*128 and scattered slot rows."""
+    o, bk, torch = env["oracle"], env["bk"], env["torch"]
+    rng = np.random.default_rng(100 + H)
+    N, rows = 1000, 5000
+    V = (rng.standard_normal((N, H, 128)) * np.exp(rng.standard_normal((1, H, 128)))).astype(np.float32)
+    K = (rng.standard_normal((N, H, 128)) * 3).astype(np.float32)
+    pos = rng.integers(0, 1 << 16, N).astype(np.int32)
+    slots = rng.choice(rows, N, replace=False).astype(np.int64)
+    T = np.stack([np.eye(128, dtype=np.float32)[rng.permutation(128)] * 2.0 for _ in range(H)])
+    say(f"odd heads H={H}")
+    big = torch.zeros((N, H + 1, 128), dtype=torch.float32, device="cuda")
+    big[:, :H] = to_dev(env, V)
+    for kind, bits in (("sym", 3), ("affine", 2)):
+        q = _bkq(env, kind)
+        out = bk.alloc_packed(rows, H, bits, q).with_slots(to_dev(env, slots))
+        bk.wushkv_quantize_values(big[:, :H], bits, q, out)
+        torch.cuda.synchronize()
+        r = o.quantize_values(V, bits, oracle_q(env, q))
+        sl = torch.from_numpy(slots).cuda()
+        g = packed_host(bk.PackedCache(out.codes[sl], out.scales[sl], None if out.zeros is None else out.zeros[sl]))
+        assert_same_packed(g, r, f"values H={H} {kind}")
+        # keys through a permutation-times-two transform are exact: bit-exact against the oracle
+        pk = run_keys(env, K, pos, T, bits, q, slots=slots, rows=rows)
+        rk = o.quantize_keys(K, pos, T, 1e6, bits, oracle_q(env, q))
+        gk = packed_host(bk.PackedCache(pk.codes[sl], pk.scales[sl], None if pk.zeros is None else pk.zeros[sl]))
+        assert_same_packed(gk, rk, f"keys H={H} {kind}")
+        back = bk.wushkv_dequantize(out, N, H, bits, q, out_dtype=torch.float32).cpu().numpy()
+        ref = o.dequantize(r["codes"], r["scales"], r["zeros"], N, H, bits, oracle_q(env, q))
+        assert np.array_equal(back.view(np.uint32), ref.view(np.uint32))
