@@ -92,6 +92,51 @@ __device__ __forceinline__ uint32_t sym2_bits(float y, float tp, float tz, int s
   return (b0 ? (1u << sh) : 0u) | (B ? (2u << sh) : 0u);
 }
 
+// Lane masks of the three 2-bit decisions: bit1 = B, bit0 = C | (A & !B).
+struct Sym2Masks {
+  uint64_t b1, b0;
+};
+__device__ __forceinline__ Sym2Masks sym2_masks(bool A, bool B, bool C) {
+  const uint64_t a = __builtin_amdgcn_ballot_w64(A), b = __builtin_amdgcn_ballot_w64(B),
+                 c = __builtin_amdgcn_ballot_w64(C);
+  return {b, c | (a & ~b)};
+}
+
+// r = 2r + bit, once per lane mask, first mask first (so it ends up most
+// significant): one v_addc_co_u32 per bit with the mask as carry-in.  The
+// leading s_nop gives the two wait states a vector compare's mask needs
+// before an add-with-carry may read it.
+__device__ __forceinline__ uint32_t shift_in8(uint32_t r, const uint64_t* m) {
+  uint64_t co;
+  asm("s_nop 1\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %2\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %3\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %4\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %5\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %6\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %7\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %8\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %9"
+      : "+v"(r), "=&s"(co)
+      : "s"(m[0]), "s"(m[1]), "s"(m[2]), "s"(m[3]), "s"(m[4]), "s"(m[5]), "s"(m[6]), "s"(m[7]));
+  return r;
+}
+
+// Thresholds that decide "x > t" for a bf16 value x from the raw 32-bit word
+// whose high half holds x (the low half holding anything): with c the
+// smallest bf16 above t, x > t iff x >= c.  For c > 0 every word with high
+// half x >= c reads as a float >= c and every other one as < c, so the test
+// is word > prev_fp32(c), whose bits are bits(t) | 0xFFFF.  For t < 0 the
+// test is word > d with d the largest bf16 <= t (a word's float lies within
+// one bf16 step below its high half, towards -inf).  Both tests also decide
+// exact bf16 values (low half zero) correctly.  t = +-inf maps to itself.
+__device__ __forceinline__ float bf16_gt_threshold(float t) {
+  const uint32_t b = __float_as_uint(t);
+  if (__builtin_isinf(t)) return t;
+  if (t >= 0.0f) return __uint_as_float(b | 0xFFFFu);
+  return __uint_as_float(((b & 0x7FFFFFFFu) + 0xFFFFu) & 0xFFFF0000u | 0x80000000u);
+}
+
 // Sum over aligned groups of 2, 4, 8 and 16 lanes by DPP moves: after step k a
 // lane holds the sum of its 2^k-lane block, each step adding the two halves'
 // sums (commutative, so both halves hold the same value).  Equal to xor

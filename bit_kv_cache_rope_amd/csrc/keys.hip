@@ -305,6 +305,7 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
       // Output element acc[m][i] is row 32*(2*half+m) + 8*(i/4) + 4*lh + (i%4) of token `col`.
       // run[m][q] packs the codes of acc[m][4q .. 4q+3] (4 consecutive rows), LSB first.
       uint32_t run[2][4];
+      uint32_t W2[2];  // 2-bit symmetric: whole words of codes
       if constexpr (QK == 0) {
         // Sum of squares as the contiguous pairwise tree over rows 0..127:
         // runs of 4 in-lane, pairs of runs across lanes l and l^32, then up.
@@ -337,19 +338,39 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
         const float tp = delta == 0.0f ? __builtin_inff() : delta;
         const float tz = delta == 0.0f ? -__builtin_inff() : 0.0f;
         const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
+        if constexpr (BITS == 2) {
+          // W[m]: the lane's 16 codes of m-tile m, run q (4 rows) in byte q,
+          // shifted in from the last row down.  Midpoint tests A = [y > -step],
+          // B = [y >= 0], C = [y > step]; code bits B and C | (A & !B).
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+          for (int m = 0; m < 2; ++m) {
+            uint32_t w = 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t r = 0;
+            for (int g = 3; g >= 0; --g) {  // 4 rows per add-with-carry block
+              uint64_t mk[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (BITS == 2) r |= sym2_bits(acc[m][4 * q + e], tp, tz, 2 * e);
-              else r |= sym_code<BITS>(acc[m][4 * q + e], tp, rd) << (BITS * e);
+              for (int e = 3; e >= 0; --e) {
+                const float y = acc[m][4 * g + e];
+                const Sym2Masks k = sym2_masks(y > -tp, y >= tz, y > tp);
+                mk[2 * (3 - e)] = k.b1;
+                mk[2 * (3 - e) + 1] = k.b0;
+              }
+              w = shift_in8(w, mk);
             }
-            asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
-            run[m][q] = r;
+            W2[m] = w;
           }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t r = 0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) r |= sym_code<BITS>(acc[m][4 * q + e], tp, rd) << (BITS * e);
+              asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
+              run[m][q] = r;
+            }
+        }
         if (half == 0 && lh == 0) sc_lds[col][hh] = dh;
       } else {
         // Percentile-clipped affine quantizer, group = one 32-row tile = rows
@@ -395,7 +416,18 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
         }
       }
 
-      // ---- pack: runs of 4 codes -> 16 contiguous rows per lane -> LDS record row
+      // ---- pack: runs of 4 codes -> 16 contiguous rows per lane -> LDS record row.
+      // Lane l (lh = 0) writes rows 0-15 of the m-tile: its runs 0, 1 interleaved
+      // with those of lane l + 32; lane l + 32 writes rows 16-31 likewise.
+      if constexpr (QK == 0 && BITS == 2) {
+        // bytes of {partner (selectors 4-7), own (0-3)}
+        const uint32_t sel = lh ? 0x03070206u : 0x05010400u;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t chunk = __builtin_amdgcn_perm(__shfl_xor(W2[m], 32), W2[m], sel);
+          *(uint32_t*)&rec_lds[col][hh * REC + 2 * (4 * (2 * half + m) + 2 * lh)] = chunk;
+        }
+      } else
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const uint32_t* rn = run[m];

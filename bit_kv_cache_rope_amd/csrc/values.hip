@@ -83,7 +83,9 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
   __shared__ __align__(16) uint16_t zr_lds[QK ? kVecs * 4 : 8];
   __shared__ int64_t row_lds[DENSE ? 1 : kVecs];
   __shared__ float ss_lds[kWaves][kPerWave];          // sum of squares per vector
-  __shared__ __align__(16) float tp_lds[kWaves][4][kU];  // threshold per (sub, u)
+  __shared__ __align__(16) float tp_lds[kWaves][4][kU];  // per (sub, u): step, or the 2-bit "> -step" threshold
+  __shared__ __align__(16) float tc_lds[kWaves][4][kU];  // 2-bit "> step" threshold
+  __shared__ __align__(16) uint32_t tb_lds[kWaves][4][kU];  // 2-bit ">= 0" bound on the raw word
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane >> 4, l16 = lane & 15;
@@ -154,9 +156,20 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
         const uint16_t sc = f16_sat_bits(d32);
         const float delta = f16_bits_to_f32(sc);
         sc_lds[wave * kPerWave + lane] = sc;
-        // BITS == 2: the threshold tp (+inf for a zero step); otherwise the step
-        // itself (+inf for a zero step, whose reciprocal 0 then yields code L/2)
-        tp_lds[wave][lane & 3][lane >> 2] = delta == 0.0f ? __builtin_inff() : delta;
+        const float tp = delta == 0.0f ? __builtin_inff() : delta;  // +inf for a zero step
+        if constexpr (BITS == 2) {
+          // Midpoint tests A = [x > -step], B = [x >= 0], C = [x > step]
+          // (ties as in the nearest-level rule).  bf16 input: A and C are
+          // decided on the raw word (bf16_gt_threshold), B as an unsigned
+          // bound (x >= 0 or x = -0); a zero step makes A and B always true
+          // and C never: code 2.
+          tp_lds[wave][lane & 3][lane >> 2] = F32IN ? -tp : bf16_gt_threshold(-tp);
+          tc_lds[wave][lane & 3][lane >> 2] = F32IN ? tp : bf16_gt_threshold(tp);
+          tb_lds[wave][lane & 3][lane >> 2] = delta == 0.0f ? 0xFFFFFFFFu : (F32IN ? 0x80000000u : 0x8000FFFFu);
+        } else {
+          // the step itself (+inf for a zero step, whose reciprocal 0 then yields code L/2)
+          tp_lds[wave][lane & 3][lane >> 2] = tp;
+        }
       }
       // (3) codes
       float tp[kU];
@@ -166,23 +179,60 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
         tp[0] = t0.x; tp[1] = t0.y; tp[2] = t0.z; tp[3] = t0.w;
         tp[4] = t1.x; tp[5] = t1.y; tp[6] = t1.z; tp[7] = t1.w;
       }
+      if constexpr (BITS == 2) {
+        float tc[kU];
+        uint32_t tb[kU];
+        {
+          const float4 c0 = *(const float4*)&tc_lds[wave][sub][0];
+          const float4 c1 = *(const float4*)&tc_lds[wave][sub][4];
+          tc[0] = c0.x; tc[1] = c0.y; tc[2] = c0.z; tc[3] = c0.w;
+          tc[4] = c1.x; tc[5] = c1.y; tc[6] = c1.z; tc[7] = c1.w;
+          const uint4 b0 = *(const uint4*)&tb_lds[wave][sub][0];
+          const uint4 b1 = *(const uint4*)&tb_lds[wave][sub][4];
+          tb[0] = b0.x; tb[1] = b0.y; tb[2] = b0.z; tb[3] = b0.w;
+          tb[4] = b1.x; tb[5] = b1.y; tb[6] = b1.z; tb[7] = b1.w;
+        }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        float x[8];
-        unpack(u, x);
-        uint32_t packed = 0;
-        if constexpr (BITS == 2) {
-          const float tz = tp[u] == __builtin_inff() ? -__builtin_inff() : 0.0f;
+        for (int u = 0; u < kU; ++u) {
+          // the 8 words to test, channel order: bf16 -> low halves shifted up,
+          // high halves raw; fp32 -> the values' bits
+          uint32_t w[8];
+          if constexpr (F32IN) {
+            const float4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
+            w[0] = __float_as_uint(p.x); w[1] = __float_as_uint(p.y); w[2] = __float_as_uint(p.z);
+            w[3] = __float_as_uint(p.w); w[4] = __float_as_uint(q.x); w[5] = __float_as_uint(q.y);
+            w[6] = __float_as_uint(q.z); w[7] = __float_as_uint(q.w);
+          } else {
+            const uint4 p = cur.v[u];
+            w[0] = p.x << 16; w[1] = p.x; w[2] = p.y << 16; w[3] = p.y;
+            w[4] = p.z << 16; w[5] = p.z; w[6] = p.w << 16; w[7] = p.w;
+          }
+          const uint32_t tbl = F32IN ? tb[u] : (tb[u] & 0xFFFF0000u);  // low halves are exact
+          uint64_t m[16];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) packed |= sym2_bits(x[e], tp[u], tz, 2 * e);
-        } else {
+          for (int e = 7; e >= 0; --e) {
+            const float f = __uint_as_float(w[e]);
+            const Sym2Masks k = sym2_masks(f > tp[u], w[e] <= ((e & 1) ? tb[u] : tbl), f > tc[u]);
+            m[2 * (7 - e)] = k.b1;
+            m[2 * (7 - e) + 1] = k.b0;
+          }
+          uint32_t packed = shift_in8(0u, m);
+          packed = shift_in8(packed, m + 8);
+          store_codes(wave * kPerWave + 4 * u + sub, packed);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          float x[8];
+          unpack(u, x);
+          uint32_t packed = 0;
           const float rd = tp[u] == __builtin_inff() ? 0.0f : __builtin_amdgcn_rcpf(tp[u]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], tp[u], rd) << (BITS * e);
+          // keep the word 32 bits wide so code counts compile to compare + add-with-carry
+          asm("" : "+v"(packed));
+          store_codes(wave * kPerWave + 4 * u + sub, packed);
         }
-        // keep the word 32 bits wide so code counts compile to compare + add-with-carry
-        asm("" : "+v"(packed));
-        store_codes(wave * kPerWave + 4 * u + sub, packed);
       }
     } else {
 #pragma unroll
