@@ -8,10 +8,10 @@
  *     orthogonal one), online, because the transform is applied after RoPE
  *     (ai4snews summary "WUSH-KV cuts 2-bit KV-cache perplexity ...", method and
  *     deployment paragraphs; arXiv abstract; cere-bro post "WUSH-KV: 2-bit
- *     KV-Cache Quantization with Data-Adaptive Transforms", Gaps: "adds a
- *     matmul per decode step").
+ *     KV-Cache Quantization with Data-Adaptive Transforms", Gaps, which counts the
+ *     extra matrix product per decode step as the method's online cost).
  *   - Values need no online transform (it is folded into the weights) and are
- *     only quantized (same sources; cere-bro flowchart "Folded into weights").
+ *     only quantized (same sources; the value branch of the cere-bro flowchart).
  *   - Both go through a clipped b-bit scalar quantizer: an RMS-clipped
  *     symmetric INT grid (the QuEST-style quantizer of the theory) or a
  *     percentile-clipped affine grid (the OSCAR-style quantizer of the

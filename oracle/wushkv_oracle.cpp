@@ -14,7 +14,7 @@
  *   values: v --clipped b-bit quantizer--> codes + scale(s) --> packed record
  *   read:   record --> unpack --> dequantize --> (keys) T~inv * y^
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - RoPE is the rotate-half form on channel pairs (i, i+64) with
  *     w_i = RN32(theta^(-2i/128)); cos and sin of the exact angle pos*w_i are
  *     rounded once to fp32.  Evaluated here in x87 extended precision.
@@ -316,7 +316,7 @@ void wko_transform_f64(const float* T, const double* x, double* y) {
 
 // Query-side pairing q' = T~^{-T} q: solve T~^T q' = q by Gaussian elimination
 // with partial pivoting in fp64.  Then q'.(T~ x) = q.x for every x: the key
-// transform "accounts for the query heads that consume the cached keys"
+// transform is built with the query heads that read the cached keys in view
 // (ai4snews summary, method paragraph).  Returns 0, or -1 if singular.
 int wko_query_pair(const float* T, const double* q, double* qp) {
   std::vector<double> A((size_t)kD * kD);
@@ -428,7 +428,7 @@ int wko_quantize_keys(const void* K, int k_dtype, int64_t N, int H, int64_t toke
 
 // Values: quantize -> pack (their transform is folded into the weights, so
 // nothing runs online before the quantizer: ai4snews deployment paragraph;
-// cere-bro flowchart "Folded into weights, zero runtime cost").
+// the value branch of the cere-bro flowchart, which costs nothing at run time).
 int wko_quantize_values(const void* V, int v_dtype, int64_t N, int H, int64_t token_stride,
                         int bits, const wko_quantizer* qz, uint8_t* codes, uint16_t* scales,
                         uint16_t* zeros, const int64_t* slots, int threads) {

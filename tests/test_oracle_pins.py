@@ -228,7 +228,7 @@ def test_identity_transform_reduces_to_plain_quantizer(oracle_mod, synth_mod):
 
 def test_query_pairing_preserves_qk(oracle_mod, synth_mod):
     """(T~^{-T} q) . (T~ x~) = q . x~ before quantization (P1 method paragraph:
-    the key transform accounts for the query heads that read the keys)."""
+    the key transform is built with the query heads that read the keys in view)."""
     w = synth_mod.WORKLOADS["qwen3_8b_prefill"]
     T, _ = synth_mod.transform(w, 0)
     rng = np.random.default_rng(6)
