@@ -7,25 +7,24 @@
 // Quantization with Data-Adaptive Transforms", Gaps).
 //
 // Work decomposition.  A block owns HG heads and walks 32-token tiles
-// (persistent: tile = first, first + blocks_per_group, ...).  Two waves serve
-// each head; wave `half` keeps rows [64*half, 64*half+64) of T~ (64 VGPRs of
-// A operands, loaded once) and computes those output rows for the tile with
-// 16 v_mfma_f32_32x32x16_bf16.  The B operand is the tile's rotated keys: lane
-// l holds token l%32 and, for k step s, channels 16s + 8(l/32) + 0..7, so the
-// RoPE partners (i, i+64) sit in one lane (k steps s and s+4).  Each wave of a
-// head loads and rotates half of the pairs (k steps 2*half, 2*half+1 and their
-// partners) and the two waves swap their bf16 operands through LDS.
+// (persistent: tile = first, first + blocks_per_group, ...).  Four waves serve
+// each head; wave wq keeps rows [32 wq, 32 wq + 32) of T~ (32 VGPRs of A
+// operands, loaded once) and computes those output rows for the tile with 8
+// v_mfma_f32_32x32x16_bf16.  The B operand is the tile's rotated keys: lane l
+// holds token l%32 and, for k step s, channels 16s + 8(l/32) + 0..7, so the
+// RoPE partners (i, i+64) sit in one lane (k steps s and s+4).  Wave wq loads
+// and rotates k step wq and its partner, and the four waves share their bf16
+// operands through LDS.  At under 128 VGPRs, four waves per SIMD are resident.
 //
-// cos/sin for a tile are computed once per block into LDS (double-buffered);
-// the two small angle tables live in LDS for the whole launch, and the
-// high-angle table entries (and slot rows) are loaded two tiles ahead, the
-// positions three tiles ahead, so that no computation waits on a fresh load.
+// cos/sin for a tile are computed once per block into LDS; the two small
+// angle tables live in LDS for the whole launch, and the high-angle table
+// entries (and slot rows) are loaded a tile ahead of their use, the positions
+// three tiles ahead, so that no computation waits on a fresh load.
 //
 // Per-tile pipeline.  Vector-memory loads retire in order, so each iteration
-// issues the loads for later tiles first (table entries, positions), then the
-// next tile's keys, and the work that consumes only older data runs while they
-// are in flight.  Every iteration ends with one explicit wait before its
-// stores, and the loop is unrolled by two over two register sets, so the
+// issues the next tile's position and keys first and its table entries last,
+// and ends with one explicit wait for all but those table entries before its
+// stores; the loop is unrolled by two over two key register sets, so the
 // compiler's own waits never cover the key prefetch.  Packed records and
 // scales are staged in LDS and written as whole 16-byte chunks (a head
 // group's records of a token are contiguous in the cache row).
@@ -49,18 +48,17 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// The four k steps a wave loads and rotates: 2h, 2h+1 and their partners +4.
-__device__ __forceinline__ int own_step(int j, int half) { return (j & 1) + 2 * half + 4 * (j >> 1); }
-
+// The two k steps a wave loads and rotates: wq (channels i < 64) and its
+// partner wq + 4 (channels i + 64).
 template <bool F32IN>
 struct RawKeys;
 template <>
-struct RawKeys<false> {  // bf16: 8 channels per 16-byte load, 4 k steps
-  uint4 v[4];
+struct RawKeys<false> {  // bf16: 8 channels per 16-byte load, 2 k steps
+  uint4 v[2];
 };
 template <>
 struct RawKeys<true> {   // fp32: 8 channels = two 16-byte loads
-  float4 v[8];
+  float4 v[4];
 };
 
 // Loads are unconditional: a token past the end reads the last token's row (its
@@ -68,11 +66,11 @@ struct RawKeys<true> {   // fp32: 8 channels = two 16-byte loads
 // conditionally issued load with its waits.
 template <bool F32IN>
 __device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, const KeysArgs& a, int64_t tok, int h, int lh,
-                                          int half) {
+                                          int wq) {
   tok = tok < a.n_tokens ? tok : a.n_tokens - 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int s = own_step(j, half);
+  for (int j = 0; j < 2; ++j) {
+    const int s = wq + 4 * j;
     if constexpr (F32IN) {
       const float* base = (const float*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh;
       r.v[2 * j] = *(const float4*)base;
@@ -106,8 +104,9 @@ struct CsStage {
 };
 
 template <int BITS, int QK, bool F32IN, int HG, bool YOUT>
-__global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
-  constexpr int NT = 128 * HG;
+__global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
+  constexpr int NT = 256 * HG;
+  constexpr int NW = NT / 64;
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
   constexpr int RECROW = HG * REC + 16;  // LDS row of one token's records (+16 B pad)
@@ -117,15 +116,18 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
 
   __shared__ __align__(16) double2 tab_lds[2][32][kPairs];  // heads of the p0 and p1 angle tables
   __shared__ __align__(16) float2 cs_lds[2][kTile][kCsStride];
-  __shared__ __align__(16) bf16x8 xb_lds[HG][8][64];        // rotated operands swapped between a head's waves
-  __shared__ int64_t slot_lds[2][kTile];
+  __shared__ __align__(16) bf16x8 xb_lds[HG][8][64];        // rotated operands shared by a head's four waves
+  __shared__ int64_t slot_lds[3][kTile];  // cache row per token, tile j in slot j % 3
   __shared__ int pos_lds[4][kTile];
-  __shared__ float red_lds[HG][2][kTile];
+  __shared__ float red_lds[HG][4][kTile];
   __shared__ __align__(16) uint8_t rec_lds[kTile][RECROW];
   __shared__ uint16_t sc_lds[kTile][HG * NSC];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hh = wave >> 1, half = wave & 1, lh = lane >> 5, col = lane & 31;
+  // Four waves per head: wave wq holds rows 32 wq .. 32 wq + 31 of T~ and
+  // rotates the RoPE pairs of k step wq (channels 16 wq + 8 (l / 32) + 0..7
+  // and their partners 64 higher).
+  const int hh = wave >> 2, wq = wave & 3, lh = lane >> 5, col = lane & 31;
   const int grp = blockIdx.x % a.n_groups;
   const int64_t first_tile = blockIdx.x / a.n_groups;
   const int h = grp * HG + hh;
@@ -133,25 +135,8 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
   if (first_tile >= n_tiles) return;  // uniform over the block
   const int64_t tile_step = a.blocks_per_group;
 
-  // This wave's half of T~ as MFMA A operands: rows 32*(2*half+m) + (lane % 32).
-  bf16x8 A[2][8];
-  {
-    const bf16x8* Tp = (const bf16x8*)a.T;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        A[m][s] = Tp[(((int64_t)h * 4 + 2 * half + m) * 8 + s) * 64 + lane];
-  }
-
-  // Angle tables t0 (p0) and t1 (p1) into LDS for the whole launch.
-  for (int e = tid; e < 2 * 32 * kPairs; e += NT) {
-    const int t = e / (32 * kPairs), r = e - t * 32 * kPairs;
-    tab_lds[t][r / kPairs][r % kPairs] = (t == 0 ? a.t0 : a.t1)[r];
-  }
-
   // Tiles are visited as j = 0, 1, 2, ...: tile(j) = first_tile + j * tile_step.
-  // Thread (wave w, lane i) computes cos/sin pair i of tokens w + (NT/64) k,
+  // Thread (wave w, lane i) computes cos/sin pair i of tokens w + NW k,
   // k < PPT, so every position it reads is wave-uniform.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int64_t last_tok = a.n_tokens - 1;
@@ -172,31 +157,35 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
   };
   auto issue_cs = [&](CsStage<PPT>& st, int64_t tile, int pb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) st.hi[k] = a.t2[(pos_of(pb, wave_u + (NT / 64) * k) >> 10) * kPairs + lane];
-    if (a.slots) {
-      const int64_t tok = tile * kTile + (tid & (kTile - 1));
-      st.slot = a.slots[tok < last_tok ? tok : last_tok];
-    }
+    for (int k = 0; k < PPT; ++k) st.hi[k] = a.t2[(pos_of(pb, wave_u + NW * k) >> 10) * kPairs + lane];
+    // Issued whether or not there are slots (a dummy 8-byte read of T~
+    // otherwise), so every iteration issues the same loads in the same order.
+    const int64_t tok = tile * kTile + (tid & (kTile - 1));
+    st.slot = a.slots ? a.slots[tok < last_tok ? tok : last_tok] : *(const int64_t*)a.T;
   };
-  // Fast path for every pair; the rare pairs whose fp32 rounding it cannot
-  // certify are redone in double-double in a loop that is not unrolled (its
-  // loads are issued only when such a pair occurs).
-  auto finish_cs = [&](const CsStage<PPT>& st, int64_t tile, int pb, int buf) __attribute__((always_inline)) {
+  // cos/sin of the next tile into cs_lds[buf]: the fast path for every pair
+  // (returns the pairs it cannot certify), the rare rest redone in
+  // double-double in a loop that is not unrolled (its loads are issued only
+  // when such a pair occurs).
+  auto finish_cs_fast = [&](const CsStage<PPT>& st, int pb, int buf) __attribute__((always_inline)) -> uint32_t {
     uint32_t bad = 0;
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int n = wave_u + (NT / 64) * k;
+      const int n = wave_u + NW * k;
       const int p = pos_of(pb, n);
       const double2 M = tab_lds[1][(p >> 5) & 31][lane], B = tab_lds[0][p & 31][lane];
       bool exact;
       cs_lds[buf][n][lane] = rope_cos_sin_fast(st.hi[k], M, B, exact);
       bad |= (uint32_t)!exact << k;
     }
+    return bad;
+  };
+  auto finish_cs_slow = [&](uint32_t bad, int pb, int buf) __attribute__((always_inline)) {
     if (__builtin_expect(bad != 0, 0)) {
 #pragma unroll 1
       for (int k = 0; k < PPT; ++k) {
         if ((bad >> k) & 1) {
-          const int n = wave_u + (NT / 64) * k;
+          const int n = wave_u + NW * k;
           const int p = pos_lds[pb][n];
           const int p2 = p >> 10, p1 = (p >> 5) & 31, p0 = p & 31;
           cs_lds[buf][n][lane] =
@@ -205,52 +194,80 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    if (tid < kTile) slot_lds[buf][tid] = a.slots ? st.slot : tile * kTile + tid;
+  };
+  auto put_slot = [&](const CsStage<PPT>& st, int64_t tile, int sb) __attribute__((always_inline)) {
+    if (tid < kTile) slot_lds[sb][tid] = a.slots ? st.slot : tile * kTile + tid;
   };
 
   RawKeys<F32IN> ra, rb;
-  CsStage<PPT> sa, sb;
+  CsStage<PPT> st;
   int64_t tile = first_tile;
   int buf = 0, j = 0;
-  load_pos(tile);
-  store_pos(0);
-  for (int d = 1; d < 3; ++d)
-    if (tile + d * tile_step < n_tiles) {
-      load_pos(tile + d * tile_step);
-      store_pos(d);
-    }
+  // Prologue: every load that depends on nothing is issued up front (the
+  // first two tiles' keys, three tiles' positions, T~, the angle tables), so
+  // their latencies overlap; only positions -> table entries -> cos/sin is a
+  // chain.  Clamped reads past the end keep every address valid.
+  load_keys<F32IN>(ra, a, tile * kTile + col, h, lh, wq);
+  int pos_d[3];
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    load_pos(tile + d * tile_step);
+    pos_d[d] = pos_r;
+  }
+  // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
+  bf16x8 A[8];
+  {
+    const bf16x8* Tp = (const bf16x8*)a.T;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
+  }
+
+  // Angle tables t0 (p0) and t1 (p1) into LDS for the whole launch.
+  for (int e = tid; e < 2 * 32 * kPairs; e += NT) {
+    const int t = e / (32 * kPairs), r = e - t * 32 * kPairs;
+    tab_lds[t][r / kPairs][r % kPairs] = (t == 0 ? a.t0 : a.t1)[r];
+  }
+
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    pos_r = pos_d[d];
+    store_pos(d);
+  }
+  if (tid < kTile) pos_lds[3][tid] = 0;  // a valid position in the fourth slot
   __syncthreads();  // angle tables and the first three tiles' positions
-  issue_cs(sa, tile, 0);
-  load_keys<F32IN>(ra, a, tile * kTile + col, h, lh, half);
-  finish_cs(sa, tile, 0, 0);
-  if (tile + tile_step < n_tiles) issue_cs(sb, tile + tile_step, 1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop starts with nothing in flight
+  issue_cs(st, tile, 0);
+  finish_cs_slow(finish_cs_fast(st, 0, 0), 0, 0);
+  put_slot(st, tile, 0);
+  issue_cs(st, tile + tile_step, 1);  // consumed in the first iteration
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (PPT + 1));  // all but those table entries
   __syncthreads();
 
-  // One tile per call: `cur` holds this tile's keys, `nxt` receives the next
-  // tile's; `rdy` holds the next tile's table entries (consumed first, so its
-  // registers are free again), `fut` receives those of the tile after.
-  // Unrolled by two with the sets swapped.
-  auto step = [&](RawKeys<F32IN>& cur, RawKeys<F32IN>& nxt, CsStage<PPT>& rdy, CsStage<PPT>& fut)
+  // One tile per call (tile j; ss = j % 3).  `cur` holds this tile's keys and
+  // `nxt` receives the next tile's.  `st` holds the next tile's table
+  // entries; they are consumed after this tile's quantizer, and `st` then
+  // receives the entries of the tile after next.  Loads for later tiles are
+  // issued unconditionally (clamped addresses past the end), so every
+  // iteration issues the same loads in the same order: position, keys, table
+  // entries + slot row.  Waiting for all but the table loads before the
+  // stores leaves exactly those in flight.  Three barriers per tile.
+  // Unrolled by two over the two key sets.
+  constexpr int kWaitTail = 0x0F70 | (PPT + 1);
+  auto step = [&](RawKeys<F32IN>& cur, RawKeys<F32IN>& nxt, int ss)
       __attribute__((always_inline)) -> bool {
     const int64_t next = tile + tile_step, next2 = next + tile_step, next3 = next2 + tile_step;
-    const bool has_next = next < n_tiles, has_next2 = next2 < n_tiles, has_next3 = next3 < n_tiles;
-    if (has_next) finish_cs(rdy, next, (j + 1) & 3, buf ^ 1);
+    const bool has_next = next < n_tiles;
+    load_pos(next3);
     __builtin_amdgcn_sched_barrier(0);
-    if (has_next2) issue_cs(fut, next2, (j + 2) & 3);
-    if (has_next3) load_pos(next3);
-    __builtin_amdgcn_sched_barrier(0);
-    if (has_next) load_keys<F32IN>(nxt, a, next * kTile + col, h, lh, half);
+    load_keys<F32IN>(nxt, a, next * kTile + col, h, lh, wq);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- RoPE (rotate-half, pairs (i, i+64)) of this wave's pairs -> bf16 operands
     bf16x8 Bop[8];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int s = 2 * half + jj;  // k step of channels i; the partners are in k step s + 4
+    {
+      const int s = wq;  // k step of channels i; the partners are in k step s + 4
       float ka[8], kb[8];
-      unpack8<F32IN>(cur, jj, ka);
-      unpack8<F32IN>(cur, jj + 2, kb);
+      unpack8<F32IN>(cur, 0, ka);
+      unpack8<F32IN>(cur, 1, kb);
       const float4* csp = (const float4*)&cs_lds[buf][col][16 * s + 8 * lh];
       float c[8], sn[8];
 #pragma unroll
@@ -270,63 +287,63 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
       xb_lds[hh][s + 4][lane] = pack8(xb);
     }
     __syncthreads();
-    // All eight operands come back from LDS: indexing registers by the
-    // wave's half would turn into select chains.
+    // All eight operands come from LDS (each wave of the head wrote two).
 #pragma unroll
     for (int s = 0; s < 8; ++s) Bop[s] = xb_lds[hh][s][lane];
 
-    // ---- y = T~ x~ for this wave's 64 rows (fp32 accumulate)
-    f32x16 acc[2];
+    // ---- y = T~ x~ for this wave's 32 rows (fp32 accumulate)
+    f32x16 acc = {};
 #pragma unroll
-    for (int m = 0; m < 2; ++m) acc[m] = (f32x16){};
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[m][s], Bop[s], acc[m], 0, 0, 0);
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bop[s], acc, 0, 0, 0);
 
+    // The next tile's cos/sin (computed for a tile past the end too: harmless,
+    // into the buffer nobody reads), then the table entries of the tile after.
+    auto next_cs = [&]() __attribute__((always_inline)) {
+      const uint32_t bad = finish_cs_fast(st, (j + 1) & 3, buf ^ 1);
+      finish_cs_slow(bad, (j + 1) & 3, buf ^ 1);
+      put_slot(st, next, ss == 2 ? 0 : ss + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_cs(st, next2, (j + 2) & 3);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     const int64_t tok = tile * kTile + col;
 
     if constexpr (YOUT) {
+      next_cs();
       if (tok < a.n_tokens) {
         float* yo = a.y_out + (tok * a.n_heads + h) * kD;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r = 32 * (2 * half + m) + 8 * jj + 4 * lh;
-            *(float4*)(yo + r) = make_float4(acc[m][4 * jj], acc[m][4 * jj + 1], acc[m][4 * jj + 2],
-                                             acc[m][4 * jj + 3]);
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 32 * wq + 8 * jj + 4 * lh;
+          *(float4*)(yo + r) = make_float4(acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);
+      store_pos((j + 3) & 3);
       __syncthreads();
     } else {
-      // Output element acc[m][i] is row 32*(2*half+m) + 8*(i/4) + 4*lh + (i%4) of token `col`.
-      // run[m][q] packs the codes of acc[m][4q .. 4q+3] (4 consecutive rows), LSB first.
-      uint32_t run[2][4];
-      uint32_t W2[2];  // 2-bit symmetric: whole words of codes
+      // Output element acc[i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of token `col`.
+      // run[q] packs the codes of acc[4q .. 4q+3] (4 consecutive rows), LSB first.
+      uint32_t run[4];
+      uint32_t W2 = 0;  // 2-bit symmetric: the whole word of codes
       if constexpr (QK == 0) {
         // Sum of squares as the contiguous pairwise tree over rows 0..127:
-        // runs of 4 in-lane, pairs of runs across lanes l and l^32, then up.
-        float P8[2][4];
+        // runs of 4 in-lane, pairs of runs across lanes l and l^32, the 32
+        // rows of this wave, then the four waves' sums ((0 + 1) + (2 + 3)).
+        float P8[4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float q0 = acc[m][4 * q] * acc[m][4 * q];
-            const float q1 = acc[m][4 * q + 1] * acc[m][4 * q + 1];
-            const float q2 = acc[m][4 * q + 2] * acc[m][4 * q + 2];
-            const float q3 = acc[m][4 * q + 3] * acc[m][4 * q + 3];
-            const float p4 = (q0 + q1) + (q2 + q3);
-            P8[m][q] = p4 + __shfl_xor(p4, 32);
-          }
-        const float P32a = (P8[0][0] + P8[0][1]) + (P8[0][2] + P8[0][3]);
-        const float P32b = (P8[1][0] + P8[1][1]) + (P8[1][2] + P8[1][3]);
-        const float P64 = P32a + P32b;
-        if (lh == 0) red_lds[hh][half][col] = P64;
+        for (int q = 0; q < 4; ++q) {
+          const float q0 = acc[4 * q] * acc[4 * q];
+          const float q1 = acc[4 * q + 1] * acc[4 * q + 1];
+          const float q2 = acc[4 * q + 2] * acc[4 * q + 2];
+          const float q3 = acc[4 * q + 3] * acc[4 * q + 3];
+          const float p4 = (q0 + q1) + (q2 + q3);
+          P8[q] = p4 + __shfl_xor(p4, 32);
+        }
+        const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
+        if (lh == 0) red_lds[hh][wq][col] = P32;
         __syncthreads();
-        const float S = red_lds[hh][0][col] + red_lds[hh][1][col];
+        const float S = (red_lds[hh][0][col] + red_lds[hh][1][col]) + (red_lds[hh][2][col] + red_lds[hh][3][col]);
         const float ms = S * 0.0078125f;  // S / 128, exact scaling
         const float rms = __builtin_sqrtf(ms);
         const float C = a.q.alpha * rms;
@@ -343,45 +360,37 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
           // shifted in from the last row down.  Midpoint tests A = [y > -step],
           // B = [y >= 0], C = [y > step]; code bits B and C | (A & !B).
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            uint32_t w = 0;
+          for (int g = 3; g >= 0; --g) {  // 4 rows per add-with-carry block
+            uint64_t mk[8];
 #pragma unroll
-            for (int g = 3; g >= 0; --g) {  // 4 rows per add-with-carry block
-              uint64_t mk[8];
-#pragma unroll
-              for (int e = 3; e >= 0; --e) {
-                const float y = acc[m][4 * g + e];
-                const Sym2Masks k = sym2_masks(y > -tp, y >= tz, y > tp);
-                mk[2 * (3 - e)] = k.b1;
-                mk[2 * (3 - e) + 1] = k.b0;
-              }
-              w = shift_in8(w, mk);
+            for (int e = 3; e >= 0; --e) {
+              const float y = acc[4 * g + e];
+              const Sym2Masks k = sym2_masks(y > -tp, y >= tz, y > tp);
+              mk[2 * (3 - e)] = k.b1;
+              mk[2 * (3 - e) + 1] = k.b0;
             }
-            W2[m] = w;
+            W2 = shift_in8(W2, mk);
           }
         } else {
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+          for (int q = 0; q < 4; ++q) {
+            uint32_t r = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint32_t r = 0;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) r |= sym_code<BITS>(acc[m][4 * q + e], tp, rd) << (BITS * e);
-              asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
-              run[m][q] = r;
-            }
+            for (int e = 0; e < 4; ++e) r |= sym_code<BITS>(acc[4 * q + e], tp, rd) << (BITS * e);
+            asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
+            run[q] = r;
+          }
         }
-        if (half == 0 && lh == 0) sc_lds[col][hh] = dh;
+        if (wq == 0 && lh == 0) sc_lds[col][hh] = dh;
       } else {
         // Percentile-clipped affine quantizer, group = one 32-row tile = rows
         // split between lanes l and l^32: two smallest and two largest values by
         // IEEE totalOrder, merged across the lane pair.
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        {
           int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int32_t k = total_order_key(acc[m][i]);
+            const int32_t k = total_order_key(acc[i]);
             mn2 = min(mn2, max(mn1, k));
             mn1 = min(mn1, k);
             mx2 = max(mx2, min(mx1, k));
@@ -404,14 +413,14 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
             uint32_t r = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(acc[m][4 * q + e], zd, sd);
+              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(acc[4 * q + e], zd, sd);
               r |= c << (BITS * e);
             }
-            run[m][q] = r;
+            run[q] = r;
           }
           if (lh == 0) {
-            sc_lds[col][hh * 8 + 2 * half + m] = sh;
-            sc_lds[col][hh * 8 + 4 + 2 * half + m] = zh;
+            sc_lds[col][hh * 8 + wq] = sh;
+            sc_lds[col][hh * 8 + 4 + wq] = zh;
           }
         }
       }
@@ -422,23 +431,17 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
       if constexpr (QK == 0 && BITS == 2) {
         // bytes of {partner (selectors 4-7), own (0-3)}
         const uint32_t sel = lh ? 0x03070206u : 0x05010400u;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const uint32_t chunk = __builtin_amdgcn_perm(__shfl_xor(W2[m], 32), W2[m], sel);
-          *(uint32_t*)&rec_lds[col][hh * REC + 2 * (4 * (2 * half + m) + 2 * lh)] = chunk;
-        }
-      } else
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint32_t* rn = run[m];
+        const uint32_t chunk = __builtin_amdgcn_perm(__shfl_xor(W2, 32), W2, sel);
+        *(uint32_t*)&rec_lds[col][hh * REC + 2 * (4 * wq + 2 * lh)] = chunk;
+      } else {
+        const uint32_t* rn = run;
         const uint32_t send = lh ? (rn[0] | (rn[1] << RB)) : (rn[2] | (rn[3] << RB));
         const uint32_t recv = __shfl_xor(send, 32);
         const uint64_t p0 = recv & ((1u << RB) - 1u), p1 = recv >> RB;
         const uint64_t chunk =
             lh ? (p0 | ((uint64_t)rn[2] << RB) | (p1 << (2 * RB)) | ((uint64_t)rn[3] << (3 * RB)))
                : ((uint64_t)rn[0] | (p0 << RB) | ((uint64_t)rn[1] << (2 * RB)) | (p1 << (3 * RB)));
-        const int mt = 2 * half + m;
-        uint8_t* dst = &rec_lds[col][hh * REC + BITS * (4 * mt + 2 * lh)];
+        uint8_t* dst = &rec_lds[col][hh * REC + BITS * (4 * wq + 2 * lh)];
         if constexpr (BITS == 2) {
           *(uint32_t*)dst = (uint32_t)chunk;
         } else if constexpr (BITS == 4) {
@@ -449,10 +452,12 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
           ((uint16_t*)dst)[2] = (uint16_t)(chunk >> 32);
         }
       }
-      // The loads for later tiles have been in flight during this tile's work;
-      // wait for them here (vmcnt = 0, expcnt and lgkmcnt untouched) so that
-      // every iteration starts with no vector-memory loads outstanding.
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      next_cs();
+      // The loads for later tiles have been in flight during this tile's work.
+      // Wait here for all but the newest keys and table entries (expcnt and
+      // lgkmcnt untouched), so the stores below never queue behind them.
+      __builtin_amdgcn_s_waitcnt(kWaitTail);
+      store_pos((j + 3) & 3);  // its load was issued before the newest keys and table entries
       __syncthreads();
 
       // ---- stores: each token's HG records are contiguous in the cache row
@@ -462,7 +467,7 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
         const int n = c / CPT, k = c - n * CPT;
         const int64_t t = tbase + n;
         if (t < a.n_tokens) {
-          const int64_t row = slot_lds[buf][n];
+          const int64_t row = slot_lds[ss][n];
           if (row >= 0 && row < a.n_rows) {
             const uint4 v = *(const uint4*)&rec_lds[n][16 * k];
             *(uint4*)(a.codes + (row * a.n_heads + grp * HG) * REC + 16 * k) = v;
@@ -473,7 +478,7 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
         const int n = c / HG, jh = c - n * HG;
         const int64_t t = tbase + n;
         if (t < a.n_tokens) {
-          const int64_t row = slot_lds[buf][n];
+          const int64_t row = slot_lds[ss][n];
           if (row >= 0 && row < a.n_rows) {
             const int64_t slot = row * a.n_heads + grp * HG + jh;
             if constexpr (QK == 0) {
@@ -489,8 +494,6 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    if (has_next3) store_pos((j + 3) & 3);  // its load has completed: every path above waits for vmcnt 0
-    __syncthreads();
     if (has_next) {
       tile = next;
       buf ^= 1;
@@ -499,8 +502,8 @@ __global__ void __launch_bounds__(128 * HG) keys_kernel(const KeysArgs a) {
     return has_next;
   };
   while (true) {
-    if (!step(ra, rb, sb, sa)) break;
-    if (!step(rb, ra, sa, sb)) break;
+    if (!step(ra, rb, j % 3)) break;
+    if (!step(rb, ra, j % 3)) break;
   }
 }
 
@@ -532,10 +535,10 @@ template <int BITS, int QK, bool F32IN, int HG, bool YOUT>
 hipError_t launch_one(KeysArgs a, int cus, hipStream_t st) {
   auto k = keys_kernel<BITS, QK, F32IN, HG, YOUT>;
   const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
-  int64_t b = (int64_t)cus * resident_blocks(k, 128 * HG) / a.n_groups;
+  int64_t b = (int64_t)cus * resident_blocks(k, 256 * HG) / a.n_groups;
   b = b < 1 ? 1 : (b > n_tiles ? n_tiles : b);
   a.blocks_per_group = (int)b;
-  k<<<dim3((unsigned)(a.n_groups * b)), 128 * HG, 0, st>>>(a);
+  k<<<dim3((unsigned)(a.n_groups * b)), 256 * HG, 0, st>>>(a);
   return hipGetLastError();
 }
 
