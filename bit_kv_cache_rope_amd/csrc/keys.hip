@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
             for (int e = 3; e >= 0; --e) {
               const float y = acc[4 * g + e];
-              const Sym2Masks k = sym2_masks(y > -tp, y >= tz, y > tp);
+              const Sym2Masks k = sym2_masks(y, -tp, tz, tp);
               mk[2 * (3 - e)] = k.b1;
               mk[2 * (3 - e) + 1] = k.b0;
             }

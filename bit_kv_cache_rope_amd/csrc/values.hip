@@ -211,8 +211,7 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
           uint64_t m[16];
 #pragma unroll
           for (int e = 7; e >= 0; --e) {
-            const float f = __uint_as_float(w[e]);
-            const Sym2Masks k = sym2_masks(f > tp[u], w[e] <= ((e & 1) ? tb[u] : tbl), f > tc[u]);
+            const Sym2Masks k = sym2_masks_raw(w[e], tp[u], (e & 1) ? tb[u] : tbl, tc[u]);
             m[2 * (7 - e)] = k.b1;
             m[2 * (7 - e) + 1] = k.b0;
           }
