@@ -298,6 +298,22 @@ wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out
   rp->t0t = base + heads;
   rp->t1t = base + heads + n0;
   rp->t2t = base + heads + 2 * n0;
+  // The (cos, sin) of every position, rounded once to fp32 from the tables:
+  // 512 bytes per position, read by the key kernel one row per token.
+  e = hipMalloc((void**)&rp->cs, (size_t)max_pos * 64 * sizeof(float2));
+  if (e != hipSuccess) {
+    (void)hipFree(rp->d_block);
+    delete rp;
+    return fail(WUSHKV_ERR_OOM, "hipMalloc for the cos/sin table failed");
+  }
+  e = wushkv::launch_build_cs_table(rp, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(rp->cs);
+    (void)hipFree(rp->d_block);
+    delete rp;
+    return hip_fail(e, "cos/sin table build");
+  }
   *out = rp;
   return WUSHKV_OK;
 }
@@ -307,6 +323,7 @@ wushkv_status wushkv_rope_destroy(wushkv_rope* r) {
   int prev = -1;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(r->device);
+  (void)hipFree(r->cs);
   (void)hipFree(r->d_block);
   if (prev >= 0) (void)hipSetDevice(prev);
   delete r;
@@ -340,7 +357,7 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
   if (dev != T_k->device || dev != rope->device)
     return fail(WUSHKV_ERR_INVALID_ARG, "handles belong to another device than the current one");
   const int cus = wushkv::device_cu_count(dev);
-  const int64_t n_tiles = (n_tokens + 31) / 32;
+  const int64_t n_tiles = (n_tokens + 63) / 64;
   const int hg = choose_hg(n_tiles, n_heads, cus, k_dtype == WUSHKV_F32 ? 2 : 4);
   wushkv::KeysArgs a{};
   a.K = K;
@@ -350,12 +367,7 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
   a.pos = pos;
   a.max_pos = rope->max_pos;
   a.T = T_k->d_swz;
-  a.t0 = rope->t0;
-  a.t1 = rope->t1;
-  a.t2 = rope->t2;
-  a.t0t = rope->t0t;
-  a.t1t = rope->t1t;
-  a.t2t = rope->t2t;
+  a.cs = rope->cs;
   if (out && !y_out) {
     a.codes = (uint8_t*)out->codes;
     a.scales = (uint16_t*)out->scales;
@@ -474,8 +486,8 @@ wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* 
   if (n < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return WUSHKV_OK;
   if (!pos || !cs_out) return fail(WUSHKV_ERR_INVALID_ARG, "pos and cs_out must be set");
-  hipError_t e = wushkv::launch_rope_cos_sin(rope, pos, n, cs_out, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "cos/sin kernel launch");
+  hipError_t e = wushkv::launch_gather_cs(rope, pos, n, cs_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cos/sin gather launch");
   return WUSHKV_OK;
 }
 

@@ -30,6 +30,7 @@ struct wushkv_rope {
   const double2* t0t;     // tails of the three
   const double2* t1t;
   const double2* t2t;
+  float2* cs;             // [max_pos][64] (cos, sin) in fp32, built from the tables above
 };
 
 namespace wushkv {
@@ -51,12 +52,7 @@ struct KeysArgs {
   const int32_t* pos;
   int32_t max_pos;
   const void* T;   // swizzled bf16
-  const double2* t0;
-  const double2* t1;
-  const double2* t2;
-  const double2* t0t;
-  const double2* t1t;
-  const double2* t2t;
+  const float2* cs;  // [max_pos][64] (cos, sin) table of the RoPE handle
   uint8_t* codes;
   uint16_t* scales;
   uint16_t* zeros;
@@ -109,7 +105,11 @@ hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_gr
 hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int n_blocks,
                           hipStream_t stream);
-hipError_t launch_rope_cos_sin(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs,
-                               hipStream_t stream);
+// Fills r->cs for every position below r->max_pos (exact: the certified
+// double path, double-double where it cannot certify).
+hipError_t launch_build_cs_table(const wushkv_rope* r, hipStream_t stream);
+// cs_out[n][64][2] = r->cs[clamp(pos[n])] (the table the key kernel reads).
+hipError_t launch_gather_cs(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs_out,
+                            hipStream_t stream);
 
 }  // namespace wushkv

@@ -6,28 +6,28 @@
 // method and deployment paragraphs; cere-bro post "WUSH-KV: 2-bit KV-Cache
 // Quantization with Data-Adaptive Transforms", Gaps).
 //
-// Work decomposition.  A block owns HG heads and walks 32-token tiles
+// Work decomposition.  A block owns HG heads and walks 64-token tiles
 // (persistent: tile = first, first + blocks_per_group, ...).  Four waves serve
 // each head; wave wq keeps rows [32 wq, 32 wq + 32) of T~ (32 VGPRs of A
-// operands, loaded once) and computes those output rows for the tile with 8
-// v_mfma_f32_32x32x16_bf16.  The B operand is the tile's rotated keys: lane l
-// holds token l%32 and, for k step s, channels 16s + 8(l/32) + 0..7, so the
-// RoPE partners (i, i+64) sit in one lane (k steps s and s+4).  Wave wq loads
-// and rotates k step wq and its partner, and the four waves share their bf16
-// operands through LDS.  At under 128 VGPRs, four waves per SIMD are resident.
+// operands, loaded once) and computes those output rows for the tile's two
+// 32-token column blocks with 16 v_mfma_f32_32x32x16_bf16 (two independent
+// accumulation chains).  The B operand is the rotated keys: lane l holds
+// token l%32 of a column block and, for k step s, channels 16s + 8(l/32) +
+// 0..7, so the RoPE partners (i, i+64) sit in one lane (k steps s and s+4).
+// Wave wq loads and rotates k step wq and its partner for both column blocks,
+// and the four waves of a head share their bf16 operands through LDS.  At
+// under 128 VGPRs four waves are resident per SIMD.
 //
-// cos/sin for a tile are computed once per block into LDS; the two small
-// angle tables live in LDS for the whole launch, and the high-angle table
-// entries (and slot rows) are loaded a tile ahead of their use, the positions
-// three tiles ahead, so that no computation waits on a fresh load.
+// cos/sin come from the RoPE handle's table (one 512-byte fp32 row per
+// position, exact): each wave copies a few of the tile's rows straight from
+// global memory into LDS (global_load_lds), a tile ahead of their use.
 //
-// Per-tile pipeline.  Vector-memory loads retire in order, so each iteration
-// issues the next tile's position and keys first and its table entries last,
-// and ends with one explicit wait for all but those table entries before its
-// stores; the loop is unrolled by two over two key register sets, so the
-// compiler's own waits never cover the key prefetch.  Packed records and
-// scales are staged in LDS and written as whole 16-byte chunks (a head
-// group's records of a token are contiguous in the cache row).
+// Per-tile pipeline, three barriers: [rows and positions for later tiles;
+// RoPE -> LDS; the next tile's keys into the registers RoPE freed] B1
+// [cos/sin copies for the next tile; MFMA; sums of squares -> LDS] B2
+// [scale(s), codes, records -> LDS; wait for every load] B3 [stores].
+// Packed records and scales are staged in LDS and written as whole 16-byte
+// chunks (a head group's records of a token are contiguous in the cache row).
 #include "device_common.h"
 #include "internal.h"
 
@@ -37,7 +37,8 @@ namespace wushkv {
 
 namespace {
 
-constexpr int kTile = 32;
+constexpr int kTile = 64;      // tokens per tile
+constexpr int kNB = 2;         // 32-token MFMA column blocks per tile
 constexpr int kCsStride = 66;  // float2 per token row of the cos/sin tile (64 + 2 pad)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -48,47 +49,51 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// The two k steps a wave loads and rotates: wq (channels i < 64) and its
-// partner wq + 4 (channels i + 64).
+// The keys a wave loads and rotates for one tile: for each column block nb,
+// k step wq (channels i < 64) and its partner wq + 4 (channels i + 64).
 template <bool F32IN>
 struct RawKeys;
 template <>
-struct RawKeys<false> {  // bf16: 8 channels per 16-byte load, 2 k steps
-  uint4 v[2];
+struct RawKeys<false> {  // bf16: 8 channels per 16-byte load; [nb][j]
+  uint4 v[2 * kNB];
 };
 template <>
 struct RawKeys<true> {   // fp32: 8 channels = two 16-byte loads
-  float4 v[4];
+  float4 v[4 * kNB];
 };
 
 // Loads are unconditional: a token past the end reads the last token's row (its
 // results are never stored), so the compiler never has to cover a
 // conditionally issued load with its waits.
 template <bool F32IN>
-__device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, const KeysArgs& a, int64_t tok, int h, int lh,
+__device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, const KeysArgs& a, int64_t tok0, int h, int lh,
                                           int wq) {
-  tok = tok < a.n_tokens ? tok : a.n_tokens - 1;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int s = wq + 4 * j;
-    if constexpr (F32IN) {
-      const float* base = (const float*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh;
-      r.v[2 * j] = *(const float4*)base;
-      r.v[2 * j + 1] = *(const float4*)(base + 4);
-    } else {
-      r.v[j] = *(const uint4*)((const uint16_t*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh);
+  for (int nb = 0; nb < kNB; ++nb) {
+    int64_t tok = tok0 + 32 * nb;
+    tok = tok < a.n_tokens ? tok : a.n_tokens - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = wq + 4 * j;
+      if constexpr (F32IN) {
+        const float* base = (const float*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh;
+        r.v[4 * nb + 2 * j] = *(const float4*)base;
+        r.v[4 * nb + 2 * j + 1] = *(const float4*)(base + 4);
+      } else {
+        r.v[2 * nb + j] = *(const uint4*)((const uint16_t*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh);
+      }
     }
   }
 }
 
 template <bool F32IN>
-__device__ __forceinline__ void unpack8(const RawKeys<F32IN>& r, int j, float* x) {
+__device__ __forceinline__ void unpack8(const RawKeys<F32IN>& r, int nb, int j, float* x) {
   if constexpr (F32IN) {
-    const float4 p = r.v[2 * j], q = r.v[2 * j + 1];
+    const float4 p = r.v[4 * nb + 2 * j], q = r.v[4 * nb + 2 * j + 1];
     x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
     x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
   } else {
-    const uint4 p = r.v[j];
+    const uint4 p = r.v[2 * nb + j];
     x[0] = bf16lo_to_f32(p.x); x[1] = bf16hi_to_f32(p.x);
     x[2] = bf16lo_to_f32(p.y); x[3] = bf16hi_to_f32(p.y);
     x[4] = bf16lo_to_f32(p.z); x[5] = bf16hi_to_f32(p.z);
@@ -96,124 +101,79 @@ __device__ __forceinline__ void unpack8(const RawKeys<F32IN>& r, int j, float* x
   }
 }
 
-// High-angle table entries and slot rows of one future tile.
-template <int PPT>
-struct CsStage {
-  double2 hi[PPT];
-  int64_t slot;
-};
-
 template <int BITS, int QK, bool F32IN, int HG, bool YOUT>
 __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   constexpr int NT = 256 * HG;
   constexpr int NW = NT / 64;
+  constexpr int TPW = kTile / NW;  // cos/sin rows each wave copies per tile
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
   constexpr int RECROW = HG * REC + 16;  // LDS row of one token's records (+16 B pad)
   constexpr int NSC = QK ? 8 : 1;        // fp16 values per (token, head): sym 1; affine 4 + 4
   constexpr int RB = 4 * BITS;           // bits in a run of 4 codes
-  constexpr int PPT = kTile * kPairs / NT;  // cos/sin pairs per thread per tile
 
-  __shared__ __align__(16) double2 tab_lds[2][32][kPairs];  // heads of the p0 and p1 angle tables
-  __shared__ __align__(16) float2 cs_lds[2][kTile][kCsStride];
-  __shared__ __align__(16) bf16x8 xb_lds[HG][8][64];        // rotated operands shared by a head's four waves
-  __shared__ int64_t slot_lds[3][kTile];  // cache row per token, tile j in slot j % 3
-  __shared__ int pos_lds[4][kTile];
+  __shared__ __align__(16) float2 cs_lds[kTile][kCsStride];   // cos/sin rows of the tile being rotated
+  __shared__ __align__(16) bf16x8 xb_lds[HG][kNB][8][64];     // rotated operands shared by a head's waves
+  __shared__ int64_t slot_lds[2][kTile];                       // cache row per token, tile j in slot j & 1
   __shared__ float red_lds[HG][4][kTile];
   __shared__ __align__(16) uint8_t rec_lds[kTile][RECROW];
   __shared__ uint16_t sc_lds[kTile][HG * NSC];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The lane index is re-derived at every tile (see the top of `step`), so
+  // the per-lane addresses are recomputed there rather than held in
+  // registers across the loop.
+  int lane = threadIdx.x & 63, lh = lane >> 5, col = lane & 31;
   // Four waves per head: wave wq holds rows 32 wq .. 32 wq + 31 of T~ and
   // rotates the RoPE pairs of k step wq (channels 16 wq + 8 (l / 32) + 0..7
   // and their partners 64 higher).
-  const int hh = wave >> 2, wq = wave & 3, lh = lane >> 5, col = lane & 31;
+  const int hh = wave_u >> 2, wq = wave_u & 3;
   const int grp = blockIdx.x % a.n_groups;
   const int64_t first_tile = blockIdx.x / a.n_groups;
   const int h = grp * HG + hh;
   const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
   if (first_tile >= n_tiles) return;  // uniform over the block
   const int64_t tile_step = a.blocks_per_group;
-
-  // Tiles are visited as j = 0, 1, 2, ...: tile(j) = first_tile + j * tile_step.
-  // Thread (wave w, lane i) computes cos/sin pair i of tokens w + NW k,
-  // k < PPT, so every position it reads is wave-uniform.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int64_t last_tok = a.n_tokens - 1;
-  int pos_r = 0;
-  auto load_pos = [&](int64_t tile) __attribute__((always_inline)) {
-    const int64_t tok = tile * kTile + (tid & (kTile - 1));
-    pos_r = a.pos[tok < last_tok ? tok : last_tok];
+
+  // Positions of the TPW tokens whose cos/sin rows this wave copies (tokens
+  // TPW*w + k of the tile): lane k loads token k's (clamped) position.
+  auto load_posv = [&](int64_t t) __attribute__((always_inline)) -> int {
+    int64_t tok = t * kTile + TPW * wave_u + (lane % TPW);
+    tok = tok < last_tok ? tok : last_tok;
+    return a.pos[tok];
   };
-  auto store_pos = [&](int pb) __attribute__((always_inline)) {
-    if (tid < kTile) {
-      const int p = pos_r;
-      pos_lds[pb][tid] = p < 0 ? 0 : (p >= a.max_pos ? a.max_pos - 1 : p);
-    }
-  };
-  // Position of token n of the tile in pos_lds slot pb (uniform over the wave).
-  auto pos_of = [&](int pb, int n) __attribute__((always_inline)) {
-    return __builtin_amdgcn_readfirstlane(pos_lds[pb][n]);
-  };
-  auto issue_cs = [&](CsStage<PPT>& st, int64_t tile, int pb) __attribute__((always_inline)) {
+  // Copy the tile's cos/sin rows into cs_lds: row k of this wave comes from
+  // the table row of its position, 32 lanes x 16 bytes straight into LDS.
+  auto copy_cs = [&](int posv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) st.hi[k] = a.t2[(pos_of(pb, wave_u + NW * k) >> 10) * kPairs + lane];
-    // Issued whether or not there are slots (a dummy 8-byte read of T~
-    // otherwise), so every iteration issues the same loads in the same order.
-    const int64_t tok = tile * kTile + (tid & (kTile - 1));
-    st.slot = a.slots ? a.slots[tok < last_tok ? tok : last_tok] : *(const int64_t*)a.T;
-  };
-  // cos/sin of the next tile into cs_lds[buf]: the fast path for every pair
-  // (returns the pairs it cannot certify), the rare rest redone in
-  // double-double in a loop that is not unrolled (its loads are issued only
-  // when such a pair occurs).
-  auto finish_cs_fast = [&](const CsStage<PPT>& st, int pb, int buf) __attribute__((always_inline)) -> uint32_t {
-    uint32_t bad = 0;
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int n = wave_u + NW * k;
-      const int p = pos_of(pb, n);
-      const double2 M = tab_lds[1][(p >> 5) & 31][lane], B = tab_lds[0][p & 31][lane];
-      bool exact;
-      cs_lds[buf][n][lane] = rope_cos_sin_fast(st.hi[k], M, B, exact);
-      bad |= (uint32_t)!exact << k;
-    }
-    return bad;
-  };
-  auto finish_cs_slow = [&](uint32_t bad, int pb, int buf) __attribute__((always_inline)) {
-    if (__builtin_expect(bad != 0, 0)) {
-#pragma unroll 1
-      for (int k = 0; k < PPT; ++k) {
-        if ((bad >> k) & 1) {
-          const int n = wave_u + NW * k;
-          const int p = pos_lds[pb][n];
-          const int p2 = p >> 10, p1 = (p >> 5) & 31, p0 = p & 31;
-          cs_lds[buf][n][lane] =
-              rope_cos_sin_slow(a.t2[p2 * kPairs + lane], a.t2t[p2 * kPairs + lane], tab_lds[1][p1][lane],
-                                a.t1t[p1 * kPairs + lane], tab_lds[0][p0][lane], a.t0t[p0 * kPairs + lane]);
-        }
+    for (int k = 0; k < TPW; ++k) {
+      int p = __builtin_amdgcn_readlane(posv, k);
+      p = p < 0 ? 0 : (p >= a.max_pos ? a.max_pos - 1 : p);
+      if (lane < 32) {
+        const float2* src = a.cs + (int64_t)p * kPairs + 2 * lane;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)&cs_lds[TPW * wave_u + k][0], 16,
+                                         0, 0);
       }
     }
   };
-  auto put_slot = [&](const CsStage<PPT>& st, int64_t tile, int sb) __attribute__((always_inline)) {
-    if (tid < kTile) slot_lds[sb][tid] = a.slots ? st.slot : tile * kTile + tid;
+  // Cache rows of a tile's tokens: wave 0, one per lane (a clamped token past
+  // the end reads the last token's slot; its row is never used).
+  auto load_rows = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
+    const int64_t tok = t * kTile + lane;
+    if (!a.slots) return tok;
+    return a.slots[tok < last_tok ? tok : last_tok];
   };
 
-  RawKeys<F32IN> ra, rb;
-  CsStage<PPT> st;
+  RawKeys<F32IN> r;  // this tile's keys until RoPE has read them, then the next tile's
   int64_t tile = first_tile;
-  int buf = 0, j = 0;
-  // Prologue: every load that depends on nothing is issued up front (the
-  // first two tiles' keys, three tiles' positions, T~, the angle tables), so
-  // their latencies overlap; only positions -> table entries -> cos/sin is a
-  // chain.  Clamped reads past the end keep every address valid.
-  load_keys<F32IN>(ra, a, tile * kTile + col, h, lh, wq);
-  int pos_d[3];
-#pragma unroll
-  for (int d = 0; d < 3; ++d) {
-    load_pos(tile + d * tile_step);
-    pos_d[d] = pos_r;
-  }
+  // Prologue: the first tile's keys, rows, positions and cos/sin; T~.
+  load_keys<F32IN>(r, a, tile * kTile + col, h, lh, wq);
+  int64_t row_r = 0;
+  if (wave_u == 0) row_r = load_rows(tile);
+  const int posv0 = load_posv(tile);
+  int posv = load_posv(tile + tile_step);  // positions of the next tile's rows
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
   bf16x8 A[8];
   {
@@ -221,54 +181,33 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
   }
-
-  // Angle tables t0 (p0) and t1 (p1) into LDS for the whole launch.
-  for (int e = tid; e < 2 * 32 * kPairs; e += NT) {
-    const int t = e / (32 * kPairs), r = e - t * 32 * kPairs;
-    tab_lds[t][r / kPairs][r % kPairs] = (t == 0 ? a.t0 : a.t1)[r];
-  }
-
-#pragma unroll
-  for (int d = 0; d < 3; ++d) {
-    pos_r = pos_d[d];
-    store_pos(d);
-  }
-  if (tid < kTile) pos_lds[3][tid] = 0;  // a valid position in the fourth slot
-  __syncthreads();  // angle tables and the first three tiles' positions
-  issue_cs(st, tile, 0);
-  finish_cs_slow(finish_cs_fast(st, 0, 0), 0, 0);
-  put_slot(st, tile, 0);
-  issue_cs(st, tile + tile_step, 1);  // consumed in the first iteration
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (PPT + 1));  // all but those table entries
+  copy_cs(posv0);
+  if (wave_u == 0) slot_lds[0][lane] = row_r;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
   __syncthreads();
 
-  // One tile per call (tile j; ss = j % 3).  `cur` holds this tile's keys and
-  // `nxt` receives the next tile's.  `st` holds the next tile's table
-  // entries; they are consumed after this tile's quantizer, and `st` then
-  // receives the entries of the tile after next.  Loads for later tiles are
-  // issued unconditionally (clamped addresses past the end), so every
-  // iteration issues the same loads in the same order: position, keys, table
-  // entries + slot row.  Waiting for all but the table loads before the
-  // stores leaves exactly those in flight.  Three barriers per tile.
-  // Unrolled by two over the two key sets.
-  constexpr int kWaitTail = 0x0F70 | (PPT + 1);
-  auto step = [&](RawKeys<F32IN>& cur, RawKeys<F32IN>& nxt, int ss)
-      __attribute__((always_inline)) -> bool {
-    const int64_t next = tile + tile_step, next2 = next + tile_step, next3 = next2 + tile_step;
+  // One tile per call (par = the tile's ordinal & 1).
+  f32x16 acc[kNB];
+  auto step = [&](int par) __attribute__((always_inline)) -> bool {
+    asm volatile("" : "+v"(lane));
+    lh = lane >> 5;
+    col = lane & 31;
+    const int tid = 64 * wave_u + lane;
+    const int64_t next = tile + tile_step;
     const bool has_next = next < n_tiles;
-    load_pos(next3);
-    __builtin_amdgcn_sched_barrier(0);
-    load_keys<F32IN>(nxt, a, next * kTile + col, h, lh, wq);
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- rows of the next tile and positions of the tile after (clamped
+    // past the end)
+    if (wave_u == 0) row_r = load_rows(next);
+    const int posv_n = load_posv(next + tile_step);
 
-    // ---- RoPE (rotate-half, pairs (i, i+64)) of this wave's pairs -> bf16 operands
-    bf16x8 Bop[8];
-    {
+    // ---- RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
       const int s = wq;  // k step of channels i; the partners are in k step s + 4
       float ka[8], kb[8];
-      unpack8<F32IN>(cur, 0, ka);
-      unpack8<F32IN>(cur, 1, kb);
-      const float4* csp = (const float4*)&cs_lds[buf][col][16 * s + 8 * lh];
+      unpack8<F32IN>(r, nb, 0, ka);
+      unpack8<F32IN>(r, nb, 1, kb);
+      const float4* csp = (const float4*)&cs_lds[32 * nb + col][16 * s + 8 * lh];
       float c[8], sn[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -283,114 +222,143 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         xa[e] = __builtin_fmaf(ka[e], c[e], -bs);
         xb[e] = __builtin_fmaf(kb[e], c[e], as);
       }
-      xb_lds[hh][s][lane] = pack8(xa);
-      xb_lds[hh][s + 4][lane] = pack8(xb);
+      xb_lds[hh][nb][s][lane] = pack8(xa);
+      xb_lds[hh][nb][s + 4][lane] = pack8(xb);
     }
-    __syncthreads();
-    // All eight operands come from LDS (each wave of the head wrote two).
-#pragma unroll
-    for (int s = 0; s < 8; ++s) Bop[s] = xb_lds[hh][s][lane];
+    // ---- the next tile's keys, into the registers RoPE has just consumed
+    load_keys<F32IN>(r, a, next * kTile + col, h, lh, wq);
+    __syncthreads();  // B1: operands in LDS; everyone is done with cs_lds
 
-    // ---- y = T~ x~ for this wave's 32 rows (fp32 accumulate)
-    f32x16 acc = {};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bop[s], acc, 0, 0, 0);
+    // ---- the next tile's cos/sin rows (in flight until the wait before B3)
+    copy_cs(posv);
 
-    // The next tile's cos/sin (computed for a tile past the end too: harmless,
-    // into the buffer nobody reads), then the table entries of the tile after.
-    auto next_cs = [&]() __attribute__((always_inline)) {
-      const uint32_t bad = finish_cs_fast(st, (j + 1) & 3, buf ^ 1);
-      finish_cs_slow(bad, (j + 1) & 3, buf ^ 1);
-      put_slot(st, next, ss == 2 ? 0 : ss + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue_cs(st, next2, (j + 2) & 3);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    const int64_t tok = tile * kTile + col;
+    // ---- y = T~ x~ for this wave's 32 rows and both column blocks
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[nb] = (f32x16){};
+    // B operands one k step ahead of the MFMAs that use them; the scheduling
+    // barriers keep the compiler from hoisting all sixteen reads (64 VGPRs).
+    {
+      bf16x8 bc[kNB], bn[kNB];
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) bc[nb] = xb_lds[hh][nb][0][lane];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s < 7) {
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) bn[nb] = xb_lds[hh][nb][s + 1][lane];
+        }
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], bc[nb], acc[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) bc[nb] = bn[nb];
+      }
+    }
 
     if constexpr (YOUT) {
-      next_cs();
-      if (tok < a.n_tokens) {
-        float* yo = a.y_out + (tok * a.n_heads + h) * kD;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 32 * wq + 8 * jj + 4 * lh;
-          *(float4*)(yo + r) = make_float4(acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]);
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int64_t tok = tile * kTile + 32 * nb + col;
+        if (tok < a.n_tokens) {
+          float* yo = a.y_out + (tok * a.n_heads + h) * kD;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * wq + 8 * q + 4 * lh;
+            *(float4*)(yo + r) = make_float4(acc[nb][4 * q], acc[nb][4 * q + 1], acc[nb][4 * q + 2],
+                                             acc[nb][4 * q + 3]);
+          }
         }
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      store_pos((j + 3) & 3);
-      __syncthreads();
+      __syncthreads();  // B2 (kept so that every tile passes three barriers)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_r;
+      __syncthreads();  // B3
     } else {
-      // Output element acc[i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of token `col`.
-      // run[q] packs the codes of acc[4q .. 4q+3] (4 consecutive rows), LSB first.
-      uint32_t run[4];
-      uint32_t W2 = 0;  // 2-bit symmetric: the whole word of codes
+      // Output element acc[nb][i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of
+      // token 32*nb + col.  run[nb][q] packs the codes of acc[nb][4q .. 4q+3]
+      // (4 consecutive rows), LSB first.
+      uint32_t run[kNB][4];
+      uint32_t W2[kNB] = {};  // 2-bit symmetric: whole words of codes
       if constexpr (QK == 0) {
         // Sum of squares as the contiguous pairwise tree over rows 0..127:
         // runs of 4 in-lane, pairs of runs across lanes l and l^32, the 32
         // rows of this wave, then the four waves' sums ((0 + 1) + (2 + 3)).
-        float P8[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float q0 = acc[4 * q] * acc[4 * q];
-          const float q1 = acc[4 * q + 1] * acc[4 * q + 1];
-          const float q2 = acc[4 * q + 2] * acc[4 * q + 2];
-          const float q3 = acc[4 * q + 3] * acc[4 * q + 3];
-          const float p4 = (q0 + q1) + (q2 + q3);
-          P8[q] = p4 + __shfl_xor(p4, 32);
+        for (int nb = 0; nb < kNB; ++nb) {
+          float P8[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float q0 = acc[nb][4 * q] * acc[nb][4 * q];
+            const float q1 = acc[nb][4 * q + 1] * acc[nb][4 * q + 1];
+            const float q2 = acc[nb][4 * q + 2] * acc[nb][4 * q + 2];
+            const float q3 = acc[nb][4 * q + 3] * acc[nb][4 * q + 3];
+            const float p4 = (q0 + q1) + (q2 + q3);
+            P8[q] = p4 + __shfl_xor(p4, 32);
+          }
+          const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
+          if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
         }
-        const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
-        if (lh == 0) red_lds[hh][wq][col] = P32;
-        __syncthreads();
-        const float S = (red_lds[hh][0][col] + red_lds[hh][1][col]) + (red_lds[hh][2][col] + red_lds[hh][3][col]);
+        __syncthreads();  // B2
+        // One step per lane for token tt = 32 lh + col (the lane pair l, l^32
+        // covers both column blocks); each block's step then comes from the
+        // lane that computed it.
+        const int tt = 32 * lh + col;
+        const float S = (red_lds[hh][0][tt] + red_lds[hh][1][tt]) + (red_lds[hh][2][tt] + red_lds[hh][3][tt]);
         const float ms = S * 0.0078125f;  // S / 128, exact scaling
         const float rms = __builtin_sqrtf(ms);
         const float C = a.q.alpha * rms;
         const float twoC = 2.0f * C;
         const float d32 = twoC / (float)(L - 1);
         const uint16_t dh = f16_sat_bits(d32);
-        const float delta = f16_bits_to_f32(dh);
-        // A zero step becomes +inf (threshold / step) so every code comes out L/2.
-        const float tp = delta == 0.0f ? __builtin_inff() : delta;
-        const float tz = delta == 0.0f ? -__builtin_inff() : 0.0f;
-        const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
-        if constexpr (BITS == 2) {
-          // W[m]: the lane's 16 codes of m-tile m, run q (4 rows) in byte q,
-          // shifted in from the last row down.  Midpoint tests A = [y > -step],
-          // B = [y >= 0], C = [y > step]; code bits B and C | (A & !B).
+        if (wq == 0) sc_lds[tt][hh] = dh;
+        const float d_own = f16_bits_to_f32(dh);
+        const float d_oth = __shfl_xor(d_own, 32);
 #pragma unroll
-          for (int g = 3; g >= 0; --g) {  // 4 rows per add-with-carry block
-            uint64_t mk[8];
+        for (int nb = 0; nb < kNB; ++nb) {
+          const float delta = (lh == nb) ? d_own : d_oth;
+          // A zero step becomes +inf (threshold / step) so every code comes out L/2.
+          const float tp = delta == 0.0f ? __builtin_inff() : delta;
+          if constexpr (BITS == 2) {
+            const float tz = delta == 0.0f ? -__builtin_inff() : 0.0f;
+            // W2[nb]: the lane's 16 codes of the block, run q (4 rows) in byte
+            // q, shifted in from the last row down.  Midpoint tests
+            // A = [y > -step], B = [y >= 0], C = [y > step]; code bits B and
+            // B ? C : A.
 #pragma unroll
-            for (int e = 3; e >= 0; --e) {
-              const float y = acc[4 * g + e];
-              const Sym2Masks k = sym2_masks(y, -tp, tz, tp);
-              mk[2 * (3 - e)] = k.b1;
-              mk[2 * (3 - e) + 1] = k.b0;
+            for (int g = 3; g >= 0; --g) {  // 4 rows per add-with-carry block
+              uint64_t mk[8];
+#pragma unroll
+              for (int e = 3; e >= 0; --e) {
+                const Sym2Masks k = sym2_masks(acc[nb][4 * g + e], -tp, tz, tp);
+                mk[2 * (3 - e)] = k.b1;
+                mk[2 * (3 - e) + 1] = k.b0;
+              }
+              W2[nb] = shift_in8(W2[nb], mk);
             }
-            W2 = shift_in8(W2, mk);
-          }
-        } else {
+          } else {
+            const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t r = 0;
+            for (int q = 0; q < 4; ++q) {
+              uint32_t r = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r |= sym_code<BITS>(acc[4 * q + e], tp, rd) << (BITS * e);
-            asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
-            run[q] = r;
+              for (int e = 0; e < 4; ++e) r |= sym_code<BITS>(acc[nb][4 * q + e], tp, rd) << (BITS * e);
+              asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
+              run[nb][q] = r;
+            }
           }
         }
-        if (wq == 0 && lh == 0) sc_lds[col][hh] = dh;
       } else {
-        // Percentile-clipped affine quantizer, group = one 32-row tile = rows
-        // split between lanes l and l^32: two smallest and two largest values by
-        // IEEE totalOrder, merged across the lane pair.
-        {
+        __syncthreads();  // B2 (the affine groups are this wave's own rows)
+        // Percentile-clipped affine quantizer, group = this wave's 32 rows of
+        // a token, split between lanes l and l^32: two smallest and two
+        // largest values by IEEE totalOrder, merged across the lane pair.
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
           int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int32_t k = total_order_key(acc[i]);
+            const int32_t k = total_order_key(acc[nb][i]);
             mn2 = min(mn2, max(mn1, k));
             mn1 = min(mn1, k);
             mx2 = max(mx2, min(mx1, k));
@@ -413,61 +381,60 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             uint32_t r = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(acc[4 * q + e], zd, sd);
+              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(acc[nb][4 * q + e], zd, sd);
               r |= c << (BITS * e);
             }
-            run[q] = r;
+            run[nb][q] = r;
           }
           if (lh == 0) {
-            sc_lds[col][hh * 8 + wq] = sh;
-            sc_lds[col][hh * 8 + 4 + wq] = zh;
+            sc_lds[32 * nb + col][hh * 8 + wq] = sh;
+            sc_lds[32 * nb + col][hh * 8 + 4 + wq] = zh;
           }
         }
       }
 
       // ---- pack: runs of 4 codes -> 16 contiguous rows per lane -> LDS record row.
-      // Lane l (lh = 0) writes rows 0-15 of the m-tile: its runs 0, 1 interleaved
-      // with those of lane l + 32; lane l + 32 writes rows 16-31 likewise.
-      if constexpr (QK == 0 && BITS == 2) {
-        // bytes of {partner (selectors 4-7), own (0-3)}
-        const uint32_t sel = lh ? 0x03070206u : 0x05010400u;
-        const uint32_t chunk = __builtin_amdgcn_perm(__shfl_xor(W2, 32), W2, sel);
-        *(uint32_t*)&rec_lds[col][hh * REC + 2 * (4 * wq + 2 * lh)] = chunk;
-      } else {
-        const uint32_t* rn = run;
-        const uint32_t send = lh ? (rn[0] | (rn[1] << RB)) : (rn[2] | (rn[3] << RB));
-        const uint32_t recv = __shfl_xor(send, 32);
-        const uint64_t p0 = recv & ((1u << RB) - 1u), p1 = recv >> RB;
-        const uint64_t chunk =
-            lh ? (p0 | ((uint64_t)rn[2] << RB) | (p1 << (2 * RB)) | ((uint64_t)rn[3] << (3 * RB)))
-               : ((uint64_t)rn[0] | (p0 << RB) | ((uint64_t)rn[1] << (2 * RB)) | (p1 << (3 * RB)));
-        uint8_t* dst = &rec_lds[col][hh * REC + BITS * (4 * wq + 2 * lh)];
-        if constexpr (BITS == 2) {
-          *(uint32_t*)dst = (uint32_t)chunk;
-        } else if constexpr (BITS == 4) {
-          *(uint64_t*)dst = chunk;
+      // Lane l (lh = 0) writes rows 0-15 of the block: its runs 0, 1
+      // interleaved with those of lane l + 32; lane l + 32 writes rows 16-31.
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        uint8_t* dst = &rec_lds[32 * nb + col][hh * REC + BITS * (4 * wq + 2 * lh)];
+        if constexpr (QK == 0 && BITS == 2) {
+          // bytes of {partner (selectors 4-7), own (0-3)}
+          const uint32_t sel = lh ? 0x03070206u : 0x05010400u;
+          *(uint32_t*)dst = __builtin_amdgcn_perm(__shfl_xor(W2[nb], 32), W2[nb], sel);
         } else {
-          ((uint16_t*)dst)[0] = (uint16_t)chunk;
-          ((uint16_t*)dst)[1] = (uint16_t)(chunk >> 16);
-          ((uint16_t*)dst)[2] = (uint16_t)(chunk >> 32);
+          const uint32_t* rn = run[nb];
+          const uint32_t send = lh ? (rn[0] | (rn[1] << RB)) : (rn[2] | (rn[3] << RB));
+          const uint32_t recv = __shfl_xor(send, 32);
+          const uint64_t p0 = recv & ((1u << RB) - 1u), p1 = recv >> RB;
+          const uint64_t chunk =
+              lh ? (p0 | ((uint64_t)rn[2] << RB) | (p1 << (2 * RB)) | ((uint64_t)rn[3] << (3 * RB)))
+                 : ((uint64_t)rn[0] | (p0 << RB) | ((uint64_t)rn[1] << (2 * RB)) | (p1 << (3 * RB)));
+          if constexpr (BITS == 2) {
+            *(uint32_t*)dst = (uint32_t)chunk;
+          } else if constexpr (BITS == 4) {
+            *(uint64_t*)dst = chunk;
+          } else {
+            ((uint16_t*)dst)[0] = (uint16_t)chunk;
+            ((uint16_t*)dst)[1] = (uint16_t)(chunk >> 16);
+            ((uint16_t*)dst)[2] = (uint16_t)(chunk >> 32);
+          }
         }
       }
-      next_cs();
-      // The loads for later tiles have been in flight during this tile's work.
-      // Wait here for all but the newest keys and table entries (expcnt and
-      // lgkmcnt untouched), so the stores below never queue behind them.
-      __builtin_amdgcn_s_waitcnt(kWaitTail);
-      store_pos((j + 3) & 3);  // its load was issued before the newest keys and table entries
-      __syncthreads();
+      // Every load of this wave has landed (next keys, rows, positions, the
+      // cos/sin copies), so the stores below never queue behind a load.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_r;
+      __syncthreads();  // B3
 
       // ---- stores: each token's HG records are contiguous in the cache row
       const int64_t tbase = tile * kTile;
       constexpr int CPT = HG * BITS;  // 16-byte chunks per token
       for (int c = tid; c < kTile * CPT; c += NT) {
         const int n = c / CPT, k = c - n * CPT;
-        const int64_t t = tbase + n;
-        if (t < a.n_tokens) {
-          const int64_t row = slot_lds[ss][n];
+        if (tbase + n < a.n_tokens) {
+          const int64_t row = slot_lds[par][n];
           if (row >= 0 && row < a.n_rows) {
             const uint4 v = *(const uint4*)&rec_lds[n][16 * k];
             *(uint4*)(a.codes + (row * a.n_heads + grp * HG) * REC + 16 * k) = v;
@@ -476,9 +443,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       }
       for (int c = tid; c < kTile * HG; c += NT) {
         const int n = c / HG, jh = c - n * HG;
-        const int64_t t = tbase + n;
-        if (t < a.n_tokens) {
-          const int64_t row = slot_lds[ss][n];
+        if (tbase + n < a.n_tokens) {
+          const int64_t row = slot_lds[par][n];
           if (row >= 0 && row < a.n_rows) {
             const int64_t slot = row * a.n_heads + grp * HG + jh;
             if constexpr (QK == 0) {
@@ -494,29 +460,31 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    if (has_next) {
-      tile = next;
-      buf ^= 1;
-      ++j;
-    }
+    posv = posv_n;
+    if (has_next) tile = next;
     return has_next;
   };
   while (true) {
-    if (!step(ra, rb, j % 3)) break;
-    if (!step(rb, ra, j % 3)) break;
+    if (!step(0)) break;
+    if (!step(1)) break;
   }
 }
 
-__global__ void rope_cos_sin_kernel(RopeTables t, int32_t max_pos, const int32_t* pos, int64_t n, float* cs) {
+// (cos, sin) of every position p < max_pos, pair i: entry p * 64 + i.
+__global__ void build_cs_table_kernel(RopeTables t, int64_t n, float2* cs) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  cs[idx] = rope_cos_sin((int)(idx / kPairs), (int)(idx % kPairs), t);
+}
+
+__global__ void gather_cs_kernel(const float2* table, int32_t max_pos, const int32_t* pos, int64_t n,
+                                 float2* out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n * kPairs) return;
   const int64_t k = idx / kPairs;
-  const int i = (int)(idx - k * kPairs);
   int p = pos[k];
   p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
-  const float2 v = rope_cos_sin(p, i, t);
-  cs[2 * idx] = v.x;
-  cs[2 * idx + 1] = v.y;
+  out[idx] = table[(int64_t)p * kPairs + (idx - k * kPairs)];
 }
 
 // Persistent grid: as many blocks per head group as fit on the chip at once.
@@ -582,13 +550,21 @@ hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int hg, int y_ou
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rope_cos_sin(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs,
-                               hipStream_t st) {
-  const int64_t total = n * kPairs;
+hipError_t launch_build_cs_table(const wushkv_rope* r, hipStream_t st) {
+  const int64_t total = (int64_t)r->max_pos * kPairs;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   const RopeTables t{r->t0, r->t1, r->t2, r->t0t, r->t1t, r->t2t};
-  rope_cos_sin_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(t, r->max_pos, pos, n, cs);
+  build_cs_table_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(t, total, r->cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cs(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs_out,
+                            hipStream_t st) {
+  const int64_t total = n * kPairs;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  gather_cs_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(r->cs, r->max_pos, pos, n, (float2*)cs_out);
   return hipGetLastError();
 }
 

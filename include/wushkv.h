@@ -119,8 +119,12 @@ wushkv_status wushkv_transform_create(const float* T_host, int n_heads, wushkv_t
 wushkv_status wushkv_transform_destroy(wushkv_transform* t);
 
 /* RoPE handle for base theta and positions [0, max_pos), max_pos <= 2^24.
- * Builds cos/sin split tables (fp64 with extended-precision tails) on the
- * current device.  Allocates device memory (not a hot-path call). */
+ * Computes the exact fp32 (cos, sin) of every position and pair once on the
+ * current device (from fp64 split tables with extended-precision tails) and
+ * keeps them as a [max_pos][64] table of fp32 pairs: 512 bytes per position,
+ * 64 MiB at 2^17 positions, 8 GiB at 2^24.  The key kernel reads one row per
+ * token.  Allocates device memory and synchronizes the device (not a
+ * hot-path call). */
 wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out);
 wushkv_status wushkv_rope_destroy(wushkv_rope* r);
 
