@@ -42,6 +42,28 @@ constexpr int kNB = 2;         // 32-token MFMA column blocks per tile
 constexpr int kCsStride = 66;  // float2 per token row of the cos/sin tile (64 + 2 pad)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw (unswizzled, stride 0) buffer resource over [base, base + bytes).  A
+// load through it returns zeros at offsets past `bytes`; the key path uses
+// that instead of clamping indices of tokens past the end (their results are
+// never stored).  Word 3 selects the 32-bit data format for untyped access.
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+// v_permlane32_swap of a value with itself: `lo` holds, in every lane l, the
+// value of lane l % 32, and `hi` the value of lane l % 32 + 32.
+struct Halves {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ Halves halves(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ Halves halves(float x) { return halves(__float_as_uint(x)); }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
@@ -55,49 +77,57 @@ template <bool F32IN>
 struct RawKeys;
 template <>
 struct RawKeys<false> {  // bf16: 8 channels per 16-byte load; [nb][j]
-  uint4 v[2 * kNB];
+  u32x4 v[2 * kNB];
 };
 template <>
 struct RawKeys<true> {   // fp32: 8 channels = two 16-byte loads
-  float4 v[4 * kNB];
+  u32x4 v[4 * kNB];
 };
 
-// Loads are unconditional: a token past the end reads the last token's row (its
-// results are never stored), so the compiler never has to cover a
-// conditionally issued load with its waits.
+// `rs` covers the tile's rows of this head (zeros past the last token);
+// `off` is the lane's byte offset in column block 0, `nb_step` the offset of
+// column block 1.
 template <bool F32IN>
-__device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, const KeysArgs& a, int64_t tok0, int h, int lh,
-                                          int wq) {
+__device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, rsrc_t rs, uint32_t off, uint32_t nb_step) {
+  constexpr uint32_t kPartner = 64 * (F32IN ? 4 : 2);  // bytes from channel i to channel i + 64
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    int64_t tok = tok0 + 32 * nb;
-    tok = tok < a.n_tokens ? tok : a.n_tokens - 1;
+    const uint32_t o = off + nb * nb_step;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int s = wq + 4 * j;
       if constexpr (F32IN) {
-        const float* base = (const float*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh;
-        r.v[4 * nb + 2 * j] = *(const float4*)base;
-        r.v[4 * nb + 2 * j + 1] = *(const float4*)(base + 4);
+        r.v[4 * nb + 2 * j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner, 0, 0);
+        r.v[4 * nb + 2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner + 16, 0, 0);
       } else {
-        r.v[2 * nb + j] = *(const uint4*)((const uint16_t*)a.K + tok * a.stride + (int64_t)h * kD + 16 * s + 8 * lh);
+        r.v[2 * nb + j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner, 0, 0);
       }
     }
   }
 }
 
+// Block barrier that orders LDS only: waits for this wave's own LDS
+// instructions, not for its global loads.  __syncthreads() would also wait
+// for the cos/sin copies (global_load_lds) in flight, and with them for every
+// earlier global load.  The "memory" clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool F32IN>
 __device__ __forceinline__ void unpack8(const RawKeys<F32IN>& r, int nb, int j, float* x) {
   if constexpr (F32IN) {
-    const float4 p = r.v[4 * nb + 2 * j], q = r.v[4 * nb + 2 * j + 1];
-    x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
-    x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+    const u32x4 p = r.v[4 * nb + 2 * j], q = r.v[4 * nb + 2 * j + 1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = __uint_as_float(p[e]);
+      x[4 + e] = __uint_as_float(q[e]);
+    }
   } else {
-    const uint4 p = r.v[2 * nb + j];
-    x[0] = bf16lo_to_f32(p.x); x[1] = bf16hi_to_f32(p.x);
-    x[2] = bf16lo_to_f32(p.y); x[3] = bf16hi_to_f32(p.y);
-    x[4] = bf16lo_to_f32(p.z); x[5] = bf16hi_to_f32(p.z);
-    x[6] = bf16lo_to_f32(p.w); x[7] = bf16hi_to_f32(p.w);
+    const u32x4 p = r.v[2 * nb + j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16lo_to_f32(p[e]);
+      x[2 * e + 1] = bf16hi_to_f32(p[e]);
+    }
   }
 }
 
@@ -111,18 +141,19 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   constexpr int RECROW = HG * REC + 16;  // LDS row of one token's records (+16 B pad)
   constexpr int NSC = QK ? 8 : 1;        // fp16 values per (token, head): sym 1; affine 4 + 4
   constexpr int RB = 4 * BITS;           // bits in a run of 4 codes
+  constexpr int ESZ = F32IN ? 4 : 2;
 
   __shared__ __align__(16) float2 cs_lds[kTile][kCsStride];   // cos/sin rows of the tile being rotated
   __shared__ __align__(16) bf16x8 xb_lds[HG][kNB][8][64];     // rotated operands shared by a head's waves
-  __shared__ int64_t slot_lds[2][kTile];                       // cache row per token, tile j in slot j & 1
+  __shared__ int32_t slot_lds[2][kTile];  // cache row per token, -1: no store; tile j in slot j & 1
   __shared__ float red_lds[HG][4][kTile];
   __shared__ __align__(16) uint8_t rec_lds[kTile][RECROW];
-  __shared__ uint16_t sc_lds[kTile][HG * NSC];
+  __shared__ __align__(16) uint16_t sc_lds[kTile][HG * NSC];
 
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // The lane index is re-derived at every tile (see the top of `step`), so
-  // the per-lane addresses are recomputed there rather than held in
-  // registers across the loop.
+  // the per-lane offsets are recomputed there rather than held in registers
+  // across the loop.
   int lane = threadIdx.x & 63, lh = lane >> 5, col = lane & 31;
   // Four waves per head: wave wq holds rows 32 wq .. 32 wq + 31 of T~ and
   // rotates the RoPE pairs of k step wq (channels 16 wq + 8 (l / 32) + 0..7
@@ -134,14 +165,25 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
   if (first_tile >= n_tiles) return;  // uniform over the block
   const int64_t tile_step = a.blocks_per_group;
-  const int64_t last_tok = a.n_tokens - 1;
-
+  const uint32_t row_bytes = (uint32_t)(a.stride * ESZ);  // bytes between tokens (< 2^26)
+  // Tokens of tile t that exist (0 past the end).
+  auto tile_len = [&](int64_t t) __attribute__((always_inline)) -> uint32_t {
+    const int64_t left = a.n_tokens - t * kTile;
+    return left <= 0 ? 0u : (left < kTile ? (uint32_t)left : (uint32_t)kTile);
+  };
+  // This head's keys of tile t.
+  auto keys_rsrc = [&](int64_t t) __attribute__((always_inline)) -> rsrc_t {
+    const char* base = (const char*)a.K + (t * kTile * a.stride + (int64_t)h * kD) * ESZ;
+    return buffer_rsrc(base, tile_len(t) * row_bytes);
+  };
+  auto keys_off = [&]() __attribute__((always_inline)) -> uint32_t {
+    return col * row_bytes + (16 * wq + 8 * lh) * ESZ;
+  };
   // Positions of the TPW tokens whose cos/sin rows this wave copies (tokens
-  // TPW*w + k of the tile): lane k loads token k's (clamped) position.
+  // TPW*w + k of tile t): lane k loads token k's position (0 past the end).
   auto load_posv = [&](int64_t t) __attribute__((always_inline)) -> int {
-    int64_t tok = t * kTile + TPW * wave_u + (lane % TPW);
-    tok = tok < last_tok ? tok : last_tok;
-    return a.pos[tok];
+    const rsrc_t rs = buffer_rsrc(a.pos + t * kTile, tile_len(t) * 4u);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (TPW * wave_u + (lane % TPW)), 0, 0);
   };
   // Copy the tile's cos/sin rows into cs_lds: row k of this wave comes from
   // the table row of its position, 32 lanes x 16 bytes straight into LDS.
@@ -158,20 +200,24 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       }
     }
   };
-  // Cache rows of a tile's tokens: wave 0, one per lane (a clamped token past
-  // the end reads the last token's slot; its row is never used).
-  auto load_rows = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
+  // Cache rows of tile t's tokens, loaded by wave 0 (lane = token): the raw
+  // slot words, turned into a row or -1 by row_of once they have arrived.
+  auto load_rows = [&](int64_t t) __attribute__((always_inline)) -> u32x2 {
+    const rsrc_t rs = buffer_rsrc(a.slots + t * kTile, tile_len(t) * 8u);
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, 0, 0);
+  };
+  auto row_of = [&](u32x2 w, int64_t t) __attribute__((always_inline)) -> int32_t {
     const int64_t tok = t * kTile + lane;
-    if (!a.slots) return tok;
-    return a.slots[tok < last_tok ? tok : last_tok];
+    const int64_t row = a.slots ? (int64_t)(((uint64_t)w[1] << 32) | w[0]) : tok;
+    return (tok < a.n_tokens && row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
   };
 
   RawKeys<F32IN> r;  // this tile's keys until RoPE has read them, then the next tile's
   int64_t tile = first_tile;
   // Prologue: the first tile's keys, rows, positions and cos/sin; T~.
-  load_keys<F32IN>(r, a, tile * kTile + col, h, lh, wq);
-  int64_t row_r = 0;
-  if (wave_u == 0) row_r = load_rows(tile);
+  load_keys<F32IN>(r, keys_rsrc(tile), keys_off(), 32 * row_bytes);
+  u32x2 row_w = {0u, 0u};  // read only when a.slots is set
+  if (a.slots && wave_u == 0) row_w = load_rows(tile);
   const int posv0 = load_posv(tile);
   int posv = load_posv(tile + tile_step);  // positions of the next tile's rows
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
@@ -182,8 +228,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
   }
   copy_cs(posv0);
-  if (wave_u == 0) slot_lds[0][lane] = row_r;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
+  if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, tile);
   __syncthreads();
 
   // One tile per call (par = the tile's ordinal & 1).
@@ -195,9 +241,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     const int tid = 64 * wave_u + lane;
     const int64_t next = tile + tile_step;
     const bool has_next = next < n_tiles;
-    // ---- rows of the next tile and positions of the tile after (clamped
-    // past the end)
-    if (wave_u == 0) row_r = load_rows(next);
+    // ---- rows of the next tile and positions of the tile after (zeros past
+    // the end)
+    if (a.slots && wave_u == 0) row_w = load_rows(next);
     const int posv_n = load_posv(next + tile_step);
 
     // ---- RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS
@@ -226,7 +272,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       xb_lds[hh][nb][s + 4][lane] = pack8(xb);
     }
     // ---- the next tile's keys, into the registers RoPE has just consumed
-    load_keys<F32IN>(r, a, next * kTile + col, h, lh, wq);
+    load_keys<F32IN>(r, keys_rsrc(next), keys_off(), 32 * row_bytes);
     __syncthreads();  // B1: operands in LDS; everyone is done with cs_lds
 
     // ---- the next tile's cos/sin rows (in flight until the wait before B3)
@@ -264,15 +310,15 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           float* yo = a.y_out + (tok * a.n_heads + h) * kD;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = 32 * wq + 8 * q + 4 * lh;
-            *(float4*)(yo + r) = make_float4(acc[nb][4 * q], acc[nb][4 * q + 1], acc[nb][4 * q + 2],
-                                             acc[nb][4 * q + 3]);
+            const int rr = 32 * wq + 8 * q + 4 * lh;
+            *(float4*)(yo + rr) = make_float4(acc[nb][4 * q], acc[nb][4 * q + 1], acc[nb][4 * q + 2],
+                                              acc[nb][4 * q + 3]);
           }
         }
       }
-      __syncthreads();  // B2 (kept so that every tile passes three barriers)
+      barrier_lds();  // B2 (kept so that every tile passes three barriers)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_r;
+      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_of(row_w, next);
       __syncthreads();  // B3
     } else {
       // Output element acc[nb][i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of
@@ -294,15 +340,16 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             const float q2 = acc[nb][4 * q + 2] * acc[nb][4 * q + 2];
             const float q3 = acc[nb][4 * q + 3] * acc[nb][4 * q + 3];
             const float p4 = (q0 + q1) + (q2 + q3);
-            P8[q] = p4 + __shfl_xor(p4, 32);
+            const Halves x = halves(p4);
+            P8[q] = __uint_as_float(x.lo) + __uint_as_float(x.hi);
           }
           const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
           if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
         }
-        __syncthreads();  // B2
+        barrier_lds();  // B2
         // One step per lane for token tt = 32 lh + col (the lane pair l, l^32
-        // covers both column blocks); each block's step then comes from the
-        // lane that computed it.
+        // covers both column blocks): column block nb's step is then the
+        // value of lane half nb.
         const int tt = 32 * lh + col;
         const float S = (red_lds[hh][0][tt] + red_lds[hh][1][tt]) + (red_lds[hh][2][tt] + red_lds[hh][3][tt]);
         const float ms = S * 0.0078125f;  // S / 128, exact scaling
@@ -312,11 +359,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         const float d32 = twoC / (float)(L - 1);
         const uint16_t dh = f16_sat_bits(d32);
         if (wq == 0) sc_lds[tt][hh] = dh;
-        const float d_own = f16_bits_to_f32(dh);
-        const float d_oth = __shfl_xor(d_own, 32);
+        const Halves dd = halves(f16_bits_to_f32(dh));
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-          const float delta = (lh == nb) ? d_own : d_oth;
+          const float delta = __uint_as_float(nb ? dd.hi : dd.lo);
           // A zero step becomes +inf (threshold / step) so every code comes out L/2.
           const float tp = delta == 0.0f ? __builtin_inff() : delta;
           if constexpr (BITS == 2) {
@@ -340,16 +386,16 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              uint32_t r = 0;
+              uint32_t rc = 0;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) r |= sym_code<BITS>(acc[nb][4 * q + e], tp, rd) << (BITS * e);
-              asm("" : "+v"(r));  // keep the word 32 bits wide (compare + add-with-carry codegen)
-              run[nb][q] = r;
+              for (int e = 0; e < 4; ++e) rc |= sym_code<BITS>(acc[nb][4 * q + e], tp, rd) << (BITS * e);
+              asm("" : "+v"(rc));  // keep the word 32 bits wide (compare + add-with-carry codegen)
+              run[nb][q] = rc;
             }
           }
         }
       } else {
-        __syncthreads();  // B2 (the affine groups are this wave's own rows)
+        barrier_lds();  // B2 (the affine groups are this wave's own rows)
         // Percentile-clipped affine quantizer, group = this wave's 32 rows of
         // a token, split between lanes l and l^32: two smallest and two
         // largest values by IEEE totalOrder, merged across the lane pair.
@@ -364,12 +410,14 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             mx2 = max(mx2, min(mx1, k));
             mx1 = max(mx1, k);
           }
-          const int32_t o1 = __shfl_xor(mn1, 32), o2 = __shfl_xor(mn2, 32);
-          const int32_t u1 = __shfl_xor(mx1, 32), u2 = __shfl_xor(mx2, 32);
-          const float s0 = total_order_value(min(mn1, o1));
-          const float s1 = total_order_value(min(max(mn1, o1), min(mn2, o2)));
-          const float s31 = total_order_value(max(mx1, u1));
-          const float s30 = total_order_value(max(min(mx1, u1), max(mx2, u2)));
+          const Halves n1 = halves((uint32_t)mn1), n2 = halves((uint32_t)mn2);
+          const Halves x1 = halves((uint32_t)mx1), x2 = halves((uint32_t)mx2);
+          const int32_t a1 = (int32_t)n1.lo, b1 = (int32_t)n1.hi, a2 = (int32_t)n2.lo, b2 = (int32_t)n2.hi;
+          const int32_t c1 = (int32_t)x1.lo, d1 = (int32_t)x1.hi, c2 = (int32_t)x2.lo, d2 = (int32_t)x2.hi;
+          const float s0 = total_order_value(min(a1, b1));
+          const float s1 = total_order_value(min(max(a1, b1), min(a2, b2)));
+          const float s31 = total_order_value(max(c1, d1));
+          const float s30 = total_order_value(max(min(c1, d1), max(c2, d2)));
           const float lo = a.q.lo_mode ? s0 : __builtin_fmaf(a.q.g_lo, s1 - s0, s0);
           const float hi = a.q.hi_mode == 0 ? __builtin_fmaf(a.q.g_hi, s31 - s30, s30)
                                             : (a.q.hi_mode == 1 ? s30 : s31);
@@ -378,13 +426,13 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           const double sd = (double)f16_bits_to_f32(sh), zd = (double)f16_bits_to_f32(zh);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            uint32_t r = 0;
+            uint32_t rc = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(acc[nb][4 * q + e], zd, sd);
-              r |= c << (BITS * e);
+              const uint32_t cd = sd == 0.0 ? 0u : affine_code<BITS>(acc[nb][4 * q + e], zd, sd);
+              rc |= cd << (BITS * e);
             }
-            run[nb][q] = r;
+            run[nb][q] = rc;
           }
           if (lh == 0) {
             sc_lds[32 * nb + col][hh * 8 + wq] = sh;
@@ -400,13 +448,15 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       for (int nb = 0; nb < kNB; ++nb) {
         uint8_t* dst = &rec_lds[32 * nb + col][hh * REC + BITS * (4 * wq + 2 * lh)];
         if constexpr (QK == 0 && BITS == 2) {
-          // bytes of {partner (selectors 4-7), own (0-3)}
-          const uint32_t sel = lh ? 0x03070206u : 0x05010400u;
-          *(uint32_t*)dst = __builtin_amdgcn_perm(__shfl_xor(W2[nb], 32), W2[nb], sel);
+          // bytes {lane half 0: selectors 0-3, lane half 1: 4-7}: lh = 0 takes
+          // bytes 0, 1 of both, lh = 1 bytes 2, 3
+          const Halves w = halves(W2[nb]);
+          *(uint32_t*)dst = __builtin_amdgcn_perm(w.hi, w.lo, lh ? 0x07030602u : 0x05010400u);
         } else {
           const uint32_t* rn = run[nb];
           const uint32_t send = lh ? (rn[0] | (rn[1] << RB)) : (rn[2] | (rn[3] << RB));
-          const uint32_t recv = __shfl_xor(send, 32);
+          const Halves w = halves(send);
+          const uint32_t recv = lh ? w.lo : w.hi;
           const uint64_t p0 = recv & ((1u << RB) - 1u), p1 = recv >> RB;
           const uint64_t chunk =
               lh ? (p0 | ((uint64_t)rn[2] << RB) | (p1 << (2 * RB)) | ((uint64_t)rn[3] << (3 * RB)))
@@ -425,37 +475,49 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       // Every load of this wave has landed (next keys, rows, positions, the
       // cos/sin copies), so the stores below never queue behind a load.
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
-      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_r;
+      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_of(row_w, next);
       __syncthreads();  // B3
 
       // ---- stores: each token's HG records are contiguous in the cache row
-      const int64_t tbase = tile * kTile;
-      constexpr int CPT = HG * BITS;  // 16-byte chunks per token
-      for (int c = tid; c < kTile * CPT; c += NT) {
-        const int n = c / CPT, k = c - n * CPT;
-        if (tbase + n < a.n_tokens) {
-          const int64_t row = slot_lds[par][n];
-          if (row >= 0 && row < a.n_rows) {
-            const uint4 v = *(const uint4*)&rec_lds[n][16 * k];
-            *(uint4*)(a.codes + (row * a.n_heads + grp * HG) * REC + 16 * k) = v;
-          }
+      // (16-byte chunks, at most one per thread), then its scales (and zeros).
+      constexpr int CPT = HG * BITS;        // 16-byte chunks per token
+      constexpr int NCH = kTile * CPT;      // <= NT
+      const uint32_t row_rec = (uint32_t)a.n_heads * REC;  // bytes per cache row
+      if (NCH == NT || tid < NCH) {
+        const int n = tid / CPT, k = tid - n * CPT;
+        const int32_t row = slot_lds[par][n];
+        if (row >= 0) {
+          const uint4 v = *(const uint4*)&rec_lds[n][16 * k];
+          uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + (grp * HG * REC + 16 * k);
+          *(uint4*)dst = v;
         }
       }
-      for (int c = tid; c < kTile * HG; c += NT) {
-        const int n = c / HG, jh = c - n * HG;
-        if (tbase + n < a.n_tokens) {
-          const int64_t row = slot_lds[par][n];
-          if (row >= 0 && row < a.n_rows) {
-            const int64_t slot = row * a.n_heads + grp * HG + jh;
-            if constexpr (QK == 0) {
-              a.scales[slot] = sc_lds[n][jh];
+      if constexpr (QK == 0) {
+        // one store of the HG fp16 steps per token, by the last wave
+        const int n = tid - (NT - 64);
+        if (n >= 0) {
+          const int32_t row = slot_lds[par][n];
+          if (row >= 0) {
+            uint16_t* dst = a.scales + (uint64_t)(uint32_t)row * a.n_heads + grp * HG;
+            if constexpr (HG == 4) {
+              *(uint2*)dst = *(const uint2*)&sc_lds[n][0];
+            } else if constexpr (HG == 2) {
+              *(uint32_t*)dst = *(const uint32_t*)&sc_lds[n][0];
             } else {
-              const uint16_t* s = &sc_lds[n][jh * 8];
-              *(uint2*)(a.scales + slot * 4) =
-                  make_uint2(s[0] | ((uint32_t)s[1] << 16), s[2] | ((uint32_t)s[3] << 16));
-              *(uint2*)(a.zeros + slot * 4) =
-                  make_uint2(s[4] | ((uint32_t)s[5] << 16), s[6] | ((uint32_t)s[7] << 16));
+              *dst = sc_lds[n][0];
             }
+          }
+        }
+      } else {
+        // per (token, head): 4 scales and 4 zeros, 8 bytes each
+        const int c = tid - (NT - 64 * HG);
+        if (c >= 0) {
+          const int n = c / HG, jh = c - n * HG;
+          const int32_t row = slot_lds[par][n];
+          if (row >= 0) {
+            const uint64_t slot = (uint64_t)(uint32_t)row * a.n_heads + grp * HG + jh;
+            *(uint2*)(a.scales + slot * 4) = *(const uint2*)&sc_lds[n][jh * 8];
+            *(uint2*)(a.zeros + slot * 4) = *(const uint2*)&sc_lds[n][jh * 8 + 4];
           }
         }
       }

@@ -39,7 +39,8 @@
  * Memory layout (all device memory, caller-owned; the library never allocates
  * on the hot path):
  *   K, V     [n_tokens][n_heads][128], element (n,h,c) at base + n*token_stride
- *            + h*128 + c; bf16 or fp32; 16-byte aligned rows.
+ *            + h*128 + c; bf16 or fp32; 16-byte aligned rows; a token row
+ *            (token_stride elements) spans at most 2^26 bytes.
  *   codes    [n_rows][n_heads][16*bits] bytes.
  *   scales   fp16; sym: [n_rows][n_heads]; affine: [n_rows][n_heads][4].
  *   zeros    fp16, affine only: [n_rows][n_heads][4].
@@ -99,7 +100,7 @@ typedef struct {
  *   slots:  int64 row per token, or NULL (row = token index).  Rows outside
  *           [0, n_rows) are skipped by writers and read as zero-filled by the
  *           reader; callers must not rely on that.
- *   n_rows: capacity of the cache in rows. */
+ *   n_rows: capacity of the cache in rows, below 2^31. */
 typedef struct {
   void* codes;
   void* scales;
