@@ -12,10 +12,12 @@ pack) + wushkv_quantize_values (quantize -> pack) over the whole layer.  Inputs
 are resident in HBM before timing; the step cycles through enough input/output
 sets (> 2x the 256 MB MALL) that no set is re-read from the MALL.
 
-Prints one JSON line.  `value` is K+V tokens/s of the whole step; `roofline`
-is for the key kernel (algorithmic bytes per launch / its mean duration, from
-HIP events on the launch stream); `cpu_baseline` is the CPU oracle as it
-stands, single-threaded, on the same workload.
+Prints one JSON line.  `value` is K+V tokens/s of the whole step, from K
+steps launched back to back between two synchronizations; `roofline` is for
+the key kernel (algorithmic bytes per launch / its mean duration, from HIP
+events around each launch on the launch stream, in a second pass over the same
+K steps); `cpu_baseline` is the CPU oracle as it stands, single-threaded, on
+the same workload.
 """
 from __future__ import annotations
 
@@ -153,16 +155,23 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Throughput: K steps back to back, bracketed by synchronizations only.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    # Per-kernel durations: the same K steps again with HIP events around each
+    # launch on the launch stream (an event between launches costs a few us
+    # of the step, so they stay out of the throughput pass).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     key_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     val_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
 
     if args.copy_probe:
         a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -106,6 +106,7 @@ wushkv_status check_tensor(const void* X, wushkv_dtype dt, int64_t n_tokens, int
   if (dt != WUSHKV_F32 && dt != WUSHKV_BF16) return fail(WUSHKV_ERR_INVALID_ARG, "dtype must be F32 or BF16");
   if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
   if (n_tokens < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (n_tokens > INT32_MAX - 128) return fail(WUSHKV_ERR_UNSUPPORTED, "n_tokens must be below 2^31 - 128");
   if (stride < (int64_t)n_heads * WUSHKV_HEAD_DIM) return fail(WUSHKV_ERR_INVALID_ARG, "token_stride < n_heads*128");
   const int64_t esz = dt == WUSHKV_F32 ? 4 : 2;
   if ((stride * esz) % 16) return fail(WUSHKV_ERR_ALIGNMENT, "token_stride must span a multiple of 16 bytes");

@@ -13,19 +13,22 @@
 // 32-token column blocks with 16 v_mfma_f32_32x32x16_bf16 (two independent
 // accumulation chains).  The B operand is the rotated keys: lane l holds
 // token l%32 of a column block and, for k step s, channels 16s + 8(l/32) +
-// 0..7, so the RoPE partners (i, i+64) sit in one lane (k steps s and s+4).
-// Wave wq loads and rotates k step wq and its partner for both column blocks,
-// and the four waves of a head share their bf16 operands through LDS.  At
-// under 128 VGPRs four waves are resident per SIMD.
+// 0..7.  Wave wq loads and rotates 16 of the tile's tokens, token-major (each
+// load instruction covers eight tokens' whole 128-byte lines; the RoPE
+// partners (i, i+64) sit in one lane), and the four waves of a head exchange
+// their bf16 operands through LDS.  At under 128 VGPRs four waves are
+// resident per SIMD.
 //
 // cos/sin come from the RoPE handle's table (one 512-byte fp32 row per
-// position, exact): each wave copies a few of the tile's rows straight from
-// global memory into LDS (global_load_lds), a tile ahead of their use.
+// position, exact): each wave loads a few of the next tile's rows into
+// registers and writes them to LDS just before the barrier that starts that
+// tile.
 //
-// Per-tile pipeline, three barriers: [rows and positions for later tiles;
-// RoPE -> LDS; the next tile's keys into the registers RoPE freed] B1
-// [cos/sin copies for the next tile; MFMA; sums of squares -> LDS] B2
-// [scale(s), codes, records -> LDS; wait for every load] B3 [stores].
+// Per-tile pipeline, three barriers: [loads of the next tile's cache rows and
+// cos/sin rows, of the positions of the tile after; RoPE -> LDS; the next
+// tile's keys into the registers RoPE freed] B1 [MFMA; sums of squares ->
+// LDS] B2 [scale(s), codes, records -> LDS; wait for every load; cos/sin rows
+// -> LDS] B3 [stores].
 // Packed records and scales are staged in LDS and written as whole 16-byte
 // chunks (a head group's records of a token are contiguous in the cache row).
 #include "device_common.h"
@@ -71,12 +74,13 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// The keys a wave loads and rotates for one tile: for each column block nb,
-// k step wq (channels i < 64) and its partner wq + 4 (channels i + 64).
+// The keys a wave loads and rotates for one tile: for each token group g
+// (tokens 16 wq + 8 g + l / 8), a chunk of 8 channels i < 64 and the partner
+// chunk i + 64.
 template <bool F32IN>
 struct RawKeys;
 template <>
-struct RawKeys<false> {  // bf16: 8 channels per 16-byte load; [nb][j]
+struct RawKeys<false> {  // bf16: 8 channels per 16-byte load; [g][partner]
   u32x4 v[2 * kNB];
 };
 template <>
@@ -85,14 +89,14 @@ struct RawKeys<true> {   // fp32: 8 channels = two 16-byte loads
 };
 
 // `rs` covers the tile's rows of this head (zeros past the last token);
-// `off` is the lane's byte offset in column block 0, `nb_step` the offset of
-// column block 1.
+// `off` is the lane's byte offset in token group 0, `g_step` the offset of
+// token group 1.
 template <bool F32IN>
-__device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, rsrc_t rs, uint32_t off, uint32_t nb_step) {
+__device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, rsrc_t rs, uint32_t off, uint32_t g_step) {
   constexpr uint32_t kPartner = 64 * (F32IN ? 4 : 2);  // bytes from channel i to channel i + 64
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    const uint32_t o = off + nb * nb_step;
+    const uint32_t o = off + nb * g_step;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (F32IN) {
@@ -106,10 +110,8 @@ __device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, rsrc_t rs, uint32_t
 }
 
 // Block barrier that orders LDS only: waits for this wave's own LDS
-// instructions, not for its global loads.  __syncthreads() would also wait
-// for the cos/sin copies (global_load_lds) in flight, and with them for every
-// earlier global load.  The "memory" clobber keeps the compiler from moving
-// memory accesses across it.
+// instructions and never for its global loads in flight.  The "memory"
+// clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <bool F32IN>
@@ -160,66 +162,75 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // and their partners 64 higher).
   const int hh = wave_u >> 2, wq = wave_u & 3;
   const int grp = blockIdx.x % a.n_groups;
-  const int64_t first_tile = blockIdx.x / a.n_groups;
+  const int first_tile = blockIdx.x / a.n_groups;
   const int h = grp * HG + hh;
-  const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
+  // Token and tile indices fit 32 bits (n_tokens < 2^31 - 2^7).
+  const int n_tok = (int)a.n_tokens;
+  const int n_tiles = (n_tok + kTile - 1) / kTile;
   if (first_tile >= n_tiles) return;  // uniform over the block
-  const int64_t tile_step = a.blocks_per_group;
+  const int tile_step = a.blocks_per_group;
   const uint32_t row_bytes = (uint32_t)(a.stride * ESZ);  // bytes between tokens (< 2^26)
   // Tokens of tile t that exist (0 past the end).
-  auto tile_len = [&](int64_t t) __attribute__((always_inline)) -> uint32_t {
-    const int64_t left = a.n_tokens - t * kTile;
-    return left <= 0 ? 0u : (left < kTile ? (uint32_t)left : (uint32_t)kTile);
+  // (readfirstlane keeps the value in an SGPR: a buffer resource built from a
+  // VGPR would be treated as divergent.)
+  auto tile_len = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    const int left = n_tok - t * kTile;
+    return __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left < kTile ? left : kTile));
   };
   // This head's keys of tile t.
-  auto keys_rsrc = [&](int64_t t) __attribute__((always_inline)) -> rsrc_t {
-    const char* base = (const char*)a.K + (t * kTile * a.stride + (int64_t)h * kD) * ESZ;
+  auto keys_rsrc = [&](int t) __attribute__((always_inline)) -> rsrc_t {
+    const char* base = (const char*)a.K + ((int64_t)(t * kTile) * a.stride + h * kD) * ESZ;
     return buffer_rsrc(base, tile_len(t) * row_bytes);
   };
+  // RoPE layout (token-major, so that every key load covers whole 128-byte
+  // lines): wave wq rotates tokens 16 wq + 8 j + (l / 8), j = 0, 1, of the
+  // tile; lane l holds channels 8 (l % 8) .. + 7 and their partners 64 higher.
   auto keys_off = [&]() __attribute__((always_inline)) -> uint32_t {
-    return col * row_bytes + (16 * wq + 8 * lh) * ESZ;
+    return (16 * wq + (lane >> 3)) * row_bytes + 8 * (lane & 7) * ESZ;
   };
-  // Positions of the TPW tokens whose cos/sin rows this wave copies (tokens
-  // TPW*w + k of tile t): lane k loads token k's position (0 past the end).
-  auto load_posv = [&](int64_t t) __attribute__((always_inline)) -> int {
+  // cos/sin rows: wave w fills rows TPW*w .. TPW*w + TPW - 1 of cs_lds, two
+  // per 16-byte-per-lane load (lanes 0-31 one row, lanes 32-63 the next).
+  // posv[i] is the position of row TPW*w + 2i + (l / 32) of a tile (0 past
+  // the end), csv[i] the matching half-row of the table.
+  constexpr int NCS = TPW / 2;
+  auto load_pos = [&](int t, int* pv) __attribute__((always_inline)) {
     const rsrc_t rs = buffer_rsrc(a.pos + t * kTile, tile_len(t) * 4u);
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (TPW * wave_u + (lane % TPW)), 0, 0);
-  };
-  // Copy the tile's cos/sin rows into cs_lds: row k of this wave comes from
-  // the table row of its position, 32 lanes x 16 bytes straight into LDS.
-  auto copy_cs = [&](int posv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      int p = __builtin_amdgcn_readlane(posv, k);
-      p = p < 0 ? 0 : (p >= a.max_pos ? a.max_pos - 1 : p);
-      if (lane < 32) {
-        const float2* src = a.cs + (int64_t)p * kPairs + 2 * lane;
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)&cs_lds[TPW * wave_u + k][0], 16,
-                                         0, 0);
-      }
+    for (int i = 0; i < NCS; ++i)
+      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (TPW * wave_u + 2 * i + lh), 0, 0);
+  };
+  auto load_cs = [&](const int* pv, u32x4* cv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) {
+      const int p = min(max(pv[i], 0), a.max_pos - 1);  // clamp to the table
+      cv[i] = *(const u32x4*)(a.cs + (int64_t)p * kPairs + 2 * col);
     }
+  };
+  auto store_cs = [&](const u32x4* cv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) *(u32x4*)&cs_lds[TPW * wave_u + 2 * i + lh][2 * col] = cv[i];
   };
   // Cache rows of tile t's tokens, loaded by wave 0 (lane = token): the raw
   // slot words, turned into a row or -1 by row_of once they have arrived.
-  auto load_rows = [&](int64_t t) __attribute__((always_inline)) -> u32x2 {
+  auto load_rows = [&](int t) __attribute__((always_inline)) -> u32x2 {
     const rsrc_t rs = buffer_rsrc(a.slots + t * kTile, tile_len(t) * 8u);
     return __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, 0, 0);
   };
-  auto row_of = [&](u32x2 w, int64_t t) __attribute__((always_inline)) -> int32_t {
-    const int64_t tok = t * kTile + lane;
+  auto row_of = [&](u32x2 w, int t) __attribute__((always_inline)) -> int32_t {
+    const int tok = t * kTile + lane;
     const int64_t row = a.slots ? (int64_t)(((uint64_t)w[1] << 32) | w[0]) : tok;
-    return (tok < a.n_tokens && row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
+    return (tok < n_tok && row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
   };
 
   RawKeys<F32IN> r;  // this tile's keys until RoPE has read them, then the next tile's
-  int64_t tile = first_tile;
+  int tile = first_tile;
   // Prologue: the first tile's keys, rows, positions and cos/sin; T~.
-  load_keys<F32IN>(r, keys_rsrc(tile), keys_off(), 32 * row_bytes);
+  load_keys<F32IN>(r, keys_rsrc(tile), keys_off(), 8 * row_bytes);
   u32x2 row_w = {0u, 0u};  // read only when a.slots is set
   if (a.slots && wave_u == 0) row_w = load_rows(tile);
-  const int posv0 = load_posv(tile);
-  int posv = load_posv(tile + tile_step);  // positions of the next tile's rows
+  int posv[NCS], posv_n[NCS];  // positions of this tile's rows, then of the next tile's
+  u32x4 csv[NCS];
+  load_pos(tile, posv);
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
   bf16x8 A[8];
   {
@@ -227,8 +238,12 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
   }
-  copy_cs(posv0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
+  load_cs(posv, csv);
+  load_pos(tile + tile_step, posv);
+  // Nothing may be in flight when the loop starts: its first wait would
+  // otherwise also cover the previous tile's stores on later iterations.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  store_cs(csv);
   if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, tile);
   __syncthreads();
 
@@ -239,21 +254,28 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     lh = lane >> 5;
     col = lane & 31;
     const int tid = 64 * wave_u + lane;
-    const int64_t next = tile + tile_step;
+    const int next = tile + tile_step;
     const bool has_next = next < n_tiles;
-    // ---- rows of the next tile and positions of the tile after (zeros past
-    // the end)
+    // ---- the next tile's rows and cos/sin rows, the positions of the tile
+    // after (zeros past the end); all land before the wait ahead of B3
     if (a.slots && wave_u == 0) row_w = load_rows(next);
-    const int posv_n = load_posv(next + tile_step);
+    load_cs(posv, csv);
+    load_pos(next + tile_step, posv_n);
 
-    // ---- RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS
+    // ---- RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS.
+    // Chunk c = l % 8 of token t is channels 8c .. 8c+7 (k step c / 2, lane
+    // half c % 2 of the B operand) and its partner chunk (k step 4 + c / 2).
+    // B-operand rows are stored with lane index lane' ^ (4 (s % 4) + 2 (lane' / 32)),
+    // which for this chunk is lane' ^ 2c: the eight chunks of a token land in
+    // eight different bank groups, and each row stays a permutation of itself.
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int s = wq;  // k step of channels i; the partners are in k step s + 4
+    for (int j = 0; j < 2; ++j) {
+      const int c8 = lane & 7, g = lane >> 3;
+      const int t = 16 * wq + 8 * j + g;  // token within the tile
       float ka[8], kb[8];
-      unpack8<F32IN>(r, nb, 0, ka);
-      unpack8<F32IN>(r, nb, 1, kb);
-      const float4* csp = (const float4*)&cs_lds[32 * nb + col][16 * s + 8 * lh];
+      unpack8<F32IN>(r, j, 0, ka);
+      unpack8<F32IN>(r, j, 1, kb);
+      const float4* csp = (const float4*)&cs_lds[t][8 * c8];
       float c[8], sn[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -268,15 +290,14 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         xa[e] = __builtin_fmaf(ka[e], c[e], -bs);
         xb[e] = __builtin_fmaf(kb[e], c[e], as);
       }
-      xb_lds[hh][nb][s][lane] = pack8(xa);
-      xb_lds[hh][nb][s + 4][lane] = pack8(xb);
+      const int nb = t >> 5, s0 = c8 >> 1;
+      const int ls = ((t & 31) + 32 * (c8 & 1)) ^ (2 * c8);
+      xb_lds[hh][nb][s0][ls] = pack8(xa);
+      xb_lds[hh][nb][s0 + 4][ls] = pack8(xb);
     }
     // ---- the next tile's keys, into the registers RoPE has just consumed
-    load_keys<F32IN>(r, keys_rsrc(next), keys_off(), 32 * row_bytes);
+    load_keys<F32IN>(r, keys_rsrc(next), keys_off(), 8 * row_bytes);
     __syncthreads();  // B1: operands in LDS; everyone is done with cs_lds
-
-    // ---- the next tile's cos/sin rows (in flight until the wait before B3)
-    copy_cs(posv);
 
     // ---- y = T~ x~ for this wave's 32 rows and both column blocks
 #pragma unroll
@@ -284,14 +305,16 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     // B operands one k step ahead of the MFMAs that use them; the scheduling
     // barriers keep the compiler from hoisting all sixteen reads (64 VGPRs).
     {
+      // lane index of k step s in the stored row: lane ^ (4 (s % 4) + 2 lh)
+      const int lsw = lane ^ (2 * lh);
       bf16x8 bc[kNB], bn[kNB];
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) bc[nb] = xb_lds[hh][nb][0][lane];
+      for (int nb = 0; nb < kNB; ++nb) bc[nb] = xb_lds[hh][nb][0][lsw];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (s < 7) {
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) bn[nb] = xb_lds[hh][nb][s + 1][lane];
+          for (int nb = 0; nb < kNB; ++nb) bn[nb] = xb_lds[hh][nb][s + 1][lsw ^ (4 * ((s + 1) & 3))];
         }
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
@@ -319,6 +342,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       barrier_lds();  // B2 (kept so that every tile passes three barriers)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       if (wave_u == 0) slot_lds[par ^ 1][lane] = row_of(row_w, next);
+      store_cs(csv);
       __syncthreads();  // B3
     } else {
       // Output element acc[nb][i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of
@@ -472,10 +496,11 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           }
         }
       }
-      // Every load of this wave has landed (next keys, rows, positions, the
-      // cos/sin copies), so the stores below never queue behind a load.
+      // Every load of this wave has landed (next keys, rows, cos/sin rows,
+      // positions), so the stores below never queue behind a load.
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
       if (wave_u == 0) slot_lds[par ^ 1][lane] = row_of(row_w, next);
+      store_cs(csv);  // RoPE of this tile finished reading cs_lds at B1
       __syncthreads();  // B3
 
       // ---- stores: each token's HG records are contiguous in the cache row
@@ -522,7 +547,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    posv = posv_n;
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
     if (has_next) tile = next;
     return has_next;
   };
