@@ -110,7 +110,7 @@ wushkv_status check_tensor(const void* X, wushkv_dtype dt, int64_t n_tokens, int
   if (stride < (int64_t)n_heads * WUSHKV_HEAD_DIM) return fail(WUSHKV_ERR_INVALID_ARG, "token_stride < n_heads*128");
   const int64_t esz = dt == WUSHKV_F32 ? 4 : 2;
   if ((stride * esz) % 16) return fail(WUSHKV_ERR_ALIGNMENT, "token_stride must span a multiple of 16 bytes");
-  if (stride * esz > (1 << 26)) return fail(WUSHKV_ERR_UNSUPPORTED, "token_stride spans more than 2^26 bytes");
+  if (stride * esz > (1 << 24)) return fail(WUSHKV_ERR_UNSUPPORTED, "token_stride spans more than 2^24 bytes");
   if (n_tokens > 0) {
     if (!X) return fail(WUSHKV_ERR_INVALID_ARG, "input tensor is NULL");
     if (!aligned(X, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "input tensor must be 16-byte aligned");

@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   const int n_tiles = (n_tok + kTile - 1) / kTile;
   if (first_tile >= n_tiles) return;  // uniform over the block
   const int tile_step = a.blocks_per_group;
-  const uint32_t row_bytes = (uint32_t)(a.stride * ESZ);  // bytes between tokens (< 2^26)
+  const uint32_t row_bytes = (uint32_t)(a.stride * ESZ);  // bytes between tokens (<= 2^24)
   // Tokens of tile t that exist (0 past the end).
   // (readfirstlane keeps the value in an SGPR: a buffer resource built from a
   // VGPR would be treated as divergent.)

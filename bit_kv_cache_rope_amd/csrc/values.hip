@@ -7,15 +7,18 @@
 // Layout: a 128-channel (token, head) vector is spread over 16 lanes, 8
 // contiguous channels per lane, so one wave load instruction covers 4 vectors
 // (1 KiB contiguous for a dense tensor).  A wave handles 32 vectors per
-// iteration (8 loads of 16 bytes per lane); the next iteration's loads are in
-// flight while the current one is quantized.  Reductions are xor butterflies
+// iteration (8 loads of 16 bytes per lane).  Reductions are xor butterflies
 // inside the 16-lane group, which realise the contiguous pairwise tree exactly
-// (offsets 1, 2, 4, 8 combine 16-, 32-, 64-, 128-channel halves).  Records and
-// scales are staged in LDS and written back as 16-byte chunks.
+// (offsets 1, 2, 4, 8 combine 16-, 32-, 64-, 128-channel halves).  One lane
+// per vector turns its sum of squares into the step and the code thresholds,
+// which reach the vector's 16 lanes through LDS.  Records and scales are
+// staged in LDS (two buffers, alternating by iteration) and written back as
+// 16-byte chunks.
 //
-// Loads are unconditional (indices are clamped to the last vector) and the
-// loop is unrolled by two over two register sets, so the only wait on the
-// prefetch is the explicit one before each iteration's stores.
+// Loads go through a raw buffer resource sized to the iteration's vectors:
+// vectors past the end read zeros and are never stored.  The next
+// iteration's loads are in flight while the current one is quantized (two
+// register sets); under 128 VGPRs four waves are resident per SIMD.
 #include "device_common.h"
 #include "internal.h"
 
@@ -26,19 +29,21 @@ namespace wushkv {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kU = 8;                     // loads per lane per iteration
+constexpr int kU = 4;                     // loads per lane per iteration
 constexpr int kPerWave = 4 * kU;          // vectors per wave per iteration
 constexpr int kVecs = kWaves * kPerWave;  // vectors per block per iteration
+constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
 
 template <bool F32IN>
-struct RawVals;
-template <>
-struct RawVals<false> {
-  uint4 v[kU];
-};
-template <>
-struct RawVals<true> {
-  float4 v[2 * kU];
+struct RawVals {
+  u32x4 v[F32IN ? 2 * kU : kU];
 };
 
 // (token, head) of a flattened vector index v < 2^31: n = v / H by a multiply-high.
@@ -46,76 +51,93 @@ __device__ __forceinline__ uint32_t div_heads(uint32_t v, const ValuesArgs& a) {
   return (__umulhi(v, a.div_m) + v) >> a.div_l;
 }
 
-// Vector indices are 32-bit: a bf16 tensor with 2^31 vectors of 256 bytes
-// would not fit one GPU.
+// Loads of block-iteration `it` (vectors it * kVecs ...): this wave's vector
+// base + 4u (u < kU), 16 bytes per lane (32 for fp32).  `rows` receives the
+// cache row of each (strided layouts only).  Vectors past the end read zeros.
 template <bool F32IN, bool DENSE>
-__device__ __forceinline__ void load_vals(RawVals<F32IN>& r, int64_t* rows, const ValuesArgs& a,
-                                          uint32_t vbase, int l16, uint32_t last) {
+__device__ __forceinline__ void load_vals(RawVals<F32IN>& r, int64_t* rows, const ValuesArgs& a, uint32_t it,
+                                          int wave, int sub, int l16) {
+  constexpr uint32_t ESZ = F32IN ? 4 : 2;
+  const uint32_t nv = (uint32_t)(a.n_tokens * a.n_heads);
+  const uint32_t v0 = it * kVecs;  // first vector of the iteration (< nv)
+  const uint32_t nvalid = nv - v0 < (uint32_t)kVecs ? nv - v0 : (uint32_t)kVecs;
+  if constexpr (DENSE) {
+    const rsrc_t rs = buffer_rsrc((const char*)a.V + (uint64_t)v0 * kD * ESZ, nvalid * kD * ESZ);
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const uint32_t v = min(vbase + 4u * u, last);
-    uint64_t off;  // element offset of the vector
-    if constexpr (DENSE) {
-      off = (uint64_t)v * kD;
-    } else {
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t off = (uint32_t)(wave * kPerWave + 4 * u + sub) * (kD * ESZ) + 8 * ESZ * l16;
+      if constexpr (F32IN) {
+        r.v[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        r.v[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+      } else {
+        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      }
+    }
+  } else {
+    // tokens n0 .. n_last of the iteration; bytes up to the end of n_last's heads
+    const uint32_t n0 = div_heads(v0, a), n_last = div_heads(v0 + nvalid - 1, a);
+    const uint64_t row_bytes = (uint64_t)a.stride * ESZ;
+    const rsrc_t rs = buffer_rsrc((const char*)a.V + n0 * row_bytes,
+                                  (uint32_t)((n_last - n0) * row_bytes + (uint64_t)a.n_heads * kD * ESZ));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t v = v0 + wave * kPerWave + 4 * u + sub;
       const uint32_t n = div_heads(v, a);
       const uint32_t h = v - n * (uint32_t)a.n_heads;
-      off = (uint64_t)n * (uint64_t)a.stride + h * kD;
-      rows[u] = a.slots ? a.slots[n] : (int64_t)n;
-    }
-    if constexpr (F32IN) {
-      const float* p = (const float*)a.V + off + 8 * l16;
-      r.v[2 * u] = *(const float4*)p;
-      r.v[2 * u + 1] = *(const float4*)(p + 4);
-    } else {
-      r.v[u] = *(const uint4*)((const uint16_t*)a.V + off + 8 * l16);
+      // a vector past the end maps past n_last: offset >= the resource size
+      const uint32_t off = (uint32_t)((n - n0) * row_bytes) + h * (kD * ESZ) + 8 * ESZ * l16;
+      if (rows) rows[u] = v < nv ? (a.slots ? a.slots[n] : (int64_t)n) : -1;
+      if constexpr (F32IN) {
+        r.v[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        r.v[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+      } else {
+        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      }
     }
   }
 }
 
 template <int BITS, int QK, bool F32IN, bool DENSE>
-__global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a) {
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(F32IN && QK ? 3 : 4)))
+values_kernel(const ValuesArgs a) {
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
   constexpr int NSC = QK ? 4 : 1;
-  __shared__ __align__(16) uint8_t rec_lds[kVecs * REC];
-  __shared__ __align__(16) uint16_t sc_lds[kVecs * NSC];
-  __shared__ __align__(16) uint16_t zr_lds[QK ? kVecs * 4 : 8];
-  __shared__ int64_t row_lds[DENSE ? 1 : kVecs];
-  __shared__ float ss_lds[kWaves][kPerWave];          // sum of squares per vector
-  __shared__ __align__(16) float tp_lds[kWaves][4][kU];  // per (sub, u): step, or the 2-bit "> -step" threshold
-  __shared__ __align__(16) float tc_lds[kWaves][4][kU];  // 2-bit "> step" threshold
-  __shared__ __align__(16) uint32_t tb_lds[kWaves][4][kU];  // 2-bit ">= 0" bound on the raw word
+  __shared__ __align__(16) uint8_t rec_lds[2][kVecs * REC];
+  __shared__ __align__(16) uint16_t sc_lds[2][kVecs * NSC];
+  __shared__ __align__(16) uint16_t zr_lds[2][QK ? kVecs * 4 : 8];
+  __shared__ int64_t row_lds[2][DENSE ? 1 : kVecs];
+  __shared__ float ss_lds[kWaves][kPerWave];              // sum of squares per vector
+  __shared__ __align__(16) float4 th_lds[kWaves][kPerWave];  // per vector: thresholds / step
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63;
   const int sub = lane >> 4, l16 = lane & 15;
   const int64_t nv = a.n_tokens * a.n_heads;
-  const uint32_t last = (uint32_t)(nv - 1);
-  const int64_t n_iter = (nv + kVecs - 1) / kVecs;
-  int64_t it = blockIdx.x;
+  const uint32_t n_iter = (uint32_t)((nv + kVecs - 1) / kVecs);
+  uint32_t it = blockIdx.x;
   if (it >= n_iter) return;
 
-  auto step = [&](RawVals<F32IN>& cur, int64_t* rcur, RawVals<F32IN>& nxt, int64_t* rnxt)
+  auto step = [&](RawVals<F32IN>& cur, int64_t* rcur, RawVals<F32IN>& nxt, int64_t* rnxt, int par)
       __attribute__((always_inline)) -> bool {
-    const int64_t it_next = it + gridDim.x;
+    const uint32_t it_next = it + gridDim.x;
     const bool has_next = it_next < n_iter;
-    if (has_next) load_vals<F32IN, DENSE>(nxt, rnxt, a, (uint32_t)(it_next * kVecs) + wave * kPerWave + sub, l16, last);
+    if (has_next) load_vals<F32IN, DENSE>(nxt, rnxt, a, it_next, wave, sub, l16);
 
     auto unpack = [&](int u, float* x) __attribute__((always_inline)) {
       if constexpr (F32IN) {
-        const float4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
-        x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w; x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+        const u32x4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[e] = __uint_as_float(p[e]); x[4 + e] = __uint_as_float(q[e]); }
       } else {
-        const uint4 p = cur.v[u];
-        x[0] = bf16lo_to_f32(p.x); x[1] = bf16hi_to_f32(p.x);
-        x[2] = bf16lo_to_f32(p.y); x[3] = bf16hi_to_f32(p.y);
-        x[4] = bf16lo_to_f32(p.z); x[5] = bf16hi_to_f32(p.z);
-        x[6] = bf16lo_to_f32(p.w); x[7] = bf16hi_to_f32(p.w);
+        const u32x4 p = cur.v[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo_to_f32(p[e]); x[2 * e + 1] = bf16hi_to_f32(p[e]); }
       }
     };
     auto store_codes = [&](int vloc, uint32_t packed) __attribute__((always_inline)) {
       // this lane's 8 codes: BITS bytes at record offset BITS * l16
-      uint8_t* dst = &rec_lds[vloc * REC + BITS * l16];
+      uint8_t* dst = &rec_lds[par][vloc * REC + BITS * l16];
       if constexpr (BITS == 2) {
         *(uint16_t*)dst = (uint16_t)packed;
       } else if constexpr (BITS == 4) {
@@ -129,7 +151,7 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
     if constexpr (!DENSE) {
 #pragma unroll
       for (int u = 0; u < kU; ++u)
-        if (l16 == 0) row_lds[wave * kPerWave + 4 * u + sub] = rcur[u];
+        if (l16 == 0) row_lds[par][wave * kPerWave + 4 * u + sub] = rcur[u];
     }
 
     if constexpr (QK == 0) {
@@ -145,7 +167,7 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
         P = dpp_sum16(P);
         if (l16 == 0) ss_lds[wave][4 * u + sub] = P;
       }
-      // (2) one lane per vector: step, fp16 scale and threshold
+      // (2) one lane per vector: step, fp16 scale and thresholds
       if (lane < kPerWave) {
         const float P = ss_lds[wave][lane];
         const float ms = P * 0.0078125f;
@@ -155,79 +177,62 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
         const float d32 = twoC / (float)(L - 1);
         const uint16_t sc = f16_sat_bits(d32);
         const float delta = f16_bits_to_f32(sc);
-        sc_lds[wave * kPerWave + lane] = sc;
+        sc_lds[par][wave * kPerWave + lane] = sc;
         const float tp = delta == 0.0f ? __builtin_inff() : delta;  // +inf for a zero step
+        float4 th;
         if constexpr (BITS == 2) {
           // Midpoint tests A = [x > -step], B = [x >= 0], C = [x > step]
           // (ties as in the nearest-level rule).  bf16 input: A and C are
           // decided on the raw word (bf16_gt_threshold), B as an unsigned
           // bound (x >= 0 or x = -0); a zero step makes A and B always true
           // and C never: code 2.
-          tp_lds[wave][lane & 3][lane >> 2] = F32IN ? -tp : bf16_gt_threshold(-tp);
-          tc_lds[wave][lane & 3][lane >> 2] = F32IN ? tp : bf16_gt_threshold(tp);
-          tb_lds[wave][lane & 3][lane >> 2] = delta == 0.0f ? 0xFFFFFFFFu : (F32IN ? 0x80000000u : 0x8000FFFFu);
+          th.x = F32IN ? -tp : bf16_gt_threshold(-tp);
+          th.y = F32IN ? tp : bf16_gt_threshold(tp);
+          th.z = __uint_as_float(delta == 0.0f ? 0xFFFFFFFFu : (F32IN ? 0x80000000u : 0x8000FFFFu));
+          th.w = 0.0f;
         } else {
           // the step itself (+inf for a zero step, whose reciprocal 0 then yields code L/2)
-          tp_lds[wave][lane & 3][lane >> 2] = tp;
+          th.x = tp;
+          th.y = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
+          th.z = th.w = 0.0f;
         }
+        th_lds[wave][lane] = th;
       }
       // (3) codes
-      float tp[kU];
-      {
-        const float4 t0 = *(const float4*)&tp_lds[wave][sub][0];
-        const float4 t1 = *(const float4*)&tp_lds[wave][sub][4];
-        tp[0] = t0.x; tp[1] = t0.y; tp[2] = t0.z; tp[3] = t0.w;
-        tp[4] = t1.x; tp[5] = t1.y; tp[6] = t1.z; tp[7] = t1.w;
-      }
-      if constexpr (BITS == 2) {
-        float tc[kU];
-        uint32_t tb[kU];
-        {
-          const float4 c0 = *(const float4*)&tc_lds[wave][sub][0];
-          const float4 c1 = *(const float4*)&tc_lds[wave][sub][4];
-          tc[0] = c0.x; tc[1] = c0.y; tc[2] = c0.z; tc[3] = c0.w;
-          tc[4] = c1.x; tc[5] = c1.y; tc[6] = c1.z; tc[7] = c1.w;
-          const uint4 b0 = *(const uint4*)&tb_lds[wave][sub][0];
-          const uint4 b1 = *(const uint4*)&tb_lds[wave][sub][4];
-          tb[0] = b0.x; tb[1] = b0.y; tb[2] = b0.z; tb[3] = b0.w;
-          tb[4] = b1.x; tb[5] = b1.y; tb[6] = b1.z; tb[7] = b1.w;
-        }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < kU; ++u) {
+        const float4 th = th_lds[wave][4 * u + sub];
+        if constexpr (BITS == 2) {
           // the 8 words to test, channel order: bf16 -> low halves shifted up,
           // high halves raw; fp32 -> the values' bits
           uint32_t w[8];
           if constexpr (F32IN) {
-            const float4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
-            w[0] = __float_as_uint(p.x); w[1] = __float_as_uint(p.y); w[2] = __float_as_uint(p.z);
-            w[3] = __float_as_uint(p.w); w[4] = __float_as_uint(q.x); w[5] = __float_as_uint(q.y);
-            w[6] = __float_as_uint(q.z); w[7] = __float_as_uint(q.w);
+            const u32x4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { w[e] = p[e]; w[4 + e] = q[e]; }
           } else {
-            const uint4 p = cur.v[u];
-            w[0] = p.x << 16; w[1] = p.x; w[2] = p.y << 16; w[3] = p.y;
-            w[4] = p.z << 16; w[5] = p.z; w[6] = p.w << 16; w[7] = p.w;
+            const u32x4 p = cur.v[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { w[2 * e] = p[e] << 16; w[2 * e + 1] = p[e]; }
           }
-          const uint32_t tbl = F32IN ? tb[u] : (tb[u] & 0xFFFF0000u);  // low halves are exact
+          const uint32_t tb = __float_as_uint(th.z);
+          const uint32_t tbl = F32IN ? tb : (tb & 0xFFFF0000u);  // low halves are exact
           uint64_t m[16];
 #pragma unroll
           for (int e = 7; e >= 0; --e) {
-            const Sym2Masks k = sym2_masks_raw(w[e], tp[u], (e & 1) ? tb[u] : tbl, tc[u]);
+            const Sym2Masks k = sym2_masks_raw(w[e], th.x, (e & 1) ? tb : tbl, th.y);
             m[2 * (7 - e)] = k.b1;
             m[2 * (7 - e) + 1] = k.b0;
           }
           uint32_t packed = shift_in8(0u, m);
           packed = shift_in8(packed, m + 8);
           store_codes(wave * kPerWave + 4 * u + sub, packed);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        } else {
           float x[8];
           unpack(u, x);
           uint32_t packed = 0;
-          const float rd = tp[u] == __builtin_inff() ? 0.0f : __builtin_amdgcn_rcpf(tp[u]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], tp[u], rd) << (BITS * e);
+          for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], th.x, th.y) << (BITS * e);
           // keep the word 32 bits wide so code counts compile to compare + add-with-carry
           asm("" : "+v"(packed));
           store_codes(wave * kPerWave + 4 * u + sub, packed);
@@ -273,8 +278,8 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
           packed |= c << (BITS * e);
         }
         if ((l16 & 3) == 0) {
-          sc_lds[vloc * 4 + (l16 >> 2)] = sh;
-          zr_lds[vloc * 4 + (l16 >> 2)] = zh;
+          sc_lds[par][vloc * 4 + (l16 >> 2)] = sh;
+          zr_lds[par][vloc * 4 + (l16 >> 2)] = zh;
         }
         store_codes(vloc, packed);
       }
@@ -282,23 +287,25 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the prefetch has landed
     __syncthreads();
 
-    // write back: records (BITS 16-byte chunks each) and scales (+ zeros)
-    const int64_t vb = it * kVecs;
+    // write back: records (BITS 16-byte chunks each) and scales (+ zeros).  The
+    // staging buffers alternate, so the next iteration may fill the other one
+    // while these stores still read this one.
+    const int64_t vb = (int64_t)it * kVecs;
     if constexpr (DENSE) {
       const int64_t nvalid = nv - vb < kVecs ? nv - vb : kVecs;
       for (int c = tid; c < kVecs * BITS; c += 64 * kWaves)
-        if (c < nvalid * BITS) *(uint4*)(a.codes + vb * REC + 16 * c) = *(const uint4*)&rec_lds[16 * c];
+        if (c < nvalid * BITS) *(uint4*)(a.codes + vb * REC + 16 * c) = *(const uint4*)&rec_lds[par][16 * c];
       constexpr int SCB = kVecs * NSC * 2 / 16;  // 16-byte chunks of scales
       for (int c = tid; c < SCB; c += 64 * kWaves) {
         const int64_t first = (int64_t)c * 8 / NSC;  // first vector of the chunk
         if (first + 8 / NSC <= nvalid) {
-          *(uint4*)(a.scales + vb * NSC + 8 * c) = *(const uint4*)&sc_lds[8 * c];
-          if constexpr (QK != 0) *(uint4*)(a.zeros + vb * NSC + 8 * c) = *(const uint4*)&zr_lds[8 * c];
+          *(uint4*)(a.scales + vb * NSC + 8 * c) = *(const uint4*)&sc_lds[par][8 * c];
+          if constexpr (QK != 0) *(uint4*)(a.zeros + vb * NSC + 8 * c) = *(const uint4*)&zr_lds[par][8 * c];
         } else {
           for (int k = 0; k < 8; ++k)
             if ((int64_t)(8 * c + k) < nvalid * NSC) {
-              a.scales[vb * NSC + 8 * c + k] = sc_lds[8 * c + k];
-              if constexpr (QK != 0) a.zeros[vb * NSC + 8 * c + k] = zr_lds[8 * c + k];
+              a.scales[vb * NSC + 8 * c + k] = sc_lds[par][8 * c + k];
+              if constexpr (QK != 0) a.zeros[vb * NSC + 8 * c + k] = zr_lds[par][8 * c + k];
             }
         }
       }
@@ -306,43 +313,42 @@ __global__ void __launch_bounds__(64 * kWaves) values_kernel(const ValuesArgs a)
       for (int c = tid; c < kVecs * BITS; c += 64 * kWaves) {
         const int vloc = c / BITS, k = c - vloc * BITS;
         const int64_t v = vb + vloc;
-        const int64_t row = row_lds[vloc];
+        const int64_t row = row_lds[par][vloc];
         if (v < nv && row >= 0 && row < a.n_rows) {
           const uint32_t n = div_heads((uint32_t)v, a);
           const int h = (int)((uint32_t)v - n * (uint32_t)a.n_heads);
-          *(uint4*)(a.codes + (row * a.n_heads + h) * REC + 16 * k) = *(const uint4*)&rec_lds[vloc * REC + 16 * k];
+          *(uint4*)(a.codes + (row * a.n_heads + h) * REC + 16 * k) = *(const uint4*)&rec_lds[par][vloc * REC + 16 * k];
         }
       }
       for (int vloc = tid; vloc < kVecs; vloc += 64 * kWaves) {
         const int64_t v = vb + vloc;
-        const int64_t row = row_lds[vloc];
+        const int64_t row = row_lds[par][vloc];
         if (v < nv && row >= 0 && row < a.n_rows) {
           const uint32_t n = div_heads((uint32_t)v, a);
           const int h = (int)((uint32_t)v - n * (uint32_t)a.n_heads);
           const int64_t slot = row * a.n_heads + h;
           if constexpr (QK == 0) {
-            a.scales[slot] = sc_lds[vloc];
+            a.scales[slot] = sc_lds[par][vloc];
           } else {
-            const uint16_t* s = &sc_lds[vloc * 4];
-            const uint16_t* z = &zr_lds[vloc * 4];
-            *(uint2*)(a.scales + slot * 4) = make_uint2(s[0] | ((uint32_t)s[1] << 16), s[2] | ((uint32_t)s[3] << 16));
-            *(uint2*)(a.zeros + slot * 4) = make_uint2(z[0] | ((uint32_t)z[1] << 16), z[2] | ((uint32_t)z[3] << 16));
+            const uint16_t* sp = &sc_lds[par][vloc * 4];
+            const uint16_t* zp = &zr_lds[par][vloc * 4];
+            *(uint2*)(a.scales + slot * 4) = make_uint2(sp[0] | ((uint32_t)sp[1] << 16), sp[2] | ((uint32_t)sp[3] << 16));
+            *(uint2*)(a.zeros + slot * 4) = make_uint2(zp[0] | ((uint32_t)zp[1] << 16), zp[2] | ((uint32_t)zp[3] << 16));
           }
         }
       }
     }
-    __syncthreads();
     if (has_next) it = it_next;
     return has_next;
   };
 
   RawVals<F32IN> ra, rb;
-  int64_t rowa[kU], rowb[kU];
-  load_vals<F32IN, DENSE>(ra, rowa, a, (uint32_t)(it * kVecs) + wave * kPerWave + sub, l16, last);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  int64_t rowa[DENSE ? 1 : kU], rowb[DENSE ? 1 : kU];
+  load_vals<F32IN, DENSE>(ra, DENSE ? nullptr : rowa, a, it, wave, sub, l16);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing in flight when the loop starts
   while (true) {
-    if (!step(ra, rowa, rb, rowb)) break;
-    if (!step(rb, rowb, ra, rowa)) break;
+    if (!step(ra, rowa, rb, rowb, 0)) break;
+    if (!step(rb, rowb, ra, rowa, 1)) break;
   }
 }
 

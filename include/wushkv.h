@@ -40,7 +40,7 @@
  * on the hot path):
  *   K, V     [n_tokens][n_heads][128], element (n,h,c) at base + n*token_stride
  *            + h*128 + c; bf16 or fp32; 16-byte aligned rows; a token row
- *            (token_stride elements) spans at most 2^26 bytes; n_tokens is
+ *            (token_stride elements) spans at most 2^24 bytes; n_tokens is
  *            below 2^31 - 128.
  *   codes    [n_rows][n_heads][16*bits] bytes.
  *   scales   fp16; sym: [n_rows][n_heads]; affine: [n_rows][n_heads][4].
