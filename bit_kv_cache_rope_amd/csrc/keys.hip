@@ -43,6 +43,7 @@ namespace {
 constexpr int kTile = 64;      // tokens per tile
 constexpr int kNB = 2;         // 32-token MFMA column blocks per tile
 constexpr int kCsStride = 66;  // float2 per token row of the cos/sin tile (64 + 2 pad)
+constexpr int kXcds = 8;       // accelerator complex dies of an MI355X (blocks spread round-robin)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -161,8 +162,19 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // rotates the RoPE pairs of k step wq (channels 16 wq + 8 (l / 32) + 0..7
   // and their partners 64 higher).
   const int hh = wave_u >> 2, wq = wave_u & 3;
-  const int grp = blockIdx.x % a.n_groups;
-  const int first_tile = blockIdx.x / a.n_groups;
+  // Blocks are dispatched to the chip's XCDs round-robin (block b on XCD
+  // b % 8).  When blocks_per_group is a multiple of 8, the head groups of one
+  // tile run on the same XCD, so the tile's cos/sin rows are fetched into
+  // that XCD's L2 once for all its head groups.
+  int grp, first_tile;
+  if (a.blocks_per_group % kXcds == 0) {
+    const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+    grp = q % a.n_groups;
+    first_tile = (q / a.n_groups) * kXcds + x;
+  } else {
+    grp = blockIdx.x % a.n_groups;
+    first_tile = blockIdx.x / a.n_groups;
+  }
   const int h = grp * HG + hh;
   // Token and tile indices fit 32 bits (n_tokens < 2^31 - 2^7).
   const int n_tok = (int)a.n_tokens;
@@ -593,6 +605,7 @@ hipError_t launch_one(KeysArgs a, int cus, hipStream_t st) {
   const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
   int64_t b = (int64_t)cus * resident_blocks(k, 256 * HG) / a.n_groups;
   b = b < 1 ? 1 : (b > n_tiles ? n_tiles : b);
+  if (b >= kXcds) b -= b % kXcds;  // multiple of 8: XCD-aware tile mapping
   a.blocks_per_group = (int)b;
   k<<<dim3((unsigned)(a.n_groups * b)), 256 * HG, 0, st>>>(a);
   return hipGetLastError();
