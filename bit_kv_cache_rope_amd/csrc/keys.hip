@@ -136,32 +136,37 @@ __device__ __forceinline__ void unpack8(const RawKeys<F32IN>& r, int nb, int j, 
 
 template <int BITS, int QK, bool F32IN, int HG, bool YOUT>
 __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
-  constexpr int NT = 256 * HG;
-  constexpr int NW = NT / 64;
-  constexpr int TPW = kTile / NW;  // cos/sin rows each wave copies per tile
+  // Head groups: with four heads per block the block runs two groups of two
+  // heads (eight waves each), one phase apart (see the interval loop below).
+  constexpr int NG = HG == 4 ? 2 : 1;
+  constexpr int HGG = HG / NG;      // heads per group
+  constexpr int WG = 4 * HGG;       // waves per group
+  constexpr int TPW = kTile / WG;   // cos/sin rows each wave of group 0 loads per tile
+  constexpr int NCS = TPW / 2;      // ... two rows per load
+  constexpr int CSB = NG;           // cos/sin tile buffers (by tile parity when two groups)
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
-  constexpr int RECROW = HG * REC + 16;  // LDS row of one token's records (+16 B pad)
-  constexpr int NSC = QK ? 8 : 1;        // fp16 values per (token, head): sym 1; affine 4 + 4
-  constexpr int RB = 4 * BITS;           // bits in a run of 4 codes
+  constexpr int RECROW = HGG * REC + 16;  // LDS row of one token's records in a group (+16 B pad)
+  constexpr int NSC = QK ? 8 : 1;         // fp16 values per (token, head): sym 1; affine 4 + 4
+  constexpr int RB = 4 * BITS;            // bits in a run of 4 codes
   constexpr int ESZ = F32IN ? 4 : 2;
 
-  __shared__ __align__(16) float2 cs_lds[kTile][kCsStride];   // cos/sin rows of the tile being rotated
-  __shared__ __align__(16) bf16x8 xb_lds[HG][kNB][8][64];     // rotated operands shared by a head's waves
+  __shared__ __align__(16) float2 cs_lds[CSB][kTile][kCsStride];  // cos/sin rows of a tile
+  __shared__ __align__(16) bf16x8 xb_lds[HG][kNB][8][64];        // rotated operands shared by a head's waves
   __shared__ int32_t slot_lds[2][kTile];  // cache row per token, -1: no store; tile j in slot j & 1
   __shared__ float red_lds[HG][4][kTile];
-  __shared__ __align__(16) uint8_t rec_lds[kTile][RECROW];
-  __shared__ __align__(16) uint16_t sc_lds[kTile][HG * NSC];
+  __shared__ __align__(16) uint8_t rec_lds[NG][kTile][RECROW];
+  __shared__ __align__(16) uint16_t sc_lds[NG][kTile][HGG * NSC];
 
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // The lane index is re-derived at every tile (see the top of `step`), so
-  // the per-lane offsets are recomputed there rather than held in registers
-  // across the loop.
+  // The lane index is re-derived at every interval (see the top of the
+  // loop), so the per-lane offsets are recomputed there rather than held in
+  // registers across it.
   int lane = threadIdx.x & 63, lh = lane >> 5, col = lane & 31;
-  // Four waves per head: wave wq holds rows 32 wq .. 32 wq + 31 of T~ and
-  // rotates the RoPE pairs of k step wq (channels 16 wq + 8 (l / 32) + 0..7
-  // and their partners 64 higher).
+  // Four waves per head: wave wq holds rows 32 wq .. 32 wq + 31 of T~.
   const int hh = wave_u >> 2, wq = wave_u & 3;
+  const int g = hh / HGG, hg = hh - g * HGG;  // head group and head within it
+  const int gw = wave_u - g * WG;             // wave within the group
   // Blocks are dispatched to the chip's XCDs round-robin (block b on XCD
   // b % 8).  When blocks_per_group is a multiple of 8, the head groups of one
   // tile run on the same XCD, so the tile's cos/sin rows are fetched into
@@ -181,6 +186,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   const int n_tiles = (n_tok + kTile - 1) / kTile;
   if (first_tile >= n_tiles) return;  // uniform over the block
   const int tile_step = a.blocks_per_group;
+  const int count = (n_tiles - first_tile + tile_step - 1) / tile_step;  // tiles of this block
+  auto tile_of = [&](int j) __attribute__((always_inline)) -> int { return first_tile + j * tile_step; };
   const uint32_t row_bytes = (uint32_t)(a.stride * ESZ);  // bytes between tokens (<= 2^24)
   // Tokens of tile t that exist (0 past the end).
   // (readfirstlane keeps the value in an SGPR: a buffer resource built from a
@@ -200,16 +207,15 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   auto keys_off = [&]() __attribute__((always_inline)) -> uint32_t {
     return (16 * wq + (lane >> 3)) * row_bytes + 8 * (lane & 7) * ESZ;
   };
-  // cos/sin rows: wave w fills rows TPW*w .. TPW*w + TPW - 1 of cs_lds, two
-  // per 16-byte-per-lane load (lanes 0-31 one row, lanes 32-63 the next).
-  // posv[i] is the position of row TPW*w + 2i + (l / 32) of a tile (0 past
-  // the end), csv[i] the matching half-row of the table.
-  constexpr int NCS = TPW / 2;
+  // cos/sin rows (group 0 only): its wave w fills rows TPW*w .. TPW*w + TPW - 1
+  // of a tile buffer, two per 16-byte-per-lane load (lanes 0-31 one row,
+  // lanes 32-63 the next).  posv[i] is the position of row TPW*w + 2i + (l / 32)
+  // of a tile (0 past the end), csv[i] the matching half-row of the table.
   auto load_pos = [&](int t, int* pv) __attribute__((always_inline)) {
     const rsrc_t rs = buffer_rsrc(a.pos + t * kTile, tile_len(t) * 4u);
 #pragma unroll
     for (int i = 0; i < NCS; ++i)
-      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (TPW * wave_u + 2 * i + lh), 0, 0);
+      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (TPW * gw + 2 * i + lh), 0, 0);
   };
   auto load_cs = [&](const int* pv, u32x4* cv) __attribute__((always_inline)) {
 #pragma unroll
@@ -218,9 +224,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       cv[i] = *(const u32x4*)(a.cs + (int64_t)p * kPairs + 2 * col);
     }
   };
-  auto store_cs = [&](const u32x4* cv) __attribute__((always_inline)) {
+  auto store_cs = [&](const u32x4* cv, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NCS; ++i) *(u32x4*)&cs_lds[TPW * wave_u + 2 * i + lh][2 * col] = cv[i];
+    for (int i = 0; i < NCS; ++i) *(u32x4*)&cs_lds[buf][TPW * gw + 2 * i + lh][2 * col] = cv[i];
   };
   // Cache rows of tile t's tokens, loaded by wave 0 (lane = token): the raw
   // slot words, turned into a row or -1 by row_of once they have arrived.
@@ -234,15 +240,16 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     return (tok < n_tok && row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
   };
 
-  RawKeys<F32IN> r;  // this tile's keys until RoPE has read them, then the next tile's
-  int tile = first_tile;
+  RawKeys<F32IN> r;  // a tile's keys until RoPE has read them, then the next tile's
   // Prologue: the first tile's keys, rows, positions and cos/sin; T~.
-  load_keys<F32IN>(r, keys_rsrc(tile), keys_off(), 8 * row_bytes);
+  load_keys<F32IN>(r, keys_rsrc(first_tile), keys_off(), 8 * row_bytes);
   u32x2 row_w = {0u, 0u};  // read only when a.slots is set
-  if (a.slots && wave_u == 0) row_w = load_rows(tile);
-  int posv[NCS], posv_n[NCS];  // positions of this tile's rows, then of the next tile's
+  int posv[NCS], posv_n[NCS];  // positions of the next tile's rows, then of the one after
   u32x4 csv[NCS];
-  load_pos(tile, posv);
+  if (g == 0) {
+    if (a.slots && wave_u == 0) row_w = load_rows(first_tile);
+    load_pos(first_tile, posv);
+  }
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
   bf16x8 A[8];
   {
@@ -250,44 +257,95 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
   }
-  load_cs(posv, csv);
-  load_pos(tile + tile_step, posv);
+  if (g == 0) {
+    load_cs(posv, csv);
+    load_pos(tile_of(1), posv);
+  }
   // Nothing may be in flight when the loop starts: its first wait would
   // otherwise also cover the previous tile's stores on later iterations.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  store_cs(csv);
-  if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, tile);
+  if (g == 0) {
+    store_cs(csv, 0);
+    if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, first_tile);
+  }
   __syncthreads();
 
-  // One tile per call (par = the tile's ordinal & 1).
   f32x16 acc[kNB];
-  auto step = [&](int par) __attribute__((always_inline)) -> bool {
-    asm volatile("" : "+v"(lane));
-    lh = lane >> 5;
-    col = lane & 31;
-    const int tid = 64 * wave_u + lane;
-    const int next = tile + tile_step;
-    const bool has_next = next < n_tiles;
-    // ---- the next tile's rows and cos/sin rows, the positions of the tile
-    // after (zeros past the end); all land before the wait ahead of B3
-    if (a.slots && wave_u == 0) row_w = load_rows(next);
-    load_cs(posv, csv);
-    load_pos(next + tile_step, posv_n);
+  int tid = threadIdx.x;
 
-    // ---- RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS.
+  // ---- phase 0 of the group's j-th tile: the stores of tile j - 1, then (for
+  // j < count) the loads for later tiles, RoPE and the next tile's keys.
+  auto phase0 = [&](int j) __attribute__((always_inline)) {
+    if constexpr (!YOUT) {
+      if (j >= 1) {
+        const int sb = (j - 1) & 1;
+        // each token's group records are contiguous in the cache row
+        // (16-byte chunks, at most one per thread), then its scales (and zeros)
+        constexpr int CPT = HGG * BITS;  // 16-byte chunks per token
+        constexpr int NCH = kTile * CPT;  // <= 64 * WG
+        const int tg = tid - 64 * WG * g;
+        const uint32_t row_rec = (uint32_t)a.n_heads * REC;  // bytes per cache row
+        if (NCH == 64 * WG || tg < NCH) {
+          const int n = tg / CPT, k = tg - n * CPT;
+          const int32_t row = slot_lds[sb][n];
+          if (row >= 0) {
+            const uint4 v = *(const uint4*)&rec_lds[g][n][16 * k];
+            uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + ((grp * HG + g * HGG) * REC + 16 * k);
+            *(uint4*)dst = v;
+          }
+        }
+        if constexpr (QK == 0) {
+          // one store of the group's HGG fp16 steps per token, by its last wave
+          const int n = tg - (64 * WG - 64);
+          if (n >= 0) {
+            const int32_t row = slot_lds[sb][n];
+            if (row >= 0) {
+              uint16_t* dst = a.scales + (uint64_t)(uint32_t)row * a.n_heads + grp * HG + g * HGG;
+              if constexpr (HGG == 2) {
+                *(uint32_t*)dst = *(const uint32_t*)&sc_lds[g][n][0];
+              } else {
+                *dst = sc_lds[g][n][0];
+              }
+            }
+          }
+        } else {
+          // per (token, head): 4 scales and 4 zeros, 8 bytes each
+          const int c = tg - (64 * WG - 64 * HGG);
+          if (c >= 0) {
+            const int n = c / HGG, jh = c - n * HGG;
+            const int32_t row = slot_lds[sb][n];
+            if (row >= 0) {
+              const uint64_t slot = (uint64_t)(uint32_t)row * a.n_heads + grp * HG + g * HGG + jh;
+              *(uint2*)(a.scales + slot * 4) = *(const uint2*)&sc_lds[g][n][jh * 8];
+              *(uint2*)(a.zeros + slot * 4) = *(const uint2*)&sc_lds[g][n][jh * 8 + 4];
+            }
+          }
+        }
+      }
+    }
+    if (j >= count) return;
+    const int next = tile_of(j + 1);
+    if (g == 0) {
+      // the next tile's cache rows and the positions of the tile after (zeros
+      // past the end); they land before phase 2 ends
+      if (a.slots && wave_u == 0) row_w = load_rows(next);
+      load_pos(tile_of(j + 2), posv_n);
+    }
+    // RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS.
     // Chunk c = l % 8 of token t is channels 8c .. 8c+7 (k step c / 2, lane
     // half c % 2 of the B operand) and its partner chunk (k step 4 + c / 2).
     // B-operand rows are stored with lane index lane' ^ (4 (s % 4) + 2 (lane' / 32)),
     // which for this chunk is lane' ^ 2c: the eight chunks of a token land in
     // eight different bank groups, and each row stays a permutation of itself.
+    const int cb = j & (CSB - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c8 = lane & 7, g = lane >> 3;
-      const int t = 16 * wq + 8 * j + g;  // token within the tile
+    for (int jj = 0; jj < 2; ++jj) {
+      const int c8 = lane & 7, gt = lane >> 3;
+      const int t = 16 * wq + 8 * jj + gt;  // token within the tile
       float ka[8], kb[8];
-      unpack8<F32IN>(r, j, 0, ka);
-      unpack8<F32IN>(r, j, 1, kb);
-      const float4* csp = (const float4*)&cs_lds[t][8 * c8];
+      unpack8<F32IN>(r, jj, 0, ka);
+      unpack8<F32IN>(r, jj, 1, kb);
+      const float4* csp = (const float4*)&cs_lds[cb][t][8 * c8];
       float c[8], sn[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -307,11 +365,16 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       xb_lds[hh][nb][s0][ls] = pack8(xa);
       xb_lds[hh][nb][s0 + 4][ls] = pack8(xb);
     }
-    // ---- the next tile's keys, into the registers RoPE has just consumed
+    // the next tile's keys, into the registers RoPE has just consumed
     load_keys<F32IN>(r, keys_rsrc(next), keys_off(), 8 * row_bytes);
-    __syncthreads();  // B1: operands in LDS; everyone is done with cs_lds
+  };
 
-    // ---- y = T~ x~ for this wave's 32 rows and both column blocks
+  // ---- phase 1: y = T~ x~ for this wave's 32 rows and both column blocks,
+  // then (symmetric) the sums of squares.
+  auto phase1 = [&](int j) __attribute__((always_inline)) {
+    // group 0: the next tile's cos/sin rows, into registers until phase 2 ends
+    // (loaded here rather than in phase 0 so they are not live during RoPE)
+    if (g == 0) load_cs(posv, csv);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = (f32x16){};
     // B operands one k step ahead of the MFMAs that use them; the scheduling
@@ -336,11 +399,11 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         for (int nb = 0; nb < kNB; ++nb) bc[nb] = bn[nb];
       }
     }
-
     if constexpr (YOUT) {
+      const int t = tile_of(j);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const int64_t tok = tile * kTile + 32 * nb + col;
+        const int64_t tok = (int64_t)t * kTile + 32 * nb + col;
         if (tok < a.n_tokens) {
           float* yo = a.y_out + (tok * a.n_heads + h) * kD;
 #pragma unroll
@@ -351,38 +414,39 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           }
         }
       }
-      barrier_lds();  // B2 (kept so that every tile passes three barriers)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_of(row_w, next);
-      store_cs(csv);
-      __syncthreads();  // B3
-    } else {
+    } else if constexpr (QK == 0) {
+      // Sum of squares as the contiguous pairwise tree over rows 0..127:
+      // runs of 4 in-lane, pairs of runs across lanes l and l^32, the 32
+      // rows of this wave, then the four waves' sums ((0 + 1) + (2 + 3)).
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        float P8[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float q0 = acc[nb][4 * q] * acc[nb][4 * q];
+          const float q1 = acc[nb][4 * q + 1] * acc[nb][4 * q + 1];
+          const float q2 = acc[nb][4 * q + 2] * acc[nb][4 * q + 2];
+          const float q3 = acc[nb][4 * q + 3] * acc[nb][4 * q + 3];
+          const float p4 = (q0 + q1) + (q2 + q3);
+          const Halves x = halves(p4);
+          P8[q] = __uint_as_float(x.lo) + __uint_as_float(x.hi);
+        }
+        const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
+        if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
+      }
+    }
+  };
+
+  // ---- phase 2: scales, codes and records of tile j -> LDS; then every load
+  // has landed and (group 0) the next tile's cos/sin rows and cache rows go to LDS.
+  auto phase2 = [&](int j) __attribute__((always_inline)) {
+    if constexpr (!YOUT) {
       // Output element acc[nb][i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of
       // token 32*nb + col.  run[nb][q] packs the codes of acc[nb][4q .. 4q+3]
       // (4 consecutive rows), LSB first.
       uint32_t run[kNB][4];
       uint32_t W2[kNB] = {};  // 2-bit symmetric: whole words of codes
       if constexpr (QK == 0) {
-        // Sum of squares as the contiguous pairwise tree over rows 0..127:
-        // runs of 4 in-lane, pairs of runs across lanes l and l^32, the 32
-        // rows of this wave, then the four waves' sums ((0 + 1) + (2 + 3)).
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          float P8[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float q0 = acc[nb][4 * q] * acc[nb][4 * q];
-            const float q1 = acc[nb][4 * q + 1] * acc[nb][4 * q + 1];
-            const float q2 = acc[nb][4 * q + 2] * acc[nb][4 * q + 2];
-            const float q3 = acc[nb][4 * q + 3] * acc[nb][4 * q + 3];
-            const float p4 = (q0 + q1) + (q2 + q3);
-            const Halves x = halves(p4);
-            P8[q] = __uint_as_float(x.lo) + __uint_as_float(x.hi);
-          }
-          const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
-          if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
-        }
-        barrier_lds();  // B2
         // One step per lane for token tt = 32 lh + col (the lane pair l, l^32
         // covers both column blocks): column block nb's step is then the
         // value of lane half nb.
@@ -394,7 +458,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         const float twoC = 2.0f * C;
         const float d32 = twoC / (float)(L - 1);
         const uint16_t dh = f16_sat_bits(d32);
-        if (wq == 0) sc_lds[tt][hh] = dh;
+        if (wq == 0) sc_lds[g][tt][hg] = dh;
         const Halves dd = halves(f16_bits_to_f32(dh));
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
@@ -408,11 +472,11 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             // A = [y > -step], B = [y >= 0], C = [y > step]; code bits B and
             // B ? C : A.
 #pragma unroll
-            for (int g = 3; g >= 0; --g) {  // 4 rows per add-with-carry block
+            for (int gq = 3; gq >= 0; --gq) {  // 4 rows per add-with-carry block
               uint64_t mk[8];
 #pragma unroll
               for (int e = 3; e >= 0; --e) {
-                const Sym2Masks k = sym2_masks(acc[nb][4 * g + e], -tp, tz, tp);
+                const Sym2Masks k = sym2_masks(acc[nb][4 * gq + e], -tp, tz, tp);
                 mk[2 * (3 - e)] = k.b1;
                 mk[2 * (3 - e) + 1] = k.b0;
               }
@@ -431,7 +495,6 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           }
         }
       } else {
-        barrier_lds();  // B2 (the affine groups are this wave's own rows)
         // Percentile-clipped affine quantizer, group = this wave's 32 rows of
         // a token, split between lanes l and l^32: two smallest and two
         // largest values by IEEE totalOrder, merged across the lane pair.
@@ -471,18 +534,18 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             run[nb][q] = rc;
           }
           if (lh == 0) {
-            sc_lds[32 * nb + col][hh * 8 + wq] = sh;
-            sc_lds[32 * nb + col][hh * 8 + 4 + wq] = zh;
+            sc_lds[g][32 * nb + col][hg * 8 + wq] = sh;
+            sc_lds[g][32 * nb + col][hg * 8 + 4 + wq] = zh;
           }
         }
       }
 
-      // ---- pack: runs of 4 codes -> 16 contiguous rows per lane -> LDS record row.
+      // pack: runs of 4 codes -> 16 contiguous rows per lane -> LDS record row.
       // Lane l (lh = 0) writes rows 0-15 of the block: its runs 0, 1
       // interleaved with those of lane l + 32; lane l + 32 writes rows 16-31.
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        uint8_t* dst = &rec_lds[32 * nb + col][hh * REC + BITS * (4 * wq + 2 * lh)];
+        uint8_t* dst = &rec_lds[g][32 * nb + col][hg * REC + BITS * (4 * wq + 2 * lh)];
         if constexpr (QK == 0 && BITS == 2) {
           // bytes {lane half 0: selectors 0-3, lane half 1: 4-7}: lh = 0 takes
           // bytes 0, 1 of both, lh = 1 bytes 2, 3
@@ -508,66 +571,47 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           }
         }
       }
-      // Every load of this wave has landed (next keys, rows, cos/sin rows,
-      // positions), so the stores below never queue behind a load.
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
-      if (wave_u == 0) slot_lds[par ^ 1][lane] = row_of(row_w, next);
-      store_cs(csv);  // RoPE of this tile finished reading cs_lds at B1
-      __syncthreads();  // B3
-
-      // ---- stores: each token's HG records are contiguous in the cache row
-      // (16-byte chunks, at most one per thread), then its scales (and zeros).
-      constexpr int CPT = HG * BITS;        // 16-byte chunks per token
-      constexpr int NCH = kTile * CPT;      // <= NT
-      const uint32_t row_rec = (uint32_t)a.n_heads * REC;  // bytes per cache row
-      if (NCH == NT || tid < NCH) {
-        const int n = tid / CPT, k = tid - n * CPT;
-        const int32_t row = slot_lds[par][n];
-        if (row >= 0) {
-          const uint4 v = *(const uint4*)&rec_lds[n][16 * k];
-          uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + (grp * HG * REC + 16 * k);
-          *(uint4*)dst = v;
-        }
-      }
-      if constexpr (QK == 0) {
-        // one store of the HG fp16 steps per token, by the last wave
-        const int n = tid - (NT - 64);
-        if (n >= 0) {
-          const int32_t row = slot_lds[par][n];
-          if (row >= 0) {
-            uint16_t* dst = a.scales + (uint64_t)(uint32_t)row * a.n_heads + grp * HG;
-            if constexpr (HG == 4) {
-              *(uint2*)dst = *(const uint2*)&sc_lds[n][0];
-            } else if constexpr (HG == 2) {
-              *(uint32_t*)dst = *(const uint32_t*)&sc_lds[n][0];
-            } else {
-              *dst = sc_lds[n][0];
-            }
-          }
-        }
-      } else {
-        // per (token, head): 4 scales and 4 zeros, 8 bytes each
-        const int c = tid - (NT - 64 * HG);
-        if (c >= 0) {
-          const int n = c / HG, jh = c - n * HG;
-          const int32_t row = slot_lds[par][n];
-          if (row >= 0) {
-            const uint64_t slot = (uint64_t)(uint32_t)row * a.n_heads + grp * HG + jh;
-            *(uint2*)(a.scales + slot * 4) = *(const uint2*)&sc_lds[n][jh * 8];
-            *(uint2*)(a.zeros + slot * 4) = *(const uint2*)&sc_lds[n][jh * 8 + 4];
-          }
-        }
-      }
     }
+    // Every load of this wave has landed (next keys; group 0: rows, cos/sin
+    // rows, positions), and its stores have drained.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+    if (g == 0) {
+      const int next = tile_of(j + 1);
+      if (wave_u == 0) slot_lds[(j + 1) & 1][lane] = row_of(row_w, next);
+      store_cs(csv, (j + 1) & (CSB - 1));
 #pragma unroll
-    for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
-    if (has_next) tile = next;
-    return has_next;
+      for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
+    }
   };
-  while (true) {
-    if (!step(0)) break;
-    if (!step(1)) break;
+
+  // Schedule.  Each group runs phase 0, 1, 2 of its tiles in turn with a
+  // block barrier after every phase; group 1 starts one barrier later (and
+  // group 0 ends one later), so group 1 trails group 0 by one phase: while one
+  // group's waves run their MFMA phase the other group's waves, on the same
+  // SIMDs, run VALU work.  Both groups pass the same number of barriers
+  // (3 count + 2), and every barrier orders the LDS hand-offs within and
+  // between the groups: cos/sin tile j lives in buffer j % CSB from group 0's
+  // phase 2 of tile j - 1 until group 1's phase 0 of tile j, and the cache
+  // rows of tile j in slot_lds[j % 2] until group 1's stores of tile j.
+  auto next_phase = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+    asm volatile("" : "+v"(lane));
+    lh = lane >> 5;
+    col = lane & 31;
+    tid = 64 * wave_u + lane;
+  };
+  if (NG == 2 && g == 1) next_phase();
+  for (int j = 0; j < count; ++j) {
+    phase0(j);
+    next_phase();
+    phase1(j);
+    next_phase();
+    phase2(j);
+    next_phase();
   }
+  phase0(count);  // the last tile's stores
+  next_phase();
+  if (NG == 2 && g == 0) next_phase();
 }
 
 // (cos, sin) of every position p < max_pos, pair i: entry p * 64 + i.
