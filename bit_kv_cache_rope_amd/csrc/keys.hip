@@ -466,22 +466,24 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           // A zero step becomes +inf (threshold / step) so every code comes out L/2.
           const float tp = delta == 0.0f ? __builtin_inff() : delta;
           if constexpr (BITS == 2) {
-            const float tz = delta == 0.0f ? -__builtin_inff() : 0.0f;
             // W2[nb]: the lane's 16 codes of the block, run q (4 rows) in byte
-            // q, shifted in from the last row down.  Midpoint tests
-            // A = [y > -step], B = [y >= 0], C = [y > step]; code bits B and
-            // B ? C : A.
+            // q, shifted in from the last row down (alignbit: w = 2w + bit 31
+            // of the operand).  Code = [y > -step] + [y >= 0] + [y > step]:
+            // the high bit is [y >= 0], the sign of y inverted (an MFMA result
+            // that starts from a +0 accumulator is never -0); the low bit is
+            // [y > t] with t = +-step carrying y's sign, i.e. the sign of
+            // t - y, which is +0 (bit clear) exactly at a tie.  A zero step
+            // gives code 2 everywhere.
+            const uint32_t db = __float_as_uint(delta);
+            uint32_t w = 0;
 #pragma unroll
-            for (int gq = 3; gq >= 0; --gq) {  // 4 rows per add-with-carry block
-              uint64_t mk[8];
-#pragma unroll
-              for (int e = 3; e >= 0; --e) {
-                const Sym2Masks k = sym2_masks(acc[nb][4 * gq + e], -tp, tz, tp);
-                mk[2 * (3 - e)] = k.b1;
-                mk[2 * (3 - e) + 1] = k.b0;
-              }
-              W2[nb] = shift_in8(W2[nb], mk);
+            for (int i = 15; i >= 0; --i) {
+              const float y = acc[nb][i];
+              const float t = __uint_as_float((__float_as_uint(y) & 0x80000000u) | db);
+              w = __builtin_amdgcn_alignbit(w, __float_as_uint(y), 31);
+              w = __builtin_amdgcn_alignbit(w, __float_as_uint(t - y), 31);
             }
+            W2[nb] = delta == 0.0f ? 0xAAAAAAAAu : w ^ 0xAAAAAAAAu;
           } else {
             const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
 #pragma unroll

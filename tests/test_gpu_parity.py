@@ -403,6 +403,37 @@ def test_keys_identity_equals_values_of_rope(env):
         assert_same_packed(g, r, "identity keys")
 
 
+def test_keys_exact_zero_outputs(env):
+    """Transformed keys that are exactly zero (cancellation and zero channels)
+    must come out as +0 from the MFMA and take code L/2 like the oracle's: at
+    position 0 RoPE is the identity, channels i + 64 copy channels i, and rows
+    r < 64 of T are e_r - e_(r+64) (T = [[I, -I], [0, I]] is invertible)."""
+    o = env["oracle"]
+    rng = np.random.default_rng(23)
+    n, H = 1000, 8
+    half = rng.integers(-8, 9, size=(n, H, 64)).astype(np.float32)
+    half[rng.random((n, H, 64)) < 0.3] = 0.0  # zero channels: signed-zero products
+    K32 = np.concatenate([half, half], axis=2)
+    K32[:, :, 5] = -0.0                        # negative zeros in both halves
+    K32[:, :, 69] = -0.0
+    Kb = (K32.view(np.uint32) >> 16).astype(np.uint16)  # exact: small integers
+    pos = np.zeros(n, np.int32)
+    T1 = np.eye(128, dtype=np.float32)
+    T1[np.arange(64), np.arange(64) + 64] = -1.0
+    T = np.stack([T1] * H)
+    say("exact-zero transformed keys: y bits")
+    yg = _y_gpu(env, Kb, pos, T)
+    zeros = (yg.view(np.uint32) & 0x7FFFFFFF) == 0
+    assert zeros[:, :, :64].all()
+    assert not (yg.view(np.uint32) == 0x80000000).any(), "an MFMA output is -0"
+    for kind, bits in (("sym", 2), ("sym", 3), ("affine", 2)):
+        q = _bkq(env, kind)
+        say(f"exact-zero transformed keys: codes {kind} {bits}")
+        g = packed_host(run_keys(env, Kb, pos, T, bits, q))
+        r = o.quantize_keys(Kb, pos, T, 1e6, bits, oracle_q(env, q))
+        assert_same_packed(g, r, "exact-zero keys")
+
+
 def test_decode_append_slots(env):
     s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
     w = s.WORKLOADS["decode_append"]
