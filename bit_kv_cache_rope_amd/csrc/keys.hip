@@ -289,9 +289,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           const int n = tg / CPT, k = tg - n * CPT;
           const int32_t row = slot_lds[sb][n];
           if (row >= 0) {
-            const uint4 v = *(const uint4*)&rec_lds[g][n][16 * k];
+            const u32x4 v = *(const u32x4*)&rec_lds[g][n][16 * k];
             uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + ((grp * HG + g * HGG) * REC + 16 * k);
-            *(uint4*)dst = v;
+            __builtin_nontemporal_store(v, (u32x4*)dst);  // written once, not read back here
           }
         }
         if constexpr (QK == 0) {

@@ -33,12 +33,19 @@ constexpr int kU = 4;                     // loads per lane per iteration
 constexpr int kPerWave = 4 * kU;          // vectors per wave per iteration
 constexpr int kVecs = kWaves * kPerWave;  // vectors per block per iteration
 constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+constexpr int kNT = 2;  // cache policy of the streaming loads: non-temporal (read once)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+// 16 bytes from LDS to global memory with a non-temporal store (the packed
+// cache is written once here and not read back by this kernel).
+__device__ __forceinline__ void store_nt16(void* dst, const void* lds_src) {
+  __builtin_nontemporal_store(*(const u32x4*)lds_src, (u32x4*)dst);
 }
 
 template <bool F32IN>
@@ -67,10 +74,10 @@ __device__ __forceinline__ void load_vals(RawVals<F32IN>& r, int64_t* rows, cons
     for (int u = 0; u < kU; ++u) {
       const uint32_t off = (uint32_t)(wave * kPerWave + 4 * u + sub) * (kD * ESZ) + 8 * ESZ * l16;
       if constexpr (F32IN) {
-        r.v[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        r.v[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+        r.v[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
+        r.v[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, kNT);
       } else {
-        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
       }
     }
   } else {
@@ -88,10 +95,10 @@ __device__ __forceinline__ void load_vals(RawVals<F32IN>& r, int64_t* rows, cons
       const uint32_t off = (uint32_t)((n - n0) * row_bytes) + h * (kD * ESZ) + 8 * ESZ * l16;
       if (rows) rows[u] = v < nv ? (a.slots ? a.slots[n] : (int64_t)n) : -1;
       if constexpr (F32IN) {
-        r.v[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        r.v[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+        r.v[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
+        r.v[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, kNT);
       } else {
-        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
       }
     }
   }
@@ -294,13 +301,13 @@ values_kernel(const ValuesArgs a) {
     if constexpr (DENSE) {
       const int64_t nvalid = nv - vb < kVecs ? nv - vb : kVecs;
       for (int c = tid; c < kVecs * BITS; c += 64 * kWaves)
-        if (c < nvalid * BITS) *(uint4*)(a.codes + vb * REC + 16 * c) = *(const uint4*)&rec_lds[par][16 * c];
+        if (c < nvalid * BITS) store_nt16(a.codes + vb * REC + 16 * c, &rec_lds[par][16 * c]);
       constexpr int SCB = kVecs * NSC * 2 / 16;  // 16-byte chunks of scales
       for (int c = tid; c < SCB; c += 64 * kWaves) {
         const int64_t first = (int64_t)c * 8 / NSC;  // first vector of the chunk
         if (first + 8 / NSC <= nvalid) {
-          *(uint4*)(a.scales + vb * NSC + 8 * c) = *(const uint4*)&sc_lds[par][8 * c];
-          if constexpr (QK != 0) *(uint4*)(a.zeros + vb * NSC + 8 * c) = *(const uint4*)&zr_lds[par][8 * c];
+          store_nt16(a.scales + vb * NSC + 8 * c, &sc_lds[par][8 * c]);
+          if constexpr (QK != 0) store_nt16(a.zeros + vb * NSC + 8 * c, &zr_lds[par][8 * c]);
         } else {
           for (int k = 0; k < 8; ++k)
             if ((int64_t)(8 * c + k) < nvalid * NSC) {
@@ -317,7 +324,7 @@ values_kernel(const ValuesArgs a) {
         if (v < nv && row >= 0 && row < a.n_rows) {
           const uint32_t n = div_heads((uint32_t)v, a);
           const int h = (int)((uint32_t)v - n * (uint32_t)a.n_heads);
-          *(uint4*)(a.codes + (row * a.n_heads + h) * REC + 16 * k) = *(const uint4*)&rec_lds[par][vloc * REC + 16 * k];
+          store_nt16(a.codes + (row * a.n_heads + h) * REC + 16 * k, &rec_lds[par][vloc * REC + 16 * k]);
         }
       }
       for (int vloc = tid; vloc < kVecs; vloc += 64 * kWaves) {
