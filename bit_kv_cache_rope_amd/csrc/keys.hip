@@ -54,6 +54,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // that instead of clamping indices of tokens past the end (their results are
 // never stored).  Word 3 selects the 32-bit data format for untyped access.
 constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kNT = 2;  // cache policy of the key loads: non-temporal (each byte is read once)
 __device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
 }
@@ -101,10 +102,10 @@ __device__ __forceinline__ void load_keys(RawKeys<F32IN>& r, rsrc_t rs, uint32_t
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (F32IN) {
-        r.v[4 * nb + 2 * j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner, 0, 0);
-        r.v[4 * nb + 2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner + 16, 0, 0);
+        r.v[4 * nb + 2 * j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner, 0, kNT);
+        r.v[4 * nb + 2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner + 16, 0, kNT);
       } else {
-        r.v[2 * nb + j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner, 0, 0);
+        r.v[2 * nb + j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + j * kPartner, 0, kNT);
       }
     }
   }
