@@ -83,13 +83,18 @@ def cpu_baseline(w, synth, seconds_hint: float = 20.0) -> dict:
     V = synth.kv(w, 0, "V", 0, n)
     pos = synth.positions(w, 0, n)
     T, _ = synth.transform(w, 0)
+    reps = 0
     t0 = time.perf_counter()
-    oracle.quantize_keys(K, pos, T, w.theta, 2, oracle.sym(w.clip_alpha), threads=1)
-    oracle.quantize_values(V, 2, oracle.sym(w.clip_alpha), threads=1)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full layer of the workload ({n} tokens x {w.heads} heads, K and V), "
-                      f"single-threaded, {dt:.1f} s"}
+    while True:  # whole layers until about seconds_hint of CPU work (at least two)
+        oracle.quantize_keys(K, pos, T, w.theta, 2, oracle.sym(w.clip_alpha), threads=1)
+        oracle.quantize_values(V, 2, oracle.sym(w.clip_alpha), threads=1)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if reps >= 2 and dt >= seconds_hint * 0.6:
+            break
+    return {"value": reps * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} passes over one full layer of the workload ({n} tokens x {w.heads} heads, "
+                      f"K and V), single-threaded, {dt:.1f} s"}
 
 
 def main() -> int:
