@@ -13,7 +13,10 @@ are resident in HBM before timing; the step cycles through enough input/output
 sets (> 2x the 256 MB MALL) that no set is re-read from the MALL.
 
 Prints one JSON line.  `value` is K+V tokens/s of the whole step, from K
-steps launched back to back between two synchronizations; `roofline` is for
+steps launched back to back between two synchronizations, each step's keys on
+the launch stream and its values on a second stream (they are independent, so
+the GPU may run them side by side; `--one-stream` serializes them);
+`roofline` is for
 the key kernel (algorithmic bytes per launch / its mean duration, from HIP
 events around each launch on the launch stream, in a second pass over the same
 K steps); `cpu_baseline` is the CPU oracle as it stands, single-threaded, on
@@ -103,6 +106,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="issue keys and values of the throughput pass on one stream")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -140,9 +145,14 @@ def main() -> int:
                          ko=bk.alloc_packed(N, H, bits, q, dev), vo=bk.alloc_packed(N, H, bits, q, dev)))
     del Kd, Vd
     stream = torch.cuda.current_stream()
+    vstream = stream if args.one_stream else torch.cuda.Stream()  # default priority
     # launches with their arguments marshalled once, so the host stays ahead of the GPU
     calls = [(bk.prepare_quantize_keys(s["K"], s["pos"], rope, tk, bits, q, s["ko"], stream=stream),
               bk.prepare_quantize_values(s["V"], bits, q, s["vo"], stream=stream)) for s in sets]
+    # the throughput pass issues each step's values on their own stream: keys and
+    # values of a step are independent, so the GPU may run one beside the other
+    tcalls = [(k, bk.prepare_quantize_values(s["V"], bits, q, s["vo"], stream=vstream))
+              for (k, _), s in zip(calls, sets)]
 
     def step(i, evs=None):
         kcall, vcall = calls[i % n_sets]
@@ -160,11 +170,18 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
 
-    # Throughput: K steps back to back, bracketed by synchronizations only.
+    # Throughput: K steps back to back (keys on the launch stream, values on a
+    # second one), bracketed by device-wide synchronizations only.
+    for i in range(args.warmup):
+        kcall, vcall = tcalls[i % n_sets]
+        kcall()
+        vcall()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        kcall, vcall = tcalls[i % n_sets]
+        kcall()
+        vcall()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
@@ -228,7 +245,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "qwen3_8b_prefill_layer", "tokens": N, "kv_heads": H, "head_dim": D,
                    "bits": bits, "quantizer": "symmetric, clip 2.0 x RMS, fp16 step per token-head",
-                   "kv_dtype": "bf16", "rope_theta": w.theta, "buffer_sets": n_sets},
+                   "kv_dtype": "bf16", "rope_theta": w.theta, "buffer_sets": n_sets,
+                   "streams": 1 if args.one_stream else 2},
         "roofline": roofline,
         "kernels": {
             "keys_us": round(key_us, 2), "values_us": round(val_us, 2),
