@@ -137,13 +137,17 @@ __device__ __forceinline__ void unpack8(const RawKeys<F32IN>& r, int nb, int j, 
 
 template <int BITS, int QK, bool F32IN, int HG, bool YOUT>
 __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
-  // Head groups: with four heads per block the block runs two groups of two
-  // heads (eight waves each), one phase apart (see the interval loop below).
-  constexpr int NG = HG == 4 ? 2 : 1;
+  // Head groups: with two or four heads per block the block runs two groups
+  // (of HG / 2 heads, four waves each per head), one phase apart (see the
+  // schedule below).
+  constexpr int NG = HG >= 2 ? 2 : 1;
   constexpr int HGG = HG / NG;      // heads per group
   constexpr int WG = 4 * HGG;       // waves per group
-  constexpr int TPW = kTile / WG;   // cos/sin rows each wave of group 0 loads per tile
+  constexpr int RPG = kTile / NG;   // cos/sin rows each group loads per tile
+  constexpr int TPW = RPG / WG;     // ... each of its waves
   constexpr int NCS = TPW / 2;      // ... two rows per load
+  constexpr int NKL = F32IN ? 8 : 4;  // key loads per lane per tile
+  static_assert(NG == 1 || NCS + NKL < 16, "vmcnt immediate");
   constexpr int CSB = NG;           // cos/sin tile buffers (by tile parity when two groups)
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
@@ -208,15 +212,15 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   auto keys_off = [&]() __attribute__((always_inline)) -> uint32_t {
     return (16 * wq + (lane >> 3)) * row_bytes + 8 * (lane & 7) * ESZ;
   };
-  // cos/sin rows (group 0 only): its wave w fills rows TPW*w .. TPW*w + TPW - 1
-  // of a tile buffer, two per 16-byte-per-lane load (lanes 0-31 one row,
-  // lanes 32-63 the next).  posv[i] is the position of row TPW*w + 2i + (l / 32)
+  // cos/sin rows: wave w of group g fills rows RPG*g + TPW*w .. + TPW - 1 of a
+  // tile buffer, two per 16-byte-per-lane load (lanes 0-31 one row, lanes
+  // 32-63 the next).  posv[i] is the position of row RPG*g + TPW*w + 2i + (l / 32)
   // of a tile (0 past the end), csv[i] the matching half-row of the table.
   auto load_pos = [&](int t, int* pv) __attribute__((always_inline)) {
     const rsrc_t rs = buffer_rsrc(a.pos + t * kTile, tile_len(t) * 4u);
 #pragma unroll
     for (int i = 0; i < NCS; ++i)
-      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (TPW * gw + 2 * i + lh), 0, 0);
+      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (RPG * g + TPW * gw + 2 * i + lh), 0, 0);
   };
   auto load_cs = [&](const int* pv, u32x4* cv) __attribute__((always_inline)) {
 #pragma unroll
@@ -227,7 +231,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   };
   auto store_cs = [&](const u32x4* cv, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NCS; ++i) *(u32x4*)&cs_lds[buf][TPW * gw + 2 * i + lh][2 * col] = cv[i];
+    for (int i = 0; i < NCS; ++i) *(u32x4*)&cs_lds[buf][RPG * g + TPW * gw + 2 * i + lh][2 * col] = cv[i];
   };
   // Cache rows of tile t's tokens, loaded by wave 0 (lane = token): the raw
   // slot words, turned into a row or -1 by row_of once they have arrived.
@@ -247,10 +251,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   u32x2 row_w = {0u, 0u};  // read only when a.slots is set
   int posv[NCS], posv_n[NCS];  // positions of the next tile's rows, then of the one after
   u32x4 csv[NCS];
-  if (g == 0) {
-    if (a.slots && wave_u == 0) row_w = load_rows(first_tile);
-    load_pos(first_tile, posv);
-  }
+  if (a.slots && wave_u == 0) row_w = load_rows(first_tile);
+  load_pos(first_tile, posv);
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
   bf16x8 A[8];
   {
@@ -258,17 +260,13 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
   }
-  if (g == 0) {
-    load_cs(posv, csv);
-    load_pos(tile_of(1), posv);
-  }
+  load_cs(posv, csv);
+  load_pos(tile_of(1), posv);
   // Nothing may be in flight when the loop starts: its first wait would
   // otherwise also cover the previous tile's stores on later iterations.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (g == 0) {
-    store_cs(csv, 0);
-    if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, first_tile);
-  }
+  store_cs(csv, 0);
+  if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, first_tile);
   __syncthreads();
 
   f32x16 acc[kNB];
@@ -326,12 +324,14 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     }
     if (j >= count) return;
     const int next = tile_of(j + 1);
-    if (g == 0) {
-      // the next tile's cache rows and the positions of the tile after (zeros
-      // past the end); they land before phase 2 ends
-      if (a.slots && wave_u == 0) row_w = load_rows(next);
-      load_pos(tile_of(j + 2), posv_n);
-    }
+    // Group 1 loads its half of the next tile's cos/sin rows here (its stores
+    // above are older, the loads below younger) and writes them to LDS at the
+    // end of its phase 1, while group 0 is in phase 2 of the same tile.
+    if (NG == 2 && g == 1) load_cs(posv, csv);
+    // the next tile's cache rows and the positions of the tile after (zeros
+    // past the end)
+    if (a.slots && wave_u == 0) row_w = load_rows(next);
+    load_pos(tile_of(j + 2), posv_n);
     // RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS.
     // Chunk c = l % 8 of token t is channels 8c .. 8c+7 (k step c / 2, lane
     // half c % 2 of the B operand) and its partner chunk (k step 4 + c / 2).
@@ -373,8 +373,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // ---- phase 1: y = T~ x~ for this wave's 32 rows and both column blocks,
   // then (symmetric) the sums of squares.
   auto phase1 = [&](int j) __attribute__((always_inline)) {
-    // group 0: the next tile's cos/sin rows, into registers until phase 2 ends
-    // (loaded here rather than in phase 0 so they are not live during RoPE)
+    // group 0: its half of the next tile's cos/sin rows, into registers until
+    // phase 2 ends (loaded here rather than in phase 0 so they are not live
+    // during RoPE)
     if (g == 0) load_cs(posv, csv);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = (f32x16){};
@@ -435,6 +436,17 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
         if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
       }
+    }
+    if (NG == 2 && g == 1) {
+      // the cos/sin rows loaded in phase 0 have landed: only the younger
+      // position and key loads (and, for the y output, its stores) may still
+      // be in flight
+      if constexpr (YOUT) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (NCS + NKL));  // vmcnt(NCS + NKL)
+      }
+      store_cs(csv, (j + 1) & 1);
     }
   };
 
@@ -575,16 +587,16 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    // Every load of this wave has landed (next keys; group 0: rows, cos/sin
-    // rows, positions), and its stores have drained.
+    // Every load of this wave has landed (next keys, positions; group 0:
+    // rows, cos/sin rows), and its stores have drained.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
     if (g == 0) {
       const int next = tile_of(j + 1);
       if (wave_u == 0) slot_lds[(j + 1) & 1][lane] = row_of(row_w, next);
       store_cs(csv, (j + 1) & (CSB - 1));
-#pragma unroll
-      for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
     }
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
   };
 
   // Schedule.  Each group runs phase 0, 1, 2 of its tiles in turn with a

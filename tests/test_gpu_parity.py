@@ -341,6 +341,31 @@ def test_keys_end_to_end(env, name, n, kind, bits):
         assert m <= MISMATCH_RATE * tot
 
 
+@pytest.mark.parametrize("name,n,dtype,hg", [
+    ("qwen3_8b_prefill", 8192, "bf16", 4), ("qwen3_8b_prefill", 8192, "f32", 2),
+    ("tiny", 16384, "bf16", 2), ("qwen3_8b_prefill", 1000, "bf16", 1)])
+def test_keys_head_group_sizes(env, name, n, dtype, hg):
+    """The key kernel runs 4, 2 or 1 heads per block (chosen from the tile count,
+    the head count and the input type): each variant, end to end and through the
+    exact permutation transform (y bit-exact)."""
+    s = env["synth"]
+    w = s.WORKLOADS[name]
+    K = s.kv(w, 0, "K", 0, n, dtype=dtype)
+    pos = s.positions(w, 0, n) if name != "tiny" else np.arange(n, dtype=np.int32)
+    T, _ = s.transform(w, 0)
+    H = K.shape[1]
+    say(f"keys head groups {name} n={n} {dtype} (heads per block {hg})")
+    for kind, bits in (("sym", 2), ("sym", 3), ("affine", 2)):
+        account_keys(env, K, pos, T, bits, _bkq(env, kind), f"keys {name} {dtype} {kind} {bits}")
+    P = np.zeros((H, 128, 128), np.float32)
+    rng = np.random.default_rng(17)
+    for hh in range(H):
+        P[hh, np.arange(128), rng.permutation(128)] = 1.0
+    yg, yr = _y_gpu(env, K, pos, P), _y_ref(env, K, pos, P)
+    bad = np.argwhere(yg.view(np.uint32) != yr.view(np.uint32))
+    assert bad.size == 0, f"permutation y differ at {bad[:5].tolist()} ({len(bad)})"
+
+
 FULL_CASES = [("qwen3_32b_full", 0, "sym", 3), ("qwen3_32b_full", 63, "sym", 4),
               ("affine_pct", 0, "affine", 2), ("affine_pct", 35, "affine", 2)]
 
