@@ -15,7 +15,9 @@ sets (> 2x the 256 MB MALL) that no set is re-read from the MALL.
 Prints one JSON line.  `value` is K+V tokens/s of the whole step, from K
 steps launched back to back between two synchronizations, each step's keys on
 the launch stream and its values on a second stream (they are independent, so
-the GPU may run them side by side; `--one-stream` serializes them);
+the GPU may run them side by side; `--one-stream` serializes them).  Both are
+streams of their own, not the null stream: work on the null stream and on the
+first stream created after it was seen to run one after the other;
 `roofline` is for
 the key kernel (algorithmic bytes per launch / its mean duration, from HIP
 events around each launch on the launch stream, in a second pass over the same
@@ -144,8 +146,8 @@ def main() -> int:
         sets.append(dict(K=Kd.clone(), V=Vd.clone(), pos=torch.from_numpy(pos).to(dev),
                          ko=bk.alloc_packed(N, H, bits, q, dev), vo=bk.alloc_packed(N, H, bits, q, dev)))
     del Kd, Vd
-    stream = torch.cuda.current_stream()
-    vstream = stream if args.one_stream else torch.cuda.Stream()  # default priority
+    stream = torch.cuda.Stream()  # the launch stream (default priority, like every stream here)
+    vstream = stream if args.one_stream else torch.cuda.Stream()
     # launches with their arguments marshalled once, so the host stays ahead of the GPU
     calls = [(bk.prepare_quantize_keys(s["K"], s["pos"], rope, tk, bits, q, s["ko"], stream=stream),
               bk.prepare_quantize_values(s["V"], bits, q, s["vo"], stream=stream)) for s in sets]

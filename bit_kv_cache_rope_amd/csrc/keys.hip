@@ -24,11 +24,13 @@
 // registers and writes them to LDS just before the barrier that starts that
 // tile.
 //
-// Per-tile pipeline, three barriers: [loads of the next tile's cache rows and
-// cos/sin rows, of the positions of the tile after; RoPE -> LDS; the next
+// Per-tile pipeline, three barriers: [loads of the next tile's cos/sin rows
+// and cache rows, of the positions of the tile after; RoPE -> LDS; the next
 // tile's keys into the registers RoPE freed] B1 [MFMA; sums of squares ->
-// LDS] B2 [scale(s), codes, records -> LDS; wait for every load; cos/sin rows
-// -> LDS] B3 [stores].
+// LDS; cos/sin rows -> LDS] B2 [scale(s), codes, records -> LDS; wait for the
+// loads older than the keys] B3 [stores] (one head per block: the cos/sin rows
+// are loaded in the MFMA phase and written after the codes, behind a wait for
+// every load).
 // Packed records and scales are staged in LDS and written as whole 16-byte
 // chunks (a head group's records of a token are contiguous in the cache row).
 #include "device_common.h"
@@ -275,6 +277,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // ---- phase 0 of the group's j-th tile: the stores of tile j - 1, then (for
   // j < count) the loads for later tiles, RoPE and the next tile's keys.
   auto phase0 = [&](int j) __attribute__((always_inline)) {
+    // Only this tile's keys can still be in flight (two groups: the phase-2
+    // wait leaves them); wait here, before the stores and loads below are
+    // issued, so that RoPE does not also wait for those.
+    if constexpr (NG == 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     if constexpr (!YOUT) {
       if (j >= 1) {
         const int sb = (j - 1) & 1;
@@ -324,10 +330,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     }
     if (j >= count) return;
     const int next = tile_of(j + 1);
-    // Group 1 loads its half of the next tile's cos/sin rows here (its stores
-    // above are older, the loads below younger) and writes them to LDS at the
-    // end of its phase 1, while group 0 is in phase 2 of the same tile.
-    if (NG == 2 && g == 1) load_cs(posv, csv);
+    // With two groups, each loads its half of the next tile's cos/sin rows
+    // here (its stores above are older, the loads below younger) and writes
+    // them to LDS at the end of its phase 1.
+    if (NG == 2) load_cs(posv, csv);
     // the next tile's cache rows and the positions of the tile after (zeros
     // past the end)
     if (a.slots && wave_u == 0) row_w = load_rows(next);
@@ -373,10 +379,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // ---- phase 1: y = T~ x~ for this wave's 32 rows and both column blocks,
   // then (symmetric) the sums of squares.
   auto phase1 = [&](int j) __attribute__((always_inline)) {
-    // group 0: its half of the next tile's cos/sin rows, into registers until
-    // phase 2 ends (loaded here rather than in phase 0 so they are not live
-    // during RoPE)
-    if (g == 0) load_cs(posv, csv);
+    // one group: the next tile's cos/sin rows, into registers until phase 2
+    // ends (loaded here rather than in phase 0 so they are not live during RoPE)
+    if (NG == 1) load_cs(posv, csv);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = (f32x16){};
     // B operands one k step ahead of the MFMAs that use them; the scheduling
@@ -437,10 +442,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
       }
     }
-    if (NG == 2 && g == 1) {
+    if (NG == 2) {
       // the cos/sin rows loaded in phase 0 have landed: only the younger
-      // position and key loads (and, for the y output, its stores) may still
-      // be in flight
+      // cache-row, position and key loads (and, for the y output, its stores)
+      // may still be in flight
       if constexpr (YOUT) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       } else {
@@ -587,13 +592,18 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    // Every load of this wave has landed (next keys, positions; group 0:
-    // rows, cos/sin rows), and its stores have drained.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+    // The cache rows and positions have landed.  With two groups the next
+    // tile's keys (the youngest loads) stay in flight until RoPE needs them;
+    // one group also waits for its cos/sin rows, loaded after the keys.
+    if constexpr (NG == 2 && !YOUT) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | NKL);  // vmcnt(NKL), expcnt and lgkmcnt untouched
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
     if (g == 0) {
       const int next = tile_of(j + 1);
       if (wave_u == 0) slot_lds[(j + 1) & 1][lane] = row_of(row_w, next);
-      store_cs(csv, (j + 1) & (CSB - 1));
+      if (NG == 1) store_cs(csv, 0);
     }
 #pragma unroll
     for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
@@ -605,8 +615,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // group's waves run their MFMA phase the other group's waves, on the same
   // SIMDs, run VALU work.  Both groups pass the same number of barriers
   // (3 count + 2), and every barrier orders the LDS hand-offs within and
-  // between the groups: cos/sin tile j lives in buffer j % CSB from group 0's
-  // phase 2 of tile j - 1 until group 1's phase 0 of tile j, and the cache
+  // between the groups: cos/sin tile j lives in buffer j % CSB from the end of
+  // each group's phase 1 of tile j - 1 until group 1's phase 0 of tile j (one
+  // group: from its phase 2 of tile j - 1 until its phase 0 of tile j), and the cache
   // rows of tile j in slot_lds[j % 2] until group 1's stores of tile j.
   auto next_phase = [&]() __attribute__((always_inline)) {
     __syncthreads();
