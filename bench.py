@@ -105,8 +105,8 @@ def cpu_baseline(w, synth, seconds_hint: float = 20.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=4000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue keys and values of the throughput pass on one stream")
@@ -167,18 +167,20 @@ def main() -> int:
         if evs is not None:
             evs[2].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(min(args.warmup, 10)):
         step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
-
-    # Throughput: K steps back to back (keys on the launch stream, values on a
-    # second one), bracketed by device-wide synchronizations only.
+    # Warm-up: W steps of the throughput pass.  The chip takes some 0.1 s of
+    # load to reach its sustained clocks (a 200-step pass right after a short
+    # warm-up ran 20% slower than the same pass repeated).
     for i in range(args.warmup):
         kcall, vcall = tcalls[i % n_sets]
         kcall()
         vcall()
     torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
+
+    # Throughput: K steps back to back (keys on the launch stream, values on a
+    # second one), bracketed by device-wide synchronizations only.
     t0 = time.perf_counter()
     for i in range(args.steps):
         kcall, vcall = tcalls[i % n_sets]
