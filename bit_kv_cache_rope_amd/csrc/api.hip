@@ -135,14 +135,6 @@ int choose_hg(int64_t n_tiles, int n_heads, int cus, int max_hg) {
   return hg;
 }
 
-int blocks_per_group(int64_t n_tiles, int n_groups, int hg, int cus) {
-  const int per_cu = 4 / hg;  // 8 waves per CU: blocks of 2*hg waves
-  int64_t b = ((int64_t)cus * per_cu) / n_groups;
-  if (b < 1) b = 1;
-  if (b > n_tiles) b = n_tiles;
-  return (int)b;
-}
-
 constexpr int kMaxDevices = 64;
 int g_cus[kMaxDevices];
 std::mutex g_cus_mu;
@@ -476,9 +468,8 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
     const int64_t n_tiles = (n_tokens + 31) / 32;
     hg = choose_hg(n_tiles, n_heads, cus, 4);
     a.n_groups = n_heads / hg;
-    a.blocks_per_group = blocks_per_group(n_tiles, a.n_groups, hg, cus);
   }
-  hipError_t e = wushkv::launch_dequant(a, bits, hg, 4 * cus, (hipStream_t)stream);
+  hipError_t e = wushkv::launch_dequant(a, bits, hg, cus, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "dequantize kernel launch");
   return WUSHKV_OK;
 }

@@ -93,7 +93,7 @@ struct DequantArgs {
   void* out;
   int out_bf16;
   int n_groups;
-  int blocks_per_group;
+  int blocks_per_group;  // set by the launcher
 };
 
 int device_cu_count(int device);
@@ -103,8 +103,7 @@ int device_cu_count(int device);
 hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_group, int y_out, int cus,
                        hipStream_t stream);
 hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
-hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int n_blocks,
-                          hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int cus, hipStream_t stream);
 // Fills r->cs for every position below r->max_pos (exact: the certified
 // double path, double-double where it cannot certify).
 hipError_t launch_build_cs_table(const wushkv_rope* r, hipStream_t stream);

@@ -658,12 +658,14 @@ __global__ void gather_cs_kernel(const float2* table, int32_t max_pos, const int
 }
 
 // Persistent grid: as many blocks per head group as fit on the chip at once.
-template <typename Kernel>
-int resident_blocks(Kernel k, int threads) {
-  static int cached = 0;  // one value per kernel instantiation
+// The cache is per kernel instantiation (K is the kernel itself, not its type,
+// which all instantiations share).
+template <auto K>
+int resident_blocks(int threads) {
+  static int cached = 0;
   if (!cached) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, threads, 0) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, K, threads, 0) != hipSuccess || n < 1) n = 1;
     cached = n;
   }
   return cached;
@@ -671,9 +673,9 @@ int resident_blocks(Kernel k, int threads) {
 
 template <int BITS, int QK, bool F32IN, int HG, bool YOUT>
 hipError_t launch_one(KeysArgs a, int cus, hipStream_t st) {
-  auto k = keys_kernel<BITS, QK, F32IN, HG, YOUT>;
+  constexpr auto k = keys_kernel<BITS, QK, F32IN, HG, YOUT>;
   const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
-  int64_t b = (int64_t)cus * resident_blocks(k, 256 * HG) / a.n_groups;
+  int64_t b = (int64_t)cus * resident_blocks<k>(256 * HG) / a.n_groups;
   b = b < 1 ? 1 : (b > n_tiles ? n_tiles : b);
   if (b >= kXcds) b -= b % kXcds;  // multiple of 8: XCD-aware tile mapping
   a.blocks_per_group = (int)b;
