@@ -209,14 +209,16 @@ def main() -> int:
     # ---- read path on the same data (keys back through T_k^-1, values plain), reported alongside
     _, Ti = synth.transform(w, 0)
     tki = bk.Transform(Ti)
-    outk = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
-    outv = torch.empty_like(outk)
-    rcalls = [(bk.prepare_dequantize(s["ko"], N, H, bits, q, outk, T_k_inv=tki, stream=stream),
-               bk.prepare_dequantize(s["vo"], N, H, bits, q, outv, stream=stream)) for s in sets]
-    rd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
-    for i in range(25):
+    # one output pair per buffer set, so that the written bytes (2 x 64 MiB per
+    # set) are not served from the MALL
+    outs = [(torch.empty((N, H, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)) for _ in sets]
+    rcalls = [(bk.prepare_dequantize(s["ko"], N, H, bits, q, ok, T_k_inv=tki, stream=stream),
+               bk.prepare_dequantize(s["vo"], N, H, bits, q, ov, stream=stream)) for s, (ok, ov) in zip(sets, outs)]
+    rd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
+    for i in range(60):
         kc, vc = rcalls[i % n_sets]
-        e = rd[i - 5] if i >= 5 else None
+        e = rd[i - 10] if i >= 10 else None
         if e:
             e[0].record(stream)
         kc()

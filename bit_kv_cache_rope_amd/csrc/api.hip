@@ -90,12 +90,14 @@ wushkv_status make_quant(const wushkv_quantizer* q, wushkv::QuantArgs* out) {
 
 wushkv_status check_packed(const wushkv_packed* p, int kind, int64_t n_tokens, bool writer) {
   if (!p) return fail(WUSHKV_ERR_INVALID_ARG, "packed cache view is NULL");
-  if (!p->codes || !p->scales) return fail(WUSHKV_ERR_INVALID_ARG, "codes and scales must be set");
-  if (kind == 1 && !p->zeros) return fail(WUSHKV_ERR_INVALID_ARG, "affine quantizer needs zeros");
+  if (p->n_rows < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_rows < 0");
+  if (p->n_rows > 0) {  // a cache of no rows is never dereferenced: its pointers may be NULL
+    if (!p->codes || !p->scales) return fail(WUSHKV_ERR_INVALID_ARG, "codes and scales must be set");
+    if (kind == 1 && !p->zeros) return fail(WUSHKV_ERR_INVALID_ARG, "affine quantizer needs zeros");
+  }
   if (!aligned(p->codes, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "codes must be 16-byte aligned");
   if (!aligned(p->scales, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "scales must be 16-byte aligned");
   if (kind == 1 && !aligned(p->zeros, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "zeros must be 16-byte aligned");
-  if (p->n_rows < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_rows < 0");
   if (p->n_rows > INT32_MAX) return fail(WUSHKV_ERR_UNSUPPORTED, "n_rows must be below 2^31");
   if (!p->slots && p->n_rows < n_tokens)
     return fail(WUSHKV_ERR_INVALID_ARG, writer ? "cache has fewer rows than tokens" : "cache has fewer rows than requested");

@@ -244,17 +244,23 @@ __global__ void __launch_bounds__(128 * HG) dequant_tinv_kernel(const DequantArg
       B[s] = __builtin_bit_cast(bf16x8, pk);
     }
 
+    // symmetric: both row blocks' accumulation chains interleaved
+    f32x16 accs[2] = {};
+    if constexpr (QK == 0) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) accs[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[m][s], B[s], accs[m], 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int mt = 2 * half + m;
       float res[16];
       if constexpr (QK == 0) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[m][s], B[s], acc, 0, 0, 0);
         const float hs = valid ? 0.5f * f16_bits_to_f32(p.sc[0]) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) res[i] = acc[i] * hs;
+        for (int i = 0; i < 16; ++i) res[i] = accs[m][i] * hs + 0.0f;  // + 0: a missing row reads +0, not -0
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) res[i] = 0.0f;

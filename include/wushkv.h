@@ -99,9 +99,10 @@ typedef struct {
  *   scales: fp16 bits, 16-byte aligned.
  *   zeros:  fp16 bits for affine (16-byte aligned), NULL for symmetric.
  *   slots:  int64 row per token, or NULL (row = token index).  Rows outside
- *           [0, n_rows) are skipped by writers and read as zero-filled by the
- *           reader; callers must not rely on that.
- *   n_rows: capacity of the cache in rows, below 2^31. */
+ *           [0, n_rows) are skipped by writers; the reader returns +0 for
+ *           every channel of such a token.
+ *   n_rows: capacity of the cache in rows, below 2^31.  With n_rows = 0 the
+ *           pointers may be NULL (nothing is read or written through them). */
 typedef struct {
   void* codes;
   void* scales;

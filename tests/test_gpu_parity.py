@@ -527,6 +527,49 @@ def test_dequant_inverse_transform(env, kind, bits):
     assert np.all(np.abs(g16 - ref) <= np.abs(ref) * 2.0 ** -8 + TRANSFORM_TOL * mag[..., None])
 
 
+@pytest.mark.parametrize("kind,bits", [("sym", 2), ("sym", 3), ("sym", 4), ("affine", 2)])
+def test_dequant_through_slots_with_missing_rows(env, kind, bits):
+    """Reads through cache rows: rows in range decode their record; -1 and rows
+    past the cache read as +0 (plain: bit-exact; through T_k^-1: within the
+    transform tolerance, exact zeros for missing rows).  Also a cache of zero
+    rows."""
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["affine_pct" if kind == "affine" else "qwen3_32b_full"]
+    rows, n = 700, 613
+    V = s.kv(w, 0, "V", 0, rows)
+    H = V.shape[1]
+    q = _bkq(env, kind)
+    say(f"dequant through slots {kind} {bits}")
+    p = run_values(env, V, bits, q)
+    h = packed_host(p)
+    rng = np.random.default_rng(5)
+    slots = rng.integers(0, rows, n).astype(np.int64)
+    slots[rng.choice(n, 40, replace=False)] = -1
+    slots[rng.choice(n, 40, replace=False)] = rows + rng.integers(0, 50, 40)
+    ok = (slots >= 0) & (slots < rows)
+    src = np.where(ok, slots, 0)
+    g = lambda a: None if a is None else a[src]
+    ref = o.dequantize(g(h["codes"]), g(h["scales"]), g(h["zeros"]), n, H, bits, oracle_q(env, q))
+    ref[~ok] = 0.0
+    ps = p.with_slots(to_dev(env, slots))
+    out32 = bk.wushkv_dequantize(ps, n, H, bits, q, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(out32.view(np.uint32), ref.view(np.uint32))
+    out16 = bk.wushkv_dequantize(ps, n, H, bits, q, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(out16.view(np.uint32), o.round_bf16(ref).view(np.uint32))
+    T, Ti = s.transform(w, 0)
+    refk = o.dequantize(g(h["codes"]), g(h["scales"]), g(h["zeros"]), n, H, bits, oracle_q(env, q), Tinv=Ti)
+    gk = bk.wushkv_dequantize(ps, n, H, bits, q, T_k_inv=bk.Transform(Ti), out_dtype=torch.float32).cpu().numpy()
+    assert np.all(gk[~ok].view(np.uint32) == 0)
+    err = np.abs(gk[ok] - refk[ok]).max(axis=2)
+    mag = np.abs(refk[ok]).max(axis=2)
+    assert np.all(err <= TRANSFORM_TOL * mag)
+    # a cache with no rows: every read is +0
+    empty = bk.PackedCache(p.codes[:0], p.scales[:0], None if p.zeros is None else p.zeros[:0], to_dev(env, slots))
+    for Tk in (None, bk.Transform(Ti)):
+        z = bk.wushkv_dequantize(empty, n, H, bits, q, T_k_inv=Tk, out_dtype=torch.float32).cpu().numpy()
+        assert np.all(z.view(np.uint32) == 0)
+
+
 # ---------------------------------------------------------------------------------- edges
 
 @pytest.mark.parametrize("n", [0, 1, 31, 33, 65])
