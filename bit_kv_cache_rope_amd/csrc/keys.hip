@@ -227,8 +227,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   auto load_cs = [&](const int* pv, u32x4* cv) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NCS; ++i) {
-      const int p = min(max(pv[i], 0), a.max_pos - 1);  // clamp to the table
-      cv[i] = *(const u32x4*)(a.cs + (int64_t)p * kPairs + 2 * col);
+      const uint32_t p = (uint32_t)min(max(pv[i], 0), a.max_pos - 1);  // clamp to the table
+      cv[i] = *(const u32x4*)((const uint8_t*)(a.cs + 2 * col) + ((uint64_t)p << 9));  // 512-byte rows
     }
   };
   auto store_cs = [&](const u32x4* cv, int buf) __attribute__((always_inline)) {
@@ -288,20 +288,21 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         // (16-byte chunks, at most one per thread), then its scales (and zeros)
         constexpr int CPT = HGG * BITS;  // 16-byte chunks per token
         constexpr int NCH = kTile * CPT;  // <= 64 * WG
-        const int tg = tid - 64 * WG * g;
+        const uint32_t tg = (uint32_t)(tid - 64 * WG * g);  // thread within the group
         const uint32_t row_rec = (uint32_t)a.n_heads * REC;  // bytes per cache row
-        if (NCH == 64 * WG || tg < NCH) {
-          const int n = tg / CPT, k = tg - n * CPT;
+        if (NCH == 64 * WG || tg < (uint32_t)NCH) {
+          const uint32_t n = tg / CPT, k = tg - n * CPT;
           const int32_t row = slot_lds[sb][n];
           if (row >= 0) {
-            const u32x4 v = *(const u32x4*)&rec_lds[g][n][16 * k];
+            // (24-bit multiply: a full 32-bit one issues at a quarter of the rate)
+            const u32x4 v = *(const u32x4*)((const uint8_t*)rec_lds[g] + __umul24(n, RECROW) + 16 * k);
             uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + ((grp * HG + g * HGG) * REC + 16 * k);
             __builtin_nontemporal_store(v, (u32x4*)dst);  // written once, not read back here
           }
         }
         if constexpr (QK == 0) {
           // one store of the group's HGG fp16 steps per token, by its last wave
-          const int n = tg - (64 * WG - 64);
+          const int n = (int)tg - (64 * WG - 64);
           if (n >= 0) {
             const int32_t row = slot_lds[sb][n];
             if (row >= 0) {
@@ -315,7 +316,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
           }
         } else {
           // per (token, head): 4 scales and 4 zeros, 8 bytes each
-          const int c = tg - (64 * WG - 64 * HGG);
+          const int c = (int)tg - (64 * WG - 64 * HGG);
           if (c >= 0) {
             const int n = c / HGG, jh = c - n * HGG;
             const int32_t row = slot_lds[sb][n];
