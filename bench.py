@@ -19,10 +19,10 @@ the GPU may run them side by side; `--one-stream` serializes them).  Both are
 streams of their own, not the null stream: work on the null stream and on the
 first stream created after it was seen to run one after the other;
 `roofline` is for
-the key kernel (algorithmic bytes per launch / its mean duration, from HIP
-events around each launch on the launch stream, in a second pass over the same
-K steps); `cpu_baseline` is the CPU oracle as it stands, single-threaded, on
-the same workload.
+the key kernel (algorithmic bytes per launch / its mean duration, from a pair
+of HIP events that each key kernel records at its own start and end on the
+launch stream, in a second pass over the same K steps); `cpu_baseline` is the
+CPU oracle as it stands, single-threaded, on the same workload.
 """
 from __future__ import annotations
 
@@ -156,16 +156,20 @@ def main() -> int:
     tcalls = [(k, bk.prepare_quantize_values(s["V"], bits, q, s["vo"], stream=vstream))
               for (k, _), s in zip(calls, sets)]
 
-    def step(i, evs=None):
+    def step(i):
         kcall, vcall = calls[i % n_sets]
-        if evs is not None:
-            evs[0].record(stream)
         kcall()
-        if evs is not None:
-            evs[1].record(stream)
         vcall()
-        if evs is not None:
-            evs[2].record(stream)
+
+    def new_events(n, k):
+        """n groups of k timing events, recorded once on the launch stream so
+        that they exist."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(n)]
+        for g in ev:
+            for e in g:
+                e.record(stream)
+        torch.cuda.synchronize()
+        return ev
 
     for i in range(min(args.warmup, 10)):
         step(i)
@@ -189,15 +193,21 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
-    # Per-kernel durations: the same K steps again with HIP events around each
-    # launch on the launch stream (an event between launches costs a few us
-    # of the step, so they stay out of the throughput pass).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-kernel durations: the same K steps again on the launch stream, each
+    # kernel recording a pair of HIP events at its own start and end
+    # (hipExtLaunchKernel through wushkv_debug_time_next_launch), so the figure
+    # is the kernel's duration without its dispatch latency.  (Events recorded
+    # around a launch read 3-4 us more.)
+    evs = new_events(args.steps, 4)
     for i in range(args.steps):
-        step(i, evs[i])
+        kcall, vcall = calls[i % n_sets]
+        bk.wushkv_debug_time_next_launch(evs[i][0], evs[i][1])
+        kcall()
+        bk.wushkv_debug_time_next_launch(evs[i][2], evs[i][3])
+        vcall()
     torch.cuda.synchronize()
     key_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    val_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    val_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
 
     if args.copy_probe:
         a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -215,21 +225,19 @@ def main() -> int:
              torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)) for _ in sets]
     rcalls = [(bk.prepare_dequantize(s["ko"], N, H, bits, q, ok, T_k_inv=tki, stream=stream),
                bk.prepare_dequantize(s["vo"], N, H, bits, q, ov, stream=stream)) for s, (ok, ov) in zip(sets, outs)]
-    rd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
+    rd = new_events(50, 4)
     for i in range(60):
         kc, vc = rcalls[i % n_sets]
         e = rd[i - 10] if i >= 10 else None
         if e:
-            e[0].record(stream)
+            bk.wushkv_debug_time_next_launch(e[0], e[1])
         kc()
         if e:
-            e[1].record(stream)
+            bk.wushkv_debug_time_next_launch(e[2], e[3])
         vc()
-        if e:
-            e[2].record(stream)
     torch.cuda.synchronize()
     rk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in rd]))
-    rv_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in rd]))
+    rv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in rd]))
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = N * args.steps / elapsed

@@ -21,7 +21,7 @@ from ._lib import WushKVError, F32, BF16, Q_SYM_RMS, Q_AFFINE_PCT  # noqa: F401
 __all__ = [
     "WushKVError", "Quantizer", "sym", "affine", "Transform", "Rope", "PackedCache", "alloc_packed",
     "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize", "wushkv_debug_rope_transform",
-    "wushkv_debug_rope_cos_sin", "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
+    "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch", "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
     "prepare_quantize_values", "prepare_dequantize",
 ]
 
@@ -277,6 +277,19 @@ def prepare_dequantize(packed: PackedCache, n_tokens: int, n_heads: int, bits: i
     args = (ctypes.byref(p), n_tokens, n_heads, bits, ctypes.byref(q), None if T_k_inv is None else T_k_inv.handle,
             ctypes.c_void_p(out.data_ptr()), F32 if out.dtype == torch.float32 else BF16, _stream(stream))
     return PreparedCall(library().wushkv_dequantize, args, (packed, q, p, out, T_k_inv))
+
+
+def wushkv_debug_time_next_launch(start: torch.cuda.Event | None, stop: torch.cuda.Event | None) -> None:
+    """The next library kernel launch on this thread records `start`/`stop`
+    at its kernel's start and end (events that have been recorded once, so
+    that they exist)."""
+    def handle(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            raise ValueError("record the event once before passing it")
+        return ctypes.c_void_p(e.cuda_event)
+    _lib.check(library().wushkv_debug_time_next_launch(handle(start), handle(stop)))
 
 
 def wushkv_rope_frequencies(theta: float):

@@ -15,8 +15,8 @@ Q_SYM_RMS, Q_AFFINE_PCT = 0, 1
 EXPORTED = [
     "wushkv_transform_create", "wushkv_transform_destroy", "wushkv_rope_create", "wushkv_rope_destroy",
     "wushkv_rope_frequencies", "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize",
-    "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_status_string",
-    "wushkv_last_error", "wushkv_version",
+    "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch",
+    "wushkv_status_string", "wushkv_last_error", "wushkv_version",
 ]
 
 
@@ -60,6 +60,7 @@ def load() -> ctypes.CDLL:
     L.wushkv_dequantize.argtypes = [pp, i64, i32, i32, qp, vp, vp, i32, vp]
     L.wushkv_debug_rope_transform.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, vp, vp]
     L.wushkv_debug_rope_cos_sin.argtypes = [vp, vp, i64, vp, vp]
+    L.wushkv_debug_time_next_launch.argtypes = [vp, vp]
     L.wushkv_status_string.argtypes = [i32]
     L.wushkv_status_string.restype = ctypes.c_char_p
     L.wushkv_last_error.argtypes = []

@@ -17,6 +17,7 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local wushkv::LaunchEvents g_launch_events;  // see wushkv_debug_time_next_launch
 
 wushkv_status fail(wushkv_status s, const std::string& msg) {
   g_err = msg;
@@ -144,6 +145,12 @@ std::mutex g_cus_mu;
 }  // namespace
 
 namespace wushkv {
+
+LaunchEvents take_launch_events() {
+  const LaunchEvents e = g_launch_events;
+  g_launch_events = LaunchEvents{};
+  return e;
+}
 
 int device_cu_count(int device) {
   if (device < 0 || device >= kMaxDevices) return 256;
@@ -473,6 +480,12 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
   }
   hipError_t e = wushkv::launch_dequant(a, bits, hg, cus, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "dequantize kernel launch");
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_debug_time_next_launch(void* start, void* stop) {
+  g_launch_events.start = (hipEvent_t)start;
+  g_launch_events.stop = (hipEvent_t)stop;
   return WUSHKV_OK;
 }
 

@@ -364,8 +364,7 @@ hipError_t launch_tinv(DequantArgs a, int cus, hipStream_t st) {
   int64_t b = (int64_t)cus * occupancy<k>(128 * HG) / a.n_groups;
   b = b < 1 ? 1 : (b > n_tiles ? n_tiles : b);
   a.blocks_per_group = (int)b;
-  k<<<dim3((unsigned)(a.n_groups * b)), 128 * HG, 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(k, dim3((unsigned)(a.n_groups * b)), dim3(128 * HG), st, a);
 }
 
 template <int BITS, int QK, bool BF16OUT>
@@ -382,9 +381,8 @@ hipError_t launch_dq(const DequantArgs& a, int hg, int cus, hipStream_t st) {
   const int64_t blocks = (nv + kPlainVecs - 1) / kPlainVecs;
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (a.slots) dequant_plain_kernel<BITS, QK, BF16OUT, true><<<(unsigned)blocks, 64 * kWaves, 0, st>>>(a);
-  else dequant_plain_kernel<BITS, QK, BF16OUT, false><<<(unsigned)blocks, 64 * kWaves, 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(a.slots ? dequant_plain_kernel<BITS, QK, BF16OUT, true> : dequant_plain_kernel<BITS, QK, BF16OUT, false>,
+                       dim3((unsigned)blocks), dim3(64 * kWaves), st, a);
 }
 
 template <int BITS, int QK>

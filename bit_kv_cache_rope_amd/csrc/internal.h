@@ -1,6 +1,7 @@
 // Internal interfaces of libwushkv: handle layouts and kernel launch arguments.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -97,6 +98,27 @@ struct DequantArgs {
 };
 
 int device_cu_count(int device);
+
+// Events that the next hot-path launch on this host thread records at its
+// kernel's start and end (set by wushkv_debug_time_next_launch; consumed by
+// that launch).  Timing support only.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents take_launch_events();
+
+// Launch kernel k with its single argument struct, recording the pending
+// launch events, if any, around the kernel itself.
+template <typename Args>
+hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, hipStream_t st, const Args& a) {
+  const LaunchEvents ev = take_launch_events();
+  if (ev.start || ev.stop) {
+    void* args[] = {const_cast<Args*>(&a)};
+    return hipExtLaunchKernel((const void*)k, grid, block, args, 0, st, ev.start, ev.stop, 0);
+  }
+  k<<<grid, block, 0, st>>>(a);
+  return hipGetLastError();
+}
 
 // Launchers size their persistent grids from the device's CU count and the
 // kernel's occupancy.

@@ -680,8 +680,7 @@ hipError_t launch_one(KeysArgs a, int cus, hipStream_t st) {
   b = b < 1 ? 1 : (b > n_tiles ? n_tiles : b);
   if (b >= kXcds) b -= b % kXcds;  // multiple of 8: XCD-aware tile mapping
   a.blocks_per_group = (int)b;
-  k<<<dim3((unsigned)(a.n_groups * b)), 256 * HG, 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(k, dim3((unsigned)(a.n_groups * b)), dim3(256 * HG), st, a);
 }
 
 template <int BITS, int QK, bool F32IN, bool YOUT>

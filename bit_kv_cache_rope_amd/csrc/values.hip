@@ -373,8 +373,7 @@ hipError_t launch_v(const ValuesArgs& a, int cus, hipStream_t st) {
   const int64_t cap = (int64_t)cus * occ;
   const int blocks = (int)(n_iter < cap ? n_iter : cap);
   if (blocks <= 0) return hipSuccess;
-  k<<<blocks, 64 * kWaves, 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(k, dim3(blocks), dim3(64 * kWaves), st, a);
 }
 
 template <int BITS, int QK>

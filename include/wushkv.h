@@ -176,6 +176,18 @@ wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, i
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
                                         int64_t n, float* cs_out, void* stream);
 
+/* Timing support: the next wushkv_quantize_keys, wushkv_quantize_values or
+ * wushkv_dequantize call on this host thread records `start` (a hipEvent_t)
+ * when its kernel starts and `stop` when it ends (hipExtLaunchKernel), so
+ * that hipEventElapsedTime(start, stop) is the kernel's own duration without
+ * its dispatch latency.  Either may be NULL.  The events must exist (created,
+ * for instance by one ordinary hipEventRecord) and belong to the device of
+ * that call; the library neither creates nor destroys them.  The setting is
+ * used once, by the next kernel launch of those calls on this thread; a call
+ * that fails or returns without launching (zero tokens) leaves it pending.
+ * Not for use while a stream is being captured into a graph. */
+wushkv_status wushkv_debug_time_next_launch(void* start, void* stop);
+
 const char* wushkv_status_string(wushkv_status s);
 /* Detail message of the last failed call on this thread ("" if none). */
 const char* wushkv_last_error(void);

@@ -570,6 +570,39 @@ def test_dequant_through_slots_with_missing_rows(env, kind, bits):
         assert np.all(z.view(np.uint32) == 0)
 
 
+def test_time_next_launch(env):
+    """The timing call: the kernel-recorded events bracket the kernel alone, so
+    they read less than events recorded around the call, and the setting is
+    used by one launch only."""
+    s, bk, torch = env["synth"], env["bk"], env["torch"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    n = 8192
+    V = to_dev(env, s.kv(w, 0, "V", 0, n))
+    q = bk.sym(2.0)
+    out = bk.alloc_packed(n, w.heads, 2, q)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record(st)
+    torch.cuda.synchronize()
+    say("timing events")
+    for _ in range(3):
+        ev[0].record(st)
+        bk.wushkv_debug_time_next_launch(ev[1], ev[2])
+        bk.wushkv_quantize_values(V, 2, q, out)
+        ev[3].record(st)
+        torch.cuda.synchronize()
+        inner, outer = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+        assert 0.0 < inner <= outer
+    # consumed: a second launch leaves the events where they were
+    before = ev[1].elapsed_time(ev[2])
+    bk.wushkv_quantize_values(V, 2, q, out)
+    torch.cuda.synchronize()
+    assert ev[1].elapsed_time(ev[2]) == before
+    with pytest.raises(ValueError):
+        bk.wushkv_debug_time_next_launch(torch.cuda.Event(enable_timing=True), None)
+
+
 # ---------------------------------------------------------------------------------- edges
 
 @pytest.mark.parametrize("n", [0, 1, 31, 33, 65])
