@@ -21,8 +21,8 @@
 //
 // cos/sin come from the RoPE handle's table (one 512-byte fp32 row per
 // position, exact): each wave loads a few of the next tile's rows into
-// registers and writes them to LDS just before the barrier that starts that
-// tile.
+// registers and writes them to one of two LDS tile buffers before that tile's
+// RoPE phase (see the pipeline below).
 //
 // Per-tile pipeline, three barriers: [loads of the next tile's cos/sin rows
 // and cache rows, of the positions of the tile after; RoPE -> LDS; the next
