@@ -81,36 +81,18 @@ __device__ __forceinline__ uint32_t sym_code(float y, float delta, float rdelta)
   }
 }
 
-// 2-bit symmetric code of y placed at bit `sh`, from per-vector thresholds.
-// With tp = delta and tz = 0 the three midpoint tests are A = [y > -delta],
-// B = [y >= 0], C = [y > delta] (ties as in the nearest-level rule) and the
-// code is A + B + C; since A >= B >= C its bits are bit1 = B and
-// bit0 = C | (A & !B).  A zero step uses tp = +inf, tz = -inf: code 2.
-__device__ __forceinline__ uint32_t sym2_bits(float y, float tp, float tz, int sh) {
-  const bool A = y > -tp, B = y >= tz, C = y > tp;
-  const bool b0 = C | (A & !B);
-  return (b0 ? (1u << sh) : 0u) | (B ? (2u << sh) : 0u);
-}
-
 // Lane masks of the two bits of a 2-bit symmetric code from the midpoint
-// tests A = [y > -step], B = [y >= 0], C = [y > step]: bit1 = B and
-// bit0 = B ? C : A, i.e. one test of y against the threshold that B selects
-// (+step or -step).  `tb` decides B (0, or -inf for a zero step), `tc` and
-// `ta` are the thresholds of C and A (+-step, or +inf / -inf for a zero
-// step, so every code comes out 2).  Two vector compares and one select per
-// code, no scalar mask logic.
+// tests A = [x > -step], B = [x >= 0], C = [x > step]: bit1 = B and
+// bit0 = B ? C : A, i.e. one test of x against the threshold that B selects
+// (+step or -step).  A zero step uses thresholds that make every code 2.
 struct Sym2Masks {
   uint64_t b1, b0;
 };
-__device__ __forceinline__ Sym2Masks sym2_masks(float y, float ta, float tb, float tc) {
-  const bool B = y >= tb;
-  const float t = B ? tc : ta;
-  return {__builtin_amdgcn_ballot_w64(B), __builtin_amdgcn_ballot_w64(y > t)};
-}
 
-// The same for a value tested as a raw 32-bit word (see bf16_gt_threshold):
-// B is the unsigned bound word <= tb (x >= 0 or x = -0), A and C compare the
-// word as a float with the bf16-rounded thresholds.
+// For a value tested as a raw 32-bit word (see bf16_gt_threshold): B is the
+// unsigned bound word <= tb (x >= 0 or x = -0), A and C compare the word as a
+// float with the bf16-rounded thresholds ta and tc.  Two vector compares and
+// one select per code, no scalar mask logic.
 __device__ __forceinline__ Sym2Masks sym2_masks_raw(uint32_t w, float ta, uint32_t tb, float tc) {
   const bool B = w <= tb;
   const float t = B ? tc : ta;
