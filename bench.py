@@ -239,6 +239,41 @@ def main() -> int:
     rk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in rd]))
     rv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in rd]))
 
+    # ---- decode append (64 sequences x 1 token, into 64 x 32768-row caches), reported alongside:
+    # a layer's K and V calls back to back on the two streams, and each kernel's own duration
+    wd = synth.WORKLOADS["decode_append"]
+    dn = wd.tokens
+    drows = 64 * 32768
+    dslots = torch.from_numpy(synth.slots(wd)).to(dev)
+    dpos = torch.from_numpy(synth.positions(wd)).to(dev)
+    dK, dV = dev_bf16(synth.kv(wd, 0, "K")), dev_bf16(synth.kv(wd, 0, "V"))
+    dT, _ = synth.transform(wd, 0)
+    dtk = bk.Transform(dT)
+    dkc = bk.alloc_packed(drows, H, bits, q, dev).with_slots(dslots)
+    dvc = bk.alloc_packed(drows, H, bits, q, dev).with_slots(dslots)
+    dk = bk.prepare_quantize_keys(dK, dpos, rope, dtk, bits, q, dkc, stream=stream)
+    dv = bk.prepare_quantize_values(dV, bits, q, dvc, stream=vstream)
+    for _ in range(200):
+        dk()
+        dv()
+    torch.cuda.synchronize()
+    n_dec = 36 * 20
+    t0 = time.perf_counter()
+    for _ in range(n_dec):
+        dk()
+        dv()
+    torch.cuda.synchronize()
+    dec_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
+    dev_ev = new_events(50, 4)
+    for e in dev_ev:
+        bk.wushkv_debug_time_next_launch(e[0], e[1])
+        dk()
+        bk.wushkv_debug_time_next_launch(e[2], e[3])
+        bk.prepare_quantize_values(dV, bits, q, dvc, stream=stream)()
+    torch.cuda.synchronize()
+    dec_k_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
+    dec_v_us = float(np.mean([e[2].elapsed_time(e[3]) for e in dev_ev])) * 1e3
+
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = N * args.steps / elapsed
     kb = N * key_bytes_per_token(H, bits) + H * D * D * 2  # + T~ read once per launch
@@ -276,6 +311,11 @@ def main() -> int:
             "tokens_per_s": round(N / ((rk_ms + rv_ms) * 1e-3), 1),
             "keys_gbs": round((N * (H * 16 * bits + H * 2 + H * D * 2) + H * D * D * 2) / (rk_ms * 1e-3) / 1e9, 1),
             "out_dtype": "bf16",
+        },
+        "decode_append": {
+            "tokens_per_layer": dn, "cache_rows": drows, "layer_us": round(dec_layer_us, 2),
+            "keys_kernel_us": round(dec_k_us, 2), "values_kernel_us": round(dec_v_us, 2),
+            "note": "one layer's K and V calls back to back, keys and values on two streams",
         },
     }
     if not args.no_cpu_baseline:
