@@ -115,7 +115,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the cache write path shards by KV head, token range or layer "
-              "with no exchange between GPUs, so this build times a single MI355X only.", file=sys.stderr)
+              "with no exchange between GPUs; bench.py times one MI355X only.", file=sys.stderr)
         return 2
 
     import torch
