@@ -484,6 +484,75 @@ def test_decode_append_slots(env):
         assert int(pk.codes.count_nonzero()) <= 64 * 8 * 32
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_symmetric_ties_take_the_even_code(env, bits):
+    """Inputs exactly on level midpoints (j * step, |j| < 2^(b-1)): the nearest-
+    level rule sends each tie to the even code; GPU and oracle must agree bit
+    for bit.  The 24 tie channels of each vector are re-placed on the step
+    that the vector ends up with until the step stops moving."""
+    o, bk = env["oracle"], env["bk"]
+    rng = np.random.default_rng(40 + bits)
+    half = 1 << (bits - 1)
+    N, H = 1024, 8
+    V = (rng.standard_normal((N, H, 128)) * np.exp(rng.standard_normal((1, H, 1)))).astype(np.float32)
+    j = rng.integers(-(half - 1), half, size=(N, H, 24)).astype(np.float32)
+    for _ in range(8):
+        step = o.quantize_values(V, bits, o.sym())["scales"].view(np.float16).astype(np.float32)
+        V[:, :, :24] = j * step[..., None]
+    r = o.quantize_values(V, bits, o.sym())
+    step = r["scales"].view(np.float16).astype(np.float32)
+    on_mid = np.all(V[:, :, :24] == j * step[..., None], axis=2) & (step > 0)
+    say(f"ties {bits}-bit: {on_mid.mean():.3f} of vectors have all 24 ties on their step")
+    assert on_mid.mean() > 0.5
+    g = packed_host(run_values(env, V, bits, bk.sym(2.0)))
+    assert_same_packed(g, r, f"ties {bits}-bit")
+
+
+def _bf16_vectors_with_step(o, bits, N, H, seed, step=0.375):
+    """bf16-exact 128-vectors built so that the symmetric quantizer's fp16 step
+    comes out as `step` for most of them: 24 channels sit on midpoints j * step
+    (|j| < 2^(b-1); j * step has at most 5 significant bits, so it is exact in
+    bf16), 100 are random and 4 bring the sum of squares to the value that
+    gives that step."""
+    rng = np.random.default_rng(seed + bits)
+    L = 1 << bits
+    half = L // 2
+    S_t = 128 * (step * (L - 1) / 4.0) ** 2  # alpha = 2: C = 2 rms, step = 2C / (L - 1)
+    y = np.zeros((N, H, 128))
+    perm = np.argsort(rng.random((N, H, 128)), axis=2)
+    j = rng.integers(-(half - 1), half, size=(N, H, 24))
+    np.put_along_axis(y, perm[..., :24], j * step, axis=2)
+    S_ties = ((j * step) ** 2).sum(axis=2)
+    sig = np.sqrt(np.maximum(0.85 * S_t - S_ties, 0) / 100)[..., None]
+    r = o.round_bf16((rng.standard_normal((N, H, 100)) * sig).astype(np.float32)).astype(np.float64)
+    np.put_along_axis(y, perm[..., 24:124], r, axis=2)
+    adj = np.sqrt(np.maximum(S_t - S_ties - (r ** 2).sum(axis=2), 0) / 4)[..., None]
+    adj = adj * np.sign(rng.standard_normal((N, H, 4)))
+    np.put_along_axis(y, perm[..., 124:], o.round_bf16(adj.astype(np.float32)).astype(np.float64), axis=2)
+    y = y.astype(np.float32)
+    assert np.array_equal(o.round_bf16(y), y)
+    return y
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_key_ties_take_the_even_code(env, bits):
+    """The key kernel on exact ties: position 0 (RoPE is the identity) and the
+    identity transform give y = the bf16 input, whose tie channels sit on
+    midpoints of the step most vectors end up with."""
+    o, bk = env["oracle"], env["bk"]
+    N, H = 4096, 8
+    y = _bf16_vectors_with_step(o, bits, N, H, seed=7)
+    K = (y.view(np.uint32) >> 16).astype(np.uint16)
+    pos = np.zeros(N, dtype=np.int32)
+    T = np.stack([np.eye(128, dtype=np.float32)] * H)
+    r = o.quantize_keys(K, pos, T, 1e6, bits, o.sym())
+    hit = (r["scales"].view(np.float16).astype(np.float32) == 0.375).mean()
+    say(f"key ties {bits}-bit: step on target for {hit:.3f} of vectors")
+    assert hit > 0.5
+    g = packed_host(run_keys(env, K, pos, T, bits, bk.sym(2.0)))
+    assert_same_packed(g, r, f"key ties {bits}-bit")
+
+
 # ---------------------------------------------------------------------------------- read path
 
 @pytest.mark.parametrize("kind,bits", QUANTS)
