@@ -81,6 +81,26 @@ __device__ __forceinline__ uint32_t sym_code(float y, float delta, float rdelta)
   }
 }
 
+// 3/4-bit symmetric code, fast path.  The midpoints are the integer multiples
+// j * step, |j| < 2^(b-1), so away from them the code is 2^(b-1) +
+// floor(y / step), clamped.  v = y * rdelta (rdelta = v_rcp_f32(step), within
+// 1 ulp) is within |y / step| * 1.8e-7 of y / step; after clamping to
+// +-(2^(b-1) - 1/2) (the codes there are the extremes, and no midpoint lies
+// between the clamp and the grid's end) that is below 1.5e-6, so when v is
+// farther than kSymNear from every integer, floor(v) = floor(y / step) and y
+// is no tie.  Otherwise `near` is set and the caller recomputes the code with
+// sym_code.  A zero step (rdelta = 0) gives v = 0, code 2^(b-1); callers drop
+// `near` for it.
+constexpr float kSymNear = 0x1p-17f;
+template <int BITS>
+__device__ __forceinline__ uint32_t sym_code_fast(float y, float rdelta, bool& near) {
+  constexpr float H = (float)(1 << (BITS - 1));
+  const float v = __builtin_amdgcn_fmed3f(y * rdelta, -H + 0.5f, H - 0.5f);
+  const float fl = __builtin_floorf(v);
+  near |= __builtin_fabsf(v - __builtin_rintf(v)) < kSymNear;
+  return (uint32_t)(fl + H);
+}
+
 // Lane masks of the two bits of a 2-bit symmetric code from the midpoint
 // tests A = [x > -step], B = [x >= 0], C = [x > step]: bit1 = B and
 // bit0 = B ? C : A, i.e. one test of x against the threshold that B selects

@@ -505,13 +505,27 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             W2[nb] = delta == 0.0f ? 0xAAAAAAAAu : w ^ 0xAAAAAAAAu;
           } else {
             const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
+            bool near = false;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               uint32_t rc = 0;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) rc |= sym_code<BITS>(acc[nb][4 * q + e], tp, rd) << (BITS * e);
-              asm("" : "+v"(rc));  // keep the word 32 bits wide (compare + add-with-carry codegen)
+              for (int e = 0; e < 4; ++e) rc |= sym_code_fast<BITS>(acc[nb][4 * q + e], rd, near) << (BITS * e);
               run[nb][q] = rc;
+            }
+            near = near && rd != 0.0f;
+            // rare: a value within rounding error of a midpoint; exact codes for those lanes
+            if (__builtin_amdgcn_ballot_w64(near) != 0) {
+              if (near) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  uint32_t rc = 0;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) rc |= sym_code<BITS>(acc[nb][4 * q + e], tp, rd) << (BITS * e);
+                  asm("" : "+v"(rc));  // keep the word 32 bits wide (compare + add-with-carry codegen)
+                  run[nb][q] = rc;
+                }
+              }
             }
           }
         }

@@ -238,10 +238,20 @@ values_kernel(const ValuesArgs a) {
           float x[8];
           unpack(u, x);
           uint32_t packed = 0;
+          bool near = false;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], th.x, th.y) << (BITS * e);
-          // keep the word 32 bits wide so code counts compile to compare + add-with-carry
-          asm("" : "+v"(packed));
+          for (int e = 0; e < 8; ++e) packed |= sym_code_fast<BITS>(x[e], th.y, near) << (BITS * e);
+          near = near && th.y != 0.0f;
+          // rare: a value within rounding error of a midpoint; exact codes for those lanes
+          if (__builtin_amdgcn_ballot_w64(near) != 0) {
+            if (near) {
+              packed = 0;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], th.x, th.y) << (BITS * e);
+              // keep the word 32 bits wide so code counts compile to compare + add-with-carry
+              asm("" : "+v"(packed));
+            }
+          }
           store_codes(wave * kPerWave + 4 * u + sub, packed);
         }
       }
