@@ -185,6 +185,22 @@ __device__ __forceinline__ uint32_t affine_code(float x, double z, double s) {
   return q;
 }
 
+// Affine code, fast path.  v = (x - zero) * rstep (rstep = v_rcp_f32(step),
+// within 1 ulp; the difference rounded once) is within |v| * 2.4e-7 of the
+// exact (x - zero) / step; clamped to [0, 2^b - 1] that is below 3.6e-6.  The
+// midpoints sit at v = k + 1/2, so when v is farther than kAffNear from every
+// half-integer, rint(v) is the nearest level and no tie; otherwise `near` is
+// set and the caller recomputes the code with affine_code.  A zero step
+// (rstep = 0) gives code 0, as affine_code's callers do.
+constexpr float kAffNear = 0x1p-16f;
+template <int BITS>
+__device__ __forceinline__ uint32_t affine_code_fast(float x, float zero, float rstep, bool& near) {
+  constexpr float Lm1 = (float)((1 << BITS) - 1);
+  const float v = __builtin_amdgcn_fmed3f((x - zero) * rstep, 0.0f, Lm1);
+  near |= __builtin_fabsf(v - __builtin_floorf(v) - 0.5f) < kAffNear;
+  return (uint32_t)__builtin_rintf(v);
+}
+
 // ---------------------------------------------------------------------------------------------
 // RoPE cos/sin of the exact angle pos * w_i, rounded once to fp32.
 //

@@ -557,16 +557,31 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
                                             : (a.q.hi_mode == 1 ? s30 : s31);
           const float s32 = (hi - lo) / (float)(L - 1);
           const uint16_t sh = f16_sat_bits(s32), zh = f16_sat_bits(lo);
-          const double sd = (double)f16_bits_to_f32(sh), zd = (double)f16_bits_to_f32(zh);
+          const float s32h = f16_bits_to_f32(sh), z32h = f16_bits_to_f32(zh);
+          const float rs = s32h == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s32h);
+          bool near = false;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             uint32_t rc = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t cd = sd == 0.0 ? 0u : affine_code<BITS>(acc[nb][4 * q + e], zd, sd);
-              rc |= cd << (BITS * e);
-            }
+            for (int e = 0; e < 4; ++e) rc |= affine_code_fast<BITS>(acc[nb][4 * q + e], z32h, rs, near) << (BITS * e);
             run[nb][q] = rc;
+          }
+          // rare: a value within rounding error of a midpoint; exact codes for those lanes
+          if (__builtin_amdgcn_ballot_w64(near) != 0) {
+            if (near) {
+              const double sd = (double)s32h, zd = (double)z32h;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                uint32_t rc = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const uint32_t cd = sd == 0.0 ? 0u : affine_code<BITS>(acc[nb][4 * q + e], zd, sd);
+                  rc |= cd << (BITS * e);
+                }
+                run[nb][q] = rc;
+              }
+            }
           }
           if (lh == 0) {
             sc_lds[g][32 * nb + col][hg * 8 + wq] = sh;

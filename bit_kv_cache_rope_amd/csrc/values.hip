@@ -288,11 +288,22 @@ values_kernel(const ValuesArgs a) {
                                           : (a.q.hi_mode == 1 ? s30 : s31);
         const float s32 = (hi - lo) / (float)(L - 1);
         const uint16_t sh = f16_sat_bits(s32), zh = f16_sat_bits(lo);
-        const double sd = (double)f16_bits_to_f32(sh), zd = (double)f16_bits_to_f32(zh);
+        const float s32h = f16_bits_to_f32(sh), z32h = f16_bits_to_f32(zh);
+        const float rs = s32h == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s32h);
+        bool near = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(x[e], zd, sd);
-          packed |= c << (BITS * e);
+        for (int e = 0; e < 8; ++e) packed |= affine_code_fast<BITS>(x[e], z32h, rs, near) << (BITS * e);
+        // rare: a value within rounding error of a midpoint; exact codes for those lanes
+        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+          if (near) {
+            const double sd = (double)s32h, zd = (double)z32h;
+            packed = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(x[e], zd, sd);
+              packed |= c << (BITS * e);
+            }
+          }
         }
         if ((l16 & 3) == 0) {
           sc_lds[par][vloc * 4 + (l16 >> 2)] = sh;

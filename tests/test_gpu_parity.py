@@ -508,6 +508,34 @@ def test_symmetric_ties_take_the_even_code(env, bits):
     assert_same_packed(g, r, f"ties {bits}-bit")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_affine_ties_take_the_even_code(env, bits):
+    """Affine groups with six channels exactly on midpoints zero + (k + 1/2) step
+    (placed among the middle ranks, re-placed until the group's zero and step
+    stop moving): GPU and oracle agree bit for bit."""
+    o, bk = env["oracle"], env["bk"]
+    L = 1 << bits
+    rng = np.random.default_rng(60 + bits)
+    N, H = 1024, 8
+    V = rng.standard_normal((N, H, 128)).astype(np.float32)
+    G = V.reshape(N, H, 4, 32)
+    k = rng.integers(0, L - 1, size=(N, H, 4, 6)).astype(np.float32) + 0.5
+    for _ in range(6):
+        r = o.quantize_values(V, bits, o.affine(1.0, 99.0))
+        sc = r["scales"].view(np.float16).astype(np.float32).reshape(N, H, 4)
+        zr = r["zeros"].view(np.float16).astype(np.float32).reshape(N, H, 4)
+        mid = np.argsort(G, axis=3)[..., 8:14]
+        np.put_along_axis(G, mid, (zr[..., None] + k * sc[..., None]).astype(np.float32), axis=3)
+    r = o.quantize_values(V, bits, o.affine(1.0, 99.0))
+    sc = r["scales"].view(np.float16).astype(np.float64).reshape(N, H, 4)
+    zr = r["zeros"].view(np.float16).astype(np.float64).reshape(N, H, 4)
+    on_mid = np.all(np.take_along_axis(G, mid, axis=3) == zr[..., None] + k * sc[..., None], axis=3)
+    say(f"affine ties {bits}-bit: {on_mid.mean():.3f} of groups have all 6 ties exact")
+    assert on_mid.mean() > 0.9
+    g = packed_host(run_values(env, V, bits, bk.affine(1.0, 99.0)))
+    assert_same_packed(g, r, f"affine ties {bits}-bit")
+
+
 def _bf16_vectors_with_step(o, bits, N, H, seed, step=0.375):
     """bf16-exact 128-vectors built so that the symmetric quantizer's fp16 step
     comes out as `step` for most of them: 24 channels sit on midpoints j * step
