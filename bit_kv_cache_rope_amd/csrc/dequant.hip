@@ -107,6 +107,24 @@ __global__ void __launch_bounds__(64 * kWaves) dequant_plain_kernel(const Dequan
       const uint32_t* d = (const uint32_t*)&rec_lds[wave][o & ~3];
       c = __builtin_amdgcn_alignbit(d[1], d[0], 8 * (o & 3)) & 0xFFFFFFu;
     }
+    if constexpr (QK == 0 && BITS == 2 && BF16OUT) {
+      // Four possible outputs per vector: their bf16 values form an 8-byte
+      // table, and one v_perm_b32 per pair of codes picks two of them.  The
+      // selector of codes (q0, q1) is bytes {2q0, 2q0+1, 2q1, 2q1+1}.  (An
+      // invalid vector has a zero step: +0 everywhere, the + 0 turning -0 into +0.)
+      const float hs = 0.5f * f16_bits_to_f32(sc_lds[wave][NSC * j]);
+      const uint32_t t01 = pack_bf16x2(-3.0f * hs + 0.0f, -hs + 0.0f);
+      const uint32_t t23 = pack_bf16x2(hs + 0.0f, 3.0f * hs + 0.0f);
+      uint32_t o4[4];
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t x = c >> (4 * pr);
+        const uint32_t t = (x & 3u) | ((x & 0xCu) << 14);  // q0 in byte 0, q1 in byte 2
+        o4[pr] = __builtin_amdgcn_perm(t23, t01, t * 0x0202u + 0x01000100u);
+      }
+      if (v < nv) *(uint4*)((uint16_t*)a.out + v * kD + 8 * l16) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      continue;
+    }
     float y[8];
     if constexpr (QK == 0) {
       // an invalid vector has a zero step: +0 everywhere (the + 0 turns -0 into +0)
