@@ -80,6 +80,11 @@ def _lib_():
         L.wko_quantize_values.restype = i32
         L.wko_dequantize.argtypes = [vp, vp, vp, vp, i64, i32, i32, qp, vp, vp, i32]
         L.wko_dequantize.restype = i32
+        L.wko_pair_queries.argtypes = [vp, i32, i64, i32, i64, vp, i32, vp]
+        L.wko_pair_queries.restype = i32
+        L.wko_decode_attention.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, i64, i32, vp, vp, f32, vp,
+                                           i32]
+        L.wko_decode_attention.restype = i32
         _lib = L
     return _lib
 
@@ -268,6 +273,40 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None, 
     rc = _lib_().wko_dequantize(codes.ctypes.data, scales.ctypes.data, _ptr(zeros), _ptr(slots), N, H,
                                 bits, ctypes.byref(q), _ptr(Tinv), out.ctypes.data,
                                 threads or threads_default())
+    if rc != 0:
+        raise ValueError("oracle rejected arguments")
+    return out
+
+
+def pair_queries(Q: np.ndarray, Tinv: np.ndarray) -> np.ndarray:
+    """Q: [N][Hq][128] float32 or uint16 (bf16 bits); Tinv: [Hkv][128][128].
+    Returns the paired queries as bf16 bits [N][Hq][128]."""
+    Q = np.ascontiguousarray(Q)
+    Tinv = _c(Tinv, np.float32)
+    N, Hq = Q.shape[0], Q.shape[1]
+    out = np.empty((N, Hq, D), dtype=np.uint16)
+    rc = _lib_().wko_pair_queries(Q.ctypes.data, _dtype_code(Q), N, Hq, Hq * D, Tinv.ctypes.data,
+                                  Tinv.shape[0], out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected arguments")
+    return out
+
+
+def decode_attention(qp: np.ndarray, k: dict, v: dict, bits: int, row0: np.ndarray, lens: np.ndarray,
+                     scale: float, threads: int | None = None) -> np.ndarray:
+    """qp: bf16 bits [B][Hq][128]; k, v: dicts with symmetric ``codes`` [rows][Hkv][16 bits] and
+    ``scales`` [rows][Hkv]; sequence b reads rows row0[b] + n, n < lens[b].  Returns fp32
+    [B][Hq][128]."""
+    qp = _c(qp, np.uint16)
+    kc, ks = _c(k["codes"], np.uint8), _c(k["scales"], np.uint16)
+    vc, vs = _c(v["codes"], np.uint8), _c(v["scales"], np.uint16)
+    row0 = _c(row0, np.int64)
+    lens = _c(lens, np.int32)
+    B, Hq = qp.shape[0], qp.shape[1]
+    out = np.empty((B, Hq, D), dtype=np.float32)
+    rc = _lib_().wko_decode_attention(qp.ctypes.data, B, Hq, kc.shape[1], kc.ctypes.data, ks.ctypes.data,
+                                      vc.ctypes.data, vs.ctypes.data, kc.shape[0], bits, row0.ctypes.data,
+                                      lens.ctypes.data, scale, out.ctypes.data, threads or threads_default())
     if rc != 0:
         raise ValueError("oracle rejected arguments")
     return out

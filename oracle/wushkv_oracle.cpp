@@ -13,6 +13,8 @@
  *           y --clipped b-bit quantizer--> codes + fp16 scale(s) --> packed record
  *   values: v --clipped b-bit quantizer--> codes + scale(s) --> packed record
  *   read:   record --> unpack --> dequantize --> (keys) T~inv * y^
+ *   attend: q --pairing--> q' = bf16(T~inv^T q) ; softmax(q'.y^ * scale) . v^
+ *           over a sequence's rows of the packed key and value caches
  *
  * Readings taken where the pages are silent:
  *   - RoPE is the rotate-half form on channel pairs (i, i+64) with
@@ -29,6 +31,11 @@
  *     even code; a zero step gives code 2^(b-1) (symmetric) or 0 (affine).
  *   - Packing: code j occupies bits [b*j, b*j+b) of an LSB-first bit stream of
  *     16*b bytes per (token, head).
+ *   - Query pairing uses the inverse transform the read path uses: q'_j =
+ *     sum_r T~inv[r][j] q_r, rounded once to fp32 and then to the bf16 operand
+ *     of the score product; q'.y^ equals q.(T~inv y^), the score against the
+ *     read path's keys.  Attention (one query per sequence, grouped query
+ *     heads) is the exact softmax-weighted mean of the dequantized values.
  *
  * Build: g++ -O2 -std=c++17 -ffp-contract=off (no fast-math), x86-64.
  */
@@ -500,6 +507,102 @@ int wko_dequantize(const uint8_t* codes, const uint16_t* scales, const uint16_t*
           std::memcpy(o, yh, sizeof(yh));
         }
       }
+    }
+  });
+  return 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// (code - m) * step for a symmetric record: exact in fp64 (a code of at most 4
+// bits times an fp16 step).
+void dequant_sym(const uint8_t* rec, uint16_t step, int bits, double* y) {
+  uint8_t q[kD];
+  unpack(rec, bits, q);
+  const double d = (double)f16_to_f32(step), m = (double)((1 << bits) - 1) / 2.0;
+  for (int j = 0; j < kD; ++j) y[j] = ((double)q[j] - m) * d;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Query-side pairing: q'_j = RN32( sum_r T~inv[r][j] q_r ) in fp64 over
+// ascending r (a bf16 entry times an fp32 query element is exact in fp64),
+// then rounded to bf16.  Query head hq reads KV head hq / (Hq / Hkv).  The
+// transform is built with the query heads that read the cached keys in view
+// (ai4snews summary, method paragraph), so scoring the transformed-basis keys
+// with q' scores the read path's keys T~inv y^ with q.
+// Q: [N][Hq][128] (fp32 or bf16 bits) with token_stride elements per token;
+// Tinv: [Hkv][128][128] fp32 (rounded to bf16 here); out: bf16 bits [N][Hq][128].
+int wko_pair_queries(const void* Q, int q_dtype, int64_t N, int Hq, int64_t token_stride,
+                     const float* Tinv, int Hkv, uint16_t* out) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || N < 0 || token_stride < (int64_t)Hq * kD) return -1;
+  const int G = Hq / Hkv;
+  for (int64_t n = 0; n < N; ++n)
+    for (int hq = 0; hq < Hq; ++hq) {
+      const float* M = Tinv + (size_t)(hq / G) * kD * kD;
+      for (int j = 0; j < kD; ++j) {
+        double acc = 0.0;
+        for (int r = 0; r < kD; ++r)
+          acc += (double)round_bf16(M[r * kD + j]) * (double)load_elem(Q, q_dtype, n * token_stride + (int64_t)hq * kD + r);
+        out[(n * Hq + hq) * kD + j] = bf16_bits((float)acc);
+      }
+    }
+  return 0;
+}
+
+// Decode attention over symmetric packed caches.  Sequence b's tokens are the
+// cache rows row0[b] + n, n < len[b]; rows outside [0, n_rows) are absent.
+// For query head hq (KV head hq / G) with paired query q' (bf16 [B][Hq][128]):
+//   s_n = scale * sum_j q'_j y^_nj        (y^: dequantized keys, fp64 sum)
+//   o   = sum_n exp(s_n - max s) v^_n / sum_n exp(s_n - max s)
+// in fp64, written as fp32 [B][Hq][128]; a sequence without tokens gives 0.
+// Keys are scored in their transformed basis and values read as stored (their
+// transform is folded into the weights): ai4snews summary, deployment paragraph.
+int wko_decode_attention(const uint16_t* qp, int B, int Hq, int Hkv, const uint8_t* kcodes,
+                         const uint16_t* kscales, const uint8_t* vcodes, const uint16_t* vscales,
+                         int64_t n_rows, int bits, const int64_t* row0, const int32_t* len,
+                         float scale, float* out, int threads) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || bits < 2 || bits > 4 || n_rows < 0) return -1;
+  const int G = Hq / Hkv;
+  const int rec = 16 * bits;
+  parallel_for((int64_t)B * Hq, threads, [&](int64_t u0, int64_t u1) {
+    double y[kD], v[kD], q[kD], o[kD];
+    std::vector<double> s;
+    std::vector<int64_t> rows;
+    for (int64_t u = u0; u < u1; ++u) {
+      const int64_t b = u / Hq;
+      const int hq = (int)(u % Hq), h = hq / G;
+      for (int j = 0; j < kD; ++j) q[j] = (double)bf16_value(qp[u * kD + j]);
+      s.clear();
+      rows.clear();
+      for (int64_t n = 0; n < (int64_t)len[b]; ++n) {
+        const int64_t row = row0[b] + n;
+        if (row < 0 || row >= n_rows) continue;
+        const int64_t slot = row * Hkv + h;
+        dequant_sym(kcodes + slot * rec, kscales[slot], bits, y);
+        double acc = 0.0;
+        for (int j = 0; j < kD; ++j) acc += q[j] * y[j];
+        s.push_back((double)scale * acc);
+        rows.push_back(row);
+      }
+      for (int j = 0; j < kD; ++j) o[j] = 0.0;
+      if (!s.empty()) {
+        const double M = *std::max_element(s.begin(), s.end());
+        double l = 0.0;
+        for (size_t i = 0; i < s.size(); ++i) {
+          const double p = std::exp(s[i] - M);
+          const int64_t slot = rows[i] * Hkv + h;
+          dequant_sym(vcodes + slot * rec, vscales[slot], bits, v);
+          for (int j = 0; j < kD; ++j) o[j] += p * v[j];
+          l += p;
+        }
+        for (int j = 0; j < kD; ++j) o[j] /= l;
+      }
+      for (int j = 0; j < kD; ++j) out[u * kD + j] = (float)o[j];
     }
   });
   return 0;
