@@ -274,6 +274,46 @@ def main() -> int:
     dec_k_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
     dec_v_us = float(np.mean([e[2].elapsed_time(e[3]) for e in dev_ev])) * 1e3
 
+    # ---- decode attention over the packed caches (64 sequences of the decode workload's lengths,
+    # 32 query heads over 8 KV heads), reported alongside: the caches hold random codes and steps
+    att_q = 32
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for c in (dkc, dvc):
+        c.codes.copy_(torch.randint(0, 256, c.codes.shape, dtype=torch.uint8, device=dev, generator=g))
+        c.scales.copy_((torch.rand(c.scales.shape, device=dev, generator=g) * 0.05 + 0.02).to(torch.float16))
+    att_len = synth.positions(wd).astype(np.int64) + 1
+    att_lens = torch.from_numpy(att_len.astype(np.int32)).to(dev)
+    att_row0 = torch.arange(dn, dtype=torch.int64, device=dev) * 32768
+    _, dTi = synth.transform(wd, 0)
+    dtki = bk.Transform(dTi)
+    att_Q = (torch.randn((dn, att_q, D), device=dev, generator=g) * 3.0).to(torch.bfloat16)
+    att_qp = torch.empty((dn, att_q, D), dtype=torch.bfloat16, device=dev)
+    att_ws = torch.empty(bk.wushkv_decode_attention_workspace(dn, att_q, H, 32768) // 4, dtype=torch.float32,
+                         device=dev)
+    att_out = torch.empty((dn, att_q, D), dtype=torch.float32, device=dev)
+    att = bk.prepare_decode_attention(att_qp, dkc, dvc, H, bits, q, att_row0, att_lens, 32768, 1.0 / np.sqrt(D),
+                                      att_ws, att_out, stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            bk.wushkv_pair_queries(att_Q, dtki, out=att_qp, stream=stream)
+            att()
+    torch.cuda.synchronize()
+    att_ev = new_events(50, 6)
+    for e in att_ev:
+        bk.wushkv_debug_time_next_launch(e[0], e[1])
+        bk.wushkv_pair_queries(att_Q, dtki, out=att_qp, stream=stream)
+        e[4].record(stream)
+        bk.wushkv_debug_time_next_launch(e[2], e[3])
+        att()
+        e[5].record(stream)
+    torch.cuda.synchronize()
+    att_pair_us = float(np.mean([e[0].elapsed_time(e[1]) for e in att_ev])) * 1e3
+    att_kernel_us = float(np.mean([e[2].elapsed_time(e[3]) for e in att_ev])) * 1e3
+    att_call_us = float(np.mean([e[4].elapsed_time(e[5]) for e in att_ev])) * 1e3
+    att_bytes = int(att_len.sum()) * H * 2 * (16 * bits + 2) + dn * att_q * D * 2 + dn * 2 * 12
+    att_flops = 4.0 * int(att_len.sum()) * att_q * D
+
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = N * args.steps / elapsed
     kb = N * key_bytes_per_token(H, bits) + H * D * D * 2  # + T~ read once per launch
@@ -316,6 +356,16 @@ def main() -> int:
             "tokens_per_layer": dn, "cache_rows": drows, "layer_us": round(dec_layer_us, 2),
             "keys_kernel_us": round(dec_k_us, 2), "values_kernel_us": round(dec_v_us, 2),
             "note": "one layer's K and V calls back to back, keys and values on two streams",
+        },
+        "decode_attention": {
+            "sequences": dn, "q_heads": att_q, "kv_heads": H, "bits": bits,
+            "cached_tokens": int(att_len.sum()), "max_len": int(att_len.max()),
+            "pair_queries_us": round(att_pair_us, 2), "attention_kernel_us": round(att_kernel_us, 2),
+            "call_us": round(att_call_us, 2), "algorithmic_bytes": att_bytes,
+            "attention_gbs": round(att_bytes / (att_kernel_us * 1e-6) / 1e9, 1),
+            "attention_hbm_frac": round(att_bytes / (att_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(att_flops / (att_kernel_us * 1e-6) / 1e12, 2),
+            "note": "packed 2-bit K and V read once; call_us = attention and split combine launched back to back",
         },
     }
     if not args.no_cpu_baseline:

@@ -7,6 +7,8 @@ The functions keep the C names:
     wushkv_quantize_keys(K, pos, rope, T_k, bits, quantizer, out)
     wushkv_quantize_values(V, bits, quantizer, out)
     wushkv_dequantize(packed, n_tokens, n_heads, bits, quantizer, T_k_inv=None, ...)
+    wushkv_pair_queries(Q, T_k_inv)
+    wushkv_decode_attention(q_paired, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0, seq_len, ...)
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ __all__ = [
     "WushKVError", "Quantizer", "sym", "affine", "Transform", "Rope", "PackedCache", "alloc_packed",
     "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize", "wushkv_debug_rope_transform",
     "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch", "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
-    "prepare_quantize_values", "prepare_dequantize",
+    "prepare_quantize_values", "prepare_dequantize", "wushkv_pair_queries", "wushkv_decode_attention_workspace",
+    "wushkv_decode_attention", "prepare_decode_attention",
 ]
 
 
@@ -296,3 +299,65 @@ def wushkv_rope_frequencies(theta: float):
     out = (ctypes.c_float * 64)()
     _lib.check(library().wushkv_rope_frequencies(ctypes.c_float(theta), out))
     return list(out)
+
+
+def wushkv_pair_queries(Q: torch.Tensor, T_k_inv: Transform, out: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Paired queries q' = bf16(T~inv^T q), bf16 [n_tokens][n_q_heads][128]."""
+    dt, n, hq, stride = _kv_args(Q)
+    if out is None:
+        out = torch.empty((n, hq, 128), dtype=torch.bfloat16, device=Q.device)
+    _check_device_tensor(out, "out", torch.bfloat16)
+    _lib.check(library().wushkv_pair_queries(
+        ctypes.c_void_p(Q.data_ptr()), dt, n, hq, stride, T_k_inv.handle, ctypes.c_void_p(out.data_ptr()),
+        _stream(stream)))
+    return out
+
+
+def wushkv_decode_attention_workspace(n_seqs: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
+    b = ctypes.c_size_t()
+    _lib.check(library().wushkv_decode_attention_workspace(n_seqs, n_q_heads, n_kv_heads, max_seq_len,
+                                                           ctypes.byref(b)))
+    return int(b.value)
+
+
+def _attention_args(q_paired, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0, seq_len, max_seq_len,
+                    scale, workspace, out, stream):
+    if q_paired.dim() != 3 or q_paired.shape[2] != 128:
+        raise ValueError("q_paired must be [n_seqs][n_q_heads][128]")
+    _check_device_tensor(q_paired, "q_paired", torch.bfloat16)
+    _check_device_tensor(seq_row0, "seq_row0", torch.int64)
+    _check_device_tensor(seq_len, "seq_len", torch.int32)
+    n_seqs, n_q_heads = int(q_paired.shape[0]), int(q_paired.shape[1])
+    if workspace is None:
+        nb = wushkv_decode_attention_workspace(n_seqs, n_q_heads, n_kv_heads, max_seq_len)
+        workspace = torch.empty(max(nb // 4, 4), dtype=torch.float32, device=q_paired.device)
+    if out is None:
+        out = torch.empty((n_seqs, n_q_heads, 128), dtype=torch.float32, device=q_paired.device)
+    _check_device_tensor(out, "out", torch.float32)
+    q, kp, vp_ = quantizer.c(), k_cache.c(), v_cache.c()
+    args = (ctypes.c_void_p(q_paired.data_ptr()), n_seqs, n_q_heads, ctypes.byref(kp), ctypes.byref(vp_), n_kv_heads,
+            bits, ctypes.byref(q), ctypes.c_void_p(seq_row0.data_ptr()), ctypes.c_void_p(seq_len.data_ptr()),
+            max_seq_len, ctypes.c_float(scale), ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(out.data_ptr()), _stream(stream))
+    return args, (q_paired, k_cache, v_cache, seq_row0, seq_len, workspace, out, q, kp, vp_), out
+
+
+def wushkv_decode_attention(q_paired: torch.Tensor, k_cache: PackedCache, v_cache: PackedCache, n_kv_heads: int,
+                            bits: int, quantizer: Quantizer, seq_row0: torch.Tensor, seq_len: torch.Tensor,
+                            max_seq_len: int, scale: float, workspace: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention over the packed caches; fp32 [n_seqs][n_q_heads][128]."""
+    args, _keep, out = _attention_args(q_paired, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0, seq_len,
+                                       max_seq_len, scale, workspace, out, stream)
+    _lib.check(library().wushkv_decode_attention(*args))
+    return out
+
+
+def prepare_decode_attention(q_paired, k_cache: PackedCache, v_cache: PackedCache, n_kv_heads: int, bits: int,
+                             quantizer: Quantizer, seq_row0, seq_len, max_seq_len: int, scale: float,
+                             workspace: torch.Tensor, out: torch.Tensor, stream=None) -> PreparedCall:
+    args, keep, _ = _attention_args(q_paired, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0, seq_len,
+                                    max_seq_len, scale, workspace, out, stream)
+    return PreparedCall(library().wushkv_decode_attention, args, keep)
+

@@ -16,7 +16,8 @@ EXPORTED = [
     "wushkv_transform_create", "wushkv_transform_destroy", "wushkv_rope_create", "wushkv_rope_destroy",
     "wushkv_rope_frequencies", "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize",
     "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch",
-    "wushkv_status_string", "wushkv_last_error", "wushkv_version",
+    "wushkv_status_string", "wushkv_last_error", "wushkv_version", "wushkv_pair_queries",
+    "wushkv_decode_attention_workspace", "wushkv_decode_attention",
 ]
 
 
@@ -61,6 +62,10 @@ def load() -> ctypes.CDLL:
     L.wushkv_debug_rope_transform.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, vp, vp]
     L.wushkv_debug_rope_cos_sin.argtypes = [vp, vp, i64, vp, vp]
     L.wushkv_debug_time_next_launch.argtypes = [vp, vp]
+    L.wushkv_pair_queries.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp]
+    L.wushkv_decode_attention_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.wushkv_decode_attention.argtypes = [vp, i32, i32, pp, pp, i32, i32, qp, vp, vp, i32, f32, vp,
+                                          ctypes.c_size_t, vp, vp]
     L.wushkv_status_string.argtypes = [i32]
     L.wushkv_status_string.restype = ctypes.c_char_p
     L.wushkv_last_error.argtypes = []

@@ -500,4 +500,110 @@ wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* 
   return WUSHKV_OK;
 }
 
+wushkv_status wushkv_pair_queries(const void* Q, wushkv_dtype q_dtype, int64_t n_tokens, int n_q_heads,
+                                  int64_t token_stride, const wushkv_transform* T_k_inv, void* q_out,
+                                  void* stream) {
+  wushkv_status st = check_tensor(Q, q_dtype, n_tokens, n_q_heads, token_stride);
+  if (st) return st;
+  if (!T_k_inv) return fail(WUSHKV_ERR_INVALID_ARG, "transform handle is NULL");
+  if (n_q_heads % T_k_inv->n_heads)
+    return fail(WUSHKV_ERR_INVALID_ARG, "n_q_heads must be a multiple of the transform's head count");
+  if (n_tokens == 0) return WUSHKV_OK;
+  if (!q_out) return fail(WUSHKV_ERR_INVALID_ARG, "q_out is NULL");
+  if (!aligned(q_out, 2)) return fail(WUSHKV_ERR_ALIGNMENT, "q_out must be 2-byte aligned");
+  if (n_tokens * (n_q_heads / T_k_inv->n_heads) > ((int64_t)1 << 35))
+    return fail(WUSHKV_ERR_UNSUPPORTED, "too many query vectors for one call");
+  int dev;
+  st = current_device(&dev);
+  if (st) return st;
+  if (dev != T_k_inv->device) return fail(WUSHKV_ERR_INVALID_ARG, "transform belongs to another device");
+  wushkv::PairArgs a{};
+  a.Q = Q;
+  a.f32_in = q_dtype == WUSHKV_F32;
+  a.n_tokens = n_tokens;
+  a.stride = token_stride;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = T_k_inv->n_heads;
+  a.G = n_q_heads / T_k_inv->n_heads;
+  a.Tinv = T_k_inv->d_swz;
+  a.out = (uint16_t*)q_out;
+  hipError_t e = wushkv::launch_pair_queries(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "query pairing launch");
+  return WUSHKV_OK;
+}
+
+static wushkv_status attention_shape(int n_seqs, int n_q_heads, int n_kv_heads, int max_seq_len) {
+  if (n_seqs < 0 || n_seqs > 65535) return fail(WUSHKV_ERR_INVALID_ARG, "n_seqs must be in [0, 65535]");
+  if (n_kv_heads < 1 || n_kv_heads > 65535) return fail(WUSHKV_ERR_INVALID_ARG, "n_kv_heads must be in [1, 65535]");
+  if (n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return fail(WUSHKV_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q_heads / n_kv_heads > 8) return fail(WUSHKV_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (n_q_heads > 65535) return fail(WUSHKV_ERR_INVALID_ARG, "n_q_heads above 65535");
+  if (max_seq_len < 0 || max_seq_len > (1 << 30)) return fail(WUSHKV_ERR_INVALID_ARG, "max_seq_len must be in [0, 2^30]");
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n_kv_heads, int max_seq_len,
+                                                size_t* bytes) {
+  if (!bytes) return fail(WUSHKV_ERR_INVALID_ARG, "bytes is NULL");
+  wushkv_status st = attention_shape(n_seqs, n_q_heads, n_kv_heads, max_seq_len);
+  if (st) return st;
+  *bytes = wushkv::attention_workspace_bytes(n_seqs, n_q_heads, max_seq_len);
+  return WUSHKV_OK;
+}
+
+wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_heads,
+                                      const wushkv_packed* k_cache, const wushkv_packed* v_cache,
+                                      int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
+                                      const int64_t* seq_row0, const int32_t* seq_len, int max_seq_len,
+                                      float scale, void* workspace, size_t workspace_bytes, float* out,
+                                      void* stream) {
+  wushkv_status st = attention_shape(n_seqs, n_q_heads, n_kv_heads, max_seq_len);
+  if (st) return st;
+  if (bits < 2 || bits > 4) return fail(WUSHKV_ERR_INVALID_ARG, "bits must be 2, 3 or 4");
+  wushkv::QuantArgs qa{};
+  st = make_quant(quantizer, &qa);
+  if (st) return st;
+  if (qa.kind != 0) return fail(WUSHKV_ERR_UNSUPPORTED, "attention reads symmetric caches only");
+  st = check_packed(k_cache, 0, 0, false);
+  if (st) return st;
+  st = check_packed(v_cache, 0, 0, false);
+  if (st) return st;
+  if (k_cache->n_rows != v_cache->n_rows) return fail(WUSHKV_ERR_INVALID_ARG, "key and value caches differ in rows");
+  if (!std::isfinite(scale)) return fail(WUSHKV_ERR_INVALID_ARG, "scale must be finite");
+  if (n_seqs == 0) return WUSHKV_OK;
+  if (!q_paired || !seq_row0 || !seq_len || !out)
+    return fail(WUSHKV_ERR_INVALID_ARG, "q_paired, seq_row0, seq_len and out must be set");
+  if (!aligned(q_paired, 2) || !aligned(seq_row0, 8) || !aligned(seq_len, 4) || !aligned(out, 4))
+    return fail(WUSHKV_ERR_ALIGNMENT, "misaligned q_paired, seq_row0, seq_len or out");
+  const size_t need = wushkv::attention_workspace_bytes(n_seqs, n_q_heads, max_seq_len);
+  if (workspace_bytes < need) return fail(WUSHKV_ERR_INVALID_ARG, "workspace smaller than wushkv_decode_attention_workspace");
+  if (need > 0 && (!workspace || !aligned(workspace, 16)))
+    return fail(workspace ? WUSHKV_ERR_ALIGNMENT : WUSHKV_ERR_INVALID_ARG, "workspace must be set and 16-byte aligned");
+  wushkv::AttnArgs a{};
+  a.qp = (const uint16_t*)q_paired;
+  a.kc = (const uint8_t*)k_cache->codes;
+  a.ks = (const uint16_t*)k_cache->scales;
+  a.vc = (const uint8_t*)v_cache->codes;
+  a.vs = (const uint16_t*)v_cache->scales;
+  a.n_rows = k_cache->n_rows;
+  a.row0 = seq_row0;
+  a.len = seq_len;
+  a.n_seqs = n_seqs;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.max_len = max_seq_len;
+  a.n_splits = wushkv::attention_splits(max_seq_len);
+  a.n_splits8 = (a.n_splits + 7) / 8;
+  if ((int64_t)8 * a.n_splits8 * n_kv_heads * n_seqs > INT32_MAX)
+    return fail(WUSHKV_ERR_UNSUPPORTED, "too many (sequence, KV head, split) blocks for one call");
+  a.c0 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+  a.part = (float*)workspace;
+  a.out = out;
+  hipError_t e = wushkv::launch_attention(a, bits, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return WUSHKV_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,562 @@
+// Decode attention straight from the packed cache, with the query paired
+// through the inverse key transform.
+//
+// The keys sit in the cache in the transformed basis y = T_k x.  A query head
+// that reads them is paired once, q' = T~inv^T q, so that q'.y^ = q.(T~inv y^):
+// the scores against the read path's keys come out without a 128x128 product
+// per cached key (ai4snews summary "WUSH-KV cuts 2-bit KV-cache perplexity
+// ...", method paragraph: the transform is built with the query heads that
+// read the cached keys in view; deployment paragraph: keys are cached after
+// the transform, the value transform is folded into the weights, so values
+// are read as stored).
+//
+// Work decomposition (one query token per sequence, grouped query heads):
+//   * pair_queries_kernel: q'_j = RN32(sum_r T~inv[r][j] q_r) in fp64 FMAs
+//     over ascending r (every product is exact), then bf16.
+//   * attention_kernel: one block of four waves per (2048-token split, KV
+//     head, sequence), in rounds of 512 tokens whose key and value records
+//     are first copied to LDS with all loads in flight at once.
+//       scores  S[n][g] = sum_j code-operand[n][j] * q'[g][j] on
+//               v_mfma_f32_16x16x32_bf16 (16 tokens x 16 columns, G used);
+//               the key codes enter as exact bf16 values 0.5 + c / SB built
+//               with one shift, mask and v_perm per pair of codes, and the
+//               constant part is subtracted after the product.
+//       softmax p = exp2(s - max) over the split, then p * step_v.
+//       values  O[g][ch] += p[g][n] * c[n][ch] on v_mfma_f32_4x4x1f32: 16
+//               blocks = 16 tokens, 4 rows = 4 query heads, 4 columns = 4
+//               channels, so each lane converts only the codes of its own
+//               token (fp32 operands: no rounding of p).
+//     A split writes (max, sum, unnormalized output) per query head.
+//   * combine_kernel merges the splits of a sequence.
+#include "device_common.h"
+#include "internal.h"
+
+namespace wushkv {
+
+namespace {
+
+constexpr int kChunk = 2048;     // tokens per split (one block)
+constexpr int kSub = 512;        // tokens staged in LDS per round
+constexpr int kPartFloats = 132;  // per (sequence, query head, split): max, sum, 2 pad, o[128]
+constexpr int kPairVecs = 16;     // query vectors per pairing block
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t swz_index(int h, int r, int c) {
+  // transform handle order: chunk (h, r / 32, c / 16), lane r % 32 + 32 ((c % 16) / 8), element c % 8
+  return ((((int64_t)h * 4 + (r >> 5)) * 8 + (c >> 4)) * 64 + (r & 31) + 32 * ((c & 15) >> 3)) * 8 + (c & 7);
+}
+
+// grid (ceil(N G / kPairVecs), Hkv), 256 threads.
+__global__ void __launch_bounds__(256) pair_queries_kernel(const PairArgs a) {
+  __shared__ uint16_t t_lds[kD][kD];  // T~inv[r][j] of this KV head (bf16 bits)
+  __shared__ float q_lds[kPairVecs][kD];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const int64_t v0 = (int64_t)blockIdx.x * kPairVecs;
+  const int64_t nv = a.n_tokens * a.G;
+  const uint16_t* T = (const uint16_t*)a.Tinv;
+  for (int i = tid; i < kD * kD; i += 256) {
+    const int r = i >> 7, c = i & 127;
+    t_lds[r][c] = T[swz_index(h, r, c)];
+  }
+  for (int i = tid; i < kPairVecs * kD; i += 256) {
+    const int vi = i >> 7, c = i & 127;
+    const int64_t v = v0 + vi;
+    float x = 0.0f;
+    if (v < nv) {
+      const int64_t n = v / a.G;
+      const int hq = h * a.G + (int)(v - n * a.G);
+      const int64_t e = n * a.stride + (int64_t)hq * kD + c;
+      x = a.f32_in ? ((const float*)a.Q)[e] : bf16lo_to_f32(((const uint16_t*)a.Q)[e]);
+    }
+    q_lds[vi][c] = x;
+  }
+  __syncthreads();
+  const int j = tid & 127;
+  for (int vi = tid >> 7; vi < kPairVecs; vi += 2) {
+    const int64_t v = v0 + vi;
+    if (v >= nv) break;
+    double acc = 0.0;
+#pragma unroll 8
+    for (int r = 0; r < kD; ++r) acc = __builtin_fma((double)bf16lo_to_f32(t_lds[r][j]), (double)q_lds[vi][r], acc);
+    const int64_t n = v / a.G;
+    const int hq = h * a.G + (int)(v - n * a.G);
+    const uint32_t w = pack_bf16x2((float)acc, 0.0f);
+    a.out[(n * a.n_q_heads + hq) * kD + j] = (uint16_t)w;
+  }
+}
+
+// Channel of element e of the score product's k step s for lane group r: the
+// order in which the code operand below lays out the lane's 32 channels.
+template <int BITS>
+__device__ __forceinline__ int score_channel(int r, int s, int e) {
+  const int u = e >> 1;
+  if constexpr (BITS == 2) {
+    // word s / 2 of the lane's 8 bytes, field 2 (s % 2) + u / 2, bytes 2 (u % 2) + e % 2
+    return 4 * (8 * r + 4 * (s >> 1) + 2 * (u & 1) + (e & 1)) + 2 * (s & 1) + (u >> 1);
+  } else if constexpr (BITS == 4) {
+    // word s of the lane's 16 bytes, nibble u / 2, bytes 2 (u % 2) + e % 2
+    return 32 * r + 8 * s + 2 * (2 * (u & 1) + (e & 1)) + (u >> 1);
+  } else {
+    return 32 * r + 8 * s + e;
+  }
+}
+
+// bf16 words 0x3F00 | (code << SH) (the value 0.5 + code / SB), two per u32:
+// bytes b0, b1 of q (each holding a code in bits SH.. of the byte) under the
+// constant high byte 0x3F.
+__device__ __forceinline__ uint32_t code_pair(uint32_t q, bool hi) {
+  return __builtin_amdgcn_perm(q, 0x3F3F3F3Fu, hi ? 0x00070006u : 0x00050004u);
+}
+
+template <int BITS>
+__device__ __forceinline__ void score_operands(const uint32_t* W, bf16x8* A) {
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t q0 = (W[w] << 5) & 0x60606060u, q1 = (W[w] << 3) & 0x60606060u;
+      const uint32_t q2 = (W[w] << 1) & 0x60606060u, q3 = (W[w] >> 1) & 0x60606060u;
+      const u32x4 a0 = {code_pair(q0, false), code_pair(q0, true), code_pair(q1, false), code_pair(q1, true)};
+      const u32x4 a1 = {code_pair(q2, false), code_pair(q2, true), code_pair(q3, false), code_pair(q3, true)};
+      A[2 * w] = __builtin_bit_cast(bf16x8, a0);
+      A[2 * w + 1] = __builtin_bit_cast(bf16x8, a1);
+    }
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t q0 = (W[s] << 3) & 0x78787878u, q1 = (W[s] >> 1) & 0x78787878u;
+      const u32x4 a = {code_pair(q0, false), code_pair(q0, true), code_pair(q1, false), code_pair(q1, true)};
+      A[s] = __builtin_bit_cast(bf16x8, a);
+    }
+  } else {
+    // 24 bits per k step: bits 24 s .. 24 s + 23 of the lane's 96
+    const uint32_t x[4] = {W[0], __builtin_amdgcn_alignbit(W[1], W[0], 24), __builtin_amdgcn_alignbit(W[2], W[1], 16),
+                           W[2] >> 8};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t c0 = (x[s] >> (6 * t)) & 7u, c1 = (x[s] >> (6 * t + 3)) & 7u;
+        a[t] = 0x3F003F00u | (c0 << 4) | (c1 << 20);
+      }
+      A[s] = __builtin_bit_cast(bf16x8, a);
+    }
+  }
+}
+
+// Value side: lane (token b = lane / 4, column x = lane % 4) of wave w holds
+// channel value_channel(w, x, k) of its token for product k = 0..7, as the
+// fp32 value code * value_scale(x).
+template <int BITS>
+__device__ __forceinline__ int value_channel(int w, int x, int k) {
+  if constexpr (BITS == 4) return 32 * w + 16 * (x >> 1) + 8 * (k >> 2) + 2 * (k & 3) + (x & 1);
+  return 32 * w + 4 * k + x;
+}
+template <int BITS>
+__device__ __forceinline__ float value_scale(int x) {
+  if constexpr (BITS == 2) return (float)(1 << (2 * x));
+  if constexpr (BITS == 4) return (x & 1) ? 16.0f : 1.0f;
+  return 1.0f;
+}
+template <int BITS>
+__device__ __forceinline__ int value_byte_offset(int w, int x) {
+  if constexpr (BITS == 2) return 8 * w;
+  if constexpr (BITS == 4) return 16 * w + 8 * (x >> 1);
+  return 12 * w;
+}
+__device__ __forceinline__ float byte_f32(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xFFu); }
+
+template <int BITS>
+__device__ __forceinline__ void value_operands(const uint32_t* U, int x, float* B) {
+  if constexpr (BITS == 2 || BITS == 4) {
+    const uint32_t mask = BITS == 2 ? (0x03030303u << (2 * x)) : (0x0F0F0F0Fu << (4 * (x & 1)));
+    const uint32_t m0 = U[0] & mask, m1 = U[1] & mask;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      B[k] = byte_f32(m0, k);
+      B[4 + k] = byte_f32(m1, k);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = 12 * k + 3 * x;  // bit of the code in the lane's 96
+      const int wi = p >> 5;
+      const uint32_t lo = wi == 0 ? U[0] : (wi == 1 ? U[1] : U[2]);
+      const uint32_t hi = wi == 0 ? U[1] : (wi == 1 ? U[2] : 0u);
+      B[k] = (float)(__builtin_amdgcn_alignbit(hi, lo, p & 31) & 7u);
+    }
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* W) {
+  if constexpr (NW == 2) {
+    const uint2 v = *(const uint2*)p;
+    W[0] = v.x; W[1] = v.y;
+  } else if constexpr (NW == 4) {
+    const uint4 v = *(const uint4*)p;
+    W[0] = v.x; W[1] = v.y; W[2] = v.z; W[3] = v.w;
+  } else {
+    const uint32_t* q = (const uint32_t*)p;
+    W[0] = q[0]; W[1] = q[1]; W[2] = q[2];
+  }
+}
+
+__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
+
+// grid 8 n_splits8 Hkv B (see the block map below), 256 threads.  A block takes up to kChunk tokens of
+// one sequence and KV head, in rounds of kSub tokens, with the running max,
+// sums and value accumulators rescaled from round to round (online softmax).
+template <int BITS, int QS>
+__global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const AttnArgs a) {
+  constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
+  constexpr int REC = 16 * BITS;
+  constexpr int SNW = BITS;    // words of key codes per lane (32 channels)
+  constexpr int VNW = BITS == 3 ? 3 : 2;  // words of value codes per lane
+  constexpr float SB = BITS == 2 ? 8.0f : (BITS == 3 ? 16.0f : 32.0f);
+  constexpr float M = (float)((1 << BITS) - 1) * 0.5f;
+  constexpr int SROW = kSub + 16;  // s_lds row (padded against bank conflicts)
+  constexpr float NINF = -__builtin_inff();
+  constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass
+  constexpr bool TWO = BITS == 2;         // score tiles two at a time
+
+  __shared__ __align__(16) uint8_t kc_lds[kSub * REC];  // the round's key records
+  __shared__ __align__(16) uint8_t vc_lds[kSub * REC];  // ... and value records
+  __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p * step_v
+  __shared__ __align__(16) float dk_lds[kSub];          // key step; < 0: token absent
+  __shared__ float dv_lds[kSub];                        // value step
+  __shared__ float q_lds[NQ][kD + 1];
+  __shared__ float k1_lds[NQ];
+  __shared__ float mx_lds[4][NQ];
+  __shared__ float sum_lds[4][NQ][2];
+
+  // Block L runs on XCD L % 8 (blocks are dispatched to the XCDs round-robin).
+  // The split s of sequence b goes to XCD (s + b) % 8, so that each XCD gets
+  // a like share of every sequence's splits, and its KV heads to blocks L
+  // eight apart (one XCD, dispatched one after the other), which then read
+  // the same cache lines (a row holds every KV head's record) through one L2.
+  const int L = blockIdx.x, xcd = L & 7, q = L >> 3;
+  const int h = q % a.n_kv_heads, q2 = q / a.n_kv_heads;
+  const int b = q2 / a.n_splits8, s8 = q2 - b * a.n_splits8;
+  const int split = 8 * s8 + ((xcd - b) & 7);
+  if (split >= a.n_splits) return;
+  const int len = min(max(a.len[b], 0), a.max_len);
+  const int n_lo = split * kChunk;
+  if (n_lo >= len) return;  // uniform over the block
+  const int cnt_all = min(len - n_lo, kChunk);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int G = a.G, Hkv = a.n_kv_heads;
+
+  for (int i = tid; i < NQ * kD; i += 256) {
+    const int g = i >> 7, c = i & 127;
+    q_lds[g][c] = g < G ? bf16lo_to_f32(a.qp[((int64_t)b * a.n_q_heads + h * G + g) * kD + c]) : 0.0f;
+  }
+  __syncthreads();
+  if (tid < 32 * NQ) {
+    // sum_j q'_j (c_j - m) = raw - (SB / 2 + m) sum_j q'_j; the sum in fp64
+    const int g = tid >> 5, part = tid & 31;
+    double sq = ((double)q_lds[g][4 * part] + (double)q_lds[g][4 * part + 1]) +
+                ((double)q_lds[g][4 * part + 2] + (double)q_lds[g][4 * part + 3]);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o, 32);
+    if (part == 0) k1_lds[g] = (float)(sq * (double)(0.5f * SB + M));
+  }
+
+  // score operands of the paired queries: lane (column col, group grp)
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 Bq[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x0 = 0.0f, x1 = 0.0f;
+      if (col < NQ) {
+        x0 = q_lds[col][score_channel<BITS>(grp, s, 2 * t)] * SB;
+        x1 = q_lds[col][score_channel<BITS>(grp, s, 2 * t + 1)] * SB;
+      }
+      v[t] = pack_bf16x2(x0, x1);  // exact: bf16 values times a power of two
+    }
+    Bq[s] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  const int tb = lane >> 2, x = lane & 3;  // value product: token block, column
+  const int voff = value_byte_offset<BITS>(w, x);
+  f32x4 acc[QS][8];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[qs][k] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run[NQ], lsum[NQ], vsum[NQ];  // running max (uniform); this thread's sums
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    m_run[g] = NINF;
+    lsum[g] = 0.0f;
+    vsum[g] = 0.0f;
+  }
+  float k1 = 0.0f;
+
+  for (int base = 0; base < cnt_all; base += kSub) {
+    const int cnt = min(cnt_all - base, kSub);
+    const int64_t r0 = a.row0[b] + n_lo + base;
+    // ---- the round's records to LDS, every load issued before the first is
+    // waited for (a record is CPT 16-byte pieces; rows outside the cache are
+    // read from row 0 and never used: their key step marks them absent)
+    constexpr int CPT = REC / 16;
+    constexpr int NLD = kSub * CPT / 256;  // pieces per thread and cache
+    constexpr int NR = NLD > 4 ? 2 : 1;    // rounds (at most 4 + 4 pieces in registers)
+    constexpr int PR = NLD / NR;
+    if (a.n_rows > 0) {  // uniform; no row exists otherwise
+#pragma unroll
+      for (int rd = 0; rd < NR; ++rd) {
+        u32x4 kr[PR], vr[PR];
+#pragma unroll
+        for (int j = 0; j < PR; ++j) {
+          const int c = tid + 256 * (rd * PR + j), tok = c / CPT, part = c - tok * CPT;
+          if (tok < cnt) {
+            int64_t row = r0 + tok;
+            row = (row >= 0 && row < a.n_rows) ? row : 0;
+            const int64_t off = (row * Hkv + h) * REC + 16 * part;
+            kr[j] = *(const u32x4*)(a.kc + off);
+            vr[j] = *(const u32x4*)(a.vc + off);
+          }
+        }
+        if (rd == 0) {
+          for (int i = tid; i < kSub; i += 256) {
+            float dk = -1.0f, dv = 0.0f;
+            const int64_t row = r0 + i;
+            if (i < cnt && row >= 0 && row < a.n_rows) {
+              dk = f16_bits_to_f32(a.ks[row * Hkv + h]);
+              dv = f16_bits_to_f32(a.vs[row * Hkv + h]);
+            }
+            dk_lds[i] = dk;
+            dv_lds[i] = dv;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < PR; ++j) {
+          const int c = tid + 256 * (rd * PR + j);
+          if (c / CPT < cnt) {
+            *(u32x4*)&kc_lds[16 * c] = kr[j];
+            *(u32x4*)&vc_lds[16 * c] = vr[j];
+          }
+        }
+      }
+    } else {
+      for (int i = tid; i < kSub; i += 256) {
+        dk_lds[i] = -1.0f;
+        dv_lds[i] = 0.0f;
+      }
+    }
+    __syncthreads();
+    if (base == 0) k1 = col < NQ ? k1_lds[col] : 0.0f;
+
+    // ---- scores: wave w takes 16-token tiles w, w + 4, ... (two at a time)
+    float mx = NINF;
+    for (int t0 = w; 16 * t0 < cnt; t0 += TWO ? 8 : 4) {
+      const bool two = TWO && 16 * (t0 + 4) < cnt;  // uniform over the wave
+      uint32_t W[2][SNW];
+      load_words<SNW>(&kc_lds[(16 * t0 + col) * REC + 4 * BITS * grp], W[0]);  // any bytes if absent
+      if (two) load_words<SNW>(&kc_lds[(16 * t0 + 64 + col) * REC + 4 * BITS * grp], W[1]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j == 1 && !two) break;
+        const int t = t0 + 4 * j;
+        bf16x8 A[4];
+        score_operands<BITS>(W[j], A);
+        f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s], Bq[s], sc, 0, 0, 0);
+        // sc[e]: token 16 t + 4 grp + e, query head col
+        const int i0 = 16 * t + 4 * grp;
+        const float4 dk4 = *(const float4*)&dk_lds[i0];
+        const float dkv[4] = {dk4.x, dk4.y, dk4.z, dk4.w};
+        float sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = dkv[e] >= 0.0f ? (sc[e] - k1) * dkv[e] * a.c0 : NINF;
+          mx = __builtin_fmaxf(mx, sv[e]);
+        }
+        if (col < NQ) *(float4*)&s_lds[col][i0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      }
+    }
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lane < NQ) mx_lds[w][lane] = mx;
+    __syncthreads();
+
+    // ---- p = exp2(s - max) and p * step_v (0 past the round's tokens); the
+    // sums and accumulators so far are rescaled to the new max
+    const int n16 = (cnt + 15) & ~15;
+    float alpha[NQ];
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) {
+      const float mr = __builtin_fmaxf(__builtin_fmaxf(mx_lds[0][g], mx_lds[1][g]),
+                                       __builtin_fmaxf(mx_lds[2][g], mx_lds[3][g]));
+      const float mn = __builtin_fmaxf(m_run[g], mr);
+      // nothing seen yet: keep scale 1 and subtract 0 (every p is then 0)
+      alpha[g] = m_run[g] == NINF ? 1.0f : __builtin_amdgcn_exp2f(m_run[g] - mn);
+      const float msub = mn == NINF ? 0.0f : mn;
+      m_run[g] = mn;
+      float ls = 0.0f, vs = 0.0f;
+      for (int n = tid; n < kSub; n += 256) {
+        float pv = 0.0f;
+        if (n < n16) {
+          const float p = __builtin_amdgcn_exp2f(s_lds[g][n] - msub);
+          pv = p * dv_lds[n];
+          ls += p;
+          vs += pv;
+        }
+        s_lds[g][n] = pv;
+      }
+      lsum[g] = lsum[g] * alpha[g] + ls;
+      vsum[g] = vsum[g] * alpha[g] + vs;
+    }
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
+    __syncthreads();
+
+    // ---- values: wave w owns channels 32 w .. 32 w + 31; PU 16-token steps
+    // per pass (the weights past the round's tokens are 0)
+    for (int u = 0; u < n16; u += 16 * PU) {
+      uint32_t U[PU][VNW];
+      float pa[PU][QS];
+#pragma unroll
+      for (int jj = 0; jj < PU; ++jj) {
+        const int i = u + 16 * jj + tb;  // < kSub
+        load_words<VNW>(&vc_lds[i * REC + voff], U[jj]);  // any bytes if absent (its weight is 0)
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) pa[jj][qs] = s_lds[4 * qs + x][i];
+      }
+#pragma unroll
+      for (int jj = 0; jj < PU; ++jj) {
+        float Bv[8];
+        value_operands<BITS>(U[jj], x, Bv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs)
+            acc[qs][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[jj][qs], Bv[k], acc[qs][k], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // before the next round overwrites the LDS
+  }
+
+  // ---- sums over the block; the 16 token blocks of the value product
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    float ls = lsum[g], vs = vsum[g];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      ls = xor_sum(ls, o);
+      vs = xor_sum(vs, o);
+    }
+    if (lane == 0) {
+      sum_lds[w][g][0] = ls;
+      sum_lds[w][g][1] = vs;
+    }
+  }
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = acc[qs][k][e];
+        v = v + dpp_f32<0x124>(v);  // row_ror:4
+        v = v + dpp_f32<0x128>(v);  // row_ror:8
+        v = xor_sum(v, 16);
+        v = xor_sum(v, 32);
+        acc[qs][k][e] = v;
+      }
+  __syncthreads();
+  if (lane < 4) {
+    const float inv = 1.0f / value_scale<BITS>(x);
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int g = 4 * qs + e;
+        if (g < G) {
+          const float vs = (sum_lds[0][g][1] + sum_lds[1][g][1]) + (sum_lds[2][g][1] + sum_lds[3][g][1]);
+          float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + 4;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[value_channel<BITS>(w, x, k)] = acc[qs][k][e] * inv - M * vs;
+        }
+      }
+  }
+  if (w == 0 && lane < G) {
+    const int g = lane;
+    float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats;
+    float m = m_run[0];
+#pragma unroll
+    for (int gg = 1; gg < NQ; ++gg)
+      if (gg == g) m = m_run[gg];
+    o[0] = m;
+    o[1] = (sum_lds[0][g][0] + sum_lds[1][g][0]) + (sum_lds[2][g][0] + sum_lds[3][g][0]);
+  }
+}
+
+// grid (Hq, B), 128 threads: out = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s.
+__global__ void __launch_bounds__(128) combine_kernel(const AttnArgs a) {
+  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int len = min(max(a.len[b], 0), a.max_len);
+  const int ns = (len + kChunk - 1) / kChunk;
+  const float* p = a.part + ((int64_t)b * a.n_q_heads + hq) * a.n_splits * kPartFloats;
+  float m = -__builtin_inff();
+  for (int s = 0; s < ns; ++s) m = __builtin_fmaxf(m, p[s * kPartFloats]);
+  float l = 0.0f, o = 0.0f;
+  if (m != -__builtin_inff()) {
+    for (int s = 0; s < ns; ++s) {
+      const float f = __builtin_amdgcn_exp2f(p[s * kPartFloats] - m);
+      l += f * p[s * kPartFloats + 1];
+      o += f * p[s * kPartFloats + 4 + c];
+    }
+  }
+  a.out[((int64_t)b * a.n_q_heads + hq) * kD + c] = l > 0.0f ? o / l : 0.0f;
+}
+
+template <int BITS>
+hipError_t launch_attention_bits(const AttnArgs& a, int qs, hipStream_t st) {
+  const dim3 grid((unsigned)(8 * (int64_t)a.n_splits8 * a.n_kv_heads * a.n_seqs));
+  return qs == 1 ? launch_kernel(attention_kernel<BITS, 1>, grid, dim3(256), st, a)
+                 : launch_kernel(attention_kernel<BITS, 2>, grid, dim3(256), st, a);
+}
+
+}  // namespace
+
+hipError_t launch_pair_queries(const PairArgs& a, hipStream_t st) {
+  const int64_t nv = a.n_tokens * a.G;
+  const dim3 grid((unsigned)((nv + kPairVecs - 1) / kPairVecs), (unsigned)a.n_kv_heads);
+  return launch_kernel(pair_queries_kernel, grid, dim3(256), st, a);
+}
+
+hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t st) {
+  const int qs = a.G > 4 ? 2 : 1;
+  hipError_t e = hipErrorInvalidValue;
+  if (a.n_splits > 0) {
+    switch (bits) {
+      case 2: e = launch_attention_bits<2>(a, qs, st); break;
+      case 3: e = launch_attention_bits<3>(a, qs, st); break;
+      case 4: e = launch_attention_bits<4>(a, qs, st); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  combine_kernel<<<dim3((unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(128), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+size_t attention_workspace_bytes(int64_t n_seqs, int n_q_heads, int max_len) {
+  const int64_t ns = ((int64_t)max_len + kChunk - 1) / kChunk;
+  return (size_t)(n_seqs * n_q_heads * ns * kPartFloats * 4);
+}
+
+int attention_splits(int max_len) { return (max_len + kChunk - 1) / kChunk; }
+
+}  // namespace wushkv

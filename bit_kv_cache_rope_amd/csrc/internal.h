@@ -97,6 +97,33 @@ struct DequantArgs {
   int blocks_per_group;  // set by the launcher
 };
 
+struct PairArgs {
+  const void* Q;          // [n_tokens][n_q_heads][128] with `stride` elements per token
+  int f32_in;
+  int64_t n_tokens;
+  int64_t stride;
+  int n_q_heads, n_kv_heads, G;
+  const void* Tinv;       // swizzled bf16 of the inverse transform
+  uint16_t* out;          // bf16 [n_tokens][n_q_heads][128]
+};
+
+struct AttnArgs {
+  const uint16_t* qp;     // paired queries, bf16 [n_seqs][n_q_heads][128]
+  const uint8_t* kc;
+  const uint16_t* ks;
+  const uint8_t* vc;
+  const uint16_t* vs;
+  int64_t n_rows;
+  const int64_t* row0;    // first cache row of each sequence
+  const int32_t* len;     // tokens of each sequence
+  int n_seqs, n_q_heads, n_kv_heads, G;
+  int max_len, n_splits;
+  int n_splits8;          // ceil(n_splits / 8)
+  float c0;               // softmax scale * log2(e)
+  float* part;            // workspace: per (sequence, query head, split) max, sum, o[128]
+  float* out;             // fp32 [n_seqs][n_q_heads][128]
+};
+
 int device_cu_count(int device);
 
 // Events that the next hot-path launch on this host thread records at its
@@ -126,6 +153,10 @@ hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_gr
                        hipStream_t stream);
 hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int cus, hipStream_t stream);
+hipError_t launch_pair_queries(const PairArgs& a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t stream);
+size_t attention_workspace_bytes(int64_t n_seqs, int n_q_heads, int max_len);
+int attention_splits(int max_len);
 // Fills r->cs for every position below r->max_pos (exact: the certified
 // double path, double-double where it cannot certify).
 hipError_t launch_build_cs_table(const wushkv_rope* r, hipStream_t stream);

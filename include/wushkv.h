@@ -55,6 +55,7 @@
 #ifndef WUSHKV_H_
 #define WUSHKV_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -164,6 +165,59 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
                                 const wushkv_transform* T_k_inv, void* out,
                                 wushkv_dtype out_dtype, void* stream);
 
+/* Query-side pairing for attention on the transformed-basis key cache: the
+ * keys are cached as y = T_k x, and a query head q that reads them is paired
+ * once as q' = T~inv^T q, so that q'.y^ = q.(T~inv y^), the score against the
+ * read path's keys (ai4snews summary "WUSH-KV cuts 2-bit KV-cache perplexity
+ * ...", method paragraph: the key transform is built with the query heads that
+ * consume the cached keys in view).
+ *   Q: device, bf16 or fp32, [n_tokens][n_q_heads][128] with token_stride
+ *      elements per token (same rules as K); query head hq reads KV head
+ *      hq / (n_q_heads / T_k_inv's head count).
+ *   T_k_inv: transform handle holding T_k^-1 (the read path's), bf16 T~inv.
+ *   q_out: device bf16 [n_tokens][n_q_heads][128], contiguous, caller-owned:
+ *      q'_j = bf16(RN32(sum_r T~inv[r][j] q_r)), the sum exact before the fp32
+ *      rounding (fp64 accumulation of exact products in ascending r).
+ * n_tokens == 0 is a no-op. */
+wushkv_status wushkv_pair_queries(const void* Q, wushkv_dtype q_dtype, int64_t n_tokens, int n_q_heads,
+                                  int64_t token_stride, const wushkv_transform* T_k_inv, void* q_out,
+                                  void* stream);
+
+/* Bytes of workspace wushkv_decode_attention needs for these sizes (host
+ * only).  The workspace holds one partial result per (sequence, query head,
+ * 2048-token split of max_seq_len). */
+wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n_kv_heads, int max_seq_len,
+                                                size_t* bytes);
+
+/* Decode attention of one query token per sequence over symmetric packed key
+ * and value caches, without dequantizing the cache to memory.  Keys are scored
+ * in their transformed basis with the paired query; values are read as stored
+ * (their transform is folded into the weights: ai4snews summary, deployment
+ * paragraph).  For sequence b and query head hq (KV head hq / G, G =
+ * n_q_heads / n_kv_heads, at most 8):
+ *   s_n = scale * q'.y^_n,  o = sum_n exp(s_n - max) v^_n / sum_n exp(s_n - max)
+ * over the cache rows seq_row0[b] + n, n < min(seq_len[b], max_seq_len); rows
+ * outside [0, n_rows) are absent; a sequence with no row present gives 0.
+ *   q_paired: device bf16 [n_seqs][n_q_heads][128] (wushkv_pair_queries).
+ *   k_cache, v_cache: symmetric caches written by wushkv_quantize_keys /
+ *      wushkv_quantize_values with the same bits and n_rows (their slots are
+ *      not used here).
+ *   seq_row0: device int64 [n_seqs]; seq_len: device int32 [n_seqs].
+ *   workspace: device, 16-byte aligned, at least the bytes reported by
+ *      wushkv_decode_attention_workspace; caller-owned scratch that the call
+ *      overwrites (two calls sharing one workspace must be ordered).
+ *   out: device fp32 [n_seqs][n_q_heads][128].
+ * Precision: codes and steps exact; q' bf16; scores accumulated in fp32 on
+ * MFMA; exp2 and the weighted sum of values in fp32 (no bf16 rounding of the
+ * weights).  Affine caches return WUSHKV_ERR_UNSUPPORTED.  n_seqs == 0 is a
+ * no-op. */
+wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_heads,
+                                      const wushkv_packed* k_cache, const wushkv_packed* v_cache,
+                                      int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
+                                      const int64_t* seq_row0, const int32_t* seq_len, int max_seq_len,
+                                      float scale, void* workspace, size_t workspace_bytes, float* out,
+                                      void* stream);
+
 /* Test support: the fp32 transformed keys y = T~ bf16(RoPE(K)) as the key
  * kernel computes them, written to y_out [n_tokens][n_heads][128] (device). */
 wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, int64_t n_tokens,
@@ -176,8 +230,9 @@ wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, i
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
                                         int64_t n, float* cs_out, void* stream);
 
-/* Timing support: the next wushkv_quantize_keys, wushkv_quantize_values or
- * wushkv_dequantize call on this host thread records `start` (a hipEvent_t)
+/* Timing support: the next wushkv_quantize_keys, wushkv_quantize_values,
+ * wushkv_dequantize, wushkv_pair_queries or wushkv_decode_attention call
+ * (its first kernel) on this host thread records `start` (a hipEvent_t)
  * when its kernel starts and `stop` when it ends (hipExtLaunchKernel), so
  * that hipEventElapsedTime(start, stop) is the kernel's own duration without
  * its dispatch latency.  Either may be NULL.  The events must exist (created,

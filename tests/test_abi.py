@@ -109,6 +109,23 @@ def test_validation_without_device(lib):
     assert L.wushkv_dequantize(ctypes.byref(p), 4, 2, 9, ctypes.byref(q), None, vp(16), 1, None) == _lib.ERR_INVALID_ARG
     assert L.wushkv_dequantize(ctypes.byref(p), 4, 2, 2, ctypes.byref(q), None, vp(16), 3, None) == _lib.ERR_INVALID_ARG
     assert L.wushkv_dequantize(ctypes.byref(p), 0, 2, 2, ctypes.byref(q), None, None, 1, None) == _lib.OK
+    # query pairing and decode attention
+    assert L.wushkv_pair_queries(vp(16), 1, 4, 8, 1024, None, vp(16), None) == _lib.ERR_INVALID_ARG
+    assert L.wushkv_pair_queries(vp(16), 1, 4, 8, 1000, None, vp(16), None) == _lib.ERR_INVALID_ARG
+    nb = ctypes.c_size_t()
+    assert L.wushkv_decode_attention_workspace(64, 32, 8, 32768, ctypes.byref(nb)) == _lib.OK
+    assert nb.value == 64 * 32 * 16 * 132 * 4
+    assert L.wushkv_decode_attention_workspace(2, 12, 8, 100, ctypes.byref(nb)) == _lib.ERR_INVALID_ARG
+    assert L.wushkv_decode_attention_workspace(2, 72, 8, 100, ctypes.byref(nb)) == _lib.ERR_UNSUPPORTED
+    att = lambda n, bits=2, qq=q, kc=p, ws=1 << 20, sc=0.1: L.wushkv_decode_attention(
+        vp(16), n, 32, ctypes.byref(kc), ctypes.byref(p), 8, bits, ctypes.byref(qq), vp(16), vp(16), 4096,
+        ctypes.c_float(sc), vp(16), ws, vp(16), None)
+    assert att(2, bits=5) == _lib.ERR_INVALID_ARG
+    assert att(2, qq=_q(kind=1, group=32)) == _lib.ERR_UNSUPPORTED
+    assert att(2, kc=_packed(rows=3)) == _lib.ERR_INVALID_ARG
+    assert att(2, ws=100) == _lib.ERR_INVALID_ARG
+    assert att(2, sc=float("inf")) == _lib.ERR_INVALID_ARG
+    assert att(0) == _lib.OK
     # handles
     h = vp()
     assert L.wushkv_rope_create(ctypes.c_float(1e6), 0, ctypes.byref(h)) == _lib.ERR_INVALID_ARG
