@@ -219,13 +219,23 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   constexpr float M = (float)((1 << BITS) - 1) * 0.5f;
   constexpr int SROW = kSub + 16;  // s_lds row (padded against bank conflicts)
   constexpr float NINF = -__builtin_inff();
-  constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass
+  constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass (4x4x1 product)
   constexpr bool TWO = BITS == 2;         // score tiles two at a time
+  // 2 and 4 bits: the value product runs on bf16 16x16x32 MFMA with the value
+  // records stored transposed (word w of token n at vt[w][n]) and the weights
+  // split into three bf16 parts (columns g + 4 part); 3 bits: fp32 4x4x1 MFMA.
+  constexpr bool VT = BITS != 3;
+  constexpr int NWV = REC / 4;            // words per record
+  constexpr int VROW = kSub + 4;          // vt row (u32)
+  constexpr int PROW = kSub + 8;          // weight row (bf16), 16-byte pieces spread over the banks
+  constexpr int KBYTES = kSub * REC > QS * 16 * PROW * 2 ? kSub * REC : QS * 16 * PROW * 2;
 
-  __shared__ __align__(16) uint8_t kc_lds[kSub * REC];  // the round's key records
-  __shared__ __align__(16) uint8_t vc_lds[kSub * REC];  // ... and value records
+  // the round's key records; after the scores, the bf16 weights [QS][16][PROW]
+  __shared__ __align__(16) uint8_t kc_lds[KBYTES];
+  __shared__ __align__(16) uint8_t vc_lds[VT ? NWV * VROW * 4 : kSub * REC];  // value records
   __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p * step_v
-  __shared__ __align__(16) float dk_lds[kSub];          // key step; < 0: token absent
+  __shared__ __align__(16) float dk_lds[kSub];          // key step * scale * log2(e); 0: token absent
+  __shared__ __align__(16) float off_lds[kSub];         // 0, or -inf for an absent token
   __shared__ float dv_lds[kSub];                        // value step
   __shared__ float q_lds[NQ][kD + 1];
   __shared__ float k1_lds[NQ];
@@ -282,13 +292,30 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     Bq[s] = __builtin_bit_cast(bf16x8, v);
   }
 
-  const int tb = lane >> 2, x = lane & 3;  // value product: token block, column
+  const int tb = lane >> 2, x = lane & 3;  // 4x4x1 value product: token block, column
   const int voff = value_byte_offset<BITS>(w, x);
-  f32x4 acc[QS][8];
+  // 4x4x1: acc[qs][k]; 16x16x32: acc[qs][mt] (mt = 16-channel tile) in acc[qs][0..1]
+  constexpr int NACC = VT ? 2 : 8;
+  f32x4 acc[QS][NACC];
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[qs][k] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < NACC; ++k) acc[qs][k] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  // 16x16x32 value product: lane (row vr_ch = 16 mt + lane % 16 of the wave's
+  // 32 channels, k group grp = 8 tokens); the code's word, byte and bit
+  const int vch = 32 * w + (lane & 15);  // + 16 mt
+  int vword[2], vrot[2];
+  uint32_t vsel[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int j = vch + 16 * mt;
+    const int bit = BITS * j;                   // in the record's bit stream
+    vword[mt] = bit >> 5;
+    const int byte = (bit & 31) >> 3, inb = bit & 7;
+    vsel[mt] = (uint32_t)byte | 0x0C00u | ((uint32_t)(4 + byte) << 16) | 0x0C000000u;
+    // rotate the code from bit inb of each half's low byte to bit SH (5: 2 bits, 3: 4 bits)
+    vrot[mt] = (inb - (BITS == 2 ? 5 : 3)) & 31;
+  }
   float m_run[NQ], lsum[NQ], vsum[NQ];  // running max (uniform); this thread's sums
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
@@ -325,13 +352,15 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         }
         if (rd == 0) {
           for (int i = tid; i < kSub; i += 256) {
-            float dk = -1.0f, dv = 0.0f;
+            float dk = 0.0f, off = NINF, dv = 0.0f;
             const int64_t row = r0 + i;
             if (i < cnt && row >= 0 && row < a.n_rows) {
-              dk = f16_bits_to_f32(a.ks[row * Hkv + h]);
+              dk = f16_bits_to_f32(a.ks[row * Hkv + h]) * a.c0;
+              off = 0.0f;
               dv = f16_bits_to_f32(a.vs[row * Hkv + h]);
             }
             dk_lds[i] = dk;
+            off_lds[i] = off;
             dv_lds[i] = dv;
           }
         }
@@ -340,13 +369,21 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           const int c = tid + 256 * (rd * PR + j);
           if (c / CPT < cnt) {
             *(u32x4*)&kc_lds[16 * c] = kr[j];
-            *(u32x4*)&vc_lds[16 * c] = vr[j];
+            if constexpr (VT) {
+              const int tok = c / CPT, part = c - tok * CPT;
+              uint32_t* vt = (uint32_t*)vc_lds;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = vr[j][e];
+            } else {
+              *(u32x4*)&vc_lds[16 * c] = vr[j];
+            }
           }
         }
       }
     } else {
       for (int i = tid; i < kSub; i += 256) {
-        dk_lds[i] = -1.0f;
+        dk_lds[i] = 0.0f;
+        off_lds[i] = NINF;
         dv_lds[i] = 0.0f;
       }
     }
@@ -372,11 +409,13 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         // sc[e]: token 16 t + 4 grp + e, query head col
         const int i0 = 16 * t + 4 * grp;
         const float4 dk4 = *(const float4*)&dk_lds[i0];
-        const float dkv[4] = {dk4.x, dk4.y, dk4.z, dk4.w};
+        const float4 of4 = *(const float4*)&off_lds[i0];
+        const float dkv[4] = {dk4.x, dk4.y, dk4.z, dk4.w}, ofv[4] = {of4.x, of4.y, of4.z, of4.w};
         float sv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sv[e] = dkv[e] >= 0.0f ? (sc[e] - k1) * dkv[e] * a.c0 : NINF;
+          // (raw - k1) * step * scale * log2(e); -inf for an absent token
+          sv[e] = __builtin_fmaf(sc[e] - k1, dkv[e], ofv[e]);
           mx = __builtin_fmaxf(mx, sv[e]);
         }
         if (col < NQ) *(float4*)&s_lds[col][i0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
@@ -409,21 +448,78 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           ls += p;
           vs += pv;
         }
-        s_lds[g][n] = pv;
+        if constexpr (VT) {
+          // pv = hi + mid + lo in bf16 (exact up to the last part's rounding)
+          uint16_t* pt = (uint16_t*)kc_lds + (g >> 2) * 16 * PROW + (g & 3) * PROW + n;
+          const uint32_t hb = pack_bf16x2(pv, 0.0f) & 0xFFFFu;
+          const float r1 = pv - bf16lo_to_f32(hb);
+          const uint32_t mb = pack_bf16x2(r1, 0.0f) & 0xFFFFu;
+          const float r2 = r1 - bf16lo_to_f32(mb);
+          pt[0] = (uint16_t)hb;
+          pt[4 * PROW] = (uint16_t)mb;
+          pt[8 * PROW] = (uint16_t)(pack_bf16x2(r2, 0.0f) & 0xFFFFu);
+        } else {
+          s_lds[g][n] = pv;
+        }
       }
       lsum[g] = lsum[g] * alpha[g] + ls;
       vsum[g] = vsum[g] * alpha[g] + vs;
     }
+    if constexpr (VT) {
+      // weight columns 12..15 carry nothing (they overlay last round's key records)
+      for (int i = tid; i < QS * 4 * PROW / 8; i += 256) {
+        const int qs = i / (4 * PROW / 8), r = i - qs * (4 * PROW / 8);
+        *(u32x4*)((uint16_t*)kc_lds + qs * 16 * PROW + 12 * PROW + 8 * r) = (u32x4){0u, 0u, 0u, 0u};
+      }
+      // column col = g + 4 part of the weights: query 4 qs + col % 4
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
+      for (int qs = 0; qs < QS; ++qs) {
+        const int cg = col & 3;
+        const float al = cg == 0 ? alpha[4 * qs] : (cg == 1 ? alpha[4 * qs + 1] : (cg == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < NACC; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
+          for (int e = 0; e < 4; ++e) acc[qs][k][e] *= al;
+      }
+    } else {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+        for (int k = 0; k < NACC; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
+    }
     __syncthreads();
 
-    // ---- values: wave w owns channels 32 w .. 32 w + 31; PU 16-token steps
-    // per pass (the weights past the round's tokens are 0)
+    // ---- values: wave w owns channels 32 w .. 32 w + 31 (the weights past
+    // the round's tokens are 0)
+    if constexpr (VT) {
+      const uint32_t* vt = (const uint32_t*)vc_lds;
+      const uint16_t* pt = (const uint16_t*)kc_lds;
+      constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : 0x00780078u;
+      for (int n0 = 0; n0 < n16; n0 += 32) {
+        const int nk = n0 + 8 * grp;  // this lane's 8 tokens
+        bf16x8 P[QS];
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) P[qs] = *(const bf16x8*)(pt + qs * 16 * PROW + col * PROW + nk);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const u32x4 wa = *(const u32x4*)(vt + vword[mt] * VROW + nk);
+          const u32x4 wb = *(const u32x4*)(vt + vword[mt] * VROW + nk + 4);
+          const uint32_t wv[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+          u32x4 av;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t pr = __builtin_amdgcn_perm(wv[2 * t + 1], wv[2 * t], vsel[mt]);
+            av[t] = (__builtin_amdgcn_alignbit(pr, pr, vrot[mt]) & VMASK) | 0x3F003F00u;
+          }
+          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs)
+            acc[qs][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P[qs], acc[qs][mt], 0, 0, 0);
+        }
+      }
+    } else
     for (int u = 0; u < n16; u += 16 * PU) {
       uint32_t U[PU][VNW];
       float pa[PU][QS];
@@ -439,7 +535,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         float Bv[8];
         value_operands<BITS>(U[jj], x, Bv);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < NACC; ++k)
 #pragma unroll
           for (int qs = 0; qs < QS; ++qs)
             acc[qs][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[jj][qs], Bv[k], acc[qs][k], 0, 0, 0);
@@ -465,18 +561,39 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < NACC; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // 16x16x32: the three weight parts (columns c, c + 4, c + 8; c + 12 is 0);
+        // 4x4x1: the 16 token blocks (lanes x, x + 4, ..., x + 60)
         float v = acc[qs][k][e];
         v = v + dpp_f32<0x124>(v);  // row_ror:4
         v = v + dpp_f32<0x128>(v);  // row_ror:8
-        v = xor_sum(v, 16);
-        v = xor_sum(v, 32);
+        if constexpr (!VT) {
+          v = xor_sum(v, 16);
+          v = xor_sum(v, 32);
+        }
         acc[qs][k][e] = v;
       }
   __syncthreads();
-  if (lane < 4) {
+  if constexpr (VT) {
+    if (col < 4) {
+      // lane (column col, group grp): channels 32 w + 16 mt + 4 grp + e
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        const int g = 4 * qs + col;
+        if (g < G) {
+          const float vs = (sum_lds[0][g][1] + sum_lds[1][g][1]) + (sum_lds[2][g][1] + sum_lds[3][g][1]);
+          const float cst = (0.5f * SB + M) * vs;
+          float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + 4;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[32 * w + 16 * mt + 4 * grp + e] = SB * acc[qs][mt][e] - cst;
+        }
+      }
+    }
+  } else if (lane < 4) {
     const float inv = 1.0f / value_scale<BITS>(x);
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs)
@@ -487,7 +604,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           const float vs = (sum_lds[0][g][1] + sum_lds[1][g][1]) + (sum_lds[2][g][1] + sum_lds[3][g][1]);
           float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + 4;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) o[value_channel<BITS>(w, x, k)] = acc[qs][k][e] * inv - M * vs;
+          for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = acc[qs][k][e] * inv - M * vs;
         }
       }
   }
