@@ -325,16 +325,81 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   }
   float k1 = 0.0f;
 
+  // ---- records of a round: CPT 16-byte pieces per record; rows outside the
+  // cache are read from row 0 and never used (their key step marks them absent)
+  constexpr int CPT = REC / 16;
+  constexpr int NLD = kSub * CPT / 256;  // pieces per thread and cache
+  constexpr int NR = NLD > 4 ? 2 : 1;    // load rounds (at most 4 + 4 pieces in registers)
+  constexpr int PR = NLD / NR;
+  // one load round: the next round's records and steps are loaded into
+  // registers while this round is worked on, and go to LDS at its end
+  constexpr bool PF = NR == 1;
+  static_assert(!PF || VT, "the prefetch path writes the transposed value layout");
+  u32x4 pk[PR], pv[PR];
+  uint32_t pks[kSub / 256], pvs[kSub / 256];
+  auto prefetch = [&](int base) __attribute__((always_inline)) {
+    const int cnt = min(cnt_all - base, kSub);
+    if (a.n_rows <= 0 || cnt <= 0) return;  // uniform
+    const int64_t r0 = a.row0[b] + n_lo + base;
+#pragma unroll
+    for (int j = 0; j < PR; ++j) {
+      const int c = tid + 256 * j, tok = c / CPT, part = c - tok * CPT;
+      if (tok < cnt) {
+        int64_t row = r0 + tok;
+        row = (row >= 0 && row < a.n_rows) ? row : 0;
+        const int64_t off = (row * Hkv + h) * REC + 16 * part;
+        pk[j] = *(const u32x4*)(a.kc + off);
+        pv[j] = *(const u32x4*)(a.vc + off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSub / 256; ++j) {
+      const int i = tid + 256 * j;
+      if (i < cnt) {
+        int64_t row = r0 + i;
+        row = (row >= 0 && row < a.n_rows) ? row : 0;
+        pks[j] = a.ks[row * Hkv + h];
+        pvs[j] = a.vs[row * Hkv + h];
+      }
+    }
+  };
+  if constexpr (PF) prefetch(0);
+
   for (int base = 0; base < cnt_all; base += kSub) {
     const int cnt = min(cnt_all - base, kSub);
     const int64_t r0 = a.row0[b] + n_lo + base;
-    // ---- the round's records to LDS, every load issued before the first is
-    // waited for (a record is CPT 16-byte pieces; rows outside the cache are
-    // read from row 0 and never used: their key step marks them absent)
-    constexpr int CPT = REC / 16;
-    constexpr int NLD = kSub * CPT / 256;  // pieces per thread and cache
-    constexpr int NR = NLD > 4 ? 2 : 1;    // rounds (at most 4 + 4 pieces in registers)
-    constexpr int PR = NLD / NR;
+    if constexpr (PF) {
+      if (a.n_rows > 0) {
+#pragma unroll
+        for (int j = 0; j < PR; ++j) {
+          const int c = tid + 256 * j;
+          if (c / CPT < cnt) {
+            *(u32x4*)&kc_lds[16 * c] = pk[j];
+            const int tok = c / CPT, part = c - tok * CPT;
+            uint32_t* vt = (uint32_t*)vc_lds;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = pv[j][e];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kSub / 256; ++j) {
+          const int i = tid + 256 * j;
+          const int64_t row = r0 + i;
+          const bool ok = i < cnt && row >= 0 && row < a.n_rows;
+          dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
+          off_lds[i] = ok ? 0.0f : NINF;
+          dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
+        }
+      } else {
+        for (int i = tid; i < kSub; i += 256) {
+          dk_lds[i] = 0.0f;
+          off_lds[i] = NINF;
+          dv_lds[i] = 0.0f;
+        }
+      }
+      __syncthreads();
+      prefetch(base + kSub);
+    } else {
     if (a.n_rows > 0) {  // uniform; no row exists otherwise
 #pragma unroll
       for (int rd = 0; rd < NR; ++rd) {
@@ -388,6 +453,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       }
     }
     __syncthreads();
+    }
     if (base == 0) k1 = col < NQ ? k1_lds[col] : 0.0f;
 
     // ---- scores: wave w takes 16-token tiles w, w + 4, ... (two at a time)
