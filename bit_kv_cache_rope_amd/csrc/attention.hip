@@ -38,27 +38,24 @@ namespace {
 constexpr int kChunk = 2048;     // tokens per split (one block)
 constexpr int kSub = 512;        // tokens staged in LDS per round
 constexpr int kPartFloats = 132;  // per (sequence, query head, split): max, sum, 2 pad, o[128]
-constexpr int kPairVecs = 16;     // query vectors per pairing block
+constexpr int kPairVecs = 4;      // query vectors per pairing block
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int64_t swz_index(int h, int r, int c) {
-  // transform handle order: chunk (h, r / 32, c / 16), lane r % 32 + 32 ((c % 16) / 8), element c % 8
-  return ((((int64_t)h * 4 + (r >> 5)) * 8 + (c >> 4)) * 64 + (r & 31) + 32 * ((c & 15) >> 3)) * 8 + (c & 7);
-}
-
 // grid (ceil(N G / kPairVecs), Hkv), 256 threads.
 __global__ void __launch_bounds__(256) pair_queries_kernel(const PairArgs a) {
-  __shared__ uint16_t t_lds[kD][kD];  // T~inv[r][j] of this KV head (bf16 bits)
+  __shared__ __align__(16) uint16_t t_lds[kD][kD];  // T~inv[r][j] of this KV head (bf16 bits)
   __shared__ float q_lds[kPairVecs][kD];
   const int h = blockIdx.y, tid = threadIdx.x;
   const int64_t v0 = (int64_t)blockIdx.x * kPairVecs;
   const int64_t nv = a.n_tokens * a.G;
-  const uint16_t* T = (const uint16_t*)a.Tinv;
-  for (int i = tid; i < kD * kD; i += 256) {
-    const int r = i >> 7, c = i & 127;
-    t_lds[r][c] = T[swz_index(h, r, c)];
+  // the handle's 16-byte chunks, read in order: chunk (mt, s, l) holds
+  // T~inv[32 mt + l % 32][16 s + 8 (l / 32) .. + 7]
+  const u32x4* T = (const u32x4*)a.Tinv + (int64_t)h * (kD * kD / 8);
+  for (int k = tid; k < kD * kD / 8; k += 256) {
+    const int l = k & 63, s = (k >> 6) & 7, mt = k >> 9;
+    *(u32x4*)&t_lds[32 * mt + (l & 31)][16 * s + 8 * (l >> 5)] = T[k];
   }
   for (int i = tid; i < kPairVecs * kD; i += 256) {
     const int vi = i >> 7, c = i & 127;

@@ -82,6 +82,13 @@ def run_values(env, V, bits, q, slots=None, rows=None):
     return out
 
 
+def dev_packed(env, h):
+    """A GPU cache holding the records of an oracle result (codes, scales, zeros)."""
+    torch, bk = env["torch"], env["bk"]
+    f16 = lambda a: None if a is None else to_dev(env, np.ascontiguousarray(a, np.uint16)).view(torch.float16)
+    return bk.PackedCache(to_dev(env, np.ascontiguousarray(h["codes"])), f16(h["scales"]), f16(h["zeros"]))
+
+
 def packed_host(p):
     return dict(codes=p.codes.cpu().numpy(), scales=host_u16(p.scales),
                 zeros=None if p.zeros is None else host_u16(p.zeros))
@@ -401,13 +408,22 @@ def test_full_size_sampled(env, name, layer, kind, bits):
     account_keys(env, K[idx], pos[idx], T, bits, q, f"full {name} keys", g=gk)
     rv = o.quantize_values(V[idx], bits, oracle_q(env, q))
     assert_same_packed(gv, rv, f"full {name} values")
-    # read path over the whole cache, checked on the sample
+    # read path over the whole cache, checked on the sample: the sampled rows
+    # first take the oracle's own records, so that the read path's input there
+    # comes from the oracle
+    rk = o.quantize_keys(K[idx], pos[idx], T, w.theta, bits, oracle_q(env, q))
+    for pc, r in ((pk, rk), (pv, rv)):
+        hc = dev_packed(env, r)
+        pc.codes[it] = hc.codes
+        pc.scales[it] = hc.scales
+        if pc.zeros is not None:
+            pc.zeros[it] = hc.zeros
     outv = bk.wushkv_dequantize(pv, N, H, bits, q, out_dtype=torch.float32)[it].cpu().numpy()
-    refv = o.dequantize(gv["codes"], gv["scales"], gv["zeros"], len(idx), H, bits, oracle_q(env, q))
+    refv = o.dequantize(rv["codes"], rv["scales"], rv["zeros"], len(idx), H, bits, oracle_q(env, q))
     assert np.array_equal(outv.view(np.uint32), refv.view(np.uint32))
     outk = bk.wushkv_dequantize(pk, N, H, bits, q, T_k_inv=bk.Transform(Ti),
                                 out_dtype=torch.float32)[it].cpu().numpy()
-    refk = o.dequantize(gk["codes"], gk["scales"], gk["zeros"], len(idx), H, bits, oracle_q(env, q), Tinv=Ti)
+    refk = o.dequantize(rk["codes"], rk["scales"], rk["zeros"], len(idx), H, bits, oracle_q(env, q), Tinv=Ti)
     err = np.abs(outk - refk).max(axis=2)
     assert np.all(err <= TRANSFORM_TOL * np.abs(refk).max(axis=2))
 
@@ -591,8 +607,8 @@ def test_dequant_plain_bit_exact(env, kind, bits):
     V = s.kv(w, 0, "V", 0, n)
     q = _bkq(env, kind)
     say(f"dequant plain {kind} {bits}")
-    p = run_values(env, V, bits, q)
-    h = packed_host(p)
+    h = o.quantize_values(V, bits, oracle_q(env, q))
+    p = dev_packed(env, h)
     ref = o.dequantize(h["codes"], h["scales"], h["zeros"], n, V.shape[1], bits, oracle_q(env, q))
     out32 = bk.wushkv_dequantize(p, n, V.shape[1], bits, q, out_dtype=torch.float32).cpu().numpy()
     assert np.array_equal(out32.view(np.uint32), ref.view(np.uint32))
@@ -610,8 +626,8 @@ def test_dequant_inverse_transform(env, kind, bits):
     T, Ti = s.transform(w, 0)
     q = _bkq(env, kind)
     say(f"dequant through T^-1 {kind} {bits}")
-    p = run_keys(env, K, pos, T, bits, q)
-    h = packed_host(p)
+    h = o.quantize_keys(K, pos, T, w.theta, bits, oracle_q(env, q))
+    p = dev_packed(env, h)
     ref = o.dequantize(h["codes"], h["scales"], h["zeros"], n, K.shape[1], bits, oracle_q(env, q), Tinv=Ti)
     g = bk.wushkv_dequantize(p, n, K.shape[1], bits, q, T_k_inv=bk.Transform(Ti), out_dtype=torch.float32)
     g = g.cpu().numpy()
@@ -637,8 +653,8 @@ def test_dequant_through_slots_with_missing_rows(env, kind, bits):
     H = V.shape[1]
     q = _bkq(env, kind)
     say(f"dequant through slots {kind} {bits}")
-    p = run_values(env, V, bits, q)
-    h = packed_host(p)
+    h = o.quantize_values(V, bits, oracle_q(env, q))
+    p = dev_packed(env, h)
     rng = np.random.default_rng(5)
     slots = rng.integers(0, rows, n).astype(np.int64)
     slots[rng.choice(n, 40, replace=False)] = -1
