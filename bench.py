@@ -273,6 +273,48 @@ def main() -> int:
     torch.cuda.synchronize()
     dec_k_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
     dec_v_us = float(np.mean([e[2].elapsed_time(e[3]) for e in dev_ev])) * 1e3
+    # 36 layers' decode K and V calls (one token per sequence) captured in one HIP graph and
+    # replayed: one launch per decode step for all layers (same inputs and caches for every
+    # layer here; each layer's kernels do the same work).  All on one stream (keys and values
+    # forked onto two streams and joined per layer inside the graph ran 423 against 319 us).
+    gst = torch.cuda.Stream()
+    gk = bk.prepare_quantize_keys(dK, dpos, rope, dtk, bits, q, dkc, stream=gst)
+    gv = bk.prepare_quantize_values(dV, bits, q, dvc, stream=gst)
+    gk()
+    gv()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gst):
+        for _ in range(36):
+            gk()
+            gv()
+    for _ in range(20):
+        graph.replay()
+    torch.cuda.synchronize()
+    n_rep = 100
+    t0 = time.perf_counter()
+    for _ in range(n_rep):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_step_us = (time.perf_counter() - t0) / n_rep * 1e6
+    # 16-token chunks: 64 sequences append 16 consecutive positions each (1024 tokens per layer call)
+    cbase = np.minimum(synth.positions(wd), 32768 - 16)
+    cpos = torch.from_numpy((cbase[:, None] + np.arange(16)).reshape(-1).astype(np.int32)).to(dev)
+    cslots = torch.from_numpy((np.arange(dn)[:, None] * 32768 + cbase[:, None] + np.arange(16)).reshape(-1)).to(dev)
+    cK = dev_bf16(synth.kv(wd, 0, "K", 0, 16 * dn))
+    cV = dev_bf16(synth.kv(wd, 0, "V", 0, 16 * dn))
+    ck = bk.prepare_quantize_keys(cK, cpos, rope, dtk, bits, q, dkc.with_slots(cslots), stream=stream)
+    cv = bk.prepare_quantize_values(cV, bits, q, dvc.with_slots(cslots), stream=vstream)
+    for _ in range(200):
+        ck()
+        cv()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_dec):
+        ck()
+        cv()
+    torch.cuda.synchronize()
+    chunk_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
 
     # ---- decode attention over the packed caches (64 sequences of the decode workload's lengths,
     # 32 query heads over 8 KV heads), reported alongside: the caches hold random codes and steps
@@ -356,6 +398,10 @@ def main() -> int:
             "tokens_per_layer": dn, "cache_rows": drows, "layer_us": round(dec_layer_us, 2),
             "keys_kernel_us": round(dec_k_us, 2), "values_kernel_us": round(dec_v_us, 2),
             "note": "one layer's K and V calls back to back, keys and values on two streams",
+            "graph_36_layers_us": round(graph_step_us, 2),
+            "graph_note": "36 layers' K and V calls in one HIP graph on one stream, replayed back to back",
+            "chunk16_tokens_per_layer": 16 * dn, "chunk16_layer_us": round(chunk_layer_us, 2),
+            "chunk16_tokens_per_s": round(16 * dn / (chunk_layer_us * 1e-6), 1),
         },
         "decode_attention": {
             "sequences": dn, "q_heads": att_q, "kv_heads": H, "bits": bits,

@@ -500,6 +500,83 @@ def test_decode_append_slots(env):
         assert int(pk.codes.count_nonzero()) <= 64 * 8 * 32
 
 
+def test_chunked_append_16_tokens(env):
+    """Appends of 16 consecutive tokens per sequence (64 sequences at the
+    decode workload's positions, clipped so that the chunk stays in its
+    sequence's 32768 rows), keys and values into 64 x 32768-row caches through
+    slots; the rows written are compared with the oracle's records."""
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["decode_append"]
+    B, C, rows = 64, 16, 64 * 32768
+    base = np.minimum(s.positions(w), 32768 - C)
+    pos = (base[:, None] + np.arange(C)).reshape(-1).astype(np.int32)
+    slots = (np.arange(B)[:, None] * 32768 + base[:, None] + np.arange(C)).reshape(-1).astype(np.int64)
+    N = B * C
+    q = bk.sym(2.0)
+    for layer in (0, 35):
+        say(f"chunked append layer {layer}")
+        K = s.kv(w, layer, "K", 0, N)
+        V = s.kv(w, layer, "V", 0, N)
+        T, _ = s.transform(w, layer)
+        pk = run_keys(env, K, pos, T, 2, q, slots=slots, rows=rows)
+        pv = run_values(env, V, 2, q, slots=slots, rows=rows)
+        sl = torch.from_numpy(slots).cuda()
+        rv = o.quantize_values(V, 2, o.sym())
+        assert_same_packed(packed_host(bk.PackedCache(pv.codes[sl], pv.scales[sl])), rv, "chunked values")
+        account_keys(env, K, pos, T, 2, q, "chunked keys",
+                     g=packed_host(bk.PackedCache(pk.codes[sl], pk.scales[sl])))
+        assert int(pv.codes.count_nonzero()) <= N * 8 * 32
+
+
+def test_decode_layers_in_a_graph(env):
+    """Three layers' decode K and V calls captured once in a HIP graph
+    (torch.cuda.CUDAGraph on a created stream) and replayed three times, with
+    eager work and synchronizations between the replays: every replay writes
+    exactly what the same calls write eagerly."""
+    s, bk, torch = env["synth"], env["bk"], env["torch"]
+    w = s.WORKLOADS["decode_append"]
+    rows = 64 * 32768
+    slots = torch.from_numpy(s.slots(w)).cuda()
+    pos = torch.from_numpy(s.positions(w)).cuda()
+    q = bk.sym(2.0)
+    rope = bk.Rope(w.theta, 1 << 15)
+    layers = []
+    for layer in range(3):
+        T, _ = s.transform(w, layer)
+        layers.append(dict(K=to_dev(env, s.kv(w, layer, "K")), V=to_dev(env, s.kv(w, layer, "V")),
+                           tk=bk.Transform(T), kc=bk.alloc_packed(rows, w.heads, 2, q).with_slots(slots),
+                           vc=bk.alloc_packed(rows, w.heads, 2, q).with_slots(slots)))
+    st = torch.cuda.Stream()
+    calls = []
+    for L in layers:
+        calls.append(bk.prepare_quantize_keys(L["K"], pos, rope, L["tk"], 2, q, L["kc"], stream=st))
+        calls.append(bk.prepare_quantize_values(L["V"], 2, q, L["vc"], stream=st))
+    with torch.cuda.stream(st):
+        for c in calls:  # eager once (also caches the launch shapes)
+            c()
+    torch.cuda.synchronize()
+    want = [(L["kc"].codes[slots].clone(), L["kc"].scales[slots].clone(), L["vc"].codes[slots].clone(),
+             L["vc"].scales[slots].clone()) for L in layers]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"graph replay {rep}")
+        for L in layers:  # clear the rows with eager work between the replays
+            L["kc"].codes[slots] = 0
+            L["vc"].codes[slots] = 0
+            L["kc"].scales[slots] = 0
+            L["vc"].scales[slots] = 0
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for L, (kc, ks, vc, vs) in zip(layers, want):
+            assert torch.equal(L["kc"].codes[slots], kc) and torch.equal(L["kc"].scales[slots], ks)
+            assert torch.equal(L["vc"].codes[slots], vc) and torch.equal(L["vc"].scales[slots], vs)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_symmetric_ties_take_the_even_code(env, bits):
     """Inputs exactly on level midpoints (j * step, |j| < 2^(b-1)): the nearest-
