@@ -102,6 +102,62 @@ def cpu_baseline(w, synth, seconds_hint: float = 20.0) -> dict:
                       f"K and V), single-threaded, {dt:.1f} s"}
 
 
+def quality_report(torch, synth, bk, dev, layers=4, n_tok=4096, n_q=64, q_scale=0.4, bits=2) -> dict:
+    """Attention-output error of the quantized cache, per transform: identity,
+    Hadamard / 8 and the workload's T_k (keys through the transform and paired
+    queries, values plain, 2-bit symmetric) against fp32 attention over the
+    unquantized bf16 keys after RoPE and bf16 values, on synthetic
+    Qwen3-8B-shaped layers.  Error = |o - o_ref|^2 / |o_ref|^2 per layer
+    (all query heads), geometric mean over the layers.  Queries are N(0, 1) x
+    q_scale: 0.4 puts the scores' spread at about 2 (a softmax that is neither
+    flat nor one-hot on these keys)."""
+    w = synth.WORKLOADS["qwen3_8b_prefill"]
+    H, G = w.heads, 4
+    q = bk.sym(w.clip_alpha)
+    rope = bk.Rope(w.theta, 1 << 17)
+    Hd = np.array([[1.0]])
+    while Hd.shape[0] < D:
+        Hd = np.block([[Hd, Hd], [Hd, -Hd]])
+    eye = bk.Transform(np.stack([np.eye(D, dtype=np.float32)] * H))
+    pos = torch.from_numpy(synth.positions(w, 0, n_tok)).to(dev)
+    errs = {"identity": [], "hadamard": [], "T_k": []}
+    for layer in range(layers):
+        K = torch.from_numpy(synth.kv(w, layer, "K", 0, n_tok).view(np.int16)).to(dev).view(torch.bfloat16)
+        V = torch.from_numpy(synth.kv(w, layer, "V", 0, n_tok).view(np.int16)).to(dev).view(torch.bfloat16)
+        X = bk.wushkv_debug_rope_transform(K, pos, rope, eye)  # bf16(RoPE(k)), exact in fp32
+        T, Ti = synth.transform(w, layer)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + layer)
+        Q = torch.randn((n_q, H * G, D), device=dev, generator=g) * q_scale
+        Qb = Q.to(torch.bfloat16)
+        scale = 1.0 / np.sqrt(D)
+        # fp32 reference: query head hq reads KV head hq // G
+        Xh = X.permute(1, 0, 2).contiguous()                  # [H][N][128]
+        Vh = V.float().permute(1, 0, 2).contiguous()          # [H][N][128]
+        Qh = Qb.float().view(n_q, H, G, D).permute(1, 0, 2, 3).reshape(H, n_q * G, D).contiguous()
+        sc = torch.matmul(Qh, Xh.transpose(1, 2).contiguous()) * scale
+        ref = torch.matmul(torch.softmax(sc, dim=-1), Vh)      # [H][n_q G][128]
+        ref = ref.view(H, n_q, G, D).permute(1, 0, 2, 3).reshape(n_q, H * G, D)
+        vc = bk.alloc_packed(n_tok, H, bits, q, dev)
+        bk.wushkv_quantize_values(V, bits, q, vc)
+        row0 = torch.zeros(n_q, dtype=torch.int64, device=dev)
+        lens = torch.full((n_q,), n_tok, dtype=torch.int32, device=dev)
+        for name, (Tm, Tim) in (("identity", (np.stack([np.eye(D, dtype=np.float32)] * H),) * 2),
+                                ("hadamard", (np.stack([Hd / 8.0] * H).astype(np.float32),
+                                              np.stack([Hd / 16.0] * H).astype(np.float32))),
+                                ("T_k", (T, Ti))):
+            kc = bk.alloc_packed(n_tok, H, bits, q, dev)
+            bk.wushkv_quantize_keys(K, pos, rope, bk.Transform(Tm), bits, q, kc)
+            qp = bk.wushkv_pair_queries(Qb, bk.Transform(Tim))
+            o = bk.wushkv_decode_attention(qp, kc, vc, H, bits, q, row0, lens, n_tok, scale)
+            errs[name].append(float(((o - ref) ** 2).sum() / (ref ** 2).sum()))
+    torch.cuda.synchronize()
+    return {k: {"geomean": float(np.exp(np.mean(np.log(v)))), "per_layer": [round(x, 6) for x in v]}
+            for k, v in errs.items()} | {"layers": layers, "tokens": n_tok, "queries": n_q, "bits": bits,
+                                         "query_scale": q_scale,
+                                         "note": "synthetic heavy-tailed keys and values; no model weights"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +166,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue keys and values of the throughput pass on one stream")
+    ap.add_argument("--quality", action="store_true",
+                    help="also report the attention-output error of the quantized cache per key transform")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -316,6 +374,31 @@ def main() -> int:
     torch.cuda.synchronize()
     chunk_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
 
+    # ---- structured key transforms through the same dense path (Hadamard / 8; four 32 x 32
+    # blocks on the diagonal): the key kernel's time on the benchmark layer, one buffer set
+    Hd = np.array([[1.0]])
+    while Hd.shape[0] < D:
+        Hd = np.block([[Hd, Hd], [Hd, -Hd]])
+    blk = np.zeros((H, D, D), np.float32)
+    brng = np.random.default_rng(77)
+    for hh in range(H):
+        for bb in range(4):
+            blk[hh, 32 * bb:32 * bb + 32, 32 * bb:32 * bb + 32] = brng.standard_normal((32, 32)) / np.sqrt(32) + 2 * np.eye(32)
+    struct_us = {}
+    for tname, Tm in (("dense", T), ("hadamard", np.stack([Hd / 8.0] * H).astype(np.float32)),
+                      ("block_diagonal", blk)):
+        th = bk.Transform(Tm)
+        call = bk.prepare_quantize_keys(sets[0]["K"], sets[0]["pos"], rope, th, bits, q, sets[0]["ko"], stream=stream)
+        for _ in range(200):
+            call()
+        tev = new_events(50, 2)
+        for e in tev:
+            bk.wushkv_debug_time_next_launch(e[0], e[1])
+            call()
+        torch.cuda.synchronize()
+        struct_us[tname] = round(float(np.mean([e[0].elapsed_time(e[1]) for e in tev])) * 1e3, 2)
+        del th
+
     # ---- decode attention over the packed caches (64 sequences of the decode workload's lengths,
     # 32 query heads over 8 KV heads), reported alongside: the caches hold random codes and steps
     att_q = 32
@@ -403,6 +486,7 @@ def main() -> int:
             "chunk16_tokens_per_layer": 16 * dn, "chunk16_layer_us": round(chunk_layer_us, 2),
             "chunk16_tokens_per_s": round(16 * dn / (chunk_layer_us * 1e-6), 1),
         },
+        "structured_transforms_keys_us": dict(struct_us, note="key kernel on the benchmark layer, one buffer set"),
         "decode_attention": {
             "sequences": dn, "q_heads": att_q, "kv_heads": H, "bits": bits,
             "cached_tokens": int(att_len.sum()), "max_len": int(att_len.max()),
@@ -414,6 +498,8 @@ def main() -> int:
             "note": "packed 2-bit K and V read once; call_us = attention and split combine launched back to back",
         },
     }
+    if args.quality:
+        out["quality"] = {f"{b}bit": quality_report(torch, synth, bk, dev, bits=b) for b in (2, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle (single thread, one layer)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, synth)

@@ -186,6 +186,51 @@ def test_transform_exact_special_cases(env, dtype):
         assert bad.size == 0, f"{tn}: differ at {bad[:5].tolist()} ({len(bad)})"
 
 
+def hadamard128():
+    H = np.array([[1.0]])
+    while H.shape[0] < 128:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def structured_transforms(H_heads, rng):
+    """Hadamard / 8 (entries +-1/8, exact in bf16; its inverse is Hadamard / 16)
+    and a block-diagonal transform of four random 32 x 32 blocks, per head,
+    with their inverses."""
+    Hd = hadamard128()
+    had = np.stack([Hd / 8.0] * H_heads).astype(np.float32)
+    had_inv = np.stack([Hd / 16.0] * H_heads).astype(np.float32)
+    blk = np.zeros((H_heads, 128, 128))
+    for h in range(H_heads):
+        for b in range(4):
+            blk[h, 32 * b:32 * b + 32, 32 * b:32 * b + 32] = rng.standard_normal((32, 32)) / np.sqrt(32) + 2 * np.eye(32)
+    return {"hadamard": (had, had_inv),
+            "block_diagonal": (blk.astype(np.float32), np.linalg.inv(blk).astype(np.float32))}
+
+
+@pytest.mark.parametrize("tname", ["hadamard", "block_diagonal"])
+def test_structured_transforms(env, tname):
+    """Structured transforms go through the same dense path: the transform
+    within tolerance, keys end to end by the same rule, the read path through
+    their inverses within tolerance, on caches the oracle wrote."""
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["qwen3_8b_prefill"]
+    n = 4096
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, Ti = structured_transforms(w.heads, np.random.default_rng(77))[tname]
+    say(f"structured transform {tname}")
+    yg, yr = _y_gpu(env, K, pos, T), _y_ref(env, K, pos, T)
+    assert np.all(np.abs(yg - yr).max(axis=2) <= TRANSFORM_TOL * np.abs(yr).max(axis=2))
+    q = bk.sym(2.0)
+    account_keys(env, K, pos, T, 2, q, f"{tname} keys")
+    rk = o.quantize_keys(K, pos, T, w.theta, 2, o.sym())
+    ref = o.dequantize(rk["codes"], rk["scales"], None, n, w.heads, 2, o.sym(), Tinv=Ti)
+    got = bk.wushkv_dequantize(dev_packed(env, rk), n, w.heads, 2, q, T_k_inv=bk.Transform(Ti),
+                               out_dtype=torch.float32).cpu().numpy()
+    assert np.all(np.abs(got - ref).max(axis=2) <= TRANSFORM_TOL * np.abs(ref).max(axis=2))
+
+
 # ---------------------------------------------------------------------------------- quantizer + packing
 
 QUANTS = [("sym", 2), ("sym", 3), ("sym", 4), ("affine", 2), ("affine", 3), ("affine", 4)]
