@@ -255,11 +255,32 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   const int cnt_all = min(len - n_lo, kChunk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.G, Hkv = a.n_kv_heads;
-
-  for (int i = tid; i < NQ * kD; i += 256) {
-    const int g = i >> 7, c = i & 127;
-    q_lds[g][c] = g < G ? bf16lo_to_f32(a.qp[((int64_t)b * a.n_q_heads + h * G + g) * kD + c]) : 0.0f;
+  if (a.n_rows <= 0) {
+    // no row exists: the split contributes nothing (max -inf, sums and output 0)
+    for (int i = tid; i < G * kPartFloats; i += 256) {
+      const int g = i / kPartFloats, e = i - g * kPartFloats;
+      a.part[(((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + e] =
+          e == 0 ? -__builtin_inff() : 0.0f;
+    }
+    return;
   }
+
+  // (the loads of all four passes are issued before the first is used)
+  uint16_t qv[NQ * kD / 256];
+#pragma unroll
+  for (int j = 0; j < NQ * kD / 256; ++j) {
+    const int i = tid + 256 * j, g = i >> 7, c = i & 127;
+    const uint16_t v = a.qp[((int64_t)b * a.n_q_heads + h * G + (g < G ? g : 0)) * kD + c];  // unconditional
+    qv[j] = g < G ? v : (uint16_t)0;
+  }
+#pragma unroll
+  for (int j = 0; j < NQ * kD / 256; ++j) {
+    const int i = tid + 256 * j;
+    q_lds[i >> 7][i & 127] = bf16lo_to_f32(qv[j]);
+  }
+  // the sequence's first row, read once (a load in the loop would be redone and
+  // waited for in every round: the compiler cannot tell it from the stores)
+  const int64_t row_base = a.row0[b] + n_lo;
   __syncthreads();
   if (tid < 32 * NQ) {
     // sum_j q'_j (c_j - m) = raw - (SB / 2 + m) sum_j q'_j; the sum in fp64
@@ -336,8 +357,8 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   uint32_t pks[kSub / 256], pvs[kSub / 256];
   auto prefetch = [&](int base) __attribute__((always_inline)) {
     const int cnt = min(cnt_all - base, kSub);
-    if (a.n_rows <= 0 || cnt <= 0) return;  // uniform
-    const int64_t r0 = a.row0[b] + n_lo + base;
+    if (cnt <= 0) return;  // uniform
+    const int64_t r0 = row_base + base;
 #pragma unroll
     for (int j = 0; j < PR; ++j) {
       const int c = tid + 256 * j, tok = c / CPT, part = c - tok * CPT;
@@ -364,19 +385,20 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
 
   for (int base = 0; base < cnt_all; base += kSub) {
     const int cnt = min(cnt_all - base, kSub);
-    const int64_t r0 = a.row0[b] + n_lo + base;
+    const int64_t r0 = row_base + base;
     if constexpr (PF) {
-      if (a.n_rows > 0) {
+      {
+        // written for every piece, also past the round's tokens (whose
+        // registers hold stale bits: those tokens are absent), so that every
+        // load is waited for here and nowhere else
 #pragma unroll
         for (int j = 0; j < PR; ++j) {
           const int c = tid + 256 * j;
-          if (c / CPT < cnt) {
-            *(u32x4*)&kc_lds[16 * c] = pk[j];
-            const int tok = c / CPT, part = c - tok * CPT;
-            uint32_t* vt = (uint32_t*)vc_lds;
+          *(u32x4*)&kc_lds[16 * c] = pk[j];
+          const int tok = c / CPT, part = c - tok * CPT;
+          uint32_t* vt = (uint32_t*)vc_lds;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = pv[j][e];
-          }
+          for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = pv[j][e];
         }
 #pragma unroll
         for (int j = 0; j < kSub / 256; ++j) {
@@ -386,12 +408,6 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
           off_lds[i] = ok ? 0.0f : NINF;
           dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
-        }
-      } else {
-        for (int i = tid; i < kSub; i += 256) {
-          dk_lds[i] = 0.0f;
-          off_lds[i] = NINF;
-          dv_lds[i] = 0.0f;
         }
       }
       __syncthreads();
