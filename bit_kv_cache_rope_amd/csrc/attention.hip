@@ -209,12 +209,15 @@ __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor
 template <int BITS, int QS>
 __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const AttnArgs a) {
   constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
+  // tokens per round: 512, or 256 for 3- and 4-bit records (so that three blocks
+  // LDS fits a CU and the records of a round fit one load round)
+  constexpr int KS = BITS == 2 ? kSub : kSub / 2;
   constexpr int REC = 16 * BITS;
   constexpr int SNW = BITS;    // words of key codes per lane (32 channels)
   constexpr int VNW = BITS == 3 ? 3 : 2;  // words of value codes per lane
   constexpr float SB = BITS == 2 ? 8.0f : (BITS == 3 ? 16.0f : 32.0f);
   constexpr float M = (float)((1 << BITS) - 1) * 0.5f;
-  constexpr int SROW = kSub + 16;  // s_lds row (padded against bank conflicts)
+  constexpr int SROW = KS + 16;  // s_lds row (padded against bank conflicts)
   constexpr float NINF = -__builtin_inff();
   constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass (4x4x1 product)
   constexpr bool TWO = BITS == 2;         // score tiles two at a time
@@ -223,17 +226,17 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   // split into three bf16 parts (columns g + 4 part); 3 bits: fp32 4x4x1 MFMA.
   constexpr bool VT = BITS != 3;
   constexpr int NWV = REC / 4;            // words per record
-  constexpr int VROW = kSub + 4;          // vt row (u32)
-  constexpr int PROW = kSub + 8;          // weight row (bf16), 16-byte pieces spread over the banks
-  constexpr int KBYTES = kSub * REC > QS * 16 * PROW * 2 ? kSub * REC : QS * 16 * PROW * 2;
+  constexpr int VROW = KS + 4;          // vt row (u32)
+  constexpr int PROW = KS + 8;          // weight row (bf16), 16-byte pieces spread over the banks
+  constexpr int KBYTES = KS * REC > QS * 16 * PROW * 2 ? KS * REC : QS * 16 * PROW * 2;
 
   // the round's key records; after the scores, the bf16 weights [QS][16][PROW]
   __shared__ __align__(16) uint8_t kc_lds[KBYTES];
-  __shared__ __align__(16) uint8_t vc_lds[VT ? NWV * VROW * 4 : kSub * REC];  // value records
+  __shared__ __align__(16) uint8_t vc_lds[VT ? NWV * VROW * 4 : KS * REC];  // value records
   __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p * step_v
-  __shared__ __align__(16) float dk_lds[kSub];          // key step * scale * log2(e); 0: token absent
-  __shared__ __align__(16) float off_lds[kSub];         // 0, or -inf for an absent token
-  __shared__ float dv_lds[kSub];                        // value step
+  __shared__ __align__(16) float dk_lds[KS];          // key step * scale * log2(e); 0: token absent
+  __shared__ __align__(16) float off_lds[KS];         // 0, or -inf for an absent token
+  __shared__ float dv_lds[KS];                        // value step
   __shared__ float q_lds[NQ][kD + 1];
   __shared__ float k1_lds[NQ];
   __shared__ float mx_lds[4][NQ];
@@ -346,17 +349,17 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   // ---- records of a round: CPT 16-byte pieces per record; rows outside the
   // cache are read from row 0 and never used (their key step marks them absent)
   constexpr int CPT = REC / 16;
-  constexpr int NLD = kSub * CPT / 256;  // pieces per thread and cache
+  constexpr int NLD = KS * CPT / 256;  // pieces per thread and cache
   constexpr int NR = NLD > 4 ? 2 : 1;    // load rounds (at most 4 + 4 pieces in registers)
   constexpr int PR = NLD / NR;
   // one load round: the next round's records and steps are loaded into
   // registers while this round is worked on, and go to LDS at its end
-  constexpr bool PF = NR == 1;
+  constexpr bool PF = NR == 1 && VT;
   static_assert(!PF || VT, "the prefetch path writes the transposed value layout");
   u32x4 pk[PR], pv[PR];
-  uint32_t pks[kSub / 256], pvs[kSub / 256];
+  uint32_t pks[KS / 256], pvs[KS / 256];
   auto prefetch = [&](int base) __attribute__((always_inline)) {
-    const int cnt = min(cnt_all - base, kSub);
+    const int cnt = min(cnt_all - base, KS);
     if (cnt <= 0) return;  // uniform
     const int64_t r0 = row_base + base;
 #pragma unroll
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       }
     }
 #pragma unroll
-    for (int j = 0; j < kSub / 256; ++j) {
+    for (int j = 0; j < KS / 256; ++j) {
       const int i = tid + 256 * j;
       if (i < cnt) {
         int64_t row = r0 + i;
@@ -383,8 +386,8 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   };
   if constexpr (PF) prefetch(0);
 
-  for (int base = 0; base < cnt_all; base += kSub) {
-    const int cnt = min(cnt_all - base, kSub);
+  for (int base = 0; base < cnt_all; base += KS) {
+    const int cnt = min(cnt_all - base, KS);
     const int64_t r0 = row_base + base;
     if constexpr (PF) {
       {
@@ -401,7 +404,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = pv[j][e];
         }
 #pragma unroll
-        for (int j = 0; j < kSub / 256; ++j) {
+        for (int j = 0; j < KS / 256; ++j) {
           const int i = tid + 256 * j;
           const int64_t row = r0 + i;
           const bool ok = i < cnt && row >= 0 && row < a.n_rows;
@@ -411,9 +414,9 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         }
       }
       __syncthreads();
-      prefetch(base + kSub);
+      prefetch(base + KS);
     } else {
-    if (a.n_rows > 0) {  // uniform; no row exists otherwise
+    {
 #pragma unroll
       for (int rd = 0; rd < NR; ++rd) {
         u32x4 kr[PR], vr[PR];
@@ -429,7 +432,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           }
         }
         if (rd == 0) {
-          for (int i = tid; i < kSub; i += 256) {
+          for (int i = tid; i < KS; i += 256) {
             float dk = 0.0f, off = NINF, dv = 0.0f;
             const int64_t row = r0 + i;
             if (i < cnt && row >= 0 && row < a.n_rows) {
@@ -442,27 +445,21 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
             dv_lds[i] = dv;
           }
         }
+        // written for every piece (past the round's tokens: stale bits of
+        // absent tokens), so that the loads are waited for here only
 #pragma unroll
         for (int j = 0; j < PR; ++j) {
           const int c = tid + 256 * (rd * PR + j);
-          if (c / CPT < cnt) {
-            *(u32x4*)&kc_lds[16 * c] = kr[j];
-            if constexpr (VT) {
-              const int tok = c / CPT, part = c - tok * CPT;
-              uint32_t* vt = (uint32_t*)vc_lds;
+          *(u32x4*)&kc_lds[16 * c] = kr[j];
+          if constexpr (VT) {
+            const int tok = c / CPT, part = c - tok * CPT;
+            uint32_t* vt = (uint32_t*)vc_lds;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = vr[j][e];
-            } else {
-              *(u32x4*)&vc_lds[16 * c] = vr[j];
-            }
+            for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = vr[j][e];
+          } else {
+            *(u32x4*)&vc_lds[16 * c] = vr[j];
           }
         }
-      }
-    } else {
-      for (int i = tid; i < kSub; i += 256) {
-        dk_lds[i] = 0.0f;
-        off_lds[i] = NINF;
-        dv_lds[i] = 0.0f;
       }
     }
     __syncthreads();
@@ -519,7 +516,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       const float msub = mn == NINF ? 0.0f : mn;
       m_run[g] = mn;
       float ls = 0.0f, vs = 0.0f;
-      for (int n = tid; n < kSub; n += 256) {
+      for (int n = tid; n < KS; n += 256) {
         float pv = 0.0f;
         if (n < n16) {
           const float p = __builtin_amdgcn_exp2f(s_lds[g][n] - msub);
@@ -604,7 +601,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       float pa[PU][QS];
 #pragma unroll
       for (int jj = 0; jj < PU; ++jj) {
-        const int i = u + 16 * jj + tb;  // < kSub
+        const int i = u + 16 * jj + tb;  // < KS
         load_words<VNW>(&vc_lds[i * REC + voff], U[jj]);  // any bytes if absent (its weight is 0)
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) pa[jj][qs] = s_lds[4 * qs + x][i];
