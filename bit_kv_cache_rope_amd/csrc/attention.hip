@@ -14,18 +14,21 @@
 //   * pair_queries_kernel: q'_j = RN32(sum_r T~inv[r][j] q_r) in fp64 FMAs
 //     over ascending r (every product is exact), then bf16.
 //   * attention_kernel: one block of four waves per (2048-token split, KV
-//     head, sequence), in rounds of 512 tokens whose key and value records
-//     are first copied to LDS with all loads in flight at once.
+//     head, sequence), in rounds of 512 tokens (256 at 3 and 4 bits) whose
+//     key and value records are first copied to LDS with all loads in flight
+//     at once (at 2 and 4 bits, the next round's during this round's work).
 //       scores  S[n][g] = sum_j code-operand[n][j] * q'[g][j] on
 //               v_mfma_f32_16x16x32_bf16 (16 tokens x 16 columns, G used);
 //               the key codes enter as exact bf16 values 0.5 + c / SB built
 //               with one shift, mask and v_perm per pair of codes, and the
 //               constant part is subtracted after the product.
 //       softmax p = exp2(s - max) over the split, then p * step_v.
-//       values  O[g][ch] += p[g][n] * c[n][ch] on v_mfma_f32_4x4x1f32: 16
-//               blocks = 16 tokens, 4 rows = 4 query heads, 4 columns = 4
-//               channels, so each lane converts only the codes of its own
-//               token (fp32 operands: no rounding of p).
+//       values  O[ch][g] += c[ch][n] * p[n][g] on v_mfma_f32_16x16x32_bf16
+//               (2 and 4 bits): rows = 16 channels, k = 32 tokens from the
+//               value records stored transposed in LDS, columns = the query
+//               heads' weights p * step_v split into three bf16 parts (exact
+//               to fp32).  3-bit codes straddle words: v_mfma_f32_4x4x1f32
+//               with fp32 weights (16 blocks = 16 tokens, rows = queries).
 //     A split writes (max, sum, unnormalized output) per query head.
 //   * combine_kernel merges the splits of a sequence.
 #include "device_common.h"
@@ -203,14 +206,15 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* W) {
 
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
-// grid 8 n_splits8 Hkv B (see the block map below), 256 threads.  A block takes up to kChunk tokens of
-// one sequence and KV head, in rounds of kSub tokens, with the running max,
-// sums and value accumulators rescaled from round to round (online softmax).
+// grid 8 * n_splits8 * Hkv * B blocks (see the block map below), 256 threads.
+// A block takes up to kChunk tokens of one sequence and KV head, in rounds of
+// KS tokens, with the running max, sums and value accumulators rescaled from
+// round to round (online softmax).
 template <int BITS, int QS>
 __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const AttnArgs a) {
   constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
-  // tokens per round: 512, or 256 for 3- and 4-bit records (so that three blocks
-  // LDS fits a CU and the records of a round fit one load round)
+  // tokens per round: 512, or 256 for 3- and 4-bit records (so that three
+  // blocks' LDS fits a CU and a 4-bit round's records fit one load round)
   constexpr int KS = BITS == 2 ? kSub : kSub / 2;
   constexpr int REC = 16 * BITS;
   constexpr int SNW = BITS;    // words of key codes per lane (32 channels)
