@@ -706,14 +706,41 @@ __global__ void __launch_bounds__(128) combine_kernel(const AttnArgs a) {
   const int len = min(max(a.len[b], 0), a.max_len);
   const int ns = (len + kChunk - 1) / kChunk;
   const float* p = a.part + ((int64_t)b * a.n_q_heads + hq) * a.n_splits * kPartFloats;
-  float m = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) m = __builtin_fmaxf(m, p[s * kPartFloats]);
-  float l = 0.0f, o = 0.0f;
-  if (m != -__builtin_inff()) {
-    for (int s = 0; s < ns; ++s) {
-      const float f = __builtin_amdgcn_exp2f(p[s * kPartFloats] - m);
-      l += f * p[s * kPartFloats + 1];
-      o += f * p[s * kPartFloats + 4 + c];
+  // the splits' maxima and sums through LDS (thread s loads split s), then
+  // every thread's output column with four splits' loads in flight at a time
+  __shared__ float ms[128], ls[128];
+  float m = -__builtin_inff(), l = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 128) {
+    const int nb = min(ns - s0, 128);
+    __syncthreads();
+    if (c < nb) {
+      ms[c] = p[(s0 + c) * kPartFloats];
+      ls[c] = p[(s0 + c) * kPartFloats + 1];
+    }
+    __syncthreads();
+    float mb = m;
+    for (int s = 0; s < nb; ++s) mb = __builtin_fmaxf(mb, ms[s]);
+    if (mb == -__builtin_inff()) continue;  // uniform: nothing present so far
+    const float r = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mb);
+    l *= r;
+    o *= r;
+    m = mb;
+    int s = 0;
+    for (; s + 4 <= nb; s += 4) {
+      float v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = p[(s0 + s + k) * kPartFloats + 4 + c];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float f = __builtin_amdgcn_exp2f(ms[s + k] - m);
+        l += f * ls[s + k];
+        o += f * v[k];
+      }
+    }
+    for (; s < nb; ++s) {
+      const float f = __builtin_amdgcn_exp2f(ms[s] - m);
+      l += f * ls[s];
+      o += f * p[(s0 + s) * kPartFloats + 4 + c];
     }
   }
   a.out[((int64_t)b * a.n_q_heads + hq) * kD + c] = l > 0.0f ? o / l : 0.0f;
