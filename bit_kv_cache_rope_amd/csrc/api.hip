@@ -511,8 +511,8 @@ wushkv_status wushkv_pair_queries(const void* Q, wushkv_dtype q_dtype, int64_t n
   if (n_tokens == 0) return WUSHKV_OK;
   if (!q_out) return fail(WUSHKV_ERR_INVALID_ARG, "q_out is NULL");
   if (!aligned(q_out, 2)) return fail(WUSHKV_ERR_ALIGNMENT, "q_out must be 2-byte aligned");
-  if (n_tokens * (n_q_heads / T_k_inv->n_heads) > ((int64_t)1 << 35))
-    return fail(WUSHKV_ERR_UNSUPPORTED, "too many query vectors for one call");
+  if (n_tokens * (n_q_heads / T_k_inv->n_heads) > ((int64_t)1 << 32))  // grid of 4 vectors per block
+    return fail(WUSHKV_ERR_UNSUPPORTED, "more than 2^32 query vectors per KV head in one call");
   int dev;
   st = current_device(&dev);
   if (st) return st;
