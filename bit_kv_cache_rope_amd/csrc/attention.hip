@@ -520,26 +520,32 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       const float msub = mn == NINF ? 0.0f : mn;
       m_run[g] = mn;
       float ls = 0.0f, vs = 0.0f;
-      for (int n = tid; n < KS; n += 256) {
-        float pv = 0.0f;
-        if (n < n16) {
-          const float p = __builtin_amdgcn_exp2f(s_lds[g][n] - msub);
-          pv = p * dv_lds[n];
-          ls += p;
-          vs += pv;
+      // two consecutive tokens per thread (paired bf16 writes)
+      for (int n = 2 * tid; n < KS; n += 512) {
+        float pv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          pv[e] = 0.0f;
+          if (n + e < n16) {
+            const float p = __builtin_amdgcn_exp2f(s_lds[g][n + e] - msub);
+            pv[e] = p * dv_lds[n + e];
+            ls += p;
+            vs += pv[e];
+          }
         }
         if constexpr (VT) {
           // pv = hi + mid + lo in bf16 (exact up to the last part's rounding)
-          uint16_t* pt = (uint16_t*)kc_lds + (g >> 2) * 16 * PROW + (g & 3) * PROW + n;
-          const uint32_t hb = pack_bf16x2(pv, 0.0f) & 0xFFFFu;
-          const float r1 = pv - bf16lo_to_f32(hb);
-          const uint32_t mb = pack_bf16x2(r1, 0.0f) & 0xFFFFu;
-          const float r2 = r1 - bf16lo_to_f32(mb);
-          pt[0] = (uint16_t)hb;
-          pt[4 * PROW] = (uint16_t)mb;
-          pt[8 * PROW] = (uint16_t)(pack_bf16x2(r2, 0.0f) & 0xFFFFu);
+          uint32_t* pt = (uint32_t*)((uint16_t*)kc_lds + (g >> 2) * 16 * PROW + (g & 3) * PROW + n);
+          const uint32_t hb = pack_bf16x2(pv[0], pv[1]);
+          const float r10 = pv[0] - bf16lo_to_f32(hb), r11 = pv[1] - bf16hi_to_f32(hb);
+          const uint32_t mb = pack_bf16x2(r10, r11);
+          const float r20 = r10 - bf16lo_to_f32(mb), r21 = r11 - bf16hi_to_f32(mb);
+          pt[0] = hb;
+          pt[2 * PROW] = mb;
+          pt[4 * PROW] = pack_bf16x2(r20, r21);
         } else {
-          s_lds[g][n] = pv;
+          s_lds[g][n] = pv[0];
+          s_lds[g][n + 1] = pv[1];
         }
       }
       lsum[g] = lsum[g] * alpha[g] + ls;
