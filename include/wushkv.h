@@ -173,7 +173,9 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
  * consume the cached keys in view).
  *   Q: device, bf16 or fp32, [n_tokens][n_q_heads][128] with token_stride
  *      elements per token (same rules as K); query head hq reads KV head
- *      hq / (n_q_heads / T_k_inv's head count).
+ *      hq / (n_q_heads / T_k_inv's head count).  At most 2^32 query vectors
+ *      per KV head (n_tokens * n_q_heads / heads) per call, else
+ *      WUSHKV_ERR_UNSUPPORTED.
  *   T_k_inv: transform handle holding T_k^-1 (the read path's), bf16 T~inv.
  *   q_out: device bf16 [n_tokens][n_q_heads][128], contiguous, caller-owned:
  *      q'_j = bf16(RN32(sum_r T~inv[r][j] q_r)), the sum exact before the fp32
