@@ -166,6 +166,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue keys and values of the throughput pass on one stream")
+    ap.add_argument("--light", action="store_true",
+                    help="few repetitions in the sections beside the throughput pass (for counter runs)")
     ap.add_argument("--quality", action="store_true",
                     help="also report the attention-output error of the quantized cache per key transform")
     ap.add_argument("--copy-probe", action="store_true",
@@ -311,18 +313,19 @@ def main() -> int:
     dvc = bk.alloc_packed(drows, H, bits, q, dev).with_slots(dslots)
     dk = bk.prepare_quantize_keys(dK, dpos, rope, dtk, bits, q, dkc, stream=stream)
     dv = bk.prepare_quantize_values(dV, bits, q, dvc, stream=vstream)
-    for _ in range(200):
+    rep = 1 if args.light else 10  # repetition scale of the sections beside the throughput pass
+    for _ in range(20 * rep):
         dk()
         dv()
     torch.cuda.synchronize()
-    n_dec = 36 * 20
+    n_dec = 36 * 2 * rep
     t0 = time.perf_counter()
     for _ in range(n_dec):
         dk()
         dv()
     torch.cuda.synchronize()
     dec_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
-    dev_ev = new_events(50, 4)
+    dev_ev = new_events(5 * rep, 4)
     for e in dev_ev:
         bk.wushkv_debug_time_next_launch(e[0], e[1])
         dk()
@@ -346,10 +349,10 @@ def main() -> int:
         for _ in range(36):
             gk()
             gv()
-    for _ in range(20):
+    for _ in range(2 * rep):
         graph.replay()
     torch.cuda.synchronize()
-    n_rep = 100
+    n_rep = 10 * rep
     t0 = time.perf_counter()
     for _ in range(n_rep):
         graph.replay()
@@ -363,7 +366,7 @@ def main() -> int:
     cV = dev_bf16(synth.kv(wd, 0, "V", 0, 16 * dn))
     ck = bk.prepare_quantize_keys(cK, cpos, rope, dtk, bits, q, dkc.with_slots(cslots), stream=stream)
     cv = bk.prepare_quantize_values(cV, bits, q, dvc.with_slots(cslots), stream=vstream)
-    for _ in range(200):
+    for _ in range(20 * rep):
         ck()
         cv()
     torch.cuda.synchronize()
@@ -389,9 +392,9 @@ def main() -> int:
                       ("block_diagonal", blk)):
         th = bk.Transform(Tm)
         call = bk.prepare_quantize_keys(sets[0]["K"], sets[0]["pos"], rope, th, bits, q, sets[0]["ko"], stream=stream)
-        for _ in range(200):
+        for _ in range(20 * rep):
             call()
-        tev = new_events(50, 2)
+        tev = new_events(5 * rep, 2)
         for e in tev:
             bk.wushkv_debug_time_next_launch(e[0], e[1])
             call()
@@ -420,11 +423,11 @@ def main() -> int:
     att = bk.prepare_decode_attention(att_qp, dkc, dvc, H, bits, q, att_row0, att_lens, 32768, 1.0 / np.sqrt(D),
                                       att_ws, att_out, stream=stream)
     with torch.cuda.stream(stream):
-        for _ in range(20):
+        for _ in range(2 * rep):
             bk.wushkv_pair_queries(att_Q, dtki, out=att_qp, stream=stream)
             att()
     torch.cuda.synchronize()
-    att_ev = new_events(50, 6)
+    att_ev = new_events(5 * rep, 6)
     for e in att_ev:
         bk.wushkv_debug_time_next_launch(e[0], e[1])
         bk.wushkv_pair_queries(att_Q, dtki, out=att_qp, stream=stream)
