@@ -146,6 +146,27 @@ def test_attention_matches_oracle(env, bits, G):
     check_attention(env, got, ref, value_max(v, bits, row0, lens, rows, Hkv), G, f"bits={bits} G={G}")
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_attention_odd_kv_heads_and_split_edges(env, bits):
+    """Three KV heads (the block map spreads heads and splits over the XCDs
+    modulo the head count) with two query heads each; lengths one past, at and
+    one short of split multiples (2048, 4096) and of round multiples (256,
+    512)."""
+    oracle = env["oracle"]
+    rng = np.random.default_rng(900 + bits)
+    Hkv, G = 3, 2
+    lens = np.array([2049, 4096, 2047, 257, 512, 511, 4097])
+    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    rows = int(lens.sum())
+    say(f"attention odd heads bits={bits} lens={lens.tolist()}")
+    k, v = random_cache(rng, rows, Hkv, bits), random_cache(rng, rows, Hkv, bits)
+    qp = bf16_bits(rng.standard_normal((len(lens), Hkv * G, D)) * 2.0)
+    scale = 1.0 / np.sqrt(D)
+    got = run_attention(env, qp, k, v, Hkv, bits, row0, lens, scale)
+    ref = oracle.decode_attention(qp, k, v, bits, row0, lens, scale)
+    check_attention(env, got, ref, value_max(v, bits, row0, lens, rows, Hkv), G, f"odd heads bits={bits}")
+
+
 def test_attention_edge_cases(env):
     oracle = env["oracle"]
     rng = np.random.default_rng(31)
