@@ -377,6 +377,30 @@ def main() -> int:
     torch.cuda.synchronize()
     chunk_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
 
+    # ---- one GPU's share under 8-way KV-head parallelism: the benchmark layer's tokens for a
+    # single KV head (keys and values of 32768 tokens x 1 head, 18 MB), kernel-recorded events
+    Kh = sets[0]["K"][:, :1].contiguous()
+    Vh = sets[0]["V"][:, :1].contiguous()
+    tk1 = bk.Transform(T[:1])
+    ko1, vo1 = bk.alloc_packed(N, 1, bits, q, dev), bk.alloc_packed(N, 1, bits, q, dev)
+    k1c = bk.prepare_quantize_keys(Kh, sets[0]["pos"], rope, tk1, bits, q, ko1, stream=stream)
+    v1c = bk.prepare_quantize_values(Vh, bits, q, vo1, stream=stream)
+    rep1 = 1 if args.light else 10
+    for _ in range(20 * rep1):
+        k1c()
+        v1c()
+    torch.cuda.synchronize()
+    ev1 = new_events(5 * rep1, 4)
+    for e in ev1:
+        bk.wushkv_debug_time_next_launch(e[0], e[1])
+        k1c()
+        bk.wushkv_debug_time_next_launch(e[2], e[3])
+        v1c()
+    torch.cuda.synchronize()
+    h1_k_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev1])) * 1e3
+    h1_v_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev1])) * 1e3
+    h1_bytes = N * (key_bytes_per_token(1, bits) + value_bytes_per_token(1, bits)) + D * D * 2
+
     # ---- structured key transforms through the same dense path (Hadamard / 8; four 32 x 32
     # blocks on the diagonal): the key kernel's time on the benchmark layer, one buffer set
     Hd = np.array([[1.0]])
@@ -489,6 +513,9 @@ def main() -> int:
             "chunk16_tokens_per_layer": 16 * dn, "chunk16_layer_us": round(chunk_layer_us, 2),
             "chunk16_tokens_per_s": round(16 * dn / (chunk_layer_us * 1e-6), 1),
         },
+        "one_kv_head_share": {"tokens": N, "kv_heads": 1, "keys_us": round(h1_k_us, 2), "values_us": round(h1_v_us, 2),
+                              "gbs": round(h1_bytes / ((h1_k_us + h1_v_us) * 1e-6) / 1e9, 1),
+                              "note": "one GPU's share under 8-way KV-head parallelism; keys then values on one stream"},
         "structured_transforms_keys_us": dict(struct_us, note="key kernel on the benchmark layer, one buffer set"),
         "decode_attention": {
             "sequences": dn, "q_heads": att_q, "kv_heads": H, "bits": bits,
