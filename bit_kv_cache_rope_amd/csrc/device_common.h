@@ -151,7 +151,7 @@ __device__ __forceinline__ float bf16_gt_threshold(float t) {
   const uint32_t b = __float_as_uint(t);
   if (__builtin_isinf(t)) return t;
   if (t >= 0.0f) return __uint_as_float(b | 0xFFFFu);
-  return __uint_as_float(((b & 0x7FFFFFFFu) + 0xFFFFu) & 0xFFFF0000u | 0x80000000u);
+  return __uint_as_float((((b & 0x7FFFFFFFu) + 0xFFFFu) & 0xFFFF0000u) | 0x80000000u);
 }
 
 // Sum over aligned groups of 2, 4, 8 and 16 lanes by DPP moves: after step k a
