@@ -275,6 +275,23 @@ def main() -> int:
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
+    # achievable device-copy rate on this chip, same run: 256 MiB read + 256 MiB written per
+    # copy (beyond the MALL), timed with events on the launch stream
+    ca = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cb = torch.empty_like(ca)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            cb.copy_(ca)
+        ce = new_events(1, 2)[0]
+        n_copy = 2 if args.light else 20
+        ce[0].record(stream)
+        for _ in range(n_copy):
+            cb.copy_(ca)
+        ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (256 << 20) * n_copy / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del ca, cb
 
     # ---- read path on the same data (keys back through T_k^-1, values plain), reported alongside
     _, Ti = synth.transform(w, 0)
@@ -489,6 +506,9 @@ def main() -> int:
                    "kv_dtype": "bf16", "rope_theta": w.theta, "buffer_sets": n_sets,
                    "streams": 1 if args.one_stream else 2},
         "roofline": roofline,
+        "achievable_copy": {"gbs": round(copy_gbs, 1), "keys_frac": round(achieved / copy_gbs, 4),
+                            "step_frac": round((kb + vb) / (ms_per_step * 1e-3) / 1e9 / copy_gbs, 4),
+                            "note": "device-to-device copy of 256 MiB (read + write) in the same run"},
         "kernels": {
             "keys_us": round(key_us, 2), "values_us": round(val_us, 2),
             "keys_algorithmic_bytes": kb, "values_algorithmic_bytes": vb,
