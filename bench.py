@@ -511,6 +511,8 @@ def main() -> int:
                             "note": "device-to-device copy of 256 MiB (read + write) in the same run"},
         "kernels": {
             "keys_us": round(key_us, 2), "values_us": round(val_us, 2),
+            "keys_us_p10_p50_p90": [round(float(np.percentile(key_ms, x)) * 1e3, 2) for x in (10, 50, 90)],
+            "values_us_p10_p50_p90": [round(float(np.percentile(val_ms, x)) * 1e3, 2) for x in (10, 50, 90)],
             "keys_algorithmic_bytes": kb, "values_algorithmic_bytes": vb,
             "values_gbs": round(vb / (val_us * 1e-6) / 1e9, 1),
             "step_gbs": round((kb + vb) / (ms_per_step * 1e-3) / 1e9, 1),
