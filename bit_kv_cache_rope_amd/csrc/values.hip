@@ -6,8 +6,8 @@
 //
 // Layout: a 128-channel (token, head) vector is spread over 16 lanes, 8
 // contiguous channels per lane, so one wave load instruction covers 4 vectors
-// (1 KiB contiguous for a dense tensor).  A wave handles 32 vectors per
-// iteration (8 loads of 16 bytes per lane).  Reductions are xor butterflies
+// (1 KiB contiguous for a dense tensor).  A wave handles 16 vectors per
+// iteration (4 loads of 16 bytes per lane, kU).  Reductions are xor butterflies
 // inside the 16-lane group, which realise the contiguous pairwise tree exactly
 // (offsets 1, 2, 4, 8 combine 16-, 32-, 64-, 128-channel halves).  One lane
 // per vector turns its sum of squares into the step and the code thresholds,

@@ -320,10 +320,37 @@ def test_sym_scale_within_rounding_bound(oracle_mod):
         assert abs(got - float(exact)) <= 0.5 * ulp16 + 1e-6 * float(exact)
 
 
+def golden_vector(spec):
+    """128 fp32 values from a golden case's spec: {"fill", "set": [[index, hex]]}
+    or {"runs": [[[hex, ...], repeat], ...]} (hex = the fp32 bit pattern)."""
+    h = lambda x: np.array([int(x, 16)], np.uint32).view(np.float32)[0]
+    if "runs" in spec:
+        y = np.array([h(x) for run, rep in spec["runs"] for _ in range(rep) for x in run], np.float32)
+    else:
+        y = np.full(128, h(spec["fill"]), np.float32)
+        for i, x in spec.get("set", []):
+            y[i] = h(x)
+    assert y.shape == (128,)
+    return y
+
+
+def test_golden_pairwise_sum(oracle_mod):
+    """The contiguous pairwise fp32 tree of the RMS (the reading of 'clip =
+    2.0*RMS per 128-vector'), worked by hand on a vector where it differs from
+    a sequential sum, a stride-64 butterfly and the exactly rounded sum."""
+    for case in GOLD["pairwise_sum"]:
+        t = golden_vector(case["terms_f32_hex"])
+        got = np.array([oracle_mod.pairwise_sum(t)], np.float32).view(np.uint32)[0]
+        assert got == int(case["S_hex"], 16), case["work"]
+        assert all(int(v, 16) != got for v in case["other_orders_hex"].values())
+
+
 def test_golden_sym_cases(oracle_mod):
     for case in GOLD["sym"]:
         y = np.zeros(128, np.float32)
-        if case["y_pattern"].startswith("alternating"):
+        if "y_f32_hex" in case:
+            y = golden_vector(case["y_f32_hex"])
+        elif case["y_pattern"].startswith("alternating"):
             y[0::2], y[1::2] = 1.0, -1.0
         elif case["y_pattern"].startswith("y[0] = 2"):
             y[0], y[1] = 2.0, -2.0
