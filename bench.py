@@ -80,26 +80,69 @@ def read_traffic():
     return t
 
 
-def cpu_baseline(w, synth, seconds_hint: float = 20.0) -> dict:
+def host_cpu() -> dict:
+    """Host cores visible to this process and the CPU model (/proc/cpuinfo)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"host_cores": cores, "cpu_model": model}
+
+
+def cpu_baseline(w, synth, seconds_hint: float = 6.0) -> dict:
+    """The CPU oracle as it stands, timed on this host: the benchmark layer
+    single-threaded (the headline figure) and with all the process's cores
+    (at most 16 threads), plus single-threaded slices of the other workloads
+    (layer 0, first 8192 tokens; the decode workload's 64 tokens)."""
     import oracle
     oracle.build()
+    hc = host_cpu()
     n = w.tokens
     K = synth.kv(w, 0, "K", 0, n)
     V = synth.kv(w, 0, "V", 0, n)
     pos = synth.positions(w, 0, n)
     T, _ = synth.transform(w, 0)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:  # whole layers until about seconds_hint of CPU work (at least two)
-        oracle.quantize_keys(K, pos, T, w.theta, 2, oracle.sym(w.clip_alpha), threads=1)
-        oracle.quantize_values(V, 2, oracle.sym(w.clip_alpha), threads=1)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if reps >= 2 and dt >= seconds_hint * 0.6:
-            break
+
+    def layer_rate(threads, min_reps):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.quantize_keys(K, pos, T, w.theta, 2, oracle.sym(w.clip_alpha), threads=threads)
+            oracle.quantize_values(V, 2, oracle.sym(w.clip_alpha), threads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if reps >= min_reps and dt >= seconds_hint * 0.5:
+                return reps, dt
+
+    reps, dt = layer_rate(1, 1)
+    all_threads = max(1, min(16, hc["host_cores"]))
+    reps_n, dt_n = layer_rate(all_threads, 2)
+    slices = {}
+    for name, bits in (("decode_append", 2), ("qwen3_32b_full", 3), ("qwen3_32b_full", 4), ("affine_pct", 2)):
+        ws = synth.WORKLOADS[name]
+        ns = min(8192, ws.tokens)
+        Ks, Vs = synth.kv(ws, 0, "K", 0, ns), synth.kv(ws, 0, "V", 0, ns)
+        ps = synth.positions(ws, 0, ns)
+        Ts, _ = synth.transform(ws, 0)
+        qz = oracle.sym(ws.clip_alpha) if ws.quant == "sym" else oracle.affine(ws.p_lo, ws.p_hi)
+        t0 = time.perf_counter()
+        oracle.quantize_keys(Ks, ps, Ts, ws.theta, bits, qz, threads=1)
+        oracle.quantize_values(Vs, bits, qz, threads=1)
+        slices[f"{name}_{bits}bit"] = {"tokens": ns, "tokens_per_s": round(ns / (time.perf_counter() - t0), 1)}
     return {"value": reps * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} passes over one full layer of the workload ({n} tokens x {w.heads} heads, "
-                      f"K and V), single-threaded, {dt:.1f} s"}
+            "sample": f"{reps} pass(es) over one full layer of the workload ({n} tokens x {w.heads} heads, "
+                      f"K and V), single-threaded, {dt:.1f} s",
+            "host_cores": hc["host_cores"], "cpu_model": hc["cpu_model"],
+            "all_cores": {"value": round(reps_n * n / dt_n, 1), "unit": "tokens/s", "threads": all_threads,
+                          "sample": f"{reps_n} passes over the same layer, {dt_n:.1f} s"},
+            "other_workloads_single_thread": slices}
 
 
 def quality_report(torch, synth, bk, dev, layers=4, n_tok=4096, n_q=64, q_scale=0.4, bits=2) -> dict:
@@ -156,6 +199,82 @@ def quality_report(torch, synth, bk, dev, layers=4, n_tok=4096, n_q=64, q_scale=
             for k, v in errs.items()} | {"layers": layers, "tokens": n_tok, "queries": n_q, "bits": bits,
                                          "query_scale": q_scale,
                                          "note": "synthetic heavy-tailed keys and values; no model weights"}
+
+
+def kernel_us(torch, bk, stream, call, reps: int, warm: int = 3) -> float:
+    """Mean duration in us of the kernel `call` launches, from the pair of HIP
+    events that the kernel itself records at its start and end
+    (wushkv_debug_time_next_launch), so dispatch latency is excluded."""
+    for _ in range(warm):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        bk.wushkv_debug_time_next_launch(e0, e1)
+        call()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+
+def other_workloads(torch, synth, bk, dev, stream, rope, light=False) -> dict:
+    """Kernel times of the other workloads at their full per-layer sizes (layer
+    0), as fractions of the 8 TB/s roofline of their algorithmic bytes: the tiny
+    workload (launch-bound), the Qwen3-32B-shaped layer at 3 and 4 bits with the
+    read back through T_k^-1, and the percentile-affine layer (16 x 16384
+    tokens) with its read back.  Read-path outputs are bf16."""
+    reps = 2 if light else 10
+    res = {}
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    for name, bits_list in (("tiny", (2,)), ("qwen3_32b_full", (3, 4)), ("affine_pct", (2,))):
+        w = synth.WORKLOADS[name]
+        N, H = w.tokens, w.heads
+        q = bk.sym(w.clip_alpha) if w.quant == "sym" else bk.affine(w.p_lo, w.p_hi)
+        K, V = dev_t(synth.kv(w, 0, "K")), dev_t(synth.kv(w, 0, "V"))
+        pos = torch.from_numpy(synth.positions(w)).to(dev)
+        T, Ti = synth.transform(w, 0)
+        tk, tki = bk.Transform(T), bk.Transform(Ti)
+        esz = 4 if w.dtype == "f32" else 2
+        nsc = 1 if w.quant == "sym" else 8  # fp16 step (sym) or 4 steps + 4 zeros (affine) per vector
+        for bits in bits_list:
+            ko, vo = bk.alloc_packed(N, H, bits, q, dev), bk.alloc_packed(N, H, bits, q, dev)
+            kc = bk.prepare_quantize_keys(K, pos, rope, tk, bits, q, ko, stream=stream)
+            vc = bk.prepare_quantize_values(V, bits, q, vo, stream=stream)
+            rec = N * H * (16 * bits + 2 * nsc)
+            kb = N * H * D * esz + 4 * N + rec + H * D * D * 2
+            vb = N * H * D * esz + rec
+            k_us, v_us = kernel_us(torch, bk, stream, kc, reps), kernel_us(torch, bk, stream, vc, reps)
+            ent = {"tokens": N, "kv_heads": H, "bits": bits, "quantizer": w.quant,
+                   "keys_us": round(k_us, 2), "values_us": round(v_us, 2),
+                   "keys_hbm_frac": round(kb / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "values_hbm_frac": round(vb / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "tokens_per_s": round(N / ((k_us + v_us) * 1e-6), 1)}
+            if w.round_trip:
+                ok = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+                ov = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+                rk = bk.prepare_dequantize(ko, N, H, bits, q, ok, T_k_inv=tki, stream=stream)
+                rv = bk.prepare_dequantize(vo, N, H, bits, q, ov, stream=stream)
+                rk_us, rv_us = kernel_us(torch, bk, stream, rk, reps), kernel_us(torch, bk, stream, rv, reps)
+                rb = rec + N * H * D * 2
+                ent.update({"read_keys_T_inv_us": round(rk_us, 2), "read_values_us": round(rv_us, 2),
+                            "read_keys_hbm_frac": round((rb + H * D * D * 2) / (rk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "read_values_hbm_frac": round(rb / (rv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                del ok, ov
+            res[f"{name}_{bits}bit"] = ent
+            del ko, vo
+        del K, V, tk, tki
+        torch.cuda.empty_cache()
+    res["note"] = ("layer 0 at full size; kernel-recorded events; fractions of 8 TB/s of algorithmic bytes "
+                   "(inputs in, packed records and fp16 steps/zeros out, T~ once per launch; reads: records in, "
+                   "bf16 out)")
+    return res
 
 
 def main() -> int:
@@ -231,28 +350,8 @@ def main() -> int:
         torch.cuda.synchronize()
         return ev
 
-    for i in range(min(args.warmup, 10)):
+    for i in range(10):
         step(i)
-    # Warm-up: W steps of the throughput pass.  The chip takes some 0.1 s of
-    # load to reach its sustained clocks (a 200-step pass right after a short
-    # warm-up ran 20% slower than the same pass repeated).
-    for i in range(args.warmup):
-        kcall, vcall = tcalls[i % n_sets]
-        kcall()
-        vcall()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
-
-    # Throughput: K steps back to back (keys on the launch stream, values on a
-    # second one), bracketed by device-wide synchronizations only.
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        kcall, vcall = tcalls[i % n_sets]
-        kcall()
-        vcall()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
     # Per-kernel durations: the same K steps again on the launch stream, each
     # kernel recording a pair of HIP events at its own start and end
     # (hipExtLaunchKernel through wushkv_debug_time_next_launch), so the figure
@@ -483,6 +582,31 @@ def main() -> int:
     att_bytes = int(att_len.sum()) * H * 2 * (16 * bits + 2) + dn * att_q * D * 2 + dn * 2 * 12
     att_flops = 4.0 * int(att_len.sum()) * att_q * D
 
+    # ---- the other workloads' kernels, each against the HBM roofline (kernel-recorded events,
+    # one buffer set: every input is at least 256 MiB, beyond the MALL).
+    other = other_workloads(torch, synth, bk, dev, stream, rope, light=args.light)
+
+    # ---- throughput (the headline): W warm-up steps of the throughput pass, then K steps.
+    # It runs after the sections above, so the chip is already at its sustained clocks (it
+    # takes about 0.1 s of load to get there: a 200-step pass right after a short warm-up ran
+    # 20% slower than the same pass repeated) even when W is small.
+    for i in range(args.warmup):
+        kcall, vcall = tcalls[i % n_sets]
+        kcall()
+        vcall()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps, {n_sets} buffer sets)", file=sys.stderr, flush=True)
+
+    # Throughput: K steps back to back (keys on the launch stream, values on a
+    # second one), bracketed by device-wide synchronizations only.
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        kcall, vcall = tcalls[i % n_sets]
+        kcall()
+        vcall()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = N * args.steps / elapsed
     kb = N * key_bytes_per_token(H, bits) + H * D * D * 2  # + T~ read once per launch
@@ -549,6 +673,7 @@ def main() -> int:
             "tflops": round(att_flops / (att_kernel_us * 1e-6) / 1e12, 2),
             "note": "packed 2-bit K and V read once; call_us = attention and split combine launched back to back",
         },
+        "other_workloads": other,
     }
     if args.quality:
         out["quality"] = {f"{b}bit": quality_report(torch, synth, bk, dev, bits=b) for b in (2, 4)}
