@@ -302,21 +302,25 @@ wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out
   rp->t0t = base + heads;
   rp->t1t = base + heads + n0;
   rp->t2t = base + heads + 2 * n0;
-  // The (cos, sin) of every position, rounded once to fp32 from the tables:
-  // 512 bytes per position, read by the key kernel one row per token.
-  e = hipMalloc((void**)&rp->cs, (size_t)max_pos * 64 * sizeof(float2));
+  // The (cos, sin) of every multiple of 32 positions (head and tail, 32 bytes per
+  // pair): the key kernel adds the angle of pos % 32 to them.
+  rp->hi2_rows = (max_pos + 31) / 32;
+  const size_t hi_bytes = (size_t)rp->hi2_rows * 64 * 2 * sizeof(double2);
+  e = hipMalloc((void**)&rp->hi, hi_bytes + (size_t)rp->hi2_rows * sizeof(uint32_t));
   if (e != hipSuccess) {
     (void)hipFree(rp->d_block);
     delete rp;
-    return fail(WUSHKV_ERR_OOM, "hipMalloc for the cos/sin table failed");
+    return fail(WUSHKV_ERR_OOM, "hipMalloc for the RoPE tables failed");
   }
-  e = wushkv::launch_build_cs_table(rp, nullptr);
+  rp->hit = rp->hi + (size_t)rp->hi2_rows * 64;
+  rp->exc = (uint32_t*)((char*)rp->hi + hi_bytes);
+  e = wushkv::launch_build_rope_hi(rp, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    (void)hipFree(rp->cs);
+    (void)hipFree(rp->hi);
     (void)hipFree(rp->d_block);
     delete rp;
-    return hip_fail(e, "cos/sin table build");
+    return hip_fail(e, "RoPE table build");
   }
   *out = rp;
   return WUSHKV_OK;
@@ -327,7 +331,7 @@ wushkv_status wushkv_rope_destroy(wushkv_rope* r) {
   int prev = -1;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(r->device);
-  (void)hipFree(r->cs);
+  (void)hipFree(r->hi);
   (void)hipFree(r->d_block);
   if (prev >= 0) (void)hipSetDevice(prev);
   delete r;
@@ -371,7 +375,11 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
   a.pos = pos;
   a.max_pos = rope->max_pos;
   a.T = T_k->d_swz;
-  a.cs = rope->cs;
+  a.rope_lo = rope->t0;
+  a.rope_lot = rope->t0t;
+  a.rope_hi = rope->hi;
+  a.rope_hit = rope->hit;
+  a.rope_exc = rope->exc;
   if (out && !y_out) {
     a.codes = (uint8_t*)out->codes;
     a.scales = (uint16_t*)out->scales;

@@ -314,4 +314,52 @@ __device__ __forceinline__ float2 rope_cos_sin(int pos, int i, const RopeTables&
   return v;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Two-level split used by the key kernel: pos = h * 32 + p0 with p0 < 32.
+//   lo[p0][i] = (cos, sin)(p0 * w_i)        32 rows: the t0 table above (kept in LDS by the key
+//                                           kernel)
+//   hi[h][i]  = (cos, sin)(h * 32 * w_i)    ceil(max_pos / 32) rows (global), built on the device
+//                                           from t1 and t2 in double-double (head, tail)
+// Fast path: one angle addition in fp64, rounded to fp32.  With every head within 2^-53 (plus
+// ~2^-63) of its exact value and |cos|, |sin| <= 1, each product carries at most 2 * 2^-53 from
+// its factors, the rounded product 2^-53 more and the fma 2^-53: below 6.1 * 2^-53 in all, so
+// the fp32 rounding differs from the exact one only for a value within that distance of an fp32
+// rounding midpoint (about 2^-24 of values).  The RoPE handle marks, once, every position for
+// which any of its 64 pairs differs (comparing with the double-double sum), in a bitmap of one
+// bit per position: exc[pos / 32] bit pos % 32.  Marked positions take the double-double path.
+__device__ __forceinline__ float2 rope2_fast(double2 H, double2 B) {
+  const double c = __builtin_fma(H.x, B.x, -(H.y * B.y));
+  const double s = __builtin_fma(H.y, B.x, H.x * B.y);
+  return make_float2((float)c, (float)s);
+}
+
+__device__ __forceinline__ float2 rope2_slow(double2 H, double2 Ht, double2 B, double2 Bt) {
+  double ch, cl, sh, sl;
+  dd_pair(H.x, Ht.x, B.x, Bt.x, H.y, Ht.y, B.y, Bt.y, -1.0, ch, cl);  // cos(h + b)
+  dd_pair(H.y, Ht.y, B.x, Bt.x, H.x, Ht.x, B.y, Bt.y, 1.0, sh, sl);   // sin(h + b)
+  return make_float2(dd_round_f32(ch, cl), dd_round_f32(sh, sl));
+}
+
+struct Rope2Tables {
+  const double2* lo;     // [32][64] heads (= t0)
+  const double2* hi;     // [hi2_rows][64] heads
+  const double2* lot;    // tails
+  const double2* hit;
+  const uint32_t* exc;   // [hi2_rows] positions whose fast sum rounds differently
+};
+
+__device__ __forceinline__ bool rope2_marked(const uint32_t* exc, int pos) {
+  return (exc[pos >> 5] >> (pos & 31)) & 1u;
+}
+
+// (cos, sin)(pos * w_i) with every table read from global memory; the key kernel computes the
+// same function with lo read from LDS.
+__device__ __forceinline__ float2 rope2_cos_sin(int pos, int i, const Rope2Tables& t) {
+  const int p0 = pos & 31, h = pos >> 5;
+  const double2 H = t.hi[h * kPairs + i], B = t.lo[p0 * kPairs + i];
+  if (__builtin_expect(rope2_marked(t.exc, pos), 0))
+    return rope2_slow(H, t.hit[h * kPairs + i], B, t.lot[p0 * kPairs + i]);
+  return rope2_fast(H, B);
+}
+
 }  // namespace wushkv

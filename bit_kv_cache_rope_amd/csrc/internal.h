@@ -18,20 +18,23 @@ struct wushkv_transform {
   float* d_gsum;   // [H][4][128]: sum over j in group g of T~[h][r][j], for affine reads
 };
 
-// RoPE handle: cos/sin split tables (see rope_cos_sin in device_common.h).
+// RoPE handle: cos/sin split tables (see rope_cos_sin and rope2_cos_sin in device_common.h).
 struct wushkv_rope {
   float theta;
   int32_t max_pos;
   int device;
-  int hi_rows;
-  void* d_block;          // one allocation holding the six tables
+  int hi_rows;            // ceil(max_pos / 1024)
+  int hi2_rows;           // ceil(max_pos / 32)
+  void* d_block;          // one allocation holding the six host-built tables
   const double2* t0;      // [32][64]       (cos, sin)(p0 * w)
   const double2* t1;      // [32][64]       (cos, sin)(p1 * 32 * w)
   const double2* t2;      // [hi_rows][64]  (cos, sin)(p2 * 1024 * w)
   const double2* t0t;     // tails of the three
   const double2* t1t;
   const double2* t2t;
-  float2* cs;             // [max_pos][64] (cos, sin) in fp32, built from the tables above
+  double2* hi;            // [hi2_rows][64] (cos, sin)(h * 32 * w): head ...
+  double2* hit;           // ... and tail, built on the device from t1 and t2
+  uint32_t* exc;          // [hi2_rows] bitmap of the positions the fast path rounds differently
 };
 
 namespace wushkv {
@@ -53,7 +56,11 @@ struct KeysArgs {
   const int32_t* pos;
   int32_t max_pos;
   const void* T;   // swizzled bf16
-  const float2* cs;  // [max_pos][64] (cos, sin) table of the RoPE handle
+  const double2* rope_lo;   // [32][64] (cos, sin)(p0 * w): heads, then tails at rope_lot
+  const double2* rope_lot;
+  const double2* rope_hi;   // [ceil(max_pos / 32)][64] (cos, sin)(h * 32 * w): heads and tails
+  const double2* rope_hit;
+  const uint32_t* rope_exc;  // [ceil(max_pos / 32)] positions that take the double-double path
   uint8_t* codes;
   uint16_t* scales;
   uint16_t* zeros;
@@ -157,10 +164,12 @@ hipError_t launch_pair_queries(const PairArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t stream);
 size_t attention_workspace_bytes(int64_t n_seqs, int n_q_heads, int max_len);
 int attention_splits(int max_len);
-// Fills r->cs for every position below r->max_pos (exact: the certified
-// double path, double-double where it cannot certify).
-hipError_t launch_build_cs_table(const wushkv_rope* r, hipStream_t stream);
-// cs_out[n][64][2] = r->cs[clamp(pos[n])] (the table the key kernel reads).
+// Fills r->hi and r->hit (the (cos, sin) of h * 32 * w_i for h < r->hi2_rows as
+// double-double (head, tail) angle sums of the t2 and t1 entries), then the bitmap
+// r->exc of the positions whose fp64 fast sum rounds differently from the
+// double-double one for some pair.
+hipError_t launch_build_rope_hi(const wushkv_rope* r, hipStream_t stream);
+// cs_out[n][64][2] = the (cos, sin) the key kernel computes for clamp(pos[n]).
 hipError_t launch_gather_cs(const wushkv_rope* r, const int32_t* pos, int64_t n, float* cs_out,
                             hipStream_t stream);
 

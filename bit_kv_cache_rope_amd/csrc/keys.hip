@@ -19,18 +19,22 @@
 // their bf16 operands through LDS.  At under 128 VGPRs four waves are
 // resident per SIMD.
 //
-// cos/sin come from the RoPE handle's table (one 512-byte fp32 row per
-// position, exact): each wave loads a few of the next tile's rows into
-// registers and writes them to one of two LDS tile buffers before that tile's
-// RoPE phase (see the pipeline below).
+// cos/sin are computed in the kernel, exactly (fp32 roundings of cos and sin
+// of the exact angle): pos = 32 h + p0, the (cos, sin) of p0 * w_i come from a
+// 32-row fp64 table the block keeps in LDS, those of 32 h * w_i from an fp64
+// table row in global memory (L2-resident: one row serves 32 positions), and
+// one fp64 angle addition rounded to fp32 gives the pair, except at the rare
+// positions the RoPE handle has marked, which take a double-double sum.  The
+// block computes a tile's 64 x 64 pairs once for all its heads into one LDS
+// tile buffer.
 //
-// Per-tile pipeline, three barriers: [loads of the next tile's cos/sin rows
-// and cache rows, of the positions of the tile after; RoPE -> LDS; the next
-// tile's keys into the registers RoPE freed] B1 [MFMA; sums of squares ->
-// LDS; cos/sin rows -> LDS] B2 [scale(s), codes, records -> LDS; wait for the
-// loads older than the keys] B3 [stores] (one head per block: the cos/sin rows
-// are loaded in the MFMA phase and written after the codes, behind a wait for
-// every load).
+// Per-tile pipeline, three barriers: [stores of the previous tile; cache rows
+// and the positions of the tile after next; the high table entries for the
+// next tile; RoPE -> LDS; the next tile's keys into the registers RoPE freed]
+// B1 [(cos, sin) of the next tile; MFMA; sums of squares -> LDS] B2
+// [scale(s), codes, records -> LDS; wait for the loads older than the keys]
+// B3.  The next tile's (cos, sin) reach the tile buffer in the interval after
+// both groups have read the current tile's (see the schedule at the end).
 // Packed records and scales are staged in LDS and written as whole 16-byte
 // chunks (a head group's records of a token are contiguous in the cache row).
 #include "device_common.h"
@@ -45,6 +49,7 @@ namespace {
 constexpr int kTile = 64;      // tokens per tile
 constexpr int kNB = 2;         // 32-token MFMA column blocks per tile
 constexpr int kCsStride = 66;  // float2 per token row of the cos/sin tile (64 + 2 pad)
+constexpr int kRopeLo = 32;    // positions covered by the LDS (cos, sin) table
 constexpr int kXcds = 8;       // accelerator complex dies of an MI355X (blocks spread round-robin)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -145,12 +150,13 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   constexpr int NG = HG >= 2 ? 2 : 1;
   constexpr int HGG = HG / NG;      // heads per group
   constexpr int WG = 4 * HGG;       // waves per group
-  constexpr int RPG = kTile / NG;   // cos/sin rows each group loads per tile
+  constexpr int RPG = kTile / NG;   // cos/sin rows each group computes per tile
   constexpr int TPW = RPG / WG;     // ... each of its waves
-  constexpr int NCS = TPW / 2;      // ... two rows per load
+  constexpr int NCS = TPW / 2;      // ... in slots of two rows (lane halves) x two pairs
+  // slots whose high entries are loaded before RoPE (the 4-bit affine kernel keeps one: its
+  // registers are the scarcest)
+  constexpr int NPRE = NCS < 2 ? NCS : ((QK && BITS == 4) ? 1 : 2);
   constexpr int NKL = F32IN ? 8 : 4;  // key loads per lane per tile
-  static_assert(NG == 1 || NCS + NKL < 16, "vmcnt immediate");
-  constexpr int CSB = NG;           // cos/sin tile buffers (by tile parity when two groups)
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
   constexpr int RECROW = HGG * REC + 16;  // LDS row of one token's records in a group (+16 B pad)
@@ -158,7 +164,13 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   constexpr int RB = 4 * BITS;            // bits in a run of 4 codes
   constexpr int ESZ = F32IN ? 4 : 2;
 
-  __shared__ __align__(16) float2 cs_lds[CSB][kTile][kCsStride];  // cos/sin rows of a tile
+  // (cos, sin) of a tile: token row t, 16-byte chunk q (pairs 2q, 2q + 1) at chunk
+  // q ^ ((q >> 3) & 2), so that the eight chunk-loads of a row that one RoPE
+  // read instruction issues (chunks 4c + e, c < 8) fall in eight bank groups.
+  __shared__ __align__(16) float2 cs_lds[kTile][kCsStride];
+  // (cos, sin)(p0 * w_i) in fp64, pair j of row p0 at (j & 1) * 32 + j / 2: a lane's two
+  // pairs 2c, 2c + 1 sit at c and 32 + c, contiguous across the lanes.
+  __shared__ __align__(16) double2 lo_lds[kRopeLo][kPairs];
   __shared__ __align__(16) bf16x8 xb_lds[HG][kNB][8][64];        // rotated operands shared by a head's waves
   __shared__ int32_t slot_lds[2][kTile];  // cache row per token, -1: no store; tile j in slot j & 1
   __shared__ float red_lds[HG][4][kTile];
@@ -214,29 +226,51 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   auto keys_off = [&]() __attribute__((always_inline)) -> uint32_t {
     return (16 * wq + (lane >> 3)) * row_bytes + 8 * (lane & 7) * ESZ;
   };
-  // cos/sin rows: wave w of group g fills rows RPG*g + TPW*w .. + TPW - 1 of a
-  // tile buffer, two per 16-byte-per-lane load (lanes 0-31 one row, lanes
-  // 32-63 the next).  posv[i] is the position of row RPG*g + TPW*w + 2i + (l / 32)
-  // of a tile (0 past the end), csv[i] the matching half-row of the table.
+  // (cos, sin) slots: wave w of group g computes rows RPG*g + TPW*w .. + TPW - 1 of a
+  // tile; slot i is row RPG*g + TPW*w + 2i + (l / 32) and pairs 2 (l % 32), 2 (l % 32) + 1
+  // (one float4 of the row).  posv[i] is the position of slot i's row (0 past the end).
   auto load_pos = [&](int t, int* pv) __attribute__((always_inline)) {
     const rsrc_t rs = buffer_rsrc(a.pos + t * kTile, tile_len(t) * 4u);
 #pragma unroll
     for (int i = 0; i < NCS; ++i)
       pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (RPG * g + TPW * gw + 2 * i + lh), 0, 0);
   };
-  auto load_cs = [&](const int* pv, u32x4* cv) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NCS; ++i) {
-      const uint32_t p = (uint32_t)min(max(pv[i], 0), a.max_pos - 1);  // clamp to the table
-      cv[i] = *(const u32x4*)((const uint8_t*)(a.cs + 2 * col) + ((uint64_t)p << 9));  // 512-byte rows
+  auto clamp_pos = [&](int p) __attribute__((always_inline)) -> int { return min(max(p, 0), a.max_pos - 1); };
+  // A slot's high-table heads (32 contiguous bytes of row p / 32) and the word
+  // of the handle's bitmap that marks the positions of that row which take the
+  // double-double path.
+  struct HiSlot {
+    double2 h[2];
+    uint32_t exc;
+  };
+  auto hi_load = [&](int p, HiSlot& hv) __attribute__((always_inline)) {
+    const uint32_t row = (uint32_t)p >> 5;
+    const double2* src = a.rope_hi + row * (uint32_t)kPairs + 2 * col;
+    hv.h[0] = src[0];
+    hv.h[1] = src[1];
+    hv.exc = a.rope_exc[row];
+  };
+  // (cos, sin) of a slot: the high heads plus the angle of p % 32 from LDS
+  auto cs_slot = [&](int p, const HiSlot& hv) __attribute__((always_inline)) -> float4 {
+    const double2 B0 = lo_lds[p & 31][col], B1 = lo_lds[p & 31][32 + col];
+    float2 v0, v1;
+    if (__builtin_expect((hv.exc >> (p & 31)) & 1u, 0)) {  // a marked position: rare
+      const uint32_t hr = ((uint32_t)p >> 5) * (uint32_t)kPairs + 2 * col, lr = (uint32_t)(p & 31) * kPairs + 2 * col;
+      v0 = rope2_slow(hv.h[0], a.rope_hit[hr], B0, a.rope_lot[lr]);
+      v1 = rope2_slow(hv.h[1], a.rope_hit[hr + 1], B1, a.rope_lot[lr + 1]);
+    } else {
+      v0 = rope2_fast(hv.h[0], B0);
+      v1 = rope2_fast(hv.h[1], B1);
     }
+    return make_float4(v0.x, v0.y, v1.x, v1.y);
   };
-  auto store_cs = [&](const u32x4* cv, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NCS; ++i) *(u32x4*)&cs_lds[buf][RPG * g + TPW * gw + 2 * i + lh][2 * col] = cv[i];
+  auto cs_store = [&](int i, float4 v) __attribute__((always_inline)) {
+    *(float4*)&cs_lds[RPG * g + TPW * gw + 2 * i + lh][2 * (col ^ ((col >> 3) & 2))] = v;
   };
-  // Cache rows of tile t's tokens, loaded by wave 0 (lane = token): the raw
-  // slot words, turned into a row or -1 by row_of once they have arrived.
+  // Cache rows of tile t's tokens, loaded by the first wave of the last group
+  // (lane = token): the raw slot words, turned into a row or -1 by row_of once
+  // they have arrived.
+  const bool row_wave = wave_u == (NG - 1) * WG;
   auto load_rows = [&](int t) __attribute__((always_inline)) -> u32x2 {
     const rsrc_t rs = buffer_rsrc(a.slots + t * kTile, tile_len(t) * 8u);
     return __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, 0, 0);
@@ -248,12 +282,19 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   };
 
   RawKeys<F32IN> r;  // a tile's keys until RoPE has read them, then the next tile's
-  // Prologue: the first tile's keys, rows, positions and cos/sin; T~.
+  // Prologue: the (cos, sin) table of p0 < 32 into LDS; the first tile's keys, rows and
+  // positions; T~; the first tile's (cos, sin).  Every load is issued before the first
+  // wait on one.
+  constexpr int NLO = kRopeLo * kPairs / (256 * HG);  // lo-table entries per thread
+  double2 lov[NLO];
+#pragma unroll
+  for (int k = 0; k < NLO; ++k) lov[k] = a.rope_lo[threadIdx.x + 256 * HG * k];
   load_keys<F32IN>(r, keys_rsrc(first_tile), keys_off(), 8 * row_bytes);
   u32x2 row_w = {0u, 0u};  // read only when a.slots is set
-  int posv[NCS], posv_n[NCS];  // positions of the next tile's rows, then of the one after
-  u32x4 csv[NCS];
-  if (a.slots && wave_u == 0) row_w = load_rows(first_tile);
+  int posv[NCS], posv_n[NCS];  // positions of the next tile's slot rows, then of the one after
+  HiSlot hv[NPRE];             // high-table entries of the next tile's first NPRE slots
+  float4 csr[NCS];             // the next tile's (cos, sin) slots, held by group 0 until phase 2
+  if (a.slots && row_wave) row_w = load_rows(first_tile);
   load_pos(first_tile, posv);
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
   bf16x8 A[8];
@@ -262,13 +303,24 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) A[s] = Tp[(((int64_t)h * 4 + wq) * 8 + s) * 64 + lane];
   }
-  load_cs(posv, csv);
+  {
+    HiSlot h0[NCS];
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) hi_load(clamp_pos(posv[i]), h0[i]);
+#pragma unroll
+    for (int k = 0; k < NLO; ++k) {
+      const int e = threadIdx.x + 256 * HG * k, j = e & 63;  // entry (e / 64, j) of the table
+      lo_lds[e >> 6][(j & 1) * 32 + (j >> 1)] = lov[k];
+    }
+    __syncthreads();  // lo_lds
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) cs_store(i, cs_slot(clamp_pos(posv[i]), h0[i]));
+  }
   load_pos(tile_of(1), posv);
   // Nothing may be in flight when the loop starts: its first wait would
   // otherwise also cover the previous tile's stores on later iterations.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  store_cs(csv, 0);
-  if (wave_u == 0) slot_lds[0][lane] = row_of(row_w, first_tile);
+  if (row_wave) slot_lds[0][lane] = row_of(row_w, first_tile);
   __syncthreads();
 
   f32x16 acc[kNB];
@@ -277,10 +329,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // ---- phase 0 of the group's j-th tile: the stores of tile j - 1, then (for
   // j < count) the loads for later tiles, RoPE and the next tile's keys.
   auto phase0 = [&](int j) __attribute__((always_inline)) {
-    // Only this tile's keys can still be in flight (two groups: the phase-2
-    // wait leaves them); wait here, before the stores and loads below are
-    // issued, so that RoPE does not also wait for those.
-    if constexpr (NG == 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // Only this tile's keys can still be in flight (the phase-2 wait leaves
+    // them); wait here, before the stores and loads below are issued, so that
+    // RoPE does not also wait for those.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     if constexpr (!YOUT) {
       if (j >= 1) {
         const int sb = (j - 1) & 1;
@@ -331,21 +383,20 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     }
     if (j >= count) return;
     const int next = tile_of(j + 1);
-    // With two groups, each loads its half of the next tile's cos/sin rows
-    // here (its stores above are older, the loads below younger) and writes
-    // them to LDS at the end of its phase 1.
-    if (NG == 2) load_cs(posv, csv);
     // the next tile's cache rows and the positions of the tile after (zeros
-    // past the end)
-    if (a.slots && wave_u == 0) row_w = load_rows(next);
+    // past the end); the high-table entries of the next tile's first slots,
+    // issued before the next tile's keys so that waiting for them in phase 1
+    // leaves the keys in flight
+    if (a.slots && row_wave) row_w = load_rows(next);
     load_pos(tile_of(j + 2), posv_n);
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) hi_load(clamp_pos(posv[i]), hv[i]);
     // RoPE (rotate-half, pairs (i, i+64)) -> bf16 operands in LDS.
     // Chunk c = l % 8 of token t is channels 8c .. 8c+7 (k step c / 2, lane
     // half c % 2 of the B operand) and its partner chunk (k step 4 + c / 2).
     // B-operand rows are stored with lane index lane' ^ (4 (s % 4) + 2 (lane' / 32)),
     // which for this chunk is lane' ^ 2c: the eight chunks of a token land in
     // eight different bank groups, and each row stays a permutation of itself.
-    const int cb = j & (CSB - 1);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int c8 = lane & 7, gt = lane >> 3;
@@ -353,11 +404,12 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       float ka[8], kb[8];
       unpack8<F32IN>(r, jj, 0, ka);
       unpack8<F32IN>(r, jj, 1, kb);
-      const float4* csp = (const float4*)&cs_lds[cb][t][8 * c8];
+      const float4* csp = (const float4*)&cs_lds[t][8 * c8];
+      const int sw = (c8 >> 1) & 2;  // the row's chunk swizzle for chunks 4 c8 .. 4 c8 + 3
       float c[8], sn[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float4 v = csp[e];
+        const float4 v = csp[e ^ sw];
         c[2 * e] = v.x; sn[2 * e] = v.y; c[2 * e + 1] = v.z; sn[2 * e + 1] = v.w;
       }
       float xa[8], xb[8];
@@ -380,9 +432,30 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // ---- phase 1: y = T~ x~ for this wave's 32 rows and both column blocks,
   // then (symmetric) the sums of squares.
   auto phase1 = [&](int j) __attribute__((always_inline)) {
-    // one group: the next tile's cos/sin rows, into registers until phase 2
-    // ends (loaded here rather than in phase 0 so they are not live during RoPE)
-    if (NG == 1) load_cs(posv, csv);
+    // (cos, sin) of the next tile's slots.  Their high entries were loaded in
+    // phase 0 before the next tile's keys, so this wait leaves the keys in
+    // flight (slots beyond NPRE, with fewer than four waves per group, load
+    // theirs here).  Group 1 (and a single group) writes them to the tile
+    // buffer now, since every wave has read the current tile's in its phase 0;
+    // group 0 at the start of its phase 2, when group 1 has passed its phase 0.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NKL);  // vmcnt(NKL)
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) {
+      const int p = clamp_pos(posv[i]);
+      float4 v;
+      if (i < NPRE) {
+        v = cs_slot(p, hv[i < NPRE ? i : 0]);
+      } else {
+        HiSlot h2;
+        hi_load(p, h2);
+        v = cs_slot(p, h2);
+      }
+      if (NG == 1 || g == 1) {
+        cs_store(i, v);
+      } else {
+        csr[i] = v;
+      }
+    }
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = (f32x16){};
     // B operands one k step ahead of the MFMAs that use them; the scheduling
@@ -443,22 +516,22 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
       }
     }
-    if (NG == 2) {
-      // the cos/sin rows loaded in phase 0 have landed: only the younger
-      // cache-row, position and key loads (and, for the y output, its stores)
-      // may still be in flight
-      if constexpr (YOUT) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (NCS + NKL));  // vmcnt(NCS + NKL)
-      }
-      store_cs(csv, (j + 1) & 1);
+    if constexpr (YOUT) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the y stores
+    } else if (row_wave) {
+      // the next tile's cache rows: group 1's phase 1 (or a single group's)
+      // runs after every store that read this slot buffer's previous tile
+      slot_lds[(j + 1) & 1][lane] = row_of(row_w, tile_of(j + 1));
     }
   };
 
   // ---- phase 2: scales, codes and records of tile j -> LDS; then every load
   // has landed and (group 0) the next tile's cos/sin rows and cache rows go to LDS.
   auto phase2 = [&](int j) __attribute__((always_inline)) {
+    if (NG == 2 && g == 0) {
+#pragma unroll
+      for (int i = 0; i < NCS; ++i) cs_store(i, csr[i]);
+    }
     if constexpr (!YOUT) {
       // Output element acc[nb][i] is row 32*wq + 8*(i/4) + 4*lh + (i%4) of
       // token 32*nb + col.  run[nb][q] packs the codes of acc[nb][4q .. 4q+3]
@@ -490,17 +563,19 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
             // of the operand).  Code = [y > -step] + [y >= 0] + [y > step]:
             // the high bit is [y >= 0], the sign of y inverted (an MFMA result
             // that starts from a +0 accumulator is never -0); the low bit is
-            // [y > t] with t = +-step carrying y's sign, i.e. the sign of
-            // t - y, which is +0 (bit clear) exactly at a tie.  A zero step
-            // gives code 2 everywhere.
-            const uint32_t db = __float_as_uint(delta);
+            // [y > step] for y >= 0 and [y > -step] for y < 0, which is the
+            // sign of m = (step - |y|) * y + 0 (one fma): for |y| != step the
+            // signs of (step - |y|) and y decide it, and at a tie |y| = step
+            // (and at y = +0) the exact product is a zero, which the +0 makes
+            // +0 (bit clear, the even code).  Two fp32 operations, no integer
+            // select.  A zero step gives code 2 everywhere.
             uint32_t w = 0;
 #pragma unroll
             for (int i = 15; i >= 0; --i) {
               const float y = acc[nb][i];
-              const float t = __uint_as_float((__float_as_uint(y) & 0x80000000u) | db);
+              const float m = __builtin_fmaf(delta - __builtin_fabsf(y), y, 0.0f);
               w = __builtin_amdgcn_alignbit(w, __float_as_uint(y), 31);
-              w = __builtin_amdgcn_alignbit(w, __float_as_uint(t - y), 31);
+              w = __builtin_amdgcn_alignbit(w, __float_as_uint(m), 31);
             }
             W2[nb] = delta == 0.0f ? 0xAAAAAAAAu : w ^ 0xAAAAAAAAu;
           } else {
@@ -622,18 +697,12 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         }
       }
     }
-    // The cache rows and positions have landed.  With two groups the next
-    // tile's keys (the youngest loads) stay in flight until RoPE needs them;
-    // one group also waits for its cos/sin rows, loaded after the keys.
-    if constexpr (NG == 2 && !YOUT) {
+    // The positions have landed; the next tile's keys (the youngest loads)
+    // stay in flight until RoPE needs them.
+    if constexpr (!YOUT) {
       __builtin_amdgcn_s_waitcnt(0x0F70 | NKL);  // vmcnt(NKL), expcnt and lgkmcnt untouched
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    }
-    if (g == 0) {
-      const int next = tile_of(j + 1);
-      if (wave_u == 0) slot_lds[(j + 1) & 1][lane] = row_of(row_w, next);
-      if (NG == 1) store_cs(csv, 0);
     }
 #pragma unroll
     for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
@@ -645,10 +714,15 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   // group's waves run their MFMA phase the other group's waves, on the same
   // SIMDs, run VALU work.  Both groups pass the same number of barriers
   // (3 count + 2), and every barrier orders the LDS hand-offs within and
-  // between the groups: cos/sin tile j lives in buffer j % CSB from the end of
-  // each group's phase 1 of tile j - 1 until group 1's phase 0 of tile j (one
-  // group: from its phase 2 of tile j - 1 until its phase 0 of tile j), and the cache
-  // rows of tile j in slot_lds[j % 2] until group 1's stores of tile j.
+  // between the groups.  The intervals between barriers run (group 0, group 1)
+  // = (P0 j, P2 j-1), (P1 j, P0 j), (P2 j, P1 j), (P0 j+1, P2 j), ...: the
+  // (cos, sin) of tile j + 1 are written in the (P2 j, P1 j) interval, after
+  // both groups' phase 0 of tile j has read tile j's and before group 0's
+  // phase 0 of tile j + 1 reads them (one group: written in its phase 1 of
+  // tile j).  The cache rows of tile j + 1 go to slot_lds[(j + 1) % 2] in the
+  // same interval (group 1's phase 1 of tile j), after both groups' stores of
+  // tile j - 1 have read that buffer, and stay there until group 1's stores of
+  // tile j + 1.
   auto next_phase = [&]() __attribute__((always_inline)) {
     __syncthreads();
     asm volatile("" : "+v"(lane));
@@ -670,21 +744,47 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   if (NG == 2 && g == 0) next_phase();
 }
 
-// (cos, sin) of every position p < max_pos, pair i: entry p * 64 + i.
-__global__ void build_cs_table_kernel(RopeTables t, int64_t n, float2* cs) {
+// (cos, sin)(h * 32 * w_i) for h < n / 64 as double-double (head, tail): the
+// angle sum of t2[h / 32] and t1[h % 32].  Entry h * 64 + i.
+__global__ void build_rope_hi_kernel(RopeTables t, int64_t n, double2* hi, double2* hit) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
-  cs[idx] = rope_cos_sin((int)(idx / kPairs), (int)(idx % kPairs), t);
+  const int h = (int)(idx / kPairs), i = (int)(idx % kPairs);
+  const int a2 = (h >> 5) * kPairs + i, a1 = (h & 31) * kPairs + i;
+  const double2 A = t.t2[a2], At = t.t2t[a2], M = t.t1[a1], Mt = t.t1t[a1];
+  double ch, cl, sh, sl;
+  dd_pair(A.x, At.x, M.x, Mt.x, A.y, At.y, M.y, Mt.y, -1.0, ch, cl);  // cos(a + m)
+  dd_pair(A.y, At.y, M.x, Mt.x, A.x, At.x, M.y, Mt.y, 1.0, sh, sl);   // sin(a + m)
+  hi[idx] = make_double2(ch, sh);
+  hit[idx] = make_double2(cl, sl);
 }
 
-__global__ void gather_cs_kernel(const float2* table, int32_t max_pos, const int32_t* pos, int64_t n,
-                                 float2* out) {
+// Bit pos % 32 of exc[pos / 32]: does the fp64 fast sum of any pair of position
+// pos round differently from the double-double sum?  One thread per position,
+// 64-thread blocks (one wave: two bitmap words).
+__global__ void __launch_bounds__(64) build_rope_exc_kernel(Rope2Tables t, int32_t max_pos, uint32_t* exc) {
+  const int pos = blockIdx.x * 64 + threadIdx.x;
+  bool marked = false;
+  if (pos < max_pos) {
+    const int p0 = pos & 31, h = pos >> 5;
+    for (int i = 0; i < kPairs; ++i) {
+      const double2 H = t.hi[h * kPairs + i], B = t.lo[p0 * kPairs + i];
+      const float2 f = rope2_fast(H, B);
+      const float2 x = rope2_slow(H, t.hit[h * kPairs + i], B, t.lot[p0 * kPairs + i]);
+      marked |= __float_as_uint(f.x) != __float_as_uint(x.x) || __float_as_uint(f.y) != __float_as_uint(x.y);
+    }
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(marked);
+  if (pos < max_pos && (threadIdx.x & 31) == 0) exc[pos >> 5] = (uint32_t)(m >> (threadIdx.x & 32));
+}
+
+__global__ void gather_cs_kernel(Rope2Tables t, int32_t max_pos, const int32_t* pos, int64_t n, float2* out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n * kPairs) return;
   const int64_t k = idx / kPairs;
   int p = pos[k];
   p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
-  out[idx] = table[(int64_t)p * kPairs + (idx - k * kPairs)];
+  out[idx] = rope2_cos_sin(p, (int)(idx - k * kPairs), t);
 }
 
 // Persistent grid: as many blocks per head group as fit on the chip at once.
@@ -752,12 +852,16 @@ hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int hg, int y_ou
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_build_cs_table(const wushkv_rope* r, hipStream_t st) {
-  const int64_t total = (int64_t)r->max_pos * kPairs;
+hipError_t launch_build_rope_hi(const wushkv_rope* r, hipStream_t st) {
+  const int64_t total = (int64_t)r->hi2_rows * kPairs;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   const RopeTables t{r->t0, r->t1, r->t2, r->t0t, r->t1t, r->t2t};
-  build_cs_table_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(t, total, r->cs);
+  build_rope_hi_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(t, total, r->hi, r->hit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const Rope2Tables t2{r->t0, r->hi, r->t0t, r->hit, r->exc};
+  build_rope_exc_kernel<<<dim3((unsigned)((r->max_pos + 63) / 64)), 64, 0, st>>>(t2, r->max_pos, r->exc);
   return hipGetLastError();
 }
 
@@ -766,7 +870,8 @@ hipError_t launch_gather_cs(const wushkv_rope* r, const int32_t* pos, int64_t n,
   const int64_t total = n * kPairs;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
-  gather_cs_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(r->cs, r->max_pos, pos, n, (float2*)cs_out);
+  const Rope2Tables t{r->t0, r->hi, r->t0t, r->hit, r->exc};
+  gather_cs_kernel<<<dim3((unsigned)blocks), threads, 0, st>>>(t, r->max_pos, pos, n, (float2*)cs_out);
   return hipGetLastError();
 }
 

@@ -123,11 +123,14 @@ wushkv_status wushkv_transform_create(const float* T_host, int n_heads, wushkv_t
 wushkv_status wushkv_transform_destroy(wushkv_transform* t);
 
 /* RoPE handle for base theta and positions [0, max_pos), max_pos <= 2^24.
- * Computes the exact fp32 (cos, sin) of every position and pair once on the
- * current device (from fp64 split tables with extended-precision tails) and
- * keeps them as a [max_pos][64] table of fp32 pairs: 512 bytes per position,
- * 64 MiB at 2^17 positions, 8 GiB at 2^24.  The key kernel reads one row per
- * token.  Allocates device memory and synchronizes the device (not a
+ * Holds fp64 (cos, sin) tables with extended-precision tails: those of
+ * p0 * w_i for p0 < 32, and those of 32 h * w_i for every h < max_pos / 32
+ * (64 bytes per position: 8 MiB at 2^17 positions, 1 GiB at 2^24), and a
+ * bitmap of the positions whose fp64 angle sum rounds to fp32 differently from
+ * the exact value for some pair (found once, at creation, against a
+ * double-double sum).  The key kernel computes each token's exact fp32
+ * (cos, sin) from them: one fp64 angle addition, double-double at the marked
+ * positions.  Allocates device memory and synchronizes the device (not a
  * hot-path call). */
 wushkv_status wushkv_rope_create(float theta, int32_t max_pos, wushkv_rope** out);
 wushkv_status wushkv_rope_destroy(wushkv_rope* r);
@@ -228,7 +231,8 @@ wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, i
                                           float* y_out, void* stream);
 
 /* Test support: the (cos, sin) pairs the key kernel uses, cs_out[n][64][2]
- * fp32 (device), for device positions pos[n]. */
+ * fp32 (device), for device positions pos[n] (clamped to [0, max_pos)),
+ * computed by the same device function. */
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
                                         int64_t n, float* cs_out, void* stream);
 
