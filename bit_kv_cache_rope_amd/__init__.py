@@ -23,7 +23,8 @@ from ._lib import WushKVError, F32, BF16, Q_SYM_RMS, Q_AFFINE_PCT  # noqa: F401
 __all__ = [
     "WushKVError", "Quantizer", "sym", "affine", "Transform", "Rope", "PackedCache", "alloc_packed",
     "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize", "wushkv_debug_rope_transform",
-    "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch", "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
+    "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch", "wushkv_decode_attention_noalloc",
+    "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
     "prepare_quantize_values", "prepare_dequantize", "wushkv_pair_queries", "wushkv_decode_attention_workspace",
     "wushkv_decode_attention", "prepare_decode_attention",
 ]
@@ -351,6 +352,26 @@ def wushkv_decode_attention(q_paired: torch.Tensor, k_cache: PackedCache, v_cach
     args, _keep, out = _attention_args(q_paired, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0, seq_len,
                                        max_seq_len, scale, workspace, out, stream)
     _lib.check(library().wushkv_decode_attention(*args))
+    return out
+
+
+def wushkv_decode_attention_noalloc(q_paired: torch.Tensor, k_cache: PackedCache, v_cache: PackedCache,
+                                    n_kv_heads: int, bits: int, quantizer: Quantizer, seq_row0: torch.Tensor,
+                                    seq_len: torch.Tensor, max_seq_len: int, scale: float, out: torch.Tensor,
+                                    stream=None) -> torch.Tensor:
+    """Decode attention with the library's own scratch buffer (no workspace argument; the
+    call allocates nothing).  `out` (fp32 [n_seqs][n_q_heads][128]) is the caller's."""
+    if q_paired.dim() != 3 or q_paired.shape[2] != 128:
+        raise ValueError("q_paired must be [n_seqs][n_q_heads][128]")
+    for t, name, dt in ((q_paired, "q_paired", torch.bfloat16), (seq_row0, "seq_row0", torch.int64),
+                        (seq_len, "seq_len", torch.int32), (out, "out", torch.float32)):
+        _check_device_tensor(t, name, dt)
+    q, kp, vp_ = quantizer.c(), k_cache.c(), v_cache.c()
+    _lib.check(library().wushkv_decode_attention_noalloc(
+        ctypes.c_void_p(q_paired.data_ptr()), int(q_paired.shape[0]), int(q_paired.shape[1]), ctypes.byref(kp),
+        ctypes.byref(vp_), n_kv_heads, bits, ctypes.byref(q), ctypes.c_void_p(seq_row0.data_ptr()),
+        ctypes.c_void_p(seq_len.data_ptr()), max_seq_len, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
+        _stream(stream)))
     return out
 
 

@@ -9,6 +9,7 @@ LIB_PATH = os.environ.get("WUSHKV_LIB", os.path.join(HERE, "libwushkv.so"))
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_NO_DEVICE, ERR_HIP, ERR_OOM = range(7)
 F32, BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 24 << 20  # WUSHKV_NOALLOC_SCRATCH_BYTES
 Q_SYM_RMS, Q_AFFINE_PCT = 0, 1
 
 # every symbol include/wushkv.h declares
@@ -17,7 +18,7 @@ EXPORTED = [
     "wushkv_rope_frequencies", "wushkv_quantize_keys", "wushkv_quantize_values", "wushkv_dequantize",
     "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch",
     "wushkv_status_string", "wushkv_last_error", "wushkv_version", "wushkv_pair_queries",
-    "wushkv_decode_attention_workspace", "wushkv_decode_attention",
+    "wushkv_decode_attention_workspace", "wushkv_decode_attention", "wushkv_decode_attention_noalloc",
 ]
 
 
@@ -66,6 +67,7 @@ def load() -> ctypes.CDLL:
     L.wushkv_decode_attention_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.wushkv_decode_attention.argtypes = [vp, i32, i32, pp, pp, i32, i32, qp, vp, vp, i32, f32, vp,
                                           ctypes.c_size_t, vp, vp]
+    L.wushkv_decode_attention_noalloc.argtypes = [vp, i32, i32, pp, pp, i32, i32, qp, vp, vp, i32, f32, vp, vp]
     L.wushkv_status_string.argtypes = [i32]
     L.wushkv_status_string.restype = ctypes.c_char_p
     L.wushkv_last_error.argtypes = []

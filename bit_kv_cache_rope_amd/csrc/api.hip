@@ -560,12 +560,11 @@ wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n
   return WUSHKV_OK;
 }
 
-wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_heads,
-                                      const wushkv_packed* k_cache, const wushkv_packed* v_cache,
-                                      int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
-                                      const int64_t* seq_row0, const int32_t* seq_len, int max_seq_len,
-                                      float scale, void* workspace, size_t workspace_bytes, float* out,
-                                      void* stream) {
+static wushkv_status attention_common(const void* q_paired, int n_seqs, int n_q_heads,
+                                      const wushkv_packed* k_cache, const wushkv_packed* v_cache, int n_kv_heads,
+                                      int bits, const wushkv_quantizer* quantizer, const int64_t* seq_row0,
+                                      const int32_t* seq_len, int max_seq_len, float scale, bool own_scratch,
+                                      void* workspace, size_t workspace_bytes, float* out, void* stream) {
   wushkv_status st = attention_shape(n_seqs, n_q_heads, n_kv_heads, max_seq_len);
   if (st) return st;
   if (bits < 2 || bits > 4) return fail(WUSHKV_ERR_INVALID_ARG, "bits must be 2, 3 or 4");
@@ -585,9 +584,22 @@ wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_
   if (!aligned(q_paired, 2) || !aligned(seq_row0, 8) || !aligned(seq_len, 4) || !aligned(out, 4))
     return fail(WUSHKV_ERR_ALIGNMENT, "misaligned q_paired, seq_row0, seq_len or out");
   const size_t need = wushkv::attention_workspace_bytes(n_seqs, n_q_heads, max_seq_len);
-  if (workspace_bytes < need) return fail(WUSHKV_ERR_INVALID_ARG, "workspace smaller than wushkv_decode_attention_workspace");
-  if (need > 0 && (!workspace || !aligned(workspace, 16)))
-    return fail(workspace ? WUSHKV_ERR_ALIGNMENT : WUSHKV_ERR_INVALID_ARG, "workspace must be set and 16-byte aligned");
+  if (own_scratch) {
+    if (need > WUSHKV_NOALLOC_SCRATCH_BYTES)
+      return fail(WUSHKV_ERR_UNSUPPORTED, "split partials of " + std::to_string(need) +
+                                              " bytes exceed the library's scratch buffer of " +
+                                              std::to_string((size_t)WUSHKV_NOALLOC_SCRATCH_BYTES) + " bytes");
+    int dev;
+    st = current_device(&dev);
+    if (st) return st;
+    const hipError_t e = wushkv::attention_scratch(dev, &workspace);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (attention scratch)");
+  } else {
+    if (workspace_bytes < need)
+      return fail(WUSHKV_ERR_INVALID_ARG, "workspace smaller than wushkv_decode_attention_workspace");
+    if (need > 0 && (!workspace || !aligned(workspace, 16)))
+      return fail(workspace ? WUSHKV_ERR_ALIGNMENT : WUSHKV_ERR_INVALID_ARG, "workspace must be set and 16-byte aligned");
+  }
   wushkv::AttnArgs a{};
   a.qp = (const uint16_t*)q_paired;
   a.kc = (const uint8_t*)k_cache->codes;
@@ -612,6 +624,25 @@ wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_
   hipError_t e = wushkv::launch_attention(a, bits, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return WUSHKV_OK;
+}
+
+wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_heads,
+                                      const wushkv_packed* k_cache, const wushkv_packed* v_cache,
+                                      int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
+                                      const int64_t* seq_row0, const int32_t* seq_len, int max_seq_len,
+                                      float scale, void* workspace, size_t workspace_bytes, float* out,
+                                      void* stream) {
+  return attention_common(q_paired, n_seqs, n_q_heads, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0,
+                          seq_len, max_seq_len, scale, false, workspace, workspace_bytes, out, stream);
+}
+
+wushkv_status wushkv_decode_attention_noalloc(const void* q_paired, int n_seqs, int n_q_heads,
+                                              const wushkv_packed* k_cache, const wushkv_packed* v_cache,
+                                              int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
+                                              const int64_t* seq_row0, const int32_t* seq_len, int max_seq_len,
+                                              float scale, float* out, void* stream) {
+  return attention_common(q_paired, n_seqs, n_q_heads, k_cache, v_cache, n_kv_heads, bits, quantizer, seq_row0,
+                          seq_len, max_seq_len, scale, true, nullptr, 0, out, stream);
 }
 
 }  // extern "C"

@@ -34,6 +34,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <mutex>
+
 namespace wushkv {
 
 namespace {
@@ -780,6 +782,33 @@ hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t st) {
   }
   combine_kernel<<<dim3((unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(128), 0, st>>>(a);
   return hipGetLastError();
+}
+
+// Split partials of the calls that bring no workspace: a buffer of fixed size
+// that each GPU the library runs on holds until the process ends.  Host code
+// never uses the array's name as an address: attention_scratch() returns the
+// device address hipGetSymbolAddress reports for the current device, looked up
+// once per device.
+static __device__ __align__(256) float scratch[WUSHKV_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void* g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t attention_scratch(int device, void** ptr) {
+  *ptr = nullptr;
+  if (device < 0 || device >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[device] = p;
+  }
+  *ptr = g_scratch[device];
+  return hipSuccess;
 }
 
 size_t attention_workspace_bytes(int64_t n_seqs, int n_q_heads, int max_len) {

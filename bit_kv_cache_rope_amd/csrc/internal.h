@@ -163,6 +163,10 @@ hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, i
 hipError_t launch_pair_queries(const PairArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t stream);
 size_t attention_workspace_bytes(int64_t n_seqs, int n_q_heads, int max_len);
+// Device address of the library's fixed attention scratch buffer
+// (WUSHKV_NOALLOC_SCRATCH_BYTES) on `device`, which must be the current device;
+// looked up once per device.
+hipError_t attention_scratch(int device, void** ptr);
 int attention_splits(int max_len);
 // Fills r->hi and r->hit (the (cos, sin) of h * 32 * w_i for h < r->hi2_rows as
 // double-double (head, tail) angle sums of the t2 and t1 entries), then the bitmap

@@ -223,6 +223,27 @@ wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_
                                       float scale, void* workspace, size_t workspace_bytes, float* out,
                                       void* stream);
 
+/* Size of the library's own attention scratch buffer, per GPU. */
+#define WUSHKV_NOALLOC_SCRATCH_BYTES (24u << 20)
+
+/* Decode attention that allocates nothing, for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc.  Arguments, results and precision are those of
+ * wushkv_decode_attention, minus the workspace: the split partials go to a
+ * buffer of WUSHKV_NOALLOC_SCRATCH_BYTES that the library holds in static
+ * device memory on every GPU it runs on, until the process ends.  Calls whose
+ * partials need more (wushkv_decode_attention_workspace reports the bytes)
+ * return WUSHKV_ERR_UNSUPPORTED before launching anything.  Every call on one
+ * GPU shares that GPU's buffer, whose contents persist from the last call
+ * (each call writes every partial it reads, so nothing is cleared): calls that
+ * may overlap on one GPU (unordered streams) race and must be ordered by the
+ * caller.  The call issues no hipMalloc, hipFree or other allocation. */
+wushkv_status wushkv_decode_attention_noalloc(const void* q_paired, int n_seqs, int n_q_heads,
+                                              const wushkv_packed* k_cache, const wushkv_packed* v_cache,
+                                              int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
+                                              const int64_t* seq_row0, const int32_t* seq_len, int max_seq_len,
+                                              float scale, float* out, void* stream);
+
 /* Test support: the fp32 transformed keys y = T~ bf16(RoPE(K)) as the key
  * kernel computes them, written to y_out [n_tokens][n_heads][128] (device). */
 wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, int64_t n_tokens,
