@@ -415,83 +415,104 @@ def main() -> int:
     rk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in rd]))
     rv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in rd]))
 
-    # ---- decode append (64 sequences x 1 token, into 64 x 32768-row caches), reported alongside:
-    # a layer's K and V calls back to back on the two streams, and each kernel's own duration
+    # ---- decode append (64 sequences x 1 token per layer, into 64 x 32768-row caches through
+    # slots), reported alongside: the 36 layers each with their own K, V and T~ (the caches are
+    # shared); the fused K+V call (one kernel per layer) and, for comparison, the separate calls
     wd = synth.WORKLOADS["decode_append"]
     dn = wd.tokens
     drows = 64 * 32768
     dslots = torch.from_numpy(synth.slots(wd)).to(dev)
     dpos = torch.from_numpy(synth.positions(wd)).to(dev)
-    dK, dV = dev_bf16(synth.kv(wd, 0, "K")), dev_bf16(synth.kv(wd, 0, "V"))
-    dT, _ = synth.transform(wd, 0)
-    dtk = bk.Transform(dT)
     dkc = bk.alloc_packed(drows, H, bits, q, dev).with_slots(dslots)
     dvc = bk.alloc_packed(drows, H, bits, q, dev).with_slots(dslots)
-    dk = bk.prepare_quantize_keys(dK, dpos, rope, dtk, bits, q, dkc, stream=stream)
-    dv = bk.prepare_quantize_values(dV, bits, q, dvc, stream=vstream)
+    dlayers = [dict(K=dev_bf16(synth.kv(wd, layer, "K")), V=dev_bf16(synth.kv(wd, layer, "V")),
+                    tk=bk.Transform(synth.transform(wd, layer)[0])) for layer in range(wd.layers)]
+    fused = [bk.prepare_quantize_kv(L["K"], L["V"], dpos, rope, L["tk"], bits, q, dkc, dvc, stream=stream)
+             for L in dlayers]
+    sep = [(bk.prepare_quantize_keys(L["K"], dpos, rope, L["tk"], bits, q, dkc, stream=stream),
+            bk.prepare_quantize_values(L["V"], bits, q, dvc, stream=stream)) for L in dlayers]
     rep = 1 if args.light else 10  # repetition scale of the sections beside the throughput pass
-    for _ in range(20 * rep):
-        dk()
-        dv()
-    torch.cuda.synchronize()
-    n_dec = 36 * 2 * rep
-    t0 = time.perf_counter()
-    for _ in range(n_dec):
-        dk()
-        dv()
-    torch.cuda.synchronize()
-    dec_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
-    dev_ev = new_events(5 * rep, 4)
-    for e in dev_ev:
+
+    def host_rate(fns, n):
+        """Wall time per call of the calls `fns` issued back to back, n rounds."""
+        for _ in range(2):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (n * len(fns)) * 1e6
+
+    dec_fused_layer_us = host_rate(fused, 2 * rep)
+    dec_sep_layer_us = host_rate([lambda k=k, v=v: (k(), v()) for k, v in sep], 2 * rep)
+    # each kernel's own duration (events at its start and end), over the 36 layers
+    fev = new_events(wd.layers * rep, 2)
+    for i, e in enumerate(fev):
         bk.wushkv_debug_time_next_launch(e[0], e[1])
-        dk()
+        fused[i % wd.layers]()
+    sev = new_events(wd.layers * rep, 4)
+    for i, e in enumerate(sev):
+        k, v = sep[i % wd.layers]
+        bk.wushkv_debug_time_next_launch(e[0], e[1])
+        k()
         bk.wushkv_debug_time_next_launch(e[2], e[3])
-        bk.prepare_quantize_values(dV, bits, q, dvc, stream=stream)()
+        v()
     torch.cuda.synchronize()
-    dec_k_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
-    dec_v_us = float(np.mean([e[2].elapsed_time(e[3]) for e in dev_ev])) * 1e3
-    # 36 layers' decode K and V calls (one token per sequence) captured in one HIP graph and
-    # replayed: one launch per decode step for all layers (same inputs and caches for every
-    # layer here; each layer's kernels do the same work).  All on one stream (keys and values
-    # forked onto two streams and joined per layer inside the graph ran 423 against 319 us).
-    gst = torch.cuda.Stream()
-    gk = bk.prepare_quantize_keys(dK, dpos, rope, dtk, bits, q, dkc, stream=gst)
-    gv = bk.prepare_quantize_values(dV, bits, q, dvc, stream=gst)
-    gk()
-    gv()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=gst):
-        for _ in range(36):
-            gk()
-            gv()
-    for _ in range(2 * rep):
-        graph.replay()
-    torch.cuda.synchronize()
-    n_rep = 10 * rep
-    t0 = time.perf_counter()
-    for _ in range(n_rep):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_step_us = (time.perf_counter() - t0) / n_rep * 1e6
+    fk = np.array([e[0].elapsed_time(e[1]) for e in fev]) * 1e3
+    dec_fused_kernel_us = float(np.median(fk))
+    dec_k_us = float(np.median([e[0].elapsed_time(e[1]) for e in sev])) * 1e3
+    dec_v_us = float(np.median([e[2].elapsed_time(e[3]) for e in sev])) * 1e3
+
+    # one decode step as one HIP graph: the 36 layers' calls captured on one stream and replayed
+    # back to back (the layer inputs, 18 MB, stay in the caches across replays)
+    def graph_us(make):
+        """Wall time per replay of one graph of the calls make(stream) issues."""
+        gst = torch.cuda.Stream()
+        fns = make(gst)
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gst):
+            for f in fns:
+                f()
+        for _ in range(2 * rep):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10 * rep):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (10 * rep) * 1e6
+
+    def fused_calls(st):
+        return [bk.prepare_quantize_kv(L["K"], L["V"], dpos, rope, L["tk"], bits, q, dkc, dvc, stream=st)
+                for L in dlayers]
+
+    def separate_calls(st):
+        out = []
+        for L in dlayers:
+            out.append(bk.prepare_quantize_keys(L["K"], dpos, rope, L["tk"], bits, q, dkc, stream=st))
+            out.append(bk.prepare_quantize_values(L["V"], bits, q, dvc, stream=st))
+        return out
+
+    graph_step_us = graph_us(fused_calls)
+    graph_sep_us = graph_us(separate_calls)
     # 16-token chunks: 64 sequences append 16 consecutive positions each (1024 tokens per layer call)
     cbase = np.minimum(synth.positions(wd), 32768 - 16)
     cpos = torch.from_numpy((cbase[:, None] + np.arange(16)).reshape(-1).astype(np.int32)).to(dev)
     cslots = torch.from_numpy((np.arange(dn)[:, None] * 32768 + cbase[:, None] + np.arange(16)).reshape(-1)).to(dev)
     cK = dev_bf16(synth.kv(wd, 0, "K", 0, 16 * dn))
     cV = dev_bf16(synth.kv(wd, 0, "V", 0, 16 * dn))
-    ck = bk.prepare_quantize_keys(cK, cpos, rope, dtk, bits, q, dkc.with_slots(cslots), stream=stream)
-    cv = bk.prepare_quantize_values(cV, bits, q, dvc.with_slots(cslots), stream=vstream)
-    for _ in range(20 * rep):
-        ck()
-        cv()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(n_dec):
-        ck()
-        cv()
-    torch.cuda.synchronize()
-    chunk_layer_us = (time.perf_counter() - t0) / n_dec * 1e6
+    ckc, cvc = dkc.with_slots(cslots), dvc.with_slots(cslots)
+    cf = bk.prepare_quantize_kv(cK, cV, cpos, rope, dlayers[0]["tk"], bits, q, ckc, cvc, stream=stream)
+    ck = bk.prepare_quantize_keys(cK, cpos, rope, dlayers[0]["tk"], bits, q, ckc, stream=stream)
+    cv = bk.prepare_quantize_values(cV, bits, q, cvc, stream=stream)
+    chunk_layer_us = host_rate([cf], 36 * rep)
+    chunk_sep_layer_us = host_rate([lambda: (ck(), cv())], 36 * rep)
 
     # ---- one GPU's share under 8-way KV-head parallelism: the benchmark layer's tokens for a
     # single KV head (keys and values of 32768 tokens x 1 head, 18 MB), kernel-recorded events
@@ -651,13 +672,21 @@ def main() -> int:
             "out_dtype": "bf16",
         },
         "decode_append": {
-            "tokens_per_layer": dn, "cache_rows": drows, "layer_us": round(dec_layer_us, 2),
-            "keys_kernel_us": round(dec_k_us, 2), "values_kernel_us": round(dec_v_us, 2),
-            "note": "one layer's K and V calls back to back, keys and values on two streams",
+            "tokens_per_layer": dn, "layers": wd.layers, "cache_rows": drows,
+            "fused_kernel_us": round(dec_fused_kernel_us, 2),
+            "fused_kernel_us_p10_p90": [round(float(np.percentile(fk, 10)), 2), round(float(np.percentile(fk, 90)), 2)],
+            "fused_layer_call_us": round(dec_fused_layer_us, 2),
             "graph_36_layers_us": round(graph_step_us, 2),
-            "graph_note": "36 layers' K and V calls in one HIP graph on one stream, replayed back to back",
+            "graph_note": "one decode step: the 36 layers' fused K+V calls (one kernel each) in one HIP graph, "
+                          "replayed back to back",
+            "separate_keys_kernel_us": round(dec_k_us, 2), "separate_values_kernel_us": round(dec_v_us, 2),
+            "separate_layer_call_us": round(dec_sep_layer_us, 2),
+            "graph_36_layers_separate_us": round(graph_sep_us, 2),
             "chunk16_tokens_per_layer": 16 * dn, "chunk16_layer_us": round(chunk_layer_us, 2),
+            "chunk16_separate_layer_us": round(chunk_sep_layer_us, 2),
             "chunk16_tokens_per_s": round(16 * dn / (chunk_layer_us * 1e-6), 1),
+            "note": "per layer: 36 distinct layers (K, V, T~ each); layer_call_us are wall time per call "
+                    "issued back to back on one stream; kernel_us from events at the kernel's start and end",
         },
         "one_kv_head_share": {"tokens": N, "kv_heads": 1, "keys_us": round(h1_k_us, 2), "values_us": round(h1_v_us, 2),
                               "gbs": round(h1_bytes / ((h1_k_us + h1_v_us) * 1e-6) / 1e9, 1),

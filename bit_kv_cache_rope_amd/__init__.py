@@ -26,7 +26,7 @@ __all__ = [
     "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch", "wushkv_decode_attention_noalloc",
     "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
     "prepare_quantize_values", "prepare_dequantize", "wushkv_pair_queries", "wushkv_decode_attention_workspace",
-    "wushkv_decode_attention", "prepare_decode_attention",
+    "wushkv_decode_attention", "prepare_decode_attention", "wushkv_quantize_kv", "prepare_quantize_kv",
 ]
 
 
@@ -209,6 +209,29 @@ def wushkv_quantize_values(V: torch.Tensor, bits: int, quantizer: Quantizer, out
         _stream(stream)))
 
 
+def _kv_fused_args(K: torch.Tensor, V: torch.Tensor, pos: torch.Tensor, rope: Rope, T_k: Transform, bits: int,
+                   quantizer: Quantizer, k_out: PackedCache, v_out: PackedCache, stream):
+    dk, n, h, ks = _kv_args(K)
+    dv, nv, hv, vs = _kv_args(V)
+    if (dk, n, h) != (dv, nv, hv):
+        raise ValueError("K and V must have the same dtype, token count and head count")
+    _check_device_tensor(pos, "pos", torch.int32)
+    _check_device_tensor(k_out.slots, "slots", torch.int64)
+    _check_device_tensor(v_out.slots, "slots", torch.int64)
+    q, pk, pv = quantizer.c(), k_out.c(), v_out.c()
+    args = (ctypes.c_void_p(K.data_ptr()), ctypes.c_void_p(V.data_ptr()), dk, n, h, ks, vs,
+            ctypes.c_void_p(pos.data_ptr()), rope.handle, T_k.handle, bits, ctypes.byref(q), ctypes.byref(pk),
+            ctypes.byref(pv), _stream(stream))
+    return args, (K, V, pos, rope, T_k, q, pk, pv, k_out, v_out)
+
+
+def wushkv_quantize_kv(K: torch.Tensor, V: torch.Tensor, pos: torch.Tensor, rope: Rope, T_k: Transform, bits: int,
+                       quantizer: Quantizer, k_out: PackedCache, v_out: PackedCache, stream=None) -> None:
+    """Keys and values of the same tokens in one kernel (the append path)."""
+    args, _keep = _kv_fused_args(K, V, pos, rope, T_k, bits, quantizer, k_out, v_out, stream)
+    _lib.check(library().wushkv_quantize_kv(*args))
+
+
 def wushkv_dequantize(packed: PackedCache, n_tokens: int, n_heads: int, bits: int, quantizer: Quantizer,
                       T_k_inv: Transform | None = None, out: torch.Tensor | None = None,
                       out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
@@ -273,6 +296,12 @@ def prepare_quantize_values(V, bits: int, quantizer: Quantizer, out: PackedCache
     args = (ctypes.c_void_p(V.data_ptr()), dt, n, h, stride, bits, ctypes.byref(q), ctypes.byref(p),
             _stream(stream))
     return PreparedCall(library().wushkv_quantize_values, args, (V, q, p, out))
+
+
+def prepare_quantize_kv(K, V, pos, rope: Rope, T_k: Transform, bits: int, quantizer: Quantizer,
+                        k_out: PackedCache, v_out: PackedCache, stream=None) -> PreparedCall:
+    args, keep = _kv_fused_args(K, V, pos, rope, T_k, bits, quantizer, k_out, v_out, stream)
+    return PreparedCall(library().wushkv_quantize_kv, args, keep)
 
 
 def prepare_dequantize(packed: PackedCache, n_tokens: int, n_heads: int, bits: int, quantizer: Quantizer,

@@ -19,6 +19,7 @@ EXPORTED = [
     "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch",
     "wushkv_status_string", "wushkv_last_error", "wushkv_version", "wushkv_pair_queries",
     "wushkv_decode_attention_workspace", "wushkv_decode_attention", "wushkv_decode_attention_noalloc",
+    "wushkv_quantize_kv",
 ]
 
 
@@ -59,6 +60,7 @@ def load() -> ctypes.CDLL:
     L.wushkv_rope_frequencies.argtypes = [f32, vp]
     L.wushkv_quantize_keys.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, i32, qp, pp, vp]
     L.wushkv_quantize_values.argtypes = [vp, i32, i64, i32, i64, i32, qp, pp, vp]
+    L.wushkv_quantize_kv.argtypes = [vp, vp, i32, i64, i32, i64, i64, vp, vp, vp, i32, qp, pp, pp, vp]
     L.wushkv_dequantize.argtypes = [pp, i64, i32, i32, qp, vp, vp, i32, vp]
     L.wushkv_debug_rope_transform.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, vp, vp]
     L.wushkv_debug_rope_cos_sin.argtypes = [vp, vp, i64, vp, vp]

@@ -446,6 +446,66 @@ wushkv_status wushkv_quantize_values(const void* V, wushkv_dtype v_dtype, int64_
   return WUSHKV_OK;
 }
 
+wushkv_status wushkv_quantize_kv(const void* K, const void* V, wushkv_dtype dtype, int64_t n_tokens, int n_heads,
+                                 int64_t k_stride, int64_t v_stride, const int32_t* pos, const wushkv_rope* rope,
+                                 const wushkv_transform* T_k, int bits, const wushkv_quantizer* quantizer,
+                                 const wushkv_packed* k_out, const wushkv_packed* v_out, void* stream) {
+  wushkv_status st = check_tensor(K, dtype, n_tokens, n_heads, k_stride);
+  if (st) return st;
+  st = check_tensor(V, dtype, n_tokens, n_heads, v_stride);
+  if (st) return st;
+  if (!rope) return fail(WUSHKV_ERR_INVALID_ARG, "rope handle is NULL");
+  if (!T_k) return fail(WUSHKV_ERR_INVALID_ARG, "transform handle is NULL");
+  if (T_k->n_heads != n_heads) return fail(WUSHKV_ERR_INVALID_ARG, "transform has a different head count");
+  if (bits < 2 || bits > 4) return fail(WUSHKV_ERR_INVALID_ARG, "bits must be 2, 3 or 4");
+  wushkv::QuantArgs qa{};
+  st = make_quant(quantizer, &qa);
+  if (st) return st;
+  st = check_packed(k_out, qa.kind, n_tokens, true);
+  if (st) return st;
+  st = check_packed(v_out, qa.kind, n_tokens, true);
+  if (st) return st;
+  if (n_tokens == 0) return WUSHKV_OK;
+  if (!pos) return fail(WUSHKV_ERR_INVALID_ARG, "pos is NULL");
+  if (n_tokens * n_heads >= (1LL << 31))
+    return fail(WUSHKV_ERR_UNSUPPORTED, "the fused call needs n_tokens * n_heads < 2^31");
+  int dev;
+  st = current_device(&dev);
+  if (st) return st;
+  if (dev != T_k->device || dev != rope->device)
+    return fail(WUSHKV_ERR_INVALID_ARG, "handles belong to another device than the current one");
+  wushkv::AppendArgs a{};
+  a.K = K;
+  a.V = V;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.k_stride = k_stride;
+  a.v_stride = v_stride;
+  a.pos = pos;
+  a.max_pos = rope->max_pos;
+  a.T = T_k->d_swz;
+  a.rope_lo = rope->t0;
+  a.rope_lot = rope->t0t;
+  a.rope_hi = rope->hi;
+  a.rope_hit = rope->hit;
+  a.rope_exc = rope->exc;
+  a.k_codes = (uint8_t*)k_out->codes;
+  a.k_scales = (uint16_t*)k_out->scales;
+  a.k_zeros = (uint16_t*)k_out->zeros;
+  a.k_slots = k_out->slots;
+  a.k_rows = k_out->n_rows;
+  a.v_codes = (uint8_t*)v_out->codes;
+  a.v_scales = (uint16_t*)v_out->scales;
+  a.v_zeros = (uint16_t*)v_out->zeros;
+  a.v_slots = v_out->slots;
+  a.v_rows = v_out->n_rows;
+  a.q = qa;
+  hipError_t e = wushkv::launch_append(a, bits, dtype == WUSHKV_F32, wushkv::device_cu_count(dev),
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused key/value kernel launch");
+  return WUSHKV_OK;
+}
+
 wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n_heads, int bits,
                                 const wushkv_quantizer* quantizer, const wushkv_transform* T_k_inv, void* out,
                                 wushkv_dtype out_dtype, void* stream) {

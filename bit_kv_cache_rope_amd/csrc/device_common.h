@@ -24,6 +24,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// v_permlane32_swap of a value with itself: `lo` holds, in every lane l, the
+// value of lane l % 32, and `hi` the value of lane l % 32 + 32.
+struct Halves {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ Halves halves(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ Halves halves(float x) { return halves(__float_as_uint(x)); }
+
 // bf16 bit patterns -> fp32 (exact).
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -36,6 +47,34 @@ __device__ __forceinline__ uint16_t f16_sat_bits(float x) {
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// x / D correctly rounded (round-to-nearest-even) for D = 3, 7, 15: q0 = x * RN(1/D),
+// then one residual correction r = q0 D - x (exact in an fma) and q = q0 - r RN(1/D);
+// written this way round, x = -0 gives -0.  An infinite x makes r NaN; q0 is then
+// the quotient (and is NaN for a NaN x).  Five VALU operations in place of the
+// general division's scale/reciprocal/fixup sequence.  Agreement with x / D for
+// every fp32 x (subnormals, zeros, infinities and NaN included) is checked on the
+// CPU by tests/test_fast_division.py.
+template <int D>
+__device__ __forceinline__ float div_small(float x) {
+  static_assert(D == 3 || D == 7 || D == 15, "exactness is shown for 3, 7 and 15 only");
+  constexpr float y = 1.0f / (float)D;
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(q0, (float)D, -x);
+  const float q = __builtin_fmaf(-r, y, q0);
+  return q == q ? q : q0;
+}
+
+// Symmetric step from the sum of squares S of a 128-vector: rms = sqrt(S / 128)
+// (correctly rounded), C = alpha rms, step = RN16sat(2C / (L - 1)).
+template <int L>
+__device__ __forceinline__ uint16_t sym_step_f16(float S, float alpha) {
+  const float ms = S * 0.0078125f;  // S / 128, exact scaling
+  const float rms = __builtin_sqrtf(ms);
+  const float C = alpha * rms;
+  const float twoC = 2.0f * C;
+  return f16_sat_bits(div_small<L - 1>(twoC));
 }
 
 // Monotone map from IEEE totalOrder on floats to signed ints (an involution).
@@ -360,6 +399,24 @@ __device__ __forceinline__ float2 rope2_cos_sin(int pos, int i, const Rope2Table
   if (__builtin_expect(rope2_marked(t.exc, pos), 0))
     return rope2_slow(H, t.hit[h * kPairs + i], B, t.lot[p0 * kPairs + i]);
   return rope2_fast(H, B);
+}
+
+// (cos, sin) of pairs 2c and 2c + 1 at position pos, as (c0, s0, c1, s1), from the heads
+// H0, H1 of hi row pos / 32, B0, B1 of lo row pos % 32 and that hi row's bitmap word; a
+// marked position reads the tails from global memory and takes the double-double sum.
+__device__ __forceinline__ float4 rope2_pair_cs(int pos, int c, double2 H0, double2 H1, uint32_t exc_word,
+                                                double2 B0, double2 B1, const double2* hit, const double2* lot) {
+  float2 v0, v1;
+  if (__builtin_expect((exc_word >> (pos & 31)) & 1u, 0)) {  // a marked position: rare
+    const uint32_t hr = ((uint32_t)pos >> 5) * (uint32_t)kPairs + 2 * c;
+    const uint32_t lr = (uint32_t)(pos & 31) * kPairs + 2 * c;
+    v0 = rope2_slow(H0, hit[hr], B0, lot[lr]);
+    v1 = rope2_slow(H1, hit[hr + 1], B1, lot[lr + 1]);
+  } else {
+    v0 = rope2_fast(H0, B0);
+    v1 = rope2_fast(H1, B1);
+  }
+  return make_float4(v0.x, v0.y, v1.x, v1.y);
 }
 
 }  // namespace wushkv

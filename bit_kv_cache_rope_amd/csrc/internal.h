@@ -87,6 +87,34 @@ struct ValuesArgs {
   QuantArgs q;
 };
 
+// Keys and values of the same tokens in one dispatch (wushkv_quantize_kv).
+struct AppendArgs {
+  const void* K;
+  const void* V;
+  int64_t n_tokens;
+  int n_heads;
+  int64_t k_stride, v_stride;  // elements between tokens
+  const int32_t* pos;
+  int32_t max_pos;
+  const void* T;               // swizzled bf16
+  const double2* rope_lo;      // as in KeysArgs
+  const double2* rope_lot;
+  const double2* rope_hi;
+  const double2* rope_hit;
+  const uint32_t* rope_exc;
+  uint8_t* k_codes;
+  uint16_t* k_scales;
+  uint16_t* k_zeros;
+  const int64_t* k_slots;
+  int64_t k_rows;
+  uint8_t* v_codes;
+  uint16_t* v_scales;
+  uint16_t* v_zeros;
+  const int64_t* v_slots;
+  int64_t v_rows;
+  QuantArgs q;
+};
+
 struct DequantArgs {
   const uint8_t* codes;
   const uint16_t* scales;
@@ -159,6 +187,7 @@ hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, hipStream_t st,
 hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_group, int y_out, int cus,
                        hipStream_t stream);
 hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int cus, hipStream_t stream);
 hipError_t launch_pair_queries(const PairArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t stream);

@@ -39,8 +39,7 @@
 // chunks (a head group's records of a token are contiguous in the cache row).
 #include "device_common.h"
 #include "internal.h"
-
-#include <climits>
+#include "key_codes.h"
 
 namespace wushkv {
 
@@ -65,17 +64,6 @@ constexpr int kNT = 2;  // cache policy of the key loads: non-temporal (each byt
 __device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
 }
-
-// v_permlane32_swap of a value with itself: `lo` holds, in every lane l, the
-// value of lane l % 32, and `hi` the value of lane l % 32 + 32.
-struct Halves {
-  uint32_t lo, hi;
-};
-__device__ __forceinline__ Halves halves(uint32_t x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return {r[0], r[1]};
-}
-__device__ __forceinline__ Halves halves(float x) { return halves(__float_as_uint(x)); }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
@@ -161,7 +149,6 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   constexpr int REC = 16 * BITS;
   constexpr int RECROW = HGG * REC + 16;  // LDS row of one token's records in a group (+16 B pad)
   constexpr int NSC = QK ? 8 : 1;         // fp16 values per (token, head): sym 1; affine 4 + 4
-  constexpr int RB = 4 * BITS;            // bits in a run of 4 codes
   constexpr int ESZ = F32IN ? 4 : 2;
 
   // (cos, sin) of a tile: token row t, 16-byte chunk q (pairs 2q, 2q + 1) at chunk
@@ -252,17 +239,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   };
   // (cos, sin) of a slot: the high heads plus the angle of p % 32 from LDS
   auto cs_slot = [&](int p, const HiSlot& hv) __attribute__((always_inline)) -> float4 {
-    const double2 B0 = lo_lds[p & 31][col], B1 = lo_lds[p & 31][32 + col];
-    float2 v0, v1;
-    if (__builtin_expect((hv.exc >> (p & 31)) & 1u, 0)) {  // a marked position: rare
-      const uint32_t hr = ((uint32_t)p >> 5) * (uint32_t)kPairs + 2 * col, lr = (uint32_t)(p & 31) * kPairs + 2 * col;
-      v0 = rope2_slow(hv.h[0], a.rope_hit[hr], B0, a.rope_lot[lr]);
-      v1 = rope2_slow(hv.h[1], a.rope_hit[hr + 1], B1, a.rope_lot[lr + 1]);
-    } else {
-      v0 = rope2_fast(hv.h[0], B0);
-      v1 = rope2_fast(hv.h[1], B1);
-    }
-    return make_float4(v0.x, v0.y, v1.x, v1.y);
+    return rope2_pair_cs(p, col, hv.h[0], hv.h[1], hv.exc, lo_lds[p & 31][col], lo_lds[p & 31][32 + col],
+                         a.rope_hit, a.rope_lot);
   };
   auto cs_store = [&](int i, float4 v) __attribute__((always_inline)) {
     *(float4*)&cs_lds[RPG * g + TPW * gw + 2 * i + lh][2 * (col ^ ((col >> 3) & 2))] = v;
@@ -501,18 +479,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       // rows of this wave, then the four waves' sums ((0 + 1) + (2 + 3)).
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        float P8[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float q0 = acc[nb][4 * q] * acc[nb][4 * q];
-          const float q1 = acc[nb][4 * q + 1] * acc[nb][4 * q + 1];
-          const float q2 = acc[nb][4 * q + 2] * acc[nb][4 * q + 2];
-          const float q3 = acc[nb][4 * q + 3] * acc[nb][4 * q + 3];
-          const float p4 = (q0 + q1) + (q2 + q3);
-          const Halves x = halves(p4);
-          P8[q] = __uint_as_float(x.lo) + __uint_as_float(x.hi);
-        }
-        const float P32 = (P8[0] + P8[1]) + (P8[2] + P8[3]);
+        const float P32 = col_sumsq32(acc[nb]);
         if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
       }
     }
@@ -544,120 +511,25 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
         // value of lane half nb.
         const int tt = 32 * lh + col;
         const float S = (red_lds[hh][0][tt] + red_lds[hh][1][tt]) + (red_lds[hh][2][tt] + red_lds[hh][3][tt]);
-        const float ms = S * 0.0078125f;  // S / 128, exact scaling
-        const float rms = __builtin_sqrtf(ms);
-        const float C = a.q.alpha * rms;
-        const float twoC = 2.0f * C;
-        const float d32 = twoC / (float)(L - 1);
-        const uint16_t dh = f16_sat_bits(d32);
+        const uint16_t dh = sym_step_f16<L>(S, a.q.alpha);
         if (wq == 0) sc_lds[g][tt][hg] = dh;
         const Halves dd = halves(f16_bits_to_f32(dh));
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           const float delta = __uint_as_float(nb ? dd.hi : dd.lo);
-          // A zero step becomes +inf (threshold / step) so every code comes out L/2.
-          const float tp = delta == 0.0f ? __builtin_inff() : delta;
           if constexpr (BITS == 2) {
-            // W2[nb]: the lane's 16 codes of the block, run q (4 rows) in byte
-            // q, shifted in from the last row down (alignbit: w = 2w + bit 31
-            // of the operand).  Code = [y > -step] + [y >= 0] + [y > step]:
-            // the high bit is [y >= 0], the sign of y inverted (an MFMA result
-            // that starts from a +0 accumulator is never -0); the low bit is
-            // [y > step] for y >= 0 and [y > -step] for y < 0, which is the
-            // sign of m = (step - |y|) * y + 0 (one fma): for |y| != step the
-            // signs of (step - |y|) and y decide it, and at a tie |y| = step
-            // (and at y = +0) the exact product is a zero, which the +0 makes
-            // +0 (bit clear, the even code).  Two fp32 operations, no integer
-            // select.  A zero step gives code 2 everywhere.
-            uint32_t w = 0;
-#pragma unroll
-            for (int i = 15; i >= 0; --i) {
-              const float y = acc[nb][i];
-              const float m = __builtin_fmaf(delta - __builtin_fabsf(y), y, 0.0f);
-              w = __builtin_amdgcn_alignbit(w, __float_as_uint(y), 31);
-              w = __builtin_amdgcn_alignbit(w, __float_as_uint(m), 31);
-            }
-            W2[nb] = delta == 0.0f ? 0xAAAAAAAAu : w ^ 0xAAAAAAAAu;
+            W2[nb] = sym2_word(acc[nb], delta);
           } else {
-            const float rd = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
-            bool near = false;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint32_t rc = 0;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) rc |= sym_code_fast<BITS>(acc[nb][4 * q + e], rd, near) << (BITS * e);
-              run[nb][q] = rc;
-            }
-            near = near && rd != 0.0f;
-            // rare: a value within rounding error of a midpoint; exact codes for those lanes
-            if (__builtin_amdgcn_ballot_w64(near) != 0) {
-              if (near) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  uint32_t rc = 0;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) rc |= sym_code<BITS>(acc[nb][4 * q + e], tp, rd) << (BITS * e);
-                  asm("" : "+v"(rc));  // keep the word 32 bits wide (compare + add-with-carry codegen)
-                  run[nb][q] = rc;
-                }
-              }
-            }
+            sym_runs<BITS>(acc[nb], delta, run[nb]);
           }
         }
       } else {
         // Percentile-clipped affine quantizer, group = this wave's 32 rows of
-        // a token, split between lanes l and l^32: two smallest and two
-        // largest values by IEEE totalOrder, merged across the lane pair.
+        // a token (see affine_runs).
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-          int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int32_t k = total_order_key(acc[nb][i]);
-            mn2 = min(mn2, max(mn1, k));
-            mn1 = min(mn1, k);
-            mx2 = max(mx2, min(mx1, k));
-            mx1 = max(mx1, k);
-          }
-          const Halves n1 = halves((uint32_t)mn1), n2 = halves((uint32_t)mn2);
-          const Halves x1 = halves((uint32_t)mx1), x2 = halves((uint32_t)mx2);
-          const int32_t a1 = (int32_t)n1.lo, b1 = (int32_t)n1.hi, a2 = (int32_t)n2.lo, b2 = (int32_t)n2.hi;
-          const int32_t c1 = (int32_t)x1.lo, d1 = (int32_t)x1.hi, c2 = (int32_t)x2.lo, d2 = (int32_t)x2.hi;
-          const float s0 = total_order_value(min(a1, b1));
-          const float s1 = total_order_value(min(max(a1, b1), min(a2, b2)));
-          const float s31 = total_order_value(max(c1, d1));
-          const float s30 = total_order_value(max(min(c1, d1), max(c2, d2)));
-          const float lo = a.q.lo_mode ? s0 : __builtin_fmaf(a.q.g_lo, s1 - s0, s0);
-          const float hi = a.q.hi_mode == 0 ? __builtin_fmaf(a.q.g_hi, s31 - s30, s30)
-                                            : (a.q.hi_mode == 1 ? s30 : s31);
-          const float s32 = (hi - lo) / (float)(L - 1);
-          const uint16_t sh = f16_sat_bits(s32), zh = f16_sat_bits(lo);
-          const float s32h = f16_bits_to_f32(sh), z32h = f16_bits_to_f32(zh);
-          const float rs = s32h == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s32h);
-          bool near = false;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t rc = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rc |= affine_code_fast<BITS>(acc[nb][4 * q + e], z32h, rs, near) << (BITS * e);
-            run[nb][q] = rc;
-          }
-          // rare: a value within rounding error of a midpoint; exact codes for those lanes
-          if (__builtin_amdgcn_ballot_w64(near) != 0) {
-            if (near) {
-              const double sd = (double)s32h, zd = (double)z32h;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                uint32_t rc = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const uint32_t cd = sd == 0.0 ? 0u : affine_code<BITS>(acc[nb][4 * q + e], zd, sd);
-                  rc |= cd << (BITS * e);
-                }
-                run[nb][q] = rc;
-              }
-            }
-          }
+          uint16_t sh, zh;
+          affine_runs<BITS>(acc[nb], a.q, run[nb], sh, zh);
           if (lh == 0) {
             sc_lds[g][32 * nb + col][hg * 8 + wq] = sh;
             sc_lds[g][32 * nb + col][hg * 8 + 4 + wq] = zh;
@@ -672,28 +544,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
       for (int nb = 0; nb < kNB; ++nb) {
         uint8_t* dst = &rec_lds[g][32 * nb + col][hg * REC + BITS * (4 * wq + 2 * lh)];
         if constexpr (QK == 0 && BITS == 2) {
-          // bytes {lane half 0: selectors 0-3, lane half 1: 4-7}: lh = 0 takes
-          // bytes 0, 1 of both, lh = 1 bytes 2, 3
-          const Halves w = halves(W2[nb]);
-          *(uint32_t*)dst = __builtin_amdgcn_perm(w.hi, w.lo, lh ? 0x07030602u : 0x05010400u);
+          put_chunk<2>(dst, record_chunk2(W2[nb], lh));
         } else {
-          const uint32_t* rn = run[nb];
-          const uint32_t send = lh ? (rn[0] | (rn[1] << RB)) : (rn[2] | (rn[3] << RB));
-          const Halves w = halves(send);
-          const uint32_t recv = lh ? w.lo : w.hi;
-          const uint64_t p0 = recv & ((1u << RB) - 1u), p1 = recv >> RB;
-          const uint64_t chunk =
-              lh ? (p0 | ((uint64_t)rn[2] << RB) | (p1 << (2 * RB)) | ((uint64_t)rn[3] << (3 * RB)))
-                 : ((uint64_t)rn[0] | (p0 << RB) | ((uint64_t)rn[1] << (2 * RB)) | (p1 << (3 * RB)));
-          if constexpr (BITS == 2) {
-            *(uint32_t*)dst = (uint32_t)chunk;
-          } else if constexpr (BITS == 4) {
-            *(uint64_t*)dst = chunk;
-          } else {
-            ((uint16_t*)dst)[0] = (uint16_t)chunk;
-            ((uint16_t*)dst)[1] = (uint16_t)(chunk >> 16);
-            ((uint16_t*)dst)[2] = (uint16_t)(chunk >> 32);
-          }
+          put_chunk<BITS>(dst, record_chunk<BITS>(run[nb], lh));
         }
       }
     }

@@ -21,8 +21,7 @@
 // register sets); under 128 VGPRs four waves are resident per SIMD.
 #include "device_common.h"
 #include "internal.h"
-
-#include <climits>
+#include "value_codes.h"
 
 namespace wushkv {
 
@@ -131,17 +130,9 @@ values_kernel(const ValuesArgs a) {
     const bool has_next = it_next < n_iter;
     if (has_next) load_vals<F32IN, DENSE>(nxt, rnxt, a, it_next, wave, sub, l16);
 
-    auto unpack = [&](int u, float* x) __attribute__((always_inline)) {
-      if constexpr (F32IN) {
-        const u32x4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { x[e] = __uint_as_float(p[e]); x[4 + e] = __uint_as_float(q[e]); }
-      } else {
-        const u32x4 p = cur.v[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo_to_f32(p[e]); x[2 * e + 1] = bf16hi_to_f32(p[e]); }
-      }
-    };
+    // the raw words of vector slot u (one 16-byte group for bf16, two for fp32)
+    auto words = [&](int u) __attribute__((always_inline)) -> const u32x4* { return &cur.v[F32IN ? 2 * u : u]; };
+    auto unpack = [&](int u, float* x) __attribute__((always_inline)) { unpack_vals<F32IN>(words(u), x); };
     auto store_codes = [&](int vloc, uint32_t packed) __attribute__((always_inline)) {
       // this lane's 8 codes: BITS bytes at record offset BITS * l16
       uint8_t* dst = &rec_lds[par][vloc * REC + BITS * l16];
@@ -166,43 +157,18 @@ values_kernel(const ValuesArgs a) {
       //     across the 16 lanes of the vector.
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        float x[8], q[8];
+        float x[8];
         unpack(u, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = x[e] * x[e];
-        float P = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-        P = dpp_sum16(P);
+        const float P = dpp_sum16(lane_sumsq8(x));
         if (l16 == 0) ss_lds[wave][4 * u + sub] = P;
       }
       // (2) one lane per vector: step, fp16 scale and thresholds
       if (lane < kPerWave) {
         const float P = ss_lds[wave][lane];
-        const float ms = P * 0.0078125f;
-        const float rms = __builtin_sqrtf(ms);
-        const float C = a.q.alpha * rms;
-        const float twoC = 2.0f * C;
-        const float d32 = twoC / (float)(L - 1);
-        const uint16_t sc = f16_sat_bits(d32);
+        const uint16_t sc = sym_step_f16<L>(P, a.q.alpha);
         const float delta = f16_bits_to_f32(sc);
         sc_lds[par][wave * kPerWave + lane] = sc;
-        const float tp = delta == 0.0f ? __builtin_inff() : delta;  // +inf for a zero step
-        float4 th;
-        if constexpr (BITS == 2) {
-          // Midpoint tests A = [x > -step], B = [x >= 0], C = [x > step]
-          // (ties as in the nearest-level rule).  bf16 input: A and C are
-          // decided on the raw word (bf16_gt_threshold), B as an unsigned
-          // bound (x >= 0 or x = -0); a zero step makes A and B always true
-          // and C never: code 2.
-          th.x = F32IN ? -tp : bf16_gt_threshold(-tp);
-          th.y = F32IN ? tp : bf16_gt_threshold(tp);
-          th.z = __uint_as_float(delta == 0.0f ? 0xFFFFFFFFu : (F32IN ? 0x80000000u : 0x8000FFFFu));
-          th.w = 0.0f;
-        } else {
-          // the step itself (+inf for a zero step, whose reciprocal 0 then yields code L/2)
-          th.x = tp;
-          th.y = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
-          th.z = th.w = 0.0f;
-        }
+        const float4 th = value_thresholds<BITS, F32IN>(delta);
         th_lds[wave][lane] = th;
       }
       // (3) codes
@@ -210,49 +176,11 @@ values_kernel(const ValuesArgs a) {
       for (int u = 0; u < kU; ++u) {
         const float4 th = th_lds[wave][4 * u + sub];
         if constexpr (BITS == 2) {
-          // the 8 words to test, channel order: bf16 -> low halves shifted up,
-          // high halves raw; fp32 -> the values' bits
-          uint32_t w[8];
-          if constexpr (F32IN) {
-            const u32x4 p = cur.v[2 * u], q = cur.v[2 * u + 1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { w[e] = p[e]; w[4 + e] = q[e]; }
-          } else {
-            const u32x4 p = cur.v[u];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { w[2 * e] = p[e] << 16; w[2 * e + 1] = p[e]; }
-          }
-          const uint32_t tb = __float_as_uint(th.z);
-          const uint32_t tbl = F32IN ? tb : (tb & 0xFFFF0000u);  // low halves are exact
-          uint64_t m[16];
-#pragma unroll
-          for (int e = 7; e >= 0; --e) {
-            const Sym2Masks k = sym2_masks_raw(w[e], th.x, (e & 1) ? tb : tbl, th.y);
-            m[2 * (7 - e)] = k.b1;
-            m[2 * (7 - e) + 1] = k.b0;
-          }
-          uint32_t packed = shift_in8(0u, m);
-          packed = shift_in8(packed, m + 8);
-          store_codes(wave * kPerWave + 4 * u + sub, packed);
+          store_codes(wave * kPerWave + 4 * u + sub, value_codes2<F32IN>(words(u), th));
         } else {
           float x[8];
           unpack(u, x);
-          uint32_t packed = 0;
-          bool near = false;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) packed |= sym_code_fast<BITS>(x[e], th.y, near) << (BITS * e);
-          near = near && th.y != 0.0f;
-          // rare: a value within rounding error of a midpoint; exact codes for those lanes
-          if (__builtin_amdgcn_ballot_w64(near) != 0) {
-            if (near) {
-              packed = 0;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) packed |= sym_code<BITS>(x[e], th.x, th.y) << (BITS * e);
-              // keep the word 32 bits wide so code counts compile to compare + add-with-carry
-              asm("" : "+v"(packed));
-            }
-          }
-          store_codes(wave * kPerWave + 4 * u + sub, packed);
+          store_codes(wave * kPerWave + 4 * u + sub, value_codes_sym<BITS>(x, th));
         }
       }
     } else {
@@ -261,50 +189,8 @@ values_kernel(const ValuesArgs a) {
         const int vloc = wave * kPerWave + 4 * u + sub;
         float x[8];
         unpack(u, x);
-        uint32_t packed = 0;
-        // group of 32 channels = 4 lanes: two extremes at each end, merged by xor 1, 2
-        int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int32_t k = total_order_key(x[e]);
-          mn2 = min(mn2, max(mn1, k));
-          mn1 = min(mn1, k);
-          mx2 = max(mx2, min(mx1, k));
-          mx1 = max(mx1, k);
-        }
-#pragma unroll
-        for (int off = 1; off <= 2; off <<= 1) {
-          const int32_t o1 = __shfl_xor(mn1, off), o2 = __shfl_xor(mn2, off);
-          const int32_t u1 = __shfl_xor(mx1, off), u2 = __shfl_xor(mx2, off);
-          mn2 = min(max(mn1, o1), min(mn2, o2));
-          mn1 = min(mn1, o1);
-          mx2 = max(min(mx1, u1), max(mx2, u2));
-          mx1 = max(mx1, u1);
-        }
-        const float s0 = total_order_value(mn1), s1 = total_order_value(mn2);
-        const float s31 = total_order_value(mx1), s30 = total_order_value(mx2);
-        const float lo = a.q.lo_mode ? s0 : __builtin_fmaf(a.q.g_lo, s1 - s0, s0);
-        const float hi = a.q.hi_mode == 0 ? __builtin_fmaf(a.q.g_hi, s31 - s30, s30)
-                                          : (a.q.hi_mode == 1 ? s30 : s31);
-        const float s32 = (hi - lo) / (float)(L - 1);
-        const uint16_t sh = f16_sat_bits(s32), zh = f16_sat_bits(lo);
-        const float s32h = f16_bits_to_f32(sh), z32h = f16_bits_to_f32(zh);
-        const float rs = s32h == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s32h);
-        bool near = false;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) packed |= affine_code_fast<BITS>(x[e], z32h, rs, near) << (BITS * e);
-        // rare: a value within rounding error of a midpoint; exact codes for those lanes
-        if (__builtin_amdgcn_ballot_w64(near) != 0) {
-          if (near) {
-            const double sd = (double)s32h, zd = (double)z32h;
-            packed = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t c = sd == 0.0 ? 0u : affine_code<BITS>(x[e], zd, sd);
-              packed |= c << (BITS * e);
-            }
-          }
-        }
+        uint16_t sh, zh;
+        const uint32_t packed = value_codes_affine<BITS>(x, a.q, sh, zh);
         if ((l16 & 3) == 0) {
           sc_lds[par][vloc * 4 + (l16 >> 2)] = sh;
           zr_lds[par][vloc * 4 + (l16 >> 2)] = zh;

@@ -158,6 +158,26 @@ wushkv_status wushkv_quantize_values(const void* V, wushkv_dtype v_dtype, int64_
                                      const wushkv_quantizer* quantizer, const wushkv_packed* out,
                                      void* stream);
 
+/* Keys and values of the same tokens in one dispatch: the append path of a
+ * paged cache, built for small calls (one decode step's tokens, one per
+ * sequence, or a 16-token chunk: ai4snews summary "WUSH-KV cuts 2-bit KV-cache
+ * perplexity ...", experiments paragraph on 16-token chunks and deployment
+ * paragraph on paged caches).  Computes exactly what wushkv_quantize_keys on K
+ * and wushkv_quantize_values on V compute (the same bytes in both caches), with
+ * one kernel instead of two; for long prefills those two calls are faster.
+ *   K, V: device, both of `dtype`, layouts as for the single calls, with their
+ *      own token strides.
+ *   pos, rope, T_k, bits, quantizer: as for wushkv_quantize_keys; the one
+ *      quantizer applies to keys and values.
+ *   k_out, v_out: the key and value caches (each with its own slots and
+ *      n_rows); their memory must not overlap.
+ *   n_tokens * n_heads must stay below 2^31 (WUSHKV_ERR_UNSUPPORTED otherwise);
+ *   n_tokens == 0 is a no-op. */
+wushkv_status wushkv_quantize_kv(const void* K, const void* V, wushkv_dtype dtype, int64_t n_tokens, int n_heads,
+                                 int64_t k_stride, int64_t v_stride, const int32_t* pos, const wushkv_rope* rope,
+                                 const wushkv_transform* T_k, int bits, const wushkv_quantizer* quantizer,
+                                 const wushkv_packed* k_out, const wushkv_packed* v_out, void* stream);
+
 /* Read path: rows in->slots[n] (or n) for n < n_tokens are unpacked and
  * dequantized into out[n_tokens][n_heads][128] (fp32 or bf16, contiguous,
  * 16-byte aligned).  T_k_inv: NULL for values (or for keys kept in the
@@ -257,7 +277,7 @@ wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, i
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
                                         int64_t n, float* cs_out, void* stream);
 
-/* Timing support: the next wushkv_quantize_keys, wushkv_quantize_values,
+/* Timing support: the next wushkv_quantize_keys, wushkv_quantize_values, wushkv_quantize_kv,
  * wushkv_dequantize, wushkv_pair_queries or wushkv_decode_attention call
  * (its first kernel) on this host thread records `start` (a hipEvent_t)
  * when its kernel starts and `stop` when it ends (hipExtLaunchKernel), so

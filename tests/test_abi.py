@@ -105,6 +105,15 @@ def test_validation_without_device(lib):
     # keys: NULL handles
     assert L.wushkv_quantize_keys(vp(16), 1, 4, 2, 256, vp(16), None, None, 2, ctypes.byref(q),
                                   ctypes.byref(p), None) == _lib.ERR_INVALID_ARG
+    # fused keys + values: both tensors are checked, then the handles
+    kv = lambda K=vp(16), V=vp(16), dt=1, ks=256, vs=256, rope=None, T=None: L.wushkv_quantize_kv(
+        K, V, dt, 4, 2, ks, vs, vp(16), rope, T, 2, ctypes.byref(q), ctypes.byref(p), ctypes.byref(p), None)
+    assert kv(dt=7) == _lib.ERR_INVALID_ARG
+    assert kv(V=vp(8)) == _lib.ERR_ALIGNMENT
+    assert kv(vs=260) == _lib.ERR_ALIGNMENT
+    assert kv(ks=200) == _lib.ERR_INVALID_ARG
+    assert kv(V=None) == _lib.ERR_INVALID_ARG
+    assert kv() == _lib.ERR_INVALID_ARG  # NULL rope and transform handles
     # read path
     assert L.wushkv_dequantize(ctypes.byref(p), 4, 2, 9, ctypes.byref(q), None, vp(16), 1, None) == _lib.ERR_INVALID_ARG
     assert L.wushkv_dequantize(ctypes.byref(p), 4, 2, 2, ctypes.byref(q), None, vp(16), 3, None) == _lib.ERR_INVALID_ARG
