@@ -46,7 +46,7 @@ MALL_BYTES = 256 << 20
 D = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "keys_qwen3_8b_prefill_traffic.md")
 KEY_KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_rope_amd", "csrc", f)
-                      for f in ("keys.hip", "device_common.h")]
+                      for f in ("keys.hip", "key_codes.h", "device_common.h")]
 
 
 def key_bytes_per_token(H: int, bits: int) -> int:
@@ -277,6 +277,64 @@ def other_workloads(torch, synth, bk, dev, stream, rope, light=False) -> dict:
     return res
 
 
+def kernel_label(name: str) -> str:
+    """Short kernel name: namespaces and the argument list dropped, template arguments kept."""
+    name = name.replace("void ", "").replace("wushkv::(anonymous namespace)::", "").replace("wushkv::", "")
+    return re.sub(r"\((?:[^()]|\([^()]*\))*\)$", "", name).strip()
+
+
+def summarize_pmc(dirs, pattern: str) -> str:
+    """Markdown table of rocprofv3 counter collections (one directory per --pmc pass,
+    each holding run_counter_collection.csv): per kernel and grid size, the mean of
+    each counter over its dispatches."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    counters = []
+    for d in dirs:
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                k = (kernel_label(r["Kernel_Name"]), int(r["Grid_Size"]))
+                if not re.search(pattern, k[0]):
+                    continue
+                c = r["Counter_Name"]
+                if c not in counters:
+                    counters.append(c)
+                acc[k][c].append(float(r["Counter_Value"]))
+    lines = ["| kernel | grid | dispatches | " + " | ".join(counters) + " |",
+             "|---|---|---|" + "---|" * len(counters)]
+    for (name, grid), m in sorted(acc.items()):
+        n = max(len(v) for v in m.values())
+        vals = [f"{np.mean(m[c]):.4g}" if c in m else "" for c in counters]
+        lines.append(f"| {name} | {grid} | {n} | " + " | ".join(vals) + " |")
+    return "\n".join(lines)
+
+
+def summarize_trace(d: str, pattern: str, part: str | None = None) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace run (run_kernel_trace.csv): per kernel
+    and grid size, the number of dispatches and their mean, min and max duration.
+    `part` = "a:b" keeps dispatches a .. b-1 of each kernel and grid in start order."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    with open(os.path.join(d, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            name = kernel_label(r["Kernel_Name"])
+            if re.search(pattern, name):
+                acc[(name, int(r["Grid_Size_X"]))].append(
+                    (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    lines = ["| kernel | grid | calls | average us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (name, grid), sv in sorted(acc.items()):
+        v = [x[1] for x in sorted(sv)]
+        if part:
+            a, b = (int(x) if x else None for x in part.split(":"))
+            v = v[a:b]
+        if not v:
+            continue
+        lines.append(f"| {name} | {grid} | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +349,21 @@ def main() -> int:
                     help="also report the attention-output error of the quantized cache per key transform")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print a table of rocprofv3 --pmc output directories and exit (no GPU)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a table of a rocprofv3 --kernel-trace output directory and exit (no GPU)")
+    ap.add_argument("--trace-slice", metavar="A:B",
+                    help="with --summarize-trace: dispatches A .. B-1 of each kernel, in start order")
+    ap.add_argument("--kernels", default=".",
+                    help="regular expression selecting the kernels the summaries list")
     args = ap.parse_args()
+    if args.summarize_pmc or args.summarize_trace:
+        if args.summarize_pmc:
+            print(summarize_pmc(args.summarize_pmc, args.kernels))
+        if args.summarize_trace:
+            print(summarize_trace(args.summarize_trace, args.kernels, args.trace_slice))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the cache write path shards by KV head, token range or layer "
               "with no exchange between GPUs; bench.py times one MI355X only.", file=sys.stderr)

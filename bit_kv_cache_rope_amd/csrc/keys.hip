@@ -260,20 +260,22 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   };
 
   RawKeys<F32IN> r;  // a tile's keys until RoPE has read them, then the next tile's
-  // Prologue: the (cos, sin) table of p0 < 32 into LDS; the first tile's keys, rows and
-  // positions; T~; the first tile's (cos, sin).  Every load is issued before the first
-  // wait on one.
+  // Prologue: the positions of the first two tiles (first: the one dependent chain,
+  // position -> high-table entries, starts from them, and the second tile's are in by
+  // the time the loop starts); the (cos, sin) table of p0 < 32 into LDS; the first
+  // tile's keys and rows; T~; the first tile's (cos, sin).
+  int posv[NCS], posv_n[NCS];  // positions of the next tile's slot rows, then of the one after
+  load_pos(first_tile, posv);
+  load_pos(tile_of(1), posv_n);
   constexpr int NLO = kRopeLo * kPairs / (256 * HG);  // lo-table entries per thread
   double2 lov[NLO];
 #pragma unroll
   for (int k = 0; k < NLO; ++k) lov[k] = a.rope_lo[threadIdx.x + 256 * HG * k];
   load_keys<F32IN>(r, keys_rsrc(first_tile), keys_off(), 8 * row_bytes);
   u32x2 row_w = {0u, 0u};  // read only when a.slots is set
-  int posv[NCS], posv_n[NCS];  // positions of the next tile's slot rows, then of the one after
   HiSlot hv[NPRE];             // high-table entries of the next tile's first NPRE slots
   float4 csr[NCS];             // the next tile's (cos, sin) slots, held by group 0 until phase 2
   if (a.slots && row_wave) row_w = load_rows(first_tile);
-  load_pos(first_tile, posv);
   // This wave's quarter of T~ as MFMA A operands: rows 32 wq + (lane % 32).
   bf16x8 A[8];
   {
@@ -294,7 +296,8 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
     for (int i = 0; i < NCS; ++i) cs_store(i, cs_slot(clamp_pos(posv[i]), h0[i]));
   }
-  load_pos(tile_of(1), posv);
+#pragma unroll
+  for (int i = 0; i < NCS; ++i) posv[i] = posv_n[i];
   // Nothing may be in flight when the loop starts: its first wait would
   // otherwise also cover the previous tile's stores on later iterations.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
