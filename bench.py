@@ -145,62 +145,6 @@ def cpu_baseline(w, synth, seconds_hint: float = 6.0) -> dict:
             "other_workloads_single_thread": slices}
 
 
-def quality_report(torch, synth, bk, dev, layers=4, n_tok=4096, n_q=64, q_scale=0.4, bits=2) -> dict:
-    """Attention-output error of the quantized cache, per transform: identity,
-    Hadamard / 8 and the workload's T_k (keys through the transform and paired
-    queries, values plain, 2-bit symmetric) against fp32 attention over the
-    unquantized bf16 keys after RoPE and bf16 values, on synthetic
-    Qwen3-8B-shaped layers.  Error = |o - o_ref|^2 / |o_ref|^2 per layer
-    (all query heads), geometric mean over the layers.  Queries are N(0, 1) x
-    q_scale: 0.4 puts the scores' spread at about 2 (a softmax that is neither
-    flat nor one-hot on these keys)."""
-    w = synth.WORKLOADS["qwen3_8b_prefill"]
-    H, G = w.heads, 4
-    q = bk.sym(w.clip_alpha)
-    rope = bk.Rope(w.theta, 1 << 17)
-    Hd = np.array([[1.0]])
-    while Hd.shape[0] < D:
-        Hd = np.block([[Hd, Hd], [Hd, -Hd]])
-    eye = bk.Transform(np.stack([np.eye(D, dtype=np.float32)] * H))
-    pos = torch.from_numpy(synth.positions(w, 0, n_tok)).to(dev)
-    errs = {"identity": [], "hadamard": [], "T_k": []}
-    for layer in range(layers):
-        K = torch.from_numpy(synth.kv(w, layer, "K", 0, n_tok).view(np.int16)).to(dev).view(torch.bfloat16)
-        V = torch.from_numpy(synth.kv(w, layer, "V", 0, n_tok).view(np.int16)).to(dev).view(torch.bfloat16)
-        X = bk.wushkv_debug_rope_transform(K, pos, rope, eye)  # bf16(RoPE(k)), exact in fp32
-        T, Ti = synth.transform(w, layer)
-        g = torch.Generator(device=dev)
-        g.manual_seed(1000 + layer)
-        Q = torch.randn((n_q, H * G, D), device=dev, generator=g) * q_scale
-        Qb = Q.to(torch.bfloat16)
-        scale = 1.0 / np.sqrt(D)
-        # fp32 reference: query head hq reads KV head hq // G
-        Xh = X.permute(1, 0, 2).contiguous()                  # [H][N][128]
-        Vh = V.float().permute(1, 0, 2).contiguous()          # [H][N][128]
-        Qh = Qb.float().view(n_q, H, G, D).permute(1, 0, 2, 3).reshape(H, n_q * G, D).contiguous()
-        sc = torch.matmul(Qh, Xh.transpose(1, 2).contiguous()) * scale
-        ref = torch.matmul(torch.softmax(sc, dim=-1), Vh)      # [H][n_q G][128]
-        ref = ref.view(H, n_q, G, D).permute(1, 0, 2, 3).reshape(n_q, H * G, D)
-        vc = bk.alloc_packed(n_tok, H, bits, q, dev)
-        bk.wushkv_quantize_values(V, bits, q, vc)
-        row0 = torch.zeros(n_q, dtype=torch.int64, device=dev)
-        lens = torch.full((n_q,), n_tok, dtype=torch.int32, device=dev)
-        for name, (Tm, Tim) in (("identity", (np.stack([np.eye(D, dtype=np.float32)] * H),) * 2),
-                                ("hadamard", (np.stack([Hd / 8.0] * H).astype(np.float32),
-                                              np.stack([Hd / 16.0] * H).astype(np.float32))),
-                                ("T_k", (T, Ti))):
-            kc = bk.alloc_packed(n_tok, H, bits, q, dev)
-            bk.wushkv_quantize_keys(K, pos, rope, bk.Transform(Tm), bits, q, kc)
-            qp = bk.wushkv_pair_queries(Qb, bk.Transform(Tim))
-            o = bk.wushkv_decode_attention(qp, kc, vc, H, bits, q, row0, lens, n_tok, scale)
-            errs[name].append(float(((o - ref) ** 2).sum() / (ref ** 2).sum()))
-    torch.cuda.synchronize()
-    return {k: {"geomean": float(np.exp(np.mean(np.log(v)))), "per_layer": [round(x, 6) for x in v]}
-            for k, v in errs.items()} | {"layers": layers, "tokens": n_tok, "queries": n_q, "bits": bits,
-                                         "query_scale": q_scale,
-                                         "note": "synthetic heavy-tailed keys and values; no model weights"}
-
-
 def kernel_us(torch, bk, stream, call, reps: int, warm: int = 3) -> float:
     """Mean duration in us of the kernel `call` launches, from the pair of HIP
     events that the kernel itself records at its start and end
@@ -346,7 +290,7 @@ def main() -> int:
     ap.add_argument("--light", action="store_true",
                     help="few repetitions in the sections beside the throughput pass (for counter runs)")
     ap.add_argument("--quality", action="store_true",
-                    help="also report the attention-output error of the quantized cache per key transform")
+                    help="attention-output error over 4 layers at 2 and 4 bits (default: 1 layer, 2 bits)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -776,8 +720,13 @@ def main() -> int:
         },
         "other_workloads": other,
     }
+    # attention-output error of the quantized cache per key transform: a light pass by default
+    # (one layer, 2-bit), four layers at 2 and 4 bits with --quality
+    from bit_kv_cache_rope_amd import quality
     if args.quality:
-        out["quality"] = {f"{b}bit": quality_report(torch, synth, bk, dev, bits=b) for b in (2, 4)}
+        out["quality"] = {f"{b}bit": quality.quality_report(synth, dev, bits=b, layers=4) for b in (2, 4)}
+    else:
+        out["quality"] = {"2bit": quality.quality_report(synth, dev, bits=2, layers=1, n_tok=2048, n_q=16)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle (single thread, one layer)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, synth)

@@ -27,6 +27,7 @@ __all__ = [
     "wushkv_rope_frequencies", "library", "PreparedCall", "prepare_quantize_keys",
     "prepare_quantize_values", "prepare_dequantize", "wushkv_pair_queries", "wushkv_decode_attention_workspace",
     "wushkv_decode_attention", "prepare_decode_attention", "wushkv_quantize_kv", "prepare_quantize_kv",
+    "wushkv_debug_check_arith",
 ]
 
 
@@ -323,6 +324,14 @@ def wushkv_debug_time_next_launch(start: torch.cuda.Event | None, stop: torch.cu
             raise ValueError("record the event once before passing it")
         return ctypes.c_void_p(e.cuda_event)
     _lib.check(library().wushkv_debug_time_next_launch(handle(start), handle(stop)))
+
+
+def wushkv_debug_check_arith(stream=None) -> list:
+    """Mismatch counts [sqrt, / 3, / 7, / 15] of the device's fp32 square root and the
+    kernels' division by 2^b - 1 over all 2^32 inputs (all zero when correctly rounded)."""
+    counts = torch.empty(4, dtype=torch.int32, device="cuda")
+    _lib.check(library().wushkv_debug_check_arith(ctypes.c_void_p(counts.data_ptr()), _stream(stream)))
+    return [int(c) for c in counts.cpu().tolist()]
 
 
 def wushkv_rope_frequencies(theta: float):

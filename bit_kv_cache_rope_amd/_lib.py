@@ -19,7 +19,7 @@ EXPORTED = [
     "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch",
     "wushkv_status_string", "wushkv_last_error", "wushkv_version", "wushkv_pair_queries",
     "wushkv_decode_attention_workspace", "wushkv_decode_attention", "wushkv_decode_attention_noalloc",
-    "wushkv_quantize_kv",
+    "wushkv_quantize_kv", "wushkv_debug_check_arith",
 ]
 
 
@@ -65,6 +65,7 @@ def load() -> ctypes.CDLL:
     L.wushkv_debug_rope_transform.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, vp, vp]
     L.wushkv_debug_rope_cos_sin.argtypes = [vp, vp, i64, vp, vp]
     L.wushkv_debug_time_next_launch.argtypes = [vp, vp]
+    L.wushkv_debug_check_arith.argtypes = [vp, vp]
     L.wushkv_pair_queries.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp]
     L.wushkv_decode_attention_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.wushkv_decode_attention.argtypes = [vp, i32, i32, pp, pp, i32, i32, qp, vp, vp, i32, f32, vp,

@@ -551,6 +551,17 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
   return WUSHKV_OK;
 }
 
+wushkv_status wushkv_debug_check_arith(uint32_t* counts, void* stream) {
+  if (!counts) return fail(WUSHKV_ERR_INVALID_ARG, "counts is NULL");
+  if (!aligned(counts, 4)) return fail(WUSHKV_ERR_ALIGNMENT, "counts must be 4-byte aligned");
+  int dev;
+  wushkv_status st = current_device(&dev);
+  if (st) return st;
+  hipError_t e = wushkv::launch_arith_check(counts, wushkv::device_cu_count(dev), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "arithmetic check launch");
+  return WUSHKV_OK;
+}
+
 wushkv_status wushkv_debug_time_next_launch(void* start, void* stop) {
   g_launch_events.start = (hipEvent_t)start;
   g_launch_events.stop = (hipEvent_t)stop;

@@ -188,6 +188,9 @@ hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_gr
                        hipStream_t stream);
 hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
+// Exhaustive device check of the correctly rounded sqrt and div_small: mismatch counts
+// for sqrt, / 3, / 7, / 15 into counts[0..3] (device memory).
+hipError_t launch_arith_check(uint32_t* counts, int cus, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int bits, int heads_per_group, int cus, hipStream_t stream);
 hipError_t launch_pair_queries(const PairArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int bits, hipStream_t stream);

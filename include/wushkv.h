@@ -277,6 +277,17 @@ wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, i
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
                                         int64_t n, float* cs_out, void* stream);
 
+/* Self-check of the device arithmetic the step computation relies on: the fp16 step
+ * comes from rms = sqrt(S / 128) and a division of the clip range by 2^b - 1, both of
+ * which the numerical contract above takes as correctly rounded.
+ * Runs, on the current device, sqrt and the division by 3, 7 and 15 exactly as the
+ * kernels compile them over all 2^32 fp32 bit patterns, checking each result exactly
+ * (sqrt against the squares of the neighbouring fp32 midpoints in fp64; the divisions
+ * against the fp32 rounding of the fp64 quotient).  counts: device uint32[4],
+ * overwritten with the mismatch counts for sqrt, / 3, / 7 and / 15 (all zero on a
+ * conforming device).  Asynchronous on `stream`; tens of milliseconds. */
+wushkv_status wushkv_debug_check_arith(uint32_t* counts, void* stream);
+
 /* Timing support: the next wushkv_quantize_keys, wushkv_quantize_values, wushkv_quantize_kv,
  * wushkv_dequantize, wushkv_pair_queries or wushkv_decode_attention call
  * (its first kernel) on this host thread records `start` (a hipEvent_t)

@@ -114,6 +114,8 @@ def test_validation_without_device(lib):
     assert kv(ks=200) == _lib.ERR_INVALID_ARG
     assert kv(V=None) == _lib.ERR_INVALID_ARG
     assert kv() == _lib.ERR_INVALID_ARG  # NULL rope and transform handles
+    assert L.wushkv_debug_check_arith(None, None) == _lib.ERR_INVALID_ARG
+    assert L.wushkv_debug_check_arith(vp(2), None) == _lib.ERR_ALIGNMENT
     # read path
     assert L.wushkv_dequantize(ctypes.byref(p), 4, 2, 9, ctypes.byref(q), None, vp(16), 1, None) == _lib.ERR_INVALID_ARG
     assert L.wushkv_dequantize(ctypes.byref(p), 4, 2, 2, ctypes.byref(q), None, vp(16), 3, None) == _lib.ERR_INVALID_ARG

@@ -130,6 +130,17 @@ def test_cos_sin_exhaustive(env):
 
 # ---------------------------------------------------------------------------------- transform
 
+def test_sqrt_and_step_division_exhaustive(env):
+    """The fp32 square root and the division by 2^b - 1 that the step computation uses,
+    compiled as in the kernels, are correctly rounded for every one of the 2^32 fp32
+    inputs on this device (checked exactly on the device: sqrt against the squares of
+    the neighbouring fp32 midpoints, the divisions against the rounded fp64 quotient)."""
+    say("exhaustive sqrt and division by 3, 7, 15 over 2^32 inputs")
+    counts = env["bk"].wushkv_debug_check_arith()
+    say(f"  mismatches [sqrt, /3, /7, /15] = {counts}")
+    assert counts == [0, 0, 0, 0]
+
+
 def _y_gpu(env, K, pos, T, theta=1e6):
     bk = env["bk"]
     rope = bk.Rope(theta, 1 << 17)
