@@ -70,20 +70,40 @@ wushkv_status make_quant(const wushkv_quantizer* q, wushkv::QuantArgs* out) {
     if (q->group != 32) return fail(WUSHKV_ERR_UNSUPPORTED, "affine quantizer needs group 32");
     if (!(q->p_lo >= 0.0f) || !(q->p_hi <= 100.0f) || !(q->p_lo <= q->p_hi))
       return fail(WUSHKV_ERR_INVALID_ARG, "need 0 <= p_lo <= p_hi <= 100");
-    out->kind = 1;
-    const double hl = 31.0 * (double)q->p_lo / 100.0;
-    if (hl >= 1.0) return fail(WUSHKV_ERR_UNSUPPORTED, "p_lo must be below 100/31 (order statistics 0 and 1)");
-    out->g_lo = (float)hl;
-    out->lo_mode = out->g_lo == 0.0f ? 1 : 0;
-    const double hh = 31.0 * (double)q->p_hi / 100.0;
-    if (hh >= 31.0) {
-      out->hi_mode = 2;
+    // order statistic i and weight g of each percentile (h >= 31: the largest, exactly)
+    auto split = [](float p, int* i, float* g, int* exact) {
+      const double h = 31.0 * (double)p / 100.0;
+      if (h >= 31.0) {
+        *i = 31;
+        *g = 0.0f;
+        *exact = 1;
+        return;
+      }
+      const double fl = std::floor(h);
+      *i = (int)fl;
+      *g = (float)(h - fl);
+      *exact = *g == 0.0f ? 1 : 0;
+    };
+    int il, ih, el, eh;
+    float gl, gh;
+    split(q->p_lo, &il, &gl, &el);
+    split(q->p_hi, &ih, &gh, &eh);
+    if (il == 0 && (ih == 30 || ih == 31)) {
+      // the extreme order statistics (the 1st/99th percentiles among them): kind 1
+      out->kind = 1;
+      out->g_lo = gl;
+      out->lo_mode = el;
+      out->g_hi = gh;
+      out->hi_mode = ih == 31 ? 2 : eh;
     } else {
-      const double fl = std::floor(hh);
-      if (fl != 30.0) return fail(WUSHKV_ERR_UNSUPPORTED, "p_hi must be at least 3000/31 (order statistics 30 and 31)");
-      out->g_hi = (float)(hh - fl);
-      out->hi_mode = out->g_hi == 0.0f ? 1 : 0;
+      out->kind = 2;
+      out->g_lo = gl;
+      out->lo_mode = el;
+      out->g_hi = gh;
+      out->hi_mode = eh;
     }
+    out->lo_i = il;
+    out->hi_i = ih;
     return WUSHKV_OK;
   }
   return fail(WUSHKV_ERR_INVALID_ARG, "unknown quantizer kind");
@@ -94,11 +114,11 @@ wushkv_status check_packed(const wushkv_packed* p, int kind, int64_t n_tokens, b
   if (p->n_rows < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n_rows < 0");
   if (p->n_rows > 0) {  // a cache of no rows is never dereferenced: its pointers may be NULL
     if (!p->codes || !p->scales) return fail(WUSHKV_ERR_INVALID_ARG, "codes and scales must be set");
-    if (kind == 1 && !p->zeros) return fail(WUSHKV_ERR_INVALID_ARG, "affine quantizer needs zeros");
+    if (kind != 0 && !p->zeros) return fail(WUSHKV_ERR_INVALID_ARG, "affine quantizer needs zeros");
   }
   if (!aligned(p->codes, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "codes must be 16-byte aligned");
   if (!aligned(p->scales, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "scales must be 16-byte aligned");
-  if (kind == 1 && !aligned(p->zeros, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "zeros must be 16-byte aligned");
+  if (kind != 0 && !aligned(p->zeros, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "zeros must be 16-byte aligned");
   if (p->n_rows > INT32_MAX) return fail(WUSHKV_ERR_UNSUPPORTED, "n_rows must be below 2^31");
   if (!p->slots && p->n_rows < n_tokens)
     return fail(WUSHKV_ERR_INVALID_ARG, writer ? "cache has fewer rows than tokens" : "cache has fewer rows than requested");
@@ -366,7 +386,9 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
     return fail(WUSHKV_ERR_INVALID_ARG, "handles belong to another device than the current one");
   const int cus = wushkv::device_cu_count(dev);
   const int64_t n_tiles = (n_tokens + 63) / 64;
-  const int hg = choose_hg(n_tiles, n_heads, cus, k_dtype == WUSHKV_F32 ? 2 : 4);
+  // fp32 keys and general percentiles (a 32-key sort per group in registers) run at up to
+  // two heads per block, where a wave has twice the registers
+  const int hg = choose_hg(n_tiles, n_heads, cus, (k_dtype == WUSHKV_F32 || qa.kind == 2) ? 2 : 4);
   wushkv::KeysArgs a{};
   a.K = K;
   a.n_tokens = n_tokens;
@@ -535,7 +557,7 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
   a.n_rows = in->n_rows;
   a.n_tokens = n_tokens;
   a.n_heads = n_heads;
-  a.kind = qa.kind;
+  a.kind = qa.kind == 0 ? 0 : 1;  // both affine kinds read z + q s
   a.out = out;
   a.out_bf16 = out_dtype == WUSHKV_BF16;
   int hg = 1;

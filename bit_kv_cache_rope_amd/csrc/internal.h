@@ -40,12 +40,18 @@ struct wushkv_rope {
 namespace wushkv {
 
 struct QuantArgs {
-  int kind;       // 0 sym, 1 affine
+  int kind;       // 0 sym; 1 affine, percentiles from the extreme order statistics; 2 affine, general
   float alpha;    // sym clip factor
-  float g_lo;     // affine: interpolation weight of the low percentile (order statistics 0, 1)
-  int lo_mode;    // 0: fma(g_lo, s1 - s0, s0); 1: s0
-  float g_hi;     // affine: weight of the high percentile (order statistics 30, 31)
-  int hi_mode;    // 0: fma(g_hi, s31 - s30, s30); 1: s30; 2: s31
+  // affine, kind 1: the low percentile from order statistics 0, 1, the high one from 30, 31
+  //   lo_mode 0: fma(g_lo, s1 - s0, s0); 1: s0
+  //   hi_mode 0: fma(g_hi, s31 - s30, s30); 1: s30; 2: s31
+  // affine, kind 2: order statistics lo_i, lo_i + 1 and hi_i, hi_i + 1 of the sorted group
+  //   mode 0: fma(g, s_{i+1} - s_i, s_i); 1: s_i
+  float g_lo;
+  int lo_mode;
+  float g_hi;
+  int hi_mode;
+  int lo_i, hi_i;
 };
 
 struct KeysArgs {

@@ -16,6 +16,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "sort32.h"
 
 namespace wushkv {
 
@@ -92,32 +93,52 @@ __device__ __forceinline__ void sym_runs(const f32x16& acc, float delta, uint32_
 }
 
 // Percentile-clipped affine codes, group = the wave's 32 rows of the token,
-// split between lanes l and l ^ 32: the two smallest and two largest values by
-// IEEE totalOrder, merged across the lane pair, give the interpolated
-// percentiles; sh, zh are the fp16 step and zero (the same in both lanes).
-template <int BITS>
+// split between lanes l and l ^ 32; sh, zh are the fp16 step and zero (the same
+// in both lanes).  GEN false: the two smallest and two largest values by IEEE
+// totalOrder, merged across the lane pair, give the percentiles (kind 1); GEN
+// true: each lane sorts its 16 keys, the pair's two lists are merged in both
+// lanes, and the order statistics are read off the 32 sorted keys (kind 2).
+template <int BITS, bool GEN = false>
 __device__ __forceinline__ void affine_runs(const f32x16& acc, const QuantArgs& qa, uint32_t* run, uint16_t& sh,
                                             uint16_t& zh) {
   constexpr int L = 1 << BITS;
-  int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
+  float lo, hi;
+  if constexpr (GEN) {
+    int32_t k[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int32_t k = total_order_key(acc[i]);
-    mn2 = min(mn2, max(mn1, k));
-    mn1 = min(mn1, k);
-    mx2 = max(mx2, min(mx1, k));
-    mx1 = max(mx1, k);
+    for (int i = 0; i < 16; ++i) k[i] = total_order_key(acc[i]);
+    bitonic_sort<16>(k);
+    int32_t a[16], b[16], srt[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const Halves hv = halves((uint32_t)k[i]);
+      a[i] = (int32_t)hv.lo;
+      b[i] = (int32_t)hv.hi;
+    }
+    bitonic_merge<16>(a, b, srt);
+    lo = percentile_sorted(srt, qa.lo_i, qa.g_lo, qa.lo_mode);
+    hi = percentile_sorted(srt, qa.hi_i, qa.g_hi, qa.hi_mode);
+  } else {
+    int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t k = total_order_key(acc[i]);
+      mn2 = min(mn2, max(mn1, k));
+      mn1 = min(mn1, k);
+      mx2 = max(mx2, min(mx1, k));
+      mx1 = max(mx1, k);
+    }
+    const Halves n1 = halves((uint32_t)mn1), n2 = halves((uint32_t)mn2);
+    const Halves x1 = halves((uint32_t)mx1), x2 = halves((uint32_t)mx2);
+    const int32_t a1 = (int32_t)n1.lo, b1 = (int32_t)n1.hi, a2 = (int32_t)n2.lo, b2 = (int32_t)n2.hi;
+    const int32_t c1 = (int32_t)x1.lo, d1 = (int32_t)x1.hi, c2 = (int32_t)x2.lo, d2 = (int32_t)x2.hi;
+    const float s0 = total_order_value(min(a1, b1));
+    const float s1 = total_order_value(min(max(a1, b1), min(a2, b2)));
+    const float s31 = total_order_value(max(c1, d1));
+    const float s30 = total_order_value(max(min(c1, d1), max(c2, d2)));
+    lo = qa.lo_mode ? s0 : __builtin_fmaf(qa.g_lo, s1 - s0, s0);
+    hi = qa.hi_mode == 0 ? __builtin_fmaf(qa.g_hi, s31 - s30, s30) : (qa.hi_mode == 1 ? s30 : s31);
   }
-  const Halves n1 = halves((uint32_t)mn1), n2 = halves((uint32_t)mn2);
-  const Halves x1 = halves((uint32_t)mx1), x2 = halves((uint32_t)mx2);
-  const int32_t a1 = (int32_t)n1.lo, b1 = (int32_t)n1.hi, a2 = (int32_t)n2.lo, b2 = (int32_t)n2.hi;
-  const int32_t c1 = (int32_t)x1.lo, d1 = (int32_t)x1.hi, c2 = (int32_t)x2.lo, d2 = (int32_t)x2.hi;
-  const float s0 = total_order_value(min(a1, b1));
-  const float s1 = total_order_value(min(max(a1, b1), min(a2, b2)));
-  const float s31 = total_order_value(max(c1, d1));
-  const float s30 = total_order_value(max(min(c1, d1), max(c2, d2)));
-  const float lo = qa.lo_mode ? s0 : __builtin_fmaf(qa.g_lo, s1 - s0, s0);
-  const float hi = qa.hi_mode == 0 ? __builtin_fmaf(qa.g_hi, s31 - s30, s30) : (qa.hi_mode == 1 ? s30 : s31);
   const float s32 = div_small<L - 1>(hi - lo);
   sh = f16_sat_bits(s32);
   zh = f16_sat_bits(lo);

@@ -532,7 +532,7 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           uint16_t sh, zh;
-          affine_runs<BITS>(acc[nb], a.q, run[nb], sh, zh);
+          affine_runs<BITS, QK == 2>(acc[nb], a.q, run[nb], sh, zh);
           if (lh == 0) {
             sc_lds[g][32 * nb + col][hg * 8 + wq] = sh;
             sc_lds[g][32 * nb + col][hg * 8 + 4 + wq] = zh;
@@ -674,7 +674,8 @@ hipError_t launch_hg(const KeysArgs& a, int hg, int cus, hipStream_t st) {
     case 1: return launch_one<BITS, QK, F32IN, 1, YOUT>(a, cus, st);
     case 2: return launch_one<BITS, QK, F32IN, 2, YOUT>(a, cus, st);
     case 4:
-      if constexpr (!F32IN) return launch_one<BITS, QK, F32IN, 4, YOUT>(a, cus, st);
+      // (general percentiles sort in registers: at most two heads per block)
+      if constexpr (!F32IN && QK != 2) return launch_one<BITS, QK, F32IN, 4, YOUT>(a, cus, st);
       break;
   }
   return hipErrorInvalidValue;
@@ -698,11 +699,17 @@ hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int hg, int y_ou
       case 3: return launch_bits<3, 0>(a, f32_in, hg, 0, cus, st);
       case 4: return launch_bits<4, 0>(a, f32_in, hg, 0, cus, st);
     }
-  } else {
+  } else if (a.q.kind == 1) {
     switch (bits) {
       case 2: return launch_bits<2, 1>(a, f32_in, hg, 0, cus, st);
       case 3: return launch_bits<3, 1>(a, f32_in, hg, 0, cus, st);
       case 4: return launch_bits<4, 1>(a, f32_in, hg, 0, cus, st);
+    }
+  } else {
+    switch (bits) {
+      case 2: return launch_bits<2, 2>(a, f32_in, hg, 0, cus, st);
+      case 3: return launch_bits<3, 2>(a, f32_in, hg, 0, cus, st);
+      case 4: return launch_bits<4, 2>(a, f32_in, hg, 0, cus, st);
     }
   }
   return hipErrorInvalidValue;

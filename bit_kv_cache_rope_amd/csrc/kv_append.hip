@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(kThreads) kv_append_kernel(const AppendArgs a)
           packed = value_codes_sym<BITS>(x, th);
         }
       } else {
-        packed = value_codes_affine<BITS>(x, a.q, sh, zh);
+        packed = value_codes_affine<BITS, QK == 2>(x, a.q, sh, zh);
       }
       const int64_t v_row = row_of(v_sw, a.v_slots, a.v_rows, jv);
       if (v_row >= 0) {
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(kThreads) kv_append_kernel(const AppendArgs a)
       }
     } else {
       uint32_t run[4];
-      affine_runs<BITS>(acc, a.q, run, ksh, kzh);
+      affine_runs<BITS, QK == 2>(acc, a.q, run, ksh, kzh);
       chunk = record_chunk<BITS>(run, lh);
       __syncthreads();  // every wave has read xb_lds before the next unit's RoPE writes it
     }
@@ -260,11 +260,17 @@ hipError_t launch_append(const AppendArgs& a, int bits, int f32_in, int cus, hip
       case 3: return launch_af<3, 0>(a, f32_in, cus, st);
       case 4: return launch_af<4, 0>(a, f32_in, cus, st);
     }
-  } else {
+  } else if (a.q.kind == 1) {
     switch (bits) {
       case 2: return launch_af<2, 1>(a, f32_in, cus, st);
       case 3: return launch_af<3, 1>(a, f32_in, cus, st);
       case 4: return launch_af<4, 1>(a, f32_in, cus, st);
+    }
+  } else {
+    switch (bits) {
+      case 2: return launch_af<2, 2>(a, f32_in, cus, st);
+      case 3: return launch_af<3, 2>(a, f32_in, cus, st);
+      case 4: return launch_af<4, 2>(a, f32_in, cus, st);
     }
   }
   return hipErrorInvalidValue;

@@ -13,6 +13,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "sort32.h"
 
 namespace wushkv {
 
@@ -124,35 +125,67 @@ __device__ __forceinline__ uint32_t value_codes_sym(const float* x, float4 th) {
   return packed;
 }
 
+// v from the lane the DPP control CTRL names (within a row of 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
 // Percentile-clipped affine codes of the lane's 8 channels, group of 32
-// channels = 4 consecutive lanes: the two extremes at each end by IEEE
-// totalOrder, merged by xor 1, 2; sh, zh are the group's fp16 step and zero.
-template <int BITS>
+// channels = 4 consecutive lanes (a DPP quad); sh, zh are the group's fp16 step
+// and zero.  GEN false: the two extremes at each end by IEEE totalOrder, merged
+// by xor 1, 2 (kind 1); GEN true: each lane sorts its 8 keys, every lane of the
+// quad gathers the quad's four sorted lists and merges them into the 32 sorted
+// keys, and the order statistics are read off those (kind 2).
+template <int BITS, bool GEN = false>
 __device__ __forceinline__ uint32_t value_codes_affine(const float* x, const QuantArgs& qa, uint16_t& sh,
                                                        uint16_t& zh) {
   constexpr int L = 1 << BITS;
-  int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
+  float lo, hi;
+  if constexpr (GEN) {
+    int32_t k[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int32_t k = total_order_key(x[e]);
-    mn2 = min(mn2, max(mn1, k));
-    mn1 = min(mn1, k);
-    mx2 = max(mx2, min(mx1, k));
-    mx1 = max(mx1, k);
-  }
+    for (int e = 0; e < 8; ++e) k[e] = total_order_key(x[e]);
+    bitonic_sort<8>(k);
+    // quad_perm [r, r, r, r]: lane r of the quad, in every lane of the quad
+    int32_t q0[8], q1[8], q2[8], q3[8];
 #pragma unroll
-  for (int off = 1; off <= 2; off <<= 1) {
-    const int32_t o1 = __shfl_xor(mn1, off), o2 = __shfl_xor(mn2, off);
-    const int32_t u1 = __shfl_xor(mx1, off), u2 = __shfl_xor(mx2, off);
-    mn2 = min(max(mn1, o1), min(mn2, o2));
-    mn1 = min(mn1, o1);
-    mx2 = max(min(mx1, u1), max(mx2, u2));
-    mx1 = max(mx1, u1);
+    for (int e = 0; e < 8; ++e) {
+      q0[e] = dpp_i32<0x00>(k[e]);
+      q1[e] = dpp_i32<0x55>(k[e]);
+      q2[e] = dpp_i32<0xAA>(k[e]);
+      q3[e] = dpp_i32<0xFF>(k[e]);
+    }
+    int32_t m01[16], m23[16], srt[32];
+    bitonic_merge<8>(q0, q1, m01);
+    bitonic_merge<8>(q2, q3, m23);
+    bitonic_merge<16>(m01, m23, srt);
+    lo = percentile_sorted(srt, qa.lo_i, qa.g_lo, qa.lo_mode);
+    hi = percentile_sorted(srt, qa.hi_i, qa.g_hi, qa.hi_mode);
+  } else {
+    int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int32_t k = total_order_key(x[e]);
+      mn2 = min(mn2, max(mn1, k));
+      mn1 = min(mn1, k);
+      mx2 = max(mx2, min(mx1, k));
+      mx1 = max(mx1, k);
+    }
+#pragma unroll
+    for (int off = 1; off <= 2; off <<= 1) {
+      const int32_t o1 = __shfl_xor(mn1, off), o2 = __shfl_xor(mn2, off);
+      const int32_t u1 = __shfl_xor(mx1, off), u2 = __shfl_xor(mx2, off);
+      mn2 = min(max(mn1, o1), min(mn2, o2));
+      mn1 = min(mn1, o1);
+      mx2 = max(min(mx1, u1), max(mx2, u2));
+      mx1 = max(mx1, u1);
+    }
+    const float s0 = total_order_value(mn1), s1 = total_order_value(mn2);
+    const float s31 = total_order_value(mx1), s30 = total_order_value(mx2);
+    lo = qa.lo_mode ? s0 : __builtin_fmaf(qa.g_lo, s1 - s0, s0);
+    hi = qa.hi_mode == 0 ? __builtin_fmaf(qa.g_hi, s31 - s30, s30) : (qa.hi_mode == 1 ? s30 : s31);
   }
-  const float s0 = total_order_value(mn1), s1 = total_order_value(mn2);
-  const float s31 = total_order_value(mx1), s30 = total_order_value(mx2);
-  const float lo = qa.lo_mode ? s0 : __builtin_fmaf(qa.g_lo, s1 - s0, s0);
-  const float hi = qa.hi_mode == 0 ? __builtin_fmaf(qa.g_hi, s31 - s30, s30) : (qa.hi_mode == 1 ? s30 : s31);
   const float s32 = div_small<L - 1>(hi - lo);
   sh = f16_sat_bits(s32);
   zh = f16_sat_bits(lo);

@@ -104,7 +104,7 @@ __device__ __forceinline__ void load_vals(RawVals<F32IN>& r, int64_t* rows, cons
 }
 
 template <int BITS, int QK, bool F32IN, bool DENSE>
-__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(F32IN && QK ? 3 : 4)))
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(QK == 2 ? 2 : (F32IN && QK ? 3 : 4))))
 values_kernel(const ValuesArgs a) {
   constexpr int L = 1 << BITS;
   constexpr int REC = 16 * BITS;
@@ -190,7 +190,7 @@ values_kernel(const ValuesArgs a) {
         float x[8];
         unpack(u, x);
         uint16_t sh, zh;
-        const uint32_t packed = value_codes_affine<BITS>(x, a.q, sh, zh);
+        const uint32_t packed = value_codes_affine<BITS, QK == 2>(x, a.q, sh, zh);
         if ((l16 & 3) == 0) {
           sc_lds[par][vloc * 4 + (l16 >> 2)] = sh;
           zr_lds[par][vloc * 4 + (l16 >> 2)] = zh;
@@ -299,11 +299,17 @@ hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hip
       case 3: return launch_vd<3, 0>(a, f32_in, cus, st);
       case 4: return launch_vd<4, 0>(a, f32_in, cus, st);
     }
-  } else {
+  } else if (a.q.kind == 1) {
     switch (bits) {
       case 2: return launch_vd<2, 1>(a, f32_in, cus, st);
       case 3: return launch_vd<3, 1>(a, f32_in, cus, st);
       case 4: return launch_vd<4, 1>(a, f32_in, cus, st);
+    }
+  } else {
+    switch (bits) {
+      case 2: return launch_vd<2, 2>(a, f32_in, cus, st);
+      case 3: return launch_vd<3, 2>(a, f32_in, cus, st);
+      case 4: return launch_vd<4, 2>(a, f32_in, cus, st);
     }
   }
   return hipErrorInvalidValue;

@@ -68,7 +68,7 @@ extern "C" {
 typedef enum {
   WUSHKV_OK = 0,
   WUSHKV_ERR_INVALID_ARG = 1,  /* NULL pointer, bad size, bad enum value        */
-  WUSHKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. percentiles) */
+  WUSHKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. affine caches in attention) */
   WUSHKV_ERR_ALIGNMENT = 3,    /* pointer or stride not aligned as required    */
   WUSHKV_ERR_NO_DEVICE = 4,    /* no HIP device visible                        */
   WUSHKV_ERR_HIP = 5,          /* a HIP runtime call failed                    */
@@ -84,10 +84,13 @@ typedef enum {
 
 /* Scalar quantizer description.
  *   WUSHKV_Q_SYM_RMS:    group must be 128; clip_alpha > 0 (2.0 in the workloads).
- *   WUSHKV_Q_AFFINE_PCT: group must be 32; 0 <= p_lo <= p_hi <= 100.  The GPU
- *     kernels select the two extreme order statistics at each end, so they need
- *     p_lo < 100/31 and p_hi >= 3000/31 (the 1st/99th percentiles qualify);
- *     other percentiles return WUSHKV_ERR_UNSUPPORTED. */
+ *   WUSHKV_Q_AFFINE_PCT: group must be 32; 0 <= p_lo <= p_hi <= 100.  Each
+ *     percentile interpolates linearly between order statistics i = floor(h)
+ *     and i + 1 of the group, h = 31 p / 100 (see the numerical contract).
+ *     When p_lo < 100/31 and p_hi >= 3000/31 (the 1st/99th percentiles among
+ *     them) the kernels select the two extreme values at each end; other
+ *     percentiles sort each group's 32 values in registers (bitonic network),
+ *     which costs several times the vector instructions. */
 typedef struct {
   int32_t kind;       /* wushkv_qkind */
   float clip_alpha;

@@ -91,8 +91,9 @@ def test_validation_without_device(lib):
     assert L.wushkv_last_error()
     # quantizer descriptions
     for qq, want in ((_q(group=32), _lib.ERR_UNSUPPORTED), (_q(alpha=0.0), _lib.ERR_INVALID_ARG),
-                     (_q(kind=1, group=32, plo=5.0), _lib.ERR_UNSUPPORTED),
-                     (_q(kind=1, group=32, phi=90.0), _lib.ERR_UNSUPPORTED),
+                     # general percentiles are accepted: these stop at the missing zeros
+                     (_q(kind=1, group=32, plo=5.0), _lib.ERR_INVALID_ARG),
+                     (_q(kind=1, group=32, phi=90.0), _lib.ERR_INVALID_ARG),
                      (_q(kind=1, group=32, plo=50.0, phi=10.0), _lib.ERR_INVALID_ARG),
                      (_q(kind=1, group=128), _lib.ERR_UNSUPPORTED), (_q(kind=7), _lib.ERR_INVALID_ARG)):
         assert call(vp(16), 1, 4, 2, 256, 2, ctypes.byref(qq), ctypes.byref(p), None) == want

@@ -307,6 +307,69 @@ def test_values_strided_and_slots(env):
     assert int(out.codes[mask].count_nonzero()) == 0
 
 
+# ---------------------------------------------------------------------------------- general percentiles
+
+PERCENTILES = [(5.0, 95.0), (10.0, 90.0), (25.0, 75.0), (50.0, 50.0), (2.0, 90.0), (4.0, 99.5)]
+
+
+@pytest.mark.parametrize("p_lo,p_hi", PERCENTILES)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_values_general_percentiles_bit_exact(env, p_lo, p_hi, bits):
+    """Percentiles that need order statistics other than the two extremes at each
+    end (the kernels sort each 32-group in registers): bit-exact against the
+    oracle, bf16 and fp32, with a ragged tail; 50/50 gives a zero step (code 0)."""
+    s, o, bk = env["synth"], env["oracle"], env["bk"]
+    w = s.WORKLOADS["affine_pct"]
+    q = bk.affine(p_lo, p_hi)
+    say(f"values percentiles {p_lo}/{p_hi} {bits}-bit")
+    for dtype, n in (("bf16", 1999), ("f32", 300)):
+        V = s.kv(w, 0, "V", 0, n, dtype=dtype)
+        g = packed_host(run_values(env, V, bits, q))
+        assert_same_packed(g, o.quantize_values(V, bits, o.affine(p_lo, p_hi)), f"values {p_lo}/{p_hi} {dtype}")
+
+
+@pytest.mark.parametrize("p_lo,p_hi", [(5.0, 95.0), (10.0, 90.0), (2.0, 90.0)])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_keys_general_percentiles(env, p_lo, p_hi, bits):
+    """Keys at general percentiles, end to end by the attribution rule, through the
+    two-head and one-head kernels (8192 and 1000 tokens) and fp32 input."""
+    s, bk = env["synth"], env["bk"]
+    w = s.WORKLOADS["affine_pct"]
+    q = bk.affine(p_lo, p_hi)
+    T, _ = s.transform(w, 0)
+    for dtype, n in (("bf16", 8192), ("bf16", 1000), ("f32", 700)):
+        say(f"keys percentiles {p_lo}/{p_hi} {bits}-bit {dtype} n={n}")
+        K = s.kv(w, 0, "K", 0, n, dtype=dtype)
+        pos = s.positions(w, 0, n)
+        account_keys(env, K, pos, T, bits, q, f"keys {p_lo}/{p_hi} {bits}-bit {dtype}")
+
+
+def test_general_percentiles_read_path_and_fused_call(env):
+    """A general-percentile cache read back plain (bit-exact against the oracle's
+    dequantization of the oracle's records, written by the library) and the fused
+    K+V call at the same quantizer (the separate calls' bytes)."""
+    s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
+    w = s.WORKLOADS["affine_pct"]
+    n, bits = 777, 3
+    q = bk.affine(5.0, 95.0)
+    V = s.kv(w, 0, "V", 0, n)
+    K = s.kv(w, 0, "K", 0, n)
+    pos = s.positions(w, 0, n)
+    T, _ = s.transform(w, 0)
+    say("general percentiles: read path and fused call")
+    pv = run_values(env, V, bits, q)
+    r = o.quantize_values(V, bits, o.affine(5.0, 95.0))
+    back = bk.wushkv_dequantize(pv, n, w.heads, bits, q, out_dtype=torch.float32).cpu().numpy()
+    ref = o.dequantize(r["codes"], r["scales"], r["zeros"], n, w.heads, bits, o.affine(5.0, 95.0))
+    assert np.array_equal(back.view(np.uint32), ref.view(np.uint32))
+    rope, tk = bk.Rope(w.theta, 1 << 17), bk.Transform(T)
+    kc, vc = bk.alloc_packed(n, w.heads, bits, q), bk.alloc_packed(n, w.heads, bits, q)
+    bk.wushkv_quantize_kv(to_dev(env, K), to_dev(env, V), to_dev(env, pos), rope, tk, bits, q, kc, vc)
+    torch.cuda.synchronize()
+    assert_same_packed(packed_host(vc), packed_host(pv), "fused values")
+    assert_same_packed(packed_host(kc), packed_host(run_keys(env, K, pos, T, bits, q)), "fused keys")
+
+
 # ---------------------------------------------------------------------------------- keys end to end
 
 def fp16_boundary_abs(x):
@@ -340,7 +403,8 @@ def account_keys(env, K, pos, T, bits, q, what, g=None):
     other side of it, or (b) its vector's step (symmetric) or its group's step
     or zero (affine) differs, which is allowed only where the oracle's value
     before the fp16 rounding lies within NEAR * step of an fp16 rounding
-    midpoint.  Returns (mismatches, elements, worst distance / step)."""
+    midpoint (for the zero, within NEAR * max(step, |zero|): the scale of the quantity
+    rounded).  Returns (mismatches, elements, worst distance / scale)."""
     o = env["oracle"]
     if g is None:
         g = packed_host(run_keys(env, K, pos, T, bits, q))
@@ -380,9 +444,11 @@ def account_keys(env, K, pos, T, bits, q, what, g=None):
             lo = np.float32(o.percentile32(grp_r, q.p_lo))
             hi = np.float32(o.percentile32(grp_r, q.p_hi))
             st = float(np.float32(np.float32(hi - lo) / np.float32(L - 1)))
-            for differs, val in ((gs[n, h, gi], st), (gz[n, h, gi], float(lo))):
+            # the scale of each rounded quantity: the step for the step, and for the zero
+            # the larger of the step and the zero's own magnitude
+            for differs, val, sc in ((gs[n, h, gi], st, abs(st)), (gz[n, h, gi], float(lo), max(abs(st), abs(float(lo))))):
                 if differs:
-                    d = float(fp16_boundary_abs(val)) / max(abs(st), 1e-30)
+                    d = float(fp16_boundary_abs(val)) / max(sc, 1e-30)
                     worst = max(worst, d)
                     assert d <= NEAR, f"{what}: step/zero of {(n, h, gi)} differs, {d:.2e} x step from an fp16 boundary"
         s_, z_ = f16(r["scales"]), f16(r["zeros"])
