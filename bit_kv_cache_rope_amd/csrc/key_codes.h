@@ -40,6 +40,31 @@ __device__ __forceinline__ float col_sumsq32(const f32x16& acc) {
   return (P8[0] + P8[1]) + (P8[2] + P8[3]);
 }
 
+// The same sums for both 32-token column blocks of a tile at once, with one
+// lane exchange per 8-row run: lane l gets block l / 32's token l % 32.  The
+// swap hands lane l < 32 block 0's run from lane l + 32 and lane l + 32 block
+// 1's run from lane l, so every lane adds (lane half 0's run) + (lane half 1's
+// run) of its own token, in the order col_sumsq32 uses.
+__device__ __forceinline__ float col_sumsq32x2(const f32x16& a0, const f32x16& a1) {
+  float P8[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float p4[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const f32x16& acc = nb ? a1 : a0;
+      const float q0 = acc[4 * q] * acc[4 * q];
+      const float q1 = acc[4 * q + 1] * acc[4 * q + 1];
+      const float q2 = acc[4 * q + 2] * acc[4 * q + 2];
+      const float q3 = acc[4 * q + 3] * acc[4 * q + 3];
+      p4[nb] = (q0 + q1) + (q2 + q3);
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p4[0]), __float_as_uint(p4[1]), false, false);
+    P8[q] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return (P8[0] + P8[1]) + (P8[2] + P8[3]);
+}
+
 // 2-bit symmetric codes of the lane's 16 rows as one word: run q (4 rows) in
 // byte q, LSB first.  The bits are shifted in from the last row down (alignbit:
 // w = 2w + bit 31 of the operand).  Code = [y > -step] + [y >= 0] + [y > step]:

@@ -271,7 +271,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
   double2 lov[NLO];
 #pragma unroll
   for (int k = 0; k < NLO; ++k) lov[k] = a.rope_lo[threadIdx.x + 256 * HG * k];
-  load_keys<F32IN>(r, keys_rsrc(first_tile), keys_off(), 8 * row_bytes);
+  // (the second group's first keys are loaded once the prologue is done: that
+  // group starts one phase later, and the first group's keys arrive sooner
+  // without them in the queue)
+  if (NG == 1 || g == 0) load_keys<F32IN>(r, keys_rsrc(first_tile), keys_off(), 8 * row_bytes);
   u32x2 row_w = {0u, 0u};  // read only when a.slots is set
   HiSlot hv[NPRE];             // high-table entries of the next tile's first NPRE slots
   float4 csr[NCS];             // the next tile's (cos, sin) slots, held by group 0 until phase 2
@@ -479,12 +482,9 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     } else if constexpr (QK == 0) {
       // Sum of squares as the contiguous pairwise tree over rows 0..127:
       // runs of 4 in-lane, pairs of runs across lanes l and l^32, the 32
-      // rows of this wave, then the four waves' sums ((0 + 1) + (2 + 3)).
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const float P32 = col_sumsq32(acc[nb]);
-        if (lh == nb) red_lds[hh][wq][32 * nb + col] = P32;
-      }
+      // rows of this wave (lane l: token l of the tile), then the four
+      // waves' sums ((0 + 1) + (2 + 3)).
+      red_lds[hh][wq][lane] = col_sumsq32x2(acc[0], acc[1]);
     }
     if constexpr (YOUT) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the y stores
@@ -586,7 +586,10 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     col = lane & 31;
     tid = 64 * wave_u + lane;
   };
-  if (NG == 2 && g == 1) next_phase();
+  if (NG == 2 && g == 1) {
+    load_keys<F32IN>(r, keys_rsrc(first_tile), keys_off(), 8 * row_bytes);
+    next_phase();
+  }
   for (int j = 0; j < count; ++j) {
     phase0(j);
     next_phase();

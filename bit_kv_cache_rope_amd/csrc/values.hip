@@ -277,9 +277,13 @@ hipError_t launch_v(const ValuesArgs& a, int cus, hipStream_t st) {
   }
   const int64_t nv = a.n_tokens * a.n_heads;
   const int64_t n_iter = (nv + kVecs - 1) / kVecs;
+  // as many blocks as fit at once, then as few as give every block the same
+  // number of iterations (a last round run by a fraction of the blocks would
+  // leave most of the chip idle)
+  if (n_iter <= 0) return hipSuccess;
   const int64_t cap = (int64_t)cus * occ;
-  const int blocks = (int)(n_iter < cap ? n_iter : cap);
-  if (blocks <= 0) return hipSuccess;
+  const int64_t per_block = (n_iter + cap - 1) / cap;
+  const int blocks = (int)((n_iter + per_block - 1) / per_block);
   return launch_kernel(k, dim3(blocks), dim3(64 * kWaves), st, a);
 }
 
