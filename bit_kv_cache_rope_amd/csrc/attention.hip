@@ -24,10 +24,12 @@
 //               constant part is subtracted after the product.
 //       softmax p = exp2(s - max) over the split, then p * step_v.
 //       values  O[ch][g] += c[ch][n] * p[n][g] on v_mfma_f32_16x16x32_bf16
-//               (2 and 4 bits): rows = 16 channels, k = 32 tokens from the
-//               value records stored transposed in LDS, columns = the query
-//               heads' weights p * step_v split into three bf16 parts (exact
-//               to fp32).  3-bit codes straddle words: v_mfma_f32_4x4x1f32
+//               (2 and 4 bits): rows = 16 channels, k = 32 tokens, columns =
+//               the query heads' weights p * step_v split into three bf16
+//               parts (exact to fp32).  The value records go to LDS as token
+//               pairs: halfword j of tokens 2i and 2i + 1 side by side in one
+//               word, so that a lane turns the word into its channel's two
+//               operands with one rotate and one mask.  3-bit codes straddle words: v_mfma_f32_4x4x1f32
 //               with fp32 weights (16 blocks = 16 tokens, rows = queries).
 //     A split writes (max, sum, unnormalized output) per query head.
 //   * combine_kernel merges the splits of a sequence.
@@ -47,6 +49,14 @@ constexpr int kPairVecs = 4;      // query vectors per pairing block
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past `bytes`
+// (including offsets that wrapped below zero) return zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
 
 // grid (ceil(N G / kPairVecs), Hkv), 256 threads.
 __global__ void __launch_bounds__(256) pair_queries_kernel(const PairArgs a) {
@@ -231,14 +241,18 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   // records stored transposed (word w of token n at vt[w][n]) and the weights
   // split into three bf16 parts (columns g + 4 part); 3 bits: fp32 4x4x1 MFMA.
   constexpr bool VT = BITS != 3;
-  constexpr int NWV = REC / 4;            // words per record
-  constexpr int VROW = KS + 4;          // vt row (u32)
+  constexpr int CPH = 16 / BITS;          // channels per halfword of a record (2 and 4 bits)
+  constexpr int NHW = REC / 2;            // halfwords per record
+  constexpr int VPROW = KS / 2 + 16;      // vp row (u32): one word per token pair, padded
+                                          // so that a read's two to four rows hit other banks
   constexpr int PROW = KS + 8;          // weight row (bf16), 16-byte pieces spread over the banks
   constexpr int KBYTES = KS * REC > QS * 16 * PROW * 2 ? KS * REC : QS * 16 * PROW * 2;
 
   // the round's key records; after the scores, the bf16 weights [QS][16][PROW]
   __shared__ __align__(16) uint8_t kc_lds[KBYTES];
-  __shared__ __align__(16) uint8_t vc_lds[VT ? NWV * VROW * 4 : KS * REC];  // value records
+  // value records: token-pair words vp[j][i] = halfword j of token 2i + 1 << 16 | that of
+  // token 2i (2 and 4 bits), or the records as stored (3 bits)
+  __shared__ __align__(16) uint8_t vc_lds[VT ? NHW * VPROW * 4 : KS * REC];
   __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p * step_v
   __shared__ __align__(16) float dk_lds[KS];          // key step * scale * log2(e); 0: token absent
   __shared__ __align__(16) float off_lds[KS];         // 0, or -inf for an absent token
@@ -328,20 +342,17 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
     for (int k = 0; k < NACC; ++k) acc[qs][k] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  // 16x16x32 value product: lane (row vr_ch = 16 mt + lane % 16 of the wave's
-  // 32 channels, k group grp = 8 tokens); the code's word, byte and bit
+  // 16x16x32 value product: lane (row 16 mt + lane % 16 of the wave's 32
+  // channels, k group grp = 8 tokens); the row of its channel's halfword in
+  // vp and the rotation that takes the code from its place in each half to
+  // bit SH (5: 2 bits, 3: 4 bits)
   const int vch = 32 * w + (lane & 15);  // + 16 mt
-  int vword[2], vrot[2];
-  uint32_t vsel[2];
+  int vrow[2], vrot[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int j = vch + 16 * mt;
-    const int bit = BITS * j;                   // in the record's bit stream
-    vword[mt] = bit >> 5;
-    const int byte = (bit & 31) >> 3, inb = bit & 7;
-    vsel[mt] = (uint32_t)byte | 0x0C00u | ((uint32_t)(4 + byte) << 16) | 0x0C000000u;
-    // rotate the code from bit inb of each half's low byte to bit SH (5: 2 bits, 3: 4 bits)
-    vrot[mt] = (inb - (BITS == 2 ? 5 : 3)) & 31;
+    const int ch = vch + 16 * mt;
+    vrow[mt] = (ch / CPH) * VPROW;
+    vrot[mt] = (BITS * (ch % CPH) - (BITS == 2 ? 5 : 3)) & 31;
   }
   float m_run[NQ], lsum[NQ], vsum[NQ];  // running max (uniform); this thread's sums
 #pragma unroll
@@ -352,123 +363,111 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   }
   float k1 = 0.0f;
 
-  // ---- records of a round: CPT 16-byte pieces per record; rows outside the
-  // cache are read from row 0 and never used (their key step marks them absent)
+  // ---- records of a round: CPT 16-byte pieces per record, one load round
+  // (2 and 4 bits: the next round's records and steps are loaded into
+  // registers while this round is worked on, and go to LDS at its end).
+  // Tokens [t0, t1) of a round have cache rows (rows r0 + t in [0, n_rows),
+  // t < the round's count); the loads go through buffer resources over those
+  // rows only, so that every other token reads zeros and moves no bytes.
   constexpr int CPT = REC / 16;
-  constexpr int NLD = KS * CPT / 256;  // pieces per thread and cache
-  constexpr int NR = NLD > 4 ? 2 : 1;    // load rounds (at most 4 + 4 pieces in registers)
-  constexpr int PR = NLD / NR;
-  // one load round: the next round's records and steps are loaded into
-  // registers while this round is worked on, and go to LDS at its end
-  constexpr bool PF = NR == 1 && VT;
-  static_assert(!PF || VT, "the prefetch path writes the transposed value layout");
+  constexpr int PR = KS * CPT / 256;  // pieces per thread and cache
+  static_assert(PR * 256 == KS * CPT && PR <= 4, "one load round of at most four pieces");
+  constexpr bool PF = VT;  // prefetch the next round (3 bits: the registers are needed elsewhere)
+  // piece c of a round: 2 and 4 bits, pairs of tokens in neighbouring lanes
+  // (piece (2i + e, part) at c = 2 (CPT i + part) + e), so that a lane finds
+  // the same part of its pair partner's record in lane c ^ 1; 3 bits, c =
+  // CPT t + part
+  auto piece_tok = [&](int c) __attribute__((always_inline)) -> int {
+    return VT ? (((c >> 1) / CPT) << 1) | (c & 1) : c / CPT;
+  };
+  auto piece_part = [&](int c) __attribute__((always_inline)) -> int {
+    return VT ? (c >> 1) % CPT : c % CPT;
+  };
+  struct RoundSrc {
+    int t0, t1;
+    rsrc_t k, v, ks, vs;
+  };
+  const uint32_t row_stride = (uint32_t)Hkv * REC;  // bytes between cache rows (< 2^22)
+  auto round_src = [&](int base) __attribute__((always_inline)) -> RoundSrc {
+    const int cnt = min(cnt_all - base, KS);
+    const int64_t r0 = row_base + base;
+    const int64_t lo = r0 < 0 ? -r0 : 0, hi = a.n_rows - r0;
+    RoundSrc R;
+    R.t0 = (int)(lo < KS ? lo : KS);
+    R.t1 = (int)(hi < cnt ? (hi > 0 ? hi : 0) : cnt);
+    R.t1 = R.t1 > R.t0 ? R.t1 : R.t0;
+    const uint32_t n = (uint32_t)(R.t1 - R.t0);
+    const int64_t row = n ? r0 + R.t0 : 0;  // first present row
+    R.k = buffer_rsrc(a.kc + (row * Hkv + h) * REC, n * row_stride);
+    R.v = buffer_rsrc(a.vc + (row * Hkv + h) * REC, n * row_stride);
+    R.ks = buffer_rsrc(a.ks + row * Hkv + h, n * (uint32_t)Hkv * 2u);
+    R.vs = buffer_rsrc(a.vs + row * Hkv + h, n * (uint32_t)Hkv * 2u);
+    return R;
+  };
   u32x4 pk[PR], pv[PR];
   uint32_t pks[KS / 256], pvs[KS / 256];
-  auto prefetch = [&](int base) __attribute__((always_inline)) {
-    const int cnt = min(cnt_all - base, KS);
-    if (cnt <= 0) return;  // uniform
-    const int64_t r0 = row_base + base;
+  auto load_round = [&](int base) __attribute__((always_inline)) {
+    const RoundSrc R = round_src(base);
 #pragma unroll
     for (int j = 0; j < PR; ++j) {
-      const int c = tid + 256 * j, tok = c / CPT, part = c - tok * CPT;
-      if (tok < cnt) {
-        int64_t row = r0 + tok;
-        row = (row >= 0 && row < a.n_rows) ? row : 0;
-        const int64_t off = (row * Hkv + h) * REC + 16 * part;
-        pk[j] = *(const u32x4*)(a.kc + off);
-        pv[j] = *(const u32x4*)(a.vc + off);
+      const int c = tid + 256 * j;
+      // (t - t0) wraps to a huge offset below the first present row
+      // (24-bit multiply: |t - t0| <= 512 and row_stride < 2^22)
+      const uint32_t off = (uint32_t)__mul24(piece_tok(c) - R.t0, (int)row_stride) + 16u * piece_part(c);
+      pk[j] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
+      pv[j] = __builtin_amdgcn_raw_buffer_load_b128(R.v, off, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < KS / 256; ++j) {
+      const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 2 * Hkv);
+      pks[j] = __builtin_amdgcn_raw_buffer_load_b16(R.ks, off, 0, 0);
+      pvs[j] = __builtin_amdgcn_raw_buffer_load_b16(R.vs, off, 0, 0);
+    }
+  };
+  // the registers of load_round(base) -> LDS: records, and per token the key
+  // step * scale * log2(e), the -inf offset of an absent token and the value step
+  auto stage_round = [&](int base) __attribute__((always_inline)) {
+    const RoundSrc R = round_src(base);
+#pragma unroll
+    for (int j = 0; j < PR; ++j) {
+      const int c = tid + 256 * j, tok = piece_tok(c), part = piece_part(c);
+      *(u32x4*)&kc_lds[16 * (tok * CPT + part)] = pk[j];
+      if constexpr (VT) {
+        // halfwords of this token and its partner (lane c ^ 1): the even token
+        // writes the pair words of its words' low halfwords, the odd one those
+        // of the high halfwords
+        uint32_t* vp = (uint32_t*)vc_lds;
+        const uint32_t sel = (tok & 1) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t own = pv[j][e];
+          const uint32_t oth = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+          vp[(2 * (4 * part + e) + (tok & 1)) * VPROW + (tok >> 1)] = __builtin_amdgcn_perm(oth, own, sel);
+        }
+      } else {
+        *(u32x4*)&vc_lds[16 * (tok * CPT + part)] = pv[j];
       }
     }
 #pragma unroll
     for (int j = 0; j < KS / 256; ++j) {
       const int i = tid + 256 * j;
-      if (i < cnt) {
-        int64_t row = r0 + i;
-        row = (row >= 0 && row < a.n_rows) ? row : 0;
-        pks[j] = a.ks[row * Hkv + h];
-        pvs[j] = a.vs[row * Hkv + h];
-      }
+      const bool ok = i >= R.t0 && i < R.t1;
+      dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
+      off_lds[i] = ok ? 0.0f : NINF;
+      dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
     }
   };
-  if constexpr (PF) prefetch(0);
+  if constexpr (PF) load_round(0);
 
   for (int base = 0; base < cnt_all; base += KS) {
     const int cnt = min(cnt_all - base, KS);
-    const int64_t r0 = row_base + base;
-    if constexpr (PF) {
-      {
-        // written for every piece, also past the round's tokens (whose
-        // registers hold stale bits: those tokens are absent), so that every
-        // load is waited for here and nowhere else
-#pragma unroll
-        for (int j = 0; j < PR; ++j) {
-          const int c = tid + 256 * j;
-          *(u32x4*)&kc_lds[16 * c] = pk[j];
-          const int tok = c / CPT, part = c - tok * CPT;
-          uint32_t* vt = (uint32_t*)vc_lds;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = pv[j][e];
-        }
-#pragma unroll
-        for (int j = 0; j < KS / 256; ++j) {
-          const int i = tid + 256 * j;
-          const int64_t row = r0 + i;
-          const bool ok = i < cnt && row >= 0 && row < a.n_rows;
-          dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
-          off_lds[i] = ok ? 0.0f : NINF;
-          dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
-        }
-      }
-      __syncthreads();
-      prefetch(base + KS);
-    } else {
-    {
-#pragma unroll
-      for (int rd = 0; rd < NR; ++rd) {
-        u32x4 kr[PR], vr[PR];
-#pragma unroll
-        for (int j = 0; j < PR; ++j) {
-          const int c = tid + 256 * (rd * PR + j), tok = c / CPT, part = c - tok * CPT;
-          if (tok < cnt) {
-            int64_t row = r0 + tok;
-            row = (row >= 0 && row < a.n_rows) ? row : 0;
-            const int64_t off = (row * Hkv + h) * REC + 16 * part;
-            kr[j] = *(const u32x4*)(a.kc + off);
-            vr[j] = *(const u32x4*)(a.vc + off);
-          }
-        }
-        if (rd == 0) {
-          for (int i = tid; i < KS; i += 256) {
-            float dk = 0.0f, off = NINF, dv = 0.0f;
-            const int64_t row = r0 + i;
-            if (i < cnt && row >= 0 && row < a.n_rows) {
-              dk = f16_bits_to_f32(a.ks[row * Hkv + h]) * a.c0;
-              off = 0.0f;
-              dv = f16_bits_to_f32(a.vs[row * Hkv + h]);
-            }
-            dk_lds[i] = dk;
-            off_lds[i] = off;
-            dv_lds[i] = dv;
-          }
-        }
-        // written for every piece (past the round's tokens: stale bits of
-        // absent tokens), so that the loads are waited for here only
-#pragma unroll
-        for (int j = 0; j < PR; ++j) {
-          const int c = tid + 256 * (rd * PR + j);
-          *(u32x4*)&kc_lds[16 * c] = kr[j];
-          if constexpr (VT) {
-            const int tok = c / CPT, part = c - tok * CPT;
-            uint32_t* vt = (uint32_t*)vc_lds;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vt[(4 * part + e) * VROW + tok] = vr[j][e];
-          } else {
-            *(u32x4*)&vc_lds[16 * c] = vr[j];
-          }
-        }
-      }
-    }
+    if constexpr (!PF) load_round(base);
+    // every piece is written (tokens past the round's end read zeros), so that
+    // the loads are waited for here and nowhere else
+    stage_round(base);
     __syncthreads();
+    if constexpr (PF) {
+      if (base + KS < cnt_all) load_round(base + KS);
     }
     if (base == 0) k1 = col < NQ ? k1_lds[col] : 0.0f;
 
@@ -582,25 +581,21 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     // ---- values: wave w owns channels 32 w .. 32 w + 31 (the weights past
     // the round's tokens are 0)
     if constexpr (VT) {
-      const uint32_t* vt = (const uint32_t*)vc_lds;
+      const uint32_t* vp = (const uint32_t*)vc_lds;
       const uint16_t* pt = (const uint16_t*)kc_lds;
       constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : 0x00780078u;
       for (int n0 = 0; n0 < n16; n0 += 32) {
-        const int nk = n0 + 8 * grp;  // this lane's 8 tokens
+        const int nk = n0 + 8 * grp;  // this lane's 8 tokens: pairs nk / 2 .. nk / 2 + 3
         bf16x8 P[QS];
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) P[qs] = *(const bf16x8*)(pt + qs * 16 * PROW + col * PROW + nk);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const u32x4 wa = *(const u32x4*)(vt + vword[mt] * VROW + nk);
-          const u32x4 wb = *(const u32x4*)(vt + vword[mt] * VROW + nk + 4);
-          const uint32_t wv[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+          const u32x4 wp = *(const u32x4*)(vp + vrow[mt] + (nk >> 1));
           u32x4 av;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t pr = __builtin_amdgcn_perm(wv[2 * t + 1], wv[2 * t], vsel[mt]);
-            av[t] = (__builtin_amdgcn_alignbit(pr, pr, vrot[mt]) & VMASK) | 0x3F003F00u;
-          }
+          for (int t = 0; t < 4; ++t)
+            av[t] = (__builtin_amdgcn_alignbit(wp[t], wp[t], vrot[mt]) & VMASK) | 0x3F003F00u;
           const bf16x8 A = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
           for (int qs = 0; qs < QS; ++qs)
