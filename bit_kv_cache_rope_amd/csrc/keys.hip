@@ -318,48 +318,59 @@ __global__ void __launch_bounds__(256 * HG) keys_kernel(const KeysArgs a) {
     // RoPE does not also wait for those.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     if constexpr (!YOUT) {
-      if (j >= 1) {
+      // The later group (the only one with one group) stores both groups'
+      // records and steps of tile j - 1: a token's records of the block's
+      // heads are one contiguous run of the cache row (a whole 128-byte line
+      // for four 2-bit heads), written at once rather than in two halves one
+      // phase apart.  The earlier group's rows stay in LDS until its next
+      // phase 2, which comes after this phase.
+      if (j >= 1 && g == NG - 1) {
         const int sb = (j - 1) & 1;
-        // each token's group records are contiguous in the cache row
-        // (16-byte chunks, at most one per thread), then its scales (and zeros)
-        constexpr int CPT = HGG * BITS;  // 16-byte chunks per token
-        constexpr int NCH = kTile * CPT;  // <= 64 * WG
+        constexpr int CPG = HGG * BITS;      // 16-byte chunks per token and group
+        constexpr int CPB = NG * CPG;        // ... and block
+        constexpr int NCH = kTile * CPB;
         const uint32_t tg = (uint32_t)(tid - 64 * WG * g);  // thread within the group
         const uint32_t row_rec = (uint32_t)a.n_heads * REC;  // bytes per cache row
-        if (NCH == 64 * WG || tg < (uint32_t)NCH) {
-          const uint32_t n = tg / CPT, k = tg - n * CPT;
+#pragma unroll
+        for (uint32_t c = tg; c < (uint32_t)NCH; c += 64 * WG) {
+          const uint32_t n = c / CPB, k = c - n * CPB, gg = k / CPG, kk = k - gg * CPG;
           const int32_t row = slot_lds[sb][n];
           if (row >= 0) {
             // (24-bit multiply: a full 32-bit one issues at a quarter of the rate)
-            const u32x4 v = *(const u32x4*)((const uint8_t*)rec_lds[g] + __umul24(n, RECROW) + 16 * k);
-            uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + ((grp * HG + g * HGG) * REC + 16 * k);
+            const u32x4 v = *(const u32x4*)((const uint8_t*)rec_lds[gg] + __umul24(n, RECROW) + 16 * kk);
+            uint8_t* dst = a.codes + (uint64_t)(uint32_t)row * row_rec + (grp * HG * REC + 16 * k);
             __builtin_nontemporal_store(v, (u32x4*)dst);  // written once, not read back here
           }
         }
-        if constexpr (QK == 0) {
-          // one store of the group's HGG fp16 steps per token, by its last wave
-          const int n = (int)tg - (64 * WG - 64);
-          if (n >= 0) {
-            const int32_t row = slot_lds[sb][n];
-            if (row >= 0) {
-              uint16_t* dst = a.scales + (uint64_t)(uint32_t)row * a.n_heads + grp * HG + g * HGG;
-              if constexpr (HGG == 2) {
-                *(uint32_t*)dst = *(const uint32_t*)&sc_lds[g][n][0];
+        // the block's HG heads' steps (and zeros) of a token, by the group's last wave
+        const int n = (int)tg - (64 * WG - 64);
+        if (n >= 0) {
+          const int32_t row = slot_lds[sb][n];
+          if (row >= 0) {
+            const uint64_t slot = (uint64_t)(uint32_t)row * a.n_heads + grp * HG;
+            if constexpr (QK == 0) {
+              uint16_t sv[HG];
+#pragma unroll
+              for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+                for (int hg2 = 0; hg2 < HGG; ++hg2) sv[gg * HGG + hg2] = sc_lds[gg][n][hg2];
+              if constexpr (HG == 4) {
+                *(uint2*)(a.scales + slot) = make_uint2(sv[0] | ((uint32_t)sv[1] << 16), sv[2] | ((uint32_t)sv[3] << 16));
+              } else if constexpr (HG == 2) {
+                *(uint32_t*)(a.scales + slot) = sv[0] | ((uint32_t)sv[1] << 16);
               } else {
-                *dst = sc_lds[g][n][0];
+                a.scales[slot] = sv[0];
               }
-            }
-          }
-        } else {
-          // per (token, head): 4 scales and 4 zeros, 8 bytes each
-          const int c = (int)tg - (64 * WG - 64 * HGG);
-          if (c >= 0) {
-            const int n = c / HGG, jh = c - n * HGG;
-            const int32_t row = slot_lds[sb][n];
-            if (row >= 0) {
-              const uint64_t slot = (uint64_t)(uint32_t)row * a.n_heads + grp * HG + g * HGG + jh;
-              *(uint2*)(a.scales + slot * 4) = *(const uint2*)&sc_lds[g][n][jh * 8];
-              *(uint2*)(a.zeros + slot * 4) = *(const uint2*)&sc_lds[g][n][jh * 8 + 4];
+            } else {
+              // per head: 4 scales and 4 zeros, 8 bytes each
+#pragma unroll
+              for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+                for (int hg2 = 0; hg2 < HGG; ++hg2) {
+                  const uint64_t sl = slot + gg * HGG + hg2;
+                  *(uint2*)(a.scales + sl * 4) = *(const uint2*)&sc_lds[gg][n][hg2 * 8];
+                  *(uint2*)(a.zeros + sl * 4) = *(const uint2*)&sc_lds[gg][n][hg2 * 8 + 4];
+                }
             }
           }
         }
