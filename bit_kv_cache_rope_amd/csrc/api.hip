@@ -544,6 +544,9 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
   if (n_tokens == 0) return WUSHKV_OK;
   if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
   if (!aligned(out, 16)) return fail(WUSHKV_ERR_ALIGNMENT, "out must be 16-byte aligned");
+  // without T_k_inv one thread per (token, head) vector, in one dispatch
+  if (!T_k_inv && n_tokens * n_heads > ((int64_t)1 << 32) - 256)
+    return fail(WUSHKV_ERR_UNSUPPORTED, "n_tokens * n_heads must be at most 2^32 - 256 without T_k_inv");
   int dev;
   st = current_device(&dev);
   if (st) return st;
@@ -592,8 +595,10 @@ wushkv_status wushkv_debug_time_next_launch(void* start, void* stop) {
 
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos, int64_t n, float* cs_out,
                                         void* stream) {
-  if (!rope) return fail(WUSHKV_ERR_INVALID_ARG, "rope handle is NULL");
   if (n < 0) return fail(WUSHKV_ERR_INVALID_ARG, "n < 0");
+  if (n > ((int64_t)1 << 26))  // one thread per (position, pair) in one dispatch
+    return fail(WUSHKV_ERR_UNSUPPORTED, "n must be at most 2^26");
+  if (!rope) return fail(WUSHKV_ERR_INVALID_ARG, "rope handle is NULL");
   if (n == 0) return WUSHKV_OK;
   if (!pos || !cs_out) return fail(WUSHKV_ERR_INVALID_ARG, "pos and cs_out must be set");
   hipError_t e = wushkv::launch_gather_cs(rope, pos, n, cs_out, (hipStream_t)stream);
@@ -601,19 +606,24 @@ wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* 
   return WUSHKV_OK;
 }
 
+static constexpr int64_t kMaxPairVecs = ((int64_t)1 << 26) - 4;
+
 wushkv_status wushkv_pair_queries(const void* Q, wushkv_dtype q_dtype, int64_t n_tokens, int n_q_heads,
                                   int64_t token_stride, const wushkv_transform* T_k_inv, void* q_out,
                                   void* stream) {
   wushkv_status st = check_tensor(Q, q_dtype, n_tokens, n_q_heads, token_stride);
   if (st) return st;
+  if (n_tokens > kMaxPairVecs)  // at least one query vector per token and KV head
+    return fail(WUSHKV_ERR_UNSUPPORTED, "more than 2^26 - 4 query vectors per KV head in one call");
   if (!T_k_inv) return fail(WUSHKV_ERR_INVALID_ARG, "transform handle is NULL");
   if (n_q_heads % T_k_inv->n_heads)
     return fail(WUSHKV_ERR_INVALID_ARG, "n_q_heads must be a multiple of the transform's head count");
   if (n_tokens == 0) return WUSHKV_OK;
   if (!q_out) return fail(WUSHKV_ERR_INVALID_ARG, "q_out is NULL");
   if (!aligned(q_out, 2)) return fail(WUSHKV_ERR_ALIGNMENT, "q_out must be 2-byte aligned");
-  if (n_tokens * (n_q_heads / T_k_inv->n_heads) > ((int64_t)1 << 32))  // grid of 4 vectors per block
-    return fail(WUSHKV_ERR_UNSUPPORTED, "more than 2^32 query vectors per KV head in one call");
+  // 256-thread blocks of 4 query vectors: fewer than 2^24 blocks per KV head
+  if (n_tokens * (n_q_heads / T_k_inv->n_heads) > kMaxPairVecs)
+    return fail(WUSHKV_ERR_UNSUPPORTED, "more than 2^26 - 4 query vectors per KV head in one call");
   int dev;
   st = current_device(&dev);
   if (st) return st;
@@ -641,6 +651,12 @@ static wushkv_status attention_shape(int n_seqs, int n_q_heads, int n_kv_heads, 
   if (n_q_heads / n_kv_heads > 8) return fail(WUSHKV_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
   if (n_q_heads > 65535) return fail(WUSHKV_ERR_INVALID_ARG, "n_q_heads above 65535");
   if (max_seq_len < 0 || max_seq_len > (1 << 30)) return fail(WUSHKV_ERR_INVALID_ARG, "max_seq_len must be in [0, 2^30]");
+  // one 256-thread block per (sequence, KV head, split), splits rounded up to
+  // a multiple of 8: a dispatch holds fewer than 2^32 work-items
+  const int64_t splits8 = ((int64_t)wushkv::attention_splits(max_seq_len) + 7) / 8;
+  if (8 * splits8 * n_kv_heads * (int64_t)n_seqs >= ((int64_t)1 << 24))
+    return fail(WUSHKV_ERR_UNSUPPORTED, "a call needs 8 * ceil(ceil(max_seq_len / 2048) / 8) * n_kv_heads * n_seqs "
+                                        "below 2^24 (one 256-thread block each)");
   return WUSHKV_OK;
 }
 
@@ -709,8 +725,6 @@ static wushkv_status attention_common(const void* q_paired, int n_seqs, int n_q_
   a.max_len = max_seq_len;
   a.n_splits = wushkv::attention_splits(max_seq_len);
   a.n_splits8 = (a.n_splits + 7) / 8;
-  if ((int64_t)8 * a.n_splits8 * n_kv_heads * n_seqs > INT32_MAX)
-    return fail(WUSHKV_ERR_UNSUPPORTED, "too many (sequence, KV head, split) blocks for one call");
   a.c0 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
   a.part = (float*)workspace;
   a.out = out;

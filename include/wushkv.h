@@ -185,7 +185,9 @@ wushkv_status wushkv_quantize_kv(const void* K, const void* V, wushkv_dtype dtyp
  * dequantized into out[n_tokens][n_heads][128] (fp32 or bf16, contiguous,
  * 16-byte aligned).  T_k_inv: NULL for values (or for keys kept in the
  * transformed basis); otherwise a transform handle holding T_k^-1, applied as
- * k^ = T~inv y^ with bf16 T~inv and fp32 accumulation. */
+ * k^ = T~inv y^ with bf16 T~inv and fp32 accumulation.  Without T_k_inv the
+ * call is one thread per vector in one dispatch: n_tokens * n_heads at most
+ * 2^32 - 256, else WUSHKV_ERR_UNSUPPORTED. */
 wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n_heads, int bits,
                                 const wushkv_quantizer* quantizer,
                                 const wushkv_transform* T_k_inv, void* out,
@@ -199,9 +201,10 @@ wushkv_status wushkv_dequantize(const wushkv_packed* in, int64_t n_tokens, int n
  * consume the cached keys in view).
  *   Q: device, bf16 or fp32, [n_tokens][n_q_heads][128] with token_stride
  *      elements per token (same rules as K); query head hq reads KV head
- *      hq / (n_q_heads / T_k_inv's head count).  At most 2^32 query vectors
- *      per KV head (n_tokens * n_q_heads / heads) per call, else
- *      WUSHKV_ERR_UNSUPPORTED.
+ *      hq / (n_q_heads / T_k_inv's head count).  At most 2^26 - 4 query
+ *      vectors per KV head (n_tokens * n_q_heads / heads) per call (one
+ *      256-thread block per four, and a dispatch holds fewer than 2^32
+ *      work-items), else WUSHKV_ERR_UNSUPPORTED.
  *   T_k_inv: transform handle holding T_k^-1 (the read path's), bf16 T~inv.
  *   q_out: device bf16 [n_tokens][n_q_heads][128], contiguous, caller-owned:
  *      q'_j = bf16(RN32(sum_r T~inv[r][j] q_r)), the sum exact before the fp32
@@ -237,8 +240,11 @@ wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n
  *   out: device fp32 [n_seqs][n_q_heads][128].
  * Precision: codes and steps exact; q' bf16; scores accumulated in fp32 on
  * MFMA; exp2 and the weighted sum of values in fp32 (no bf16 rounding of the
- * weights).  Affine caches return WUSHKV_ERR_UNSUPPORTED.  n_seqs == 0 is a
- * no-op. */
+ * weights).  Affine caches return WUSHKV_ERR_UNSUPPORTED, and so do calls
+ * with 8 * ceil(ceil(max_seq_len / 2048) / 8) * n_kv_heads * n_seqs at or
+ * above 2^24 (one 256-thread block each; a dispatch holds fewer than 2^32
+ * work-items), also from wushkv_decode_attention_workspace.  n_seqs == 0 is
+ * a no-op. */
 wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_heads,
                                       const wushkv_packed* k_cache, const wushkv_packed* v_cache,
                                       int n_kv_heads, int bits, const wushkv_quantizer* quantizer,
@@ -276,7 +282,8 @@ wushkv_status wushkv_debug_rope_transform(const void* K, wushkv_dtype k_dtype, i
 
 /* Test support: the (cos, sin) pairs the key kernel uses, cs_out[n][64][2]
  * fp32 (device), for device positions pos[n] (clamped to [0, max_pos)),
- * computed by the same device function. */
+ * computed by the same device function.  n at most 2^26 (one thread per
+ * position and pair), else WUSHKV_ERR_UNSUPPORTED. */
 wushkv_status wushkv_debug_rope_cos_sin(const wushkv_rope* rope, const int32_t* pos,
                                         int64_t n, float* cs_out, void* stream);
 

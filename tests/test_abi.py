@@ -138,6 +138,20 @@ def test_validation_without_device(lib):
     assert att(2, ws=100) == _lib.ERR_INVALID_ARG
     assert att(2, sc=float("inf")) == _lib.ERR_INVALID_ARG
     assert att(0) == _lib.OK
+    # dispatch sizes: every grid stays below 2^32 work-items (256-thread blocks)
+    assert L.wushkv_decode_attention_workspace(65535, 64, 8, 131072, ctypes.byref(nb)) == _lib.ERR_UNSUPPORTED
+    assert L.wushkv_decode_attention_workspace(32767, 64, 8, 131072, ctypes.byref(nb)) == _lib.OK  # 2^24 - 512 blocks
+    big = lambda n, H, heads, dl: L.wushkv_decode_attention(
+        vp(16), n, H, ctypes.byref(p), ctypes.byref(p), heads, 2, ctypes.byref(q), vp(16), vp(16), dl,
+        ctypes.c_float(0.1), vp(16), 1 << 20, vp(16), None)
+    assert big(65535, 64, 8, 131072) == _lib.ERR_UNSUPPORTED
+    assert L.wushkv_pair_queries(vp(16), 1, (1 << 26) - 3, 8, 1024, None, vp(16), None) == _lib.ERR_UNSUPPORTED
+    assert L.wushkv_pair_queries(vp(16), 1, (1 << 26) - 4, 8, 1024, None, vp(16), None) == _lib.ERR_INVALID_ARG
+    huge = _packed(rows=(1 << 31) - 1)
+    assert L.wushkv_dequantize(ctypes.byref(huge), 1 << 24, 512, 2, ctypes.byref(q), None, vp(16), 1,
+                               None) == _lib.ERR_UNSUPPORTED
+    assert L.wushkv_debug_rope_cos_sin(None, vp(16), (1 << 26) + 1, vp(16), None) == _lib.ERR_UNSUPPORTED
+    assert L.wushkv_debug_rope_cos_sin(None, vp(16), 1 << 26, vp(16), None) == _lib.ERR_INVALID_ARG
     # handles
     h = vp()
     assert L.wushkv_rope_create(ctypes.c_float(1e6), 0, ctypes.byref(h)) == _lib.ERR_INVALID_ARG
