@@ -554,8 +554,9 @@ def main() -> int:
     h1_v_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev1])) * 1e3
     h1_bytes = N * (key_bytes_per_token(1, bits) + value_bytes_per_token(1, bits)) + D * D * 2
 
-    # ---- structured key transforms through the same dense path (Hadamard / 8; four 32 x 32
-    # blocks on the diagonal): the key kernel's time on the benchmark layer, one buffer set
+    # ---- structured key transforms (Hadamard / 8; four 32 x 32 blocks on the diagonal): the key
+    # kernel's time on the benchmark layer, one buffer set, through the dense MFMA path, and
+    # Hadamard / 8 also through the in-register fast Walsh-Hadamard path (Transform.hadamard)
     Hd = np.array([[1.0]])
     while Hd.shape[0] < D:
         Hd = np.block([[Hd, Hd], [Hd, -Hd]])
@@ -566,8 +567,8 @@ def main() -> int:
             blk[hh, 32 * bb:32 * bb + 32, 32 * bb:32 * bb + 32] = brng.standard_normal((32, 32)) / np.sqrt(32) + 2 * np.eye(32)
     struct_us = {}
     for tname, Tm in (("dense", T), ("hadamard", np.stack([Hd / 8.0] * H).astype(np.float32)),
-                      ("block_diagonal", blk)):
-        th = bk.Transform(Tm)
+                      ("block_diagonal", blk), ("hadamard_fwht", None)):
+        th = bk.Transform(Tm) if Tm is not None else bk.Transform.hadamard(H)
         call = bk.prepare_quantize_keys(sets[0]["K"], sets[0]["pos"], rope, th, bits, q, sets[0]["ko"], stream=stream)
         for _ in range(20 * rep):
             call()
@@ -707,7 +708,9 @@ def main() -> int:
         "one_kv_head_share": {"tokens": N, "kv_heads": 1, "keys_us": round(h1_k_us, 2), "values_us": round(h1_v_us, 2),
                               "gbs": round(h1_bytes / ((h1_k_us + h1_v_us) * 1e-6) / 1e9, 1),
                               "note": "one GPU's share under 8-way KV-head parallelism; keys then values on one stream"},
-        "structured_transforms_keys_us": dict(struct_us, note="key kernel on the benchmark layer, one buffer set"),
+        "structured_transforms_keys_us": dict(struct_us, note="key kernel on the benchmark layer, one buffer set; "
+                                              "hadamard: H/8 through the dense MFMA path, hadamard_fwht: the same "
+                                              "transform as an in-register fast Walsh-Hadamard transform"),
         "decode_attention": {
             "sequences": dn, "q_heads": att_q, "kv_heads": H, "bits": bits,
             "cached_tokens": int(att_len.sum()), "max_len": int(att_len.max()),

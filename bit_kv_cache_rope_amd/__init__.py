@@ -79,7 +79,9 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 class Transform:
-    """Key transform handle (T_k, or T_k^-1 for reads); T: [H][128][128] fp32, y = T x."""
+    """Key transform handle (T_k, or T_k^-1 for reads); T: [H][128][128] fp32, y = T x.
+    Transform.hadamard(H) is the structured handle T = H_128 / 8 whose key path is a fast
+    Walsh-Hadamard transform (wushkv_transform_create_hadamard)."""
 
     def __init__(self, T):
         T = torch.as_tensor(T).detach().to("cpu", torch.float32).contiguous()
@@ -89,6 +91,15 @@ class Transform:
         h = ctypes.c_void_p()
         _lib.check(library().wushkv_transform_create(ctypes.c_void_p(T.data_ptr()), self.n_heads, ctypes.byref(h)))
         self._h = h
+
+    @classmethod
+    def hadamard(cls, n_heads: int) -> "Transform":
+        t = cls.__new__(cls)
+        t.n_heads = int(n_heads)
+        h = ctypes.c_void_p()
+        _lib.check(library().wushkv_transform_create_hadamard(t.n_heads, ctypes.byref(h)))
+        t._h = h
+        return t
 
     @property
     def handle(self) -> ctypes.c_void_p:

@@ -19,7 +19,7 @@ EXPORTED = [
     "wushkv_debug_rope_transform", "wushkv_debug_rope_cos_sin", "wushkv_debug_time_next_launch",
     "wushkv_status_string", "wushkv_last_error", "wushkv_version", "wushkv_pair_queries",
     "wushkv_decode_attention_workspace", "wushkv_decode_attention", "wushkv_decode_attention_noalloc",
-    "wushkv_quantize_kv", "wushkv_debug_check_arith",
+    "wushkv_quantize_kv", "wushkv_debug_check_arith", "wushkv_transform_create_hadamard",
 ]
 
 
@@ -54,6 +54,7 @@ def load() -> ctypes.CDLL:
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     qp, pp = ctypes.POINTER(Quantizer), ctypes.POINTER(Packed)
     L.wushkv_transform_create.argtypes = [vp, i32, ctypes.POINTER(vp)]
+    L.wushkv_transform_create_hadamard.argtypes = [i32, ctypes.POINTER(vp)]
     L.wushkv_transform_destroy.argtypes = [vp]
     L.wushkv_rope_create.argtypes = [f32, ctypes.c_int32, ctypes.POINTER(vp)]
     L.wushkv_rope_destroy.argtypes = [vp]

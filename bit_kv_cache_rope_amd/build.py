@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "wushkv")
 LIB_PATH = os.path.join(HERE, "libwushkv.so")
-SOURCES = ["api.hip", "keys.hip", "values.hip", "kv_append.hip", "dequant.hip", "attention.hip", "arith_check.hip"]
+SOURCES = ["api.hip", "keys.hip", "keys_fwht.hip", "values.hip", "kv_append.hip", "dequant.hip", "attention.hip", "arith_check.hip"]
 HEADERS = ["device_common.h", "internal.h"]
 ARCH = os.environ.get("WUSHKV_OFFLOAD_ARCH", "gfx950")
 

@@ -211,11 +211,7 @@ wushkv_status wushkv_rope_frequencies(float theta, float* omega_out) {
   return WUSHKV_OK;
 }
 
-wushkv_status wushkv_transform_create(const float* T, int n_heads, wushkv_transform** out) {
-  if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
-  if (!T) return fail(WUSHKV_ERR_INVALID_ARG, "T is NULL");
-  if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
+static wushkv_status transform_create(const float* T, int n_heads, int hadamard, wushkv_transform** out) {
   int dev;
   wushkv_status st = current_device(&dev);
   if (st) return st;
@@ -244,6 +240,7 @@ wushkv_status wushkv_transform_create(const float* T, int n_heads, wushkv_transf
   if (!t) return fail(WUSHKV_ERR_OOM, "host allocation failed");
   t->n_heads = n_heads;
   t->device = dev;
+  t->hadamard = hadamard;
   hipError_t e = hipMalloc(&t->d_swz, swz.size() * 2);
   if (e != hipSuccess) { delete t; return fail(WUSHKV_ERR_OOM, "hipMalloc for the transform failed"); }
   e = hipMalloc((void**)&t->d_gsum, gsum.size() * 4);
@@ -256,6 +253,28 @@ wushkv_status wushkv_transform_create(const float* T, int n_heads, wushkv_transf
   }
   *out = t;
   return WUSHKV_OK;
+}
+
+wushkv_status wushkv_transform_create(const float* T, int n_heads, wushkv_transform** out) {
+  if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!T) return fail(WUSHKV_ERR_INVALID_ARG, "T is NULL");
+  if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
+  return transform_create(T, n_heads, 0, out);
+}
+
+wushkv_status wushkv_transform_create_hadamard(int n_heads, wushkv_transform** out) {
+  if (!out) return fail(WUSHKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (n_heads < 1 || n_heads > 4096) return fail(WUSHKV_ERR_INVALID_ARG, "n_heads out of range");
+  // the dense matrix as well (H[r][c] = (-1)^popcount(r & c) / 8), for the calls
+  // that read it: the fused append kernel and the debug transform of dense handles
+  const size_t D = WUSHKV_HEAD_DIM;
+  std::vector<float> T((size_t)n_heads * D * D);
+  for (size_t h = 0; h < (size_t)n_heads; ++h)
+    for (size_t r = 0; r < D; ++r)
+      for (size_t c = 0; c < D; ++c) T[(h * D + r) * D + c] = (__builtin_popcountll(r & c) & 1) ? -0.125f : 0.125f;
+  return transform_create(T.data(), n_heads, 1, out);
 }
 
 wushkv_status wushkv_transform_destroy(wushkv_transform* t) {
@@ -412,7 +431,9 @@ static wushkv_status keys_common(const void* K, wushkv_dtype k_dtype, int64_t n_
   a.q = qa;
   a.y_out = y_out;
   a.n_groups = n_heads / hg;
-  hipError_t e = wushkv::launch_keys(a, bits, k_dtype == WUSHKV_F32, hg, y_out != nullptr, cus, (hipStream_t)stream);
+  hipError_t e = T_k->hadamard
+                     ? wushkv::launch_keys_fwht(a, bits, k_dtype == WUSHKV_F32, y_out != nullptr, cus, (hipStream_t)stream)
+                     : wushkv::launch_keys(a, bits, k_dtype == WUSHKV_F32, hg, y_out != nullptr, cus, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "key kernel launch");
   return WUSHKV_OK;
 }

@@ -14,6 +14,7 @@
 struct wushkv_transform {
   int n_heads;
   int device;
+  int hadamard;    // 1: T = H_128 / 8 for every head, and the key path takes the FWHT kernel
   void* d_swz;     // bf16 [H][4][8][64][8]
   float* d_gsum;   // [H][4][128]: sum over j in group g of T~[h][r][j], for affine reads
 };
@@ -192,6 +193,9 @@ hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, hipStream_t st,
 // kernel's occupancy.
 hipError_t launch_keys(const KeysArgs& a, int bits, int f32_in, int heads_per_group, int y_out, int cus,
                        hipStream_t stream);
+// Keys through T = H_128 / 8 as an in-register fast Walsh-Hadamard transform
+// (handles made by wushkv_transform_create_hadamard); a.T is not read.
+hipError_t launch_keys_fwht(const KeysArgs& a, int bits, int f32_in, int y_out, int cus, hipStream_t st);
 hipError_t launch_values(const ValuesArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int bits, int f32_in, int cus, hipStream_t stream);
 // Exhaustive device check of the correctly rounded sqrt and div_small: mismatch counts

@@ -123,6 +123,19 @@ typedef struct wushkv_rope wushkv_rope;           /* opaque, library-owned */
  * operand order the kernels read.  The same call prepares T_k^-1 for reads.
  * Allocates device memory (not a hot-path call). */
 wushkv_status wushkv_transform_create(const float* T_host, int n_heads, wushkv_transform** out);
+
+/* Structured key transform: T = H_128 / 8 for every head, H the Sylvester
+ * Hadamard matrix (H[r][c] = (-1)^popcount(r & c)), the pages' fixed-rotation
+ * baseline (ai4snews summary "WUSH-KV cuts 2-bit KV-cache perplexity ...",
+ * method paragraph; cheaper structured transforms: limitations paragraph).
+ * wushkv_quantize_keys and wushkv_debug_rope_transform take such a handle
+ * through an in-register fast Walsh-Hadamard transform (7 butterfly stages in
+ * fp32, no matrix product); the same T given to wushkv_transform_create runs
+ * through the dense MFMA product.  Both compute y = T bf16(RoPE(k)) with fp32
+ * accumulation and differ only in the order of the roundings.  The handle
+ * holds the dense bf16 matrix too, which wushkv_quantize_kv uses.  Allocates
+ * device memory (not a hot-path call). */
+wushkv_status wushkv_transform_create_hadamard(int n_heads, wushkv_transform** out);
 wushkv_status wushkv_transform_destroy(wushkv_transform* t);
 
 /* RoPE handle for base theta and positions [0, max_pos), max_pos <= 2^24.

@@ -394,9 +394,11 @@ def unpack_codes(codes, bits):
 NEAR = 1e-6
 
 
-def account_keys(env, K, pos, T, bits, q, what, g=None):
+def account_keys(env, K, pos, T, bits, q, what, g=None, y_gpu=None):
     """Compare GPU keys with the oracle and attribute every mismatch.  `g`: the
-    GPU's packed rows for exactly these tokens (else the keys are run here).
+    GPU's packed rows for exactly these tokens (else the keys are run here);
+    `y_gpu`: the GPU's transformed keys that produced them (else those of the
+    dense path through T).
 
     A code may differ only if (a) the oracle's y lies within NEAR * step of the
     level midpoint that separates the two codes and the GPU's y lies on the
@@ -410,7 +412,7 @@ def account_keys(env, K, pos, T, bits, q, what, g=None):
         g = packed_host(run_keys(env, K, pos, T, bits, q))
     r = o.quantize_keys(K, pos, T, 1e6, bits, oracle_q(env, q), want_y=True)
     yr = r["y"].astype(np.float64)
-    yg = _y_gpu(env, K, pos, T).astype(np.float64)
+    yg = (_y_gpu(env, K, pos, T) if y_gpu is None else y_gpu).astype(np.float64)
     gq, rq = unpack_codes(g["codes"], bits), unpack_codes(r["codes"], bits)
     mism = gq != rq
     L = 1 << bits
