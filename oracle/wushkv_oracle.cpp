@@ -525,6 +525,16 @@ void dequant_sym(const uint8_t* rec, uint16_t step, int bits, double* y) {
   for (int j = 0; j < kD; ++j) y[j] = ((double)q[j] - m) * d;
 }
 
+// z_g + code * s_g for a percentile-clipped affine record (group g = j / 32, four
+// fp16 steps and zeros per record): exact in fp64 (an fp16 zero plus a code of at
+// most 4 bits times an fp16 step).  ai4snews summary, end-to-end paragraph.
+void dequant_affine(const uint8_t* rec, const uint16_t* steps, const uint16_t* zeros, int bits, double* y) {
+  uint8_t q[kD];
+  unpack(rec, bits, q);
+  for (int j = 0; j < kD; ++j)
+    y[j] = (double)f16_to_f32(zeros[j / 32]) + (double)q[j] * (double)f16_to_f32(steps[j / 32]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -554,8 +564,10 @@ int wko_pair_queries(const void* Q, int q_dtype, int64_t N, int Hq, int64_t toke
   return 0;
 }
 
-// Decode attention over symmetric packed caches.  Sequence b's tokens are the
-// cache rows row0[b] + n, n < len[b]; rows outside [0, n_rows) are absent.
+// Decode attention over packed caches: symmetric (kzeros and vzeros NULL, one
+// step per record) or percentile-clipped affine (both set; four steps and four
+// zeros per record).  Sequence b's tokens are the cache rows row0[b] + n,
+// n < len[b]; rows outside [0, n_rows) are absent.
 // For query head hq (KV head hq / G) with paired query q' (bf16 [B][Hq][128]):
 //   s_n = scale * sum_j q'_j y^_nj        (y^: dequantized keys, fp64 sum)
 //   o   = sum_n exp(s_n - max s) v^_n / sum_n exp(s_n - max s)
@@ -563,12 +575,21 @@ int wko_pair_queries(const void* Q, int q_dtype, int64_t N, int Hq, int64_t toke
 // Keys are scored in their transformed basis and values read as stored (their
 // transform is folded into the weights): ai4snews summary, deployment paragraph.
 int wko_decode_attention(const uint16_t* qp, int B, int Hq, int Hkv, const uint8_t* kcodes,
-                         const uint16_t* kscales, const uint8_t* vcodes, const uint16_t* vscales,
-                         int64_t n_rows, int bits, const int64_t* row0, const int32_t* len,
-                         float scale, float* out, int threads) {
+                         const uint16_t* kscales, const uint16_t* kzeros, const uint8_t* vcodes,
+                         const uint16_t* vscales, const uint16_t* vzeros, int64_t n_rows, int bits,
+                         const int64_t* row0, const int32_t* len, float scale, float* out, int threads) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || bits < 2 || bits > 4 || n_rows < 0) return -1;
+  if ((kzeros == nullptr) != (vzeros == nullptr)) return -1;
+  const bool affine = kzeros != nullptr;
   const int G = Hq / Hkv;
   const int rec = 16 * bits;
+  auto dequant = [&](const uint8_t* codes, const uint16_t* steps, const uint16_t* zeros, int64_t slot, double* y) {
+    if (affine) {
+      dequant_affine(codes + slot * rec, steps + slot * 4, zeros + slot * 4, bits, y);
+    } else {
+      dequant_sym(codes + slot * rec, steps[slot], bits, y);
+    }
+  };
   parallel_for((int64_t)B * Hq, threads, [&](int64_t u0, int64_t u1) {
     double y[kD], v[kD], q[kD], o[kD];
     std::vector<double> s;
@@ -583,7 +604,7 @@ int wko_decode_attention(const uint16_t* qp, int B, int Hq, int Hkv, const uint8
         const int64_t row = row0[b] + n;
         if (row < 0 || row >= n_rows) continue;
         const int64_t slot = row * Hkv + h;
-        dequant_sym(kcodes + slot * rec, kscales[slot], bits, y);
+        dequant(kcodes, kscales, kzeros, slot, y);
         double acc = 0.0;
         for (int j = 0; j < kD; ++j) acc += q[j] * y[j];
         s.push_back((double)scale * acc);
@@ -596,7 +617,7 @@ int wko_decode_attention(const uint16_t* qp, int B, int Hq, int Hkv, const uint8
         for (size_t i = 0; i < s.size(); ++i) {
           const double p = std::exp(s[i] - M);
           const int64_t slot = rows[i] * Hkv + h;
-          dequant_sym(vcodes + slot * rec, vscales[slot], bits, v);
+          dequant(vcodes, vscales, vzeros, slot, v);
           for (int j = 0; j < kD; ++j) o[j] += p * v[j];
           l += p;
         }

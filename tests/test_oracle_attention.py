@@ -164,3 +164,79 @@ def test_absent_rows_and_empty_sequences(oracle_mod):
     cut = oracle_mod.decode_attention(qp[:2], k, v, bits, np.array([40, 0]), np.array([10, 5]), 0.2)
     np.testing.assert_array_equal(out[:2], cut)
     np.testing.assert_array_equal(out[2], np.zeros((1, D), np.float32))
+
+
+# ------------------------------------------------------------------ affine caches (P1 end-to-end paragraph)
+
+def random_affine_cache(rng, rows, H, bits):
+    """Random codes with four fp16 steps (positive) and zeros per record."""
+    codes = rng.integers(0, 256, (rows, H, 16 * bits), dtype=np.uint8)
+    steps = np.abs(rng.standard_normal((rows, H, 4)) * 0.05 + 0.1).astype(np.float16).view(np.uint16)
+    zeros = (rng.standard_normal((rows, H, 4)) * 0.3).astype(np.float16).view(np.uint16)
+    return dict(codes=codes, scales=steps, zeros=zeros)
+
+
+def dequant_affine(rec, steps, zeros, bits):
+    """z_g + q s_g per 32-channel group g, from the fp16 bit patterns."""
+    q = unpack_codes(rec, bits).astype(np.float64)
+    s = np.asarray(steps, np.uint16).view(np.float16).astype(np.float64)
+    z = np.asarray(zeros, np.uint16).view(np.float16).astype(np.float64)
+    g = np.arange(D) // 32
+    return z[g] + q * s[g]
+
+
+def test_affine_single_token_returns_its_value(oracle_mod):
+    rng = np.random.default_rng(23)
+    for bits in (2, 3, 4):
+        k, v = random_affine_cache(rng, 5, 2, bits), random_affine_cache(rng, 5, 2, bits)
+        qp = bf16_bits_of(rng.standard_normal((1, 4, D)))
+        out = oracle_mod.decode_attention(qp, k, v, bits, np.array([2]), np.array([1]), 0.3)
+        for hq in range(4):
+            h = hq // 2
+            want = dequant_affine(v["codes"][2, h], v["scales"][2, h], v["zeros"][2, h], bits).astype(np.float32)
+            np.testing.assert_array_equal(out[0, hq], want)
+
+
+def test_affine_zero_query_gives_the_mean(oracle_mod):
+    rng = np.random.default_rng(24)
+    bits, rows = 3, 40
+    k, v = random_affine_cache(rng, rows, 1, bits), random_affine_cache(rng, rows, 1, bits)
+    qp = np.zeros((1, 1, D), np.uint16)
+    out = oracle_mod.decode_attention(qp, k, v, bits, np.array([4]), np.array([30]), 1.0)
+    vals = np.stack([dequant_affine(v["codes"][r, 0], v["scales"][r, 0], v["zeros"][r, 0], bits)
+                     for r in range(4, 34)])
+    np.testing.assert_allclose(out[0, 0], vals.mean(axis=0).astype(np.float32), rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_affine_attention_is_attention_on_the_dequantized_cache(oracle_mod, bits):
+    """Affine keys and values: torch's fp64 attention of q over k^ = T~inv y^ and v^,
+    both dequantized per 32-channel group as z + q s."""
+    rng = np.random.default_rng(26 + bits)
+    Hkv, G, rows = 2, 4, 200
+    Hq = Hkv * G
+    T, _, _ = signed_perm(rng, Hkv)
+    k, v = random_affine_cache(rng, rows, Hkv, bits), random_affine_cache(rng, rows, Hkv, bits)
+    q = bf16_bits_of(rng.standard_normal((2, Hq, D)) * 0.5)
+    row0, lens, scale = np.array([0, 50]), np.array([120, 150]), 0.125
+    out = oracle_mod.decode_attention(oracle_mod.pair_queries(q, T), k, v, bits, row0, lens, scale)
+    qv = bf16_value(q).astype(np.float64)
+    for b in range(2):
+        r = np.arange(row0[b], row0[b] + lens[b])
+        for hq in range(Hq):
+            h = hq // G
+            Y = np.stack([dequant_affine(k["codes"][i, h], k["scales"][i, h], k["zeros"][i, h], bits) for i in r])
+            V = np.stack([dequant_affine(v["codes"][i, h], v["scales"][i, h], v["zeros"][i, h], bits) for i in r])
+            Kh = Y @ T[h].astype(np.float64).T
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qv[b, hq][None, None, None]), torch.from_numpy(Kh[None, None]),
+                torch.from_numpy(V[None, None]), scale=scale)[0, 0, 0].numpy()
+            np.testing.assert_allclose(out[b, hq], ref.astype(np.float32), rtol=2e-7, atol=1e-7)
+
+
+def test_affine_and_symmetric_caches_do_not_mix(oracle_mod):
+    rng = np.random.default_rng(27)
+    k = random_affine_cache(rng, 4, 1, 2)
+    v = random_cache(rng, 4, 1, 2)
+    with pytest.raises(ValueError):
+        oracle_mod.decode_attention(np.zeros((1, 1, D), np.uint16), k, v, 2, np.array([0]), np.array([4]), 1.0)
