@@ -619,6 +619,26 @@ def main() -> int:
     att_call_us = float(np.mean([e[4].elapsed_time(e[5]) for e in att_ev])) * 1e3
     att_bytes = int(att_len.sum()) * H * 2 * (16 * bits + 2) + dn * att_q * D * 2 + dn * 2 * 12
     att_flops = 4.0 * int(att_len.sum()) * att_q * D
+    # the same batch over percentile-clipped affine caches (the same codes, four steps and four
+    # zeros per record)
+    rows_all = dkc.codes.shape[0]
+    aff = [bk.PackedCache(c.codes, (torch.rand((rows_all, H, 4), device=dev, generator=g) * 0.05 + 0.02).to(torch.float16),
+                          (torch.randn((rows_all, H, 4), device=dev, generator=g) * 0.2).to(torch.float16))
+           for c in (dkc, dvc)]
+    att_aff = bk.prepare_decode_attention(att_qp, aff[0], aff[1], H, bits, bk.affine(), att_row0, att_lens, 32768,
+                                          1.0 / np.sqrt(D), att_ws, att_out, stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(2 * rep):
+            att_aff()
+    torch.cuda.synchronize()
+    aff_ev = new_events(5 * rep, 2)
+    for e in aff_ev:
+        bk.wushkv_debug_time_next_launch(e[0], e[1])
+        att_aff()
+    torch.cuda.synchronize()
+    aff_kernel_us = float(np.mean([e[0].elapsed_time(e[1]) for e in aff_ev])) * 1e3
+    aff_bytes = int(att_len.sum()) * H * 2 * (16 * bits + 16) + dn * att_q * D * 2 + dn * 2 * 12
+    del aff, att_aff
 
     # ---- the other workloads' kernels, each against the HBM roofline (kernel-recorded events,
     # one buffer set: every input is at least 256 MiB, beyond the MALL).
@@ -720,6 +740,10 @@ def main() -> int:
             "attention_hbm_frac": round(att_bytes / (att_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(att_flops / (att_kernel_us * 1e-6) / 1e12, 2),
             "note": "packed 2-bit K and V read once; call_us = attention and split combine launched back to back",
+            "affine_attention_kernel_us": round(aff_kernel_us, 2),
+            "affine_algorithmic_bytes": aff_bytes,
+            "affine_attention_hbm_frac": round(aff_bytes / (aff_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "affine_note": "the same batch and codes as affine caches (four fp16 steps and zeros per record)",
         },
         "other_workloads": other,
     }

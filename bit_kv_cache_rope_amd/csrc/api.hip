@@ -701,10 +701,11 @@ static wushkv_status attention_common(const void* q_paired, int n_seqs, int n_q_
   wushkv::QuantArgs qa{};
   st = make_quant(quantizer, &qa);
   if (st) return st;
-  if (qa.kind != 0) return fail(WUSHKV_ERR_UNSUPPORTED, "attention reads symmetric caches only");
-  st = check_packed(k_cache, 0, 0, false);
+  // symmetric (one step per record) or affine (four steps and zeros) caches, both
+  // written with this quantizer
+  st = check_packed(k_cache, qa.kind, 0, false);
   if (st) return st;
-  st = check_packed(v_cache, 0, 0, false);
+  st = check_packed(v_cache, qa.kind, 0, false);
   if (st) return st;
   if (k_cache->n_rows != v_cache->n_rows) return fail(WUSHKV_ERR_INVALID_ARG, "key and value caches differ in rows");
   if (!std::isfinite(scale)) return fail(WUSHKV_ERR_INVALID_ARG, "scale must be finite");
@@ -736,6 +737,8 @@ static wushkv_status attention_common(const void* q_paired, int n_seqs, int n_q_
   a.ks = (const uint16_t*)k_cache->scales;
   a.vc = (const uint8_t*)v_cache->codes;
   a.vs = (const uint16_t*)v_cache->scales;
+  a.kz = qa.kind ? (const uint16_t*)k_cache->zeros : nullptr;
+  a.vz = qa.kind ? (const uint16_t*)v_cache->zeros : nullptr;
   a.n_rows = k_cache->n_rows;
   a.row0 = seq_row0;
   a.len = seq_len;

@@ -49,6 +49,7 @@ constexpr int kPairVecs = 4;      // query vectors per pairing block
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past `bytes`
@@ -218,16 +219,26 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* W) {
 
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
+// (x & m) | c as one v_and_or_b32: m from an SGPR, c from a VGPR (a VOP3
+// instruction reads at most one scalar operand on this chip, so with both as
+// constants the compiler would split it into an and and an or).
+__device__ __forceinline__ uint32_t and_or_sv(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+
 // grid 8 * n_splits8 * Hkv * B blocks (see the block map below), 256 threads.
 // A block takes up to kChunk tokens of one sequence and KV head, in rounds of
 // KS tokens, with the running max, sums and value accumulators rescaled from
 // round to round (online softmax).
-template <int BITS, int QS>
+template <int BITS, int QS, bool AF>
 __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const AttnArgs a) {
   constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
-  // tokens per round: 512, or 256 for 3- and 4-bit records (so that three
-  // blocks' LDS fits a CU and a 4-bit round's records fit one load round)
-  constexpr int KS = BITS == 2 ? kSub : kSub / 2;
+  // tokens per round: 512, or 256 for 3- and 4-bit records and affine caches
+  // (so that three blocks' LDS fits a CU and a 4-bit round's records fit one
+  // load round)
+  constexpr int KS = (BITS == 2 && !AF) ? kSub : kSub / 2;
   constexpr int REC = 16 * BITS;
   constexpr int SNW = BITS;    // words of key codes per lane (32 channels)
   constexpr int VNW = BITS == 3 ? 3 : 2;  // words of value codes per lane
@@ -236,11 +247,12 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   constexpr int SROW = KS + 16;  // s_lds row (padded against bank conflicts)
   constexpr float NINF = -__builtin_inff();
   constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass (4x4x1 product)
-  constexpr bool TWO = BITS == 2;         // score tiles two at a time
-  // 2 and 4 bits: the value product runs on bf16 16x16x32 MFMA with the value
-  // records stored transposed (word w of token n at vt[w][n]) and the weights
-  // split into three bf16 parts (columns g + 4 part); 3 bits: fp32 4x4x1 MFMA.
-  constexpr bool VT = BITS != 3;
+  constexpr bool TWO = BITS == 2 && !AF;  // score tiles two at a time
+  // 2 and 4 bits, symmetric: the value product runs on bf16 16x16x32 MFMA with
+  // the value records staged as token pairs and the weights split into three
+  // bf16 parts (columns g + 4 part); 3 bits and affine caches: fp32 4x4x1 MFMA,
+  // where wave w owns channels 32 w .. 32 w + 31, one affine group.
+  constexpr bool VT = BITS != 3 && !AF;
   constexpr int CPH = 16 / BITS;          // channels per halfword of a record (2 and 4 bits)
   constexpr int NHW = REC / 2;            // halfwords per record
   constexpr int VPROW = KS / 2 + 16;      // vp row (u32): one word per token pair, padded
@@ -261,6 +273,14 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   __shared__ float k1_lds[NQ];
   __shared__ float mx_lds[4][NQ];
   __shared__ float sum_lds[4][NQ][2];
+  // affine caches, per group g and token n at [g * KS + n]: the key step and zero
+  // times scale * log2(e), the value step and zero (0 for an absent token)
+  constexpr int NAF = AF ? 4 * KS : 4;
+  __shared__ __align__(16) float ksc_lds[NAF];
+  __shared__ __align__(16) float kzr_lds[NAF];
+  __shared__ __align__(16) float vsc_lds[NAF];
+  __shared__ __align__(16) float vzr_lds[NAF];
+  __shared__ float zsum_lds[4][NQ];  // affine: sum_n p_n z_n of wave w's group, per query
 
   // Block L runs on XCD L % 8 (blocks are dispatched to the XCDs round-robin).
   // The split s of sequence b goes to XCD (s + b) % 8, so that each XCD gets
@@ -332,6 +352,38 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     }
     Bq[s] = __builtin_bit_cast(bf16x8, v);
   }
+  // Affine keys: the score product's 16 columns are (query gq = col / 4, group
+  // ga = col % 4) of each 4-query set qs: a lane's operand holds its query's
+  // channels of group ga only where its k group grp is that group (lane group
+  // grp holds channels 32 grp .. 32 grp + 31), so each column sums one group:
+  // raw = sum_{j in ga} (0.5 + c_j / SB) q'_j SB = (SB / 2) Q + sum_{j in ga} c_j q'_j,
+  // with Q = sum_{j in ga} q'_j (fp64, then fp32).
+  bf16x8 Bqa[AF ? QS : 1][4];
+  float kqa[AF ? QS : 1], Qa[AF ? QS : 1];
+  if constexpr (AF) {
+    const int gq = col >> 2, ga = col & 3;
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      double sq = 0.0;
+      for (int j = 32 * ga; j < 32 * ga + 32; ++j) sq += (double)q_lds[4 * qs + gq][j];
+      Qa[qs] = (float)sq;
+      kqa[qs] = (float)(sq * (double)(0.5f * SB));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float x0 = 0.0f, x1 = 0.0f;
+          if (ga == grp) {
+            x0 = q_lds[4 * qs + gq][score_channel<BITS>(grp, s, 2 * t)] * SB;
+            x1 = q_lds[4 * qs + gq][score_channel<BITS>(grp, s, 2 * t + 1)] * SB;
+          }
+          v[t] = pack_bf16x2(x0, x1);
+        }
+        Bqa[qs][s] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
 
   const int tb = lane >> 2, x = lane & 3;  // 4x4x1 value product: token block, column
   const int voff = value_byte_offset<BITS>(w, x);
@@ -342,6 +394,10 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
     for (int k = 0; k < NACC; ++k) acc[qs][k] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  // affine values: this lane's sum_n p_n z_n (wave w's group) for query 4 qs + x
+  float zs[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) zs[qs] = 0.0f;
   // 16x16x32 value product: lane (row 16 mt + lane % 16 of the wave's 32
   // channels, k group grp = 8 tokens); the row of its channel's halfword in
   // vp and the rotation that takes the code from its place in each half to
@@ -385,8 +441,9 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   };
   struct RoundSrc {
     int t0, t1;
-    rsrc_t k, v, ks, vs;
+    rsrc_t k, v, ks, vs, kz, vz;
   };
+  constexpr uint32_t NSC = AF ? 4 : 1;  // fp16 steps (and zeros) per record
   const uint32_t row_stride = (uint32_t)Hkv * REC;  // bytes between cache rows (< 2^22)
   auto round_src = [&](int base) __attribute__((always_inline)) -> RoundSrc {
     const int cnt = min(cnt_all - base, KS);
@@ -400,12 +457,17 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     const int64_t row = n ? r0 + R.t0 : 0;  // first present row
     R.k = buffer_rsrc(a.kc + (row * Hkv + h) * REC, n * row_stride);
     R.v = buffer_rsrc(a.vc + (row * Hkv + h) * REC, n * row_stride);
-    R.ks = buffer_rsrc(a.ks + row * Hkv + h, n * (uint32_t)Hkv * 2u);
-    R.vs = buffer_rsrc(a.vs + row * Hkv + h, n * (uint32_t)Hkv * 2u);
+    R.ks = buffer_rsrc(a.ks + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
+    R.vs = buffer_rsrc(a.vs + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
+    if constexpr (AF) {
+      R.kz = buffer_rsrc(a.kz + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
+      R.vz = buffer_rsrc(a.vz + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
+    }
     return R;
   };
   u32x4 pk[PR], pv[PR];
   uint32_t pks[KS / 256], pvs[KS / 256];
+  u32x2 aks[AF ? KS / 256 : 1], akz[AF ? KS / 256 : 1], avs[AF ? KS / 256 : 1], avz[AF ? KS / 256 : 1];
   auto load_round = [&](int base) __attribute__((always_inline)) {
     const RoundSrc R = round_src(base);
 #pragma unroll
@@ -419,9 +481,17 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     }
 #pragma unroll
     for (int j = 0; j < KS / 256; ++j) {
-      const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 2 * Hkv);
-      pks[j] = __builtin_amdgcn_raw_buffer_load_b16(R.ks, off, 0, 0);
-      pvs[j] = __builtin_amdgcn_raw_buffer_load_b16(R.vs, off, 0, 0);
+      if constexpr (AF) {
+        const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 8 * Hkv);
+        aks[j] = __builtin_amdgcn_raw_buffer_load_b64(R.ks, off, 0, 0);
+        akz[j] = __builtin_amdgcn_raw_buffer_load_b64(R.kz, off, 0, 0);
+        avs[j] = __builtin_amdgcn_raw_buffer_load_b64(R.vs, off, 0, 0);
+        avz[j] = __builtin_amdgcn_raw_buffer_load_b64(R.vz, off, 0, 0);
+      } else {
+        const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 2 * Hkv);
+        pks[j] = __builtin_amdgcn_raw_buffer_load_b16(R.ks, off, 0, 0);
+        pvs[j] = __builtin_amdgcn_raw_buffer_load_b16(R.vs, off, 0, 0);
+      }
     }
   };
   // the registers of load_round(base) -> LDS: records, and per token the key
@@ -452,9 +522,23 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     for (int j = 0; j < KS / 256; ++j) {
       const int i = tid + 256 * j;
       const bool ok = i >= R.t0 && i < R.t1;
-      dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
       off_lds[i] = ok ? 0.0f : NINF;
-      dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
+      if constexpr (AF) {
+        // the weights p * 1; the group steps and zeros go to the value product
+        dv_lds[i] = ok ? 1.0f : 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t sw = aks[j][g >> 1] >> (16 * (g & 1)), zw = akz[j][g >> 1] >> (16 * (g & 1));
+          const uint32_t vw = avs[j][g >> 1] >> (16 * (g & 1)), uw = avz[j][g >> 1] >> (16 * (g & 1));
+          ksc_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)sw) * a.c0 : 0.0f;
+          kzr_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)zw) * a.c0 : 0.0f;
+          vsc_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)vw) : 0.0f;
+          vzr_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)uw) : 0.0f;
+        }
+      } else {
+        dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
+        dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
+      }
     }
   };
   if constexpr (PF) load_round(0);
@@ -473,6 +557,49 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
 
     // ---- scores: wave w takes 16-token tiles w, w + 4, ... (two at a time)
     float mx = NINF;
+    if constexpr (AF) {
+      // per column (query gq, group ga): s_ga (raw - (SB / 2) Q) + z_ga Q, with the
+      // step and zero already times scale * log2(e); the quad of a query's four
+      // groups then sums them (every lane of the quad holds the score)
+      float mxa[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) mxa[qs] = NINF;
+      const int gq = col >> 2, ga = col & 3;
+      for (int t0 = w; 16 * t0 < cnt; t0 += 4) {
+        uint32_t W[SNW];
+        load_words<SNW>(&kc_lds[(16 * t0 + col) * REC + 4 * BITS * grp], W);  // any bytes if absent
+        bf16x8 A[4];
+        score_operands<BITS>(W, A);
+        const int i0 = 16 * t0 + 4 * grp;  // rows of the product: tokens i0 .. i0 + 3
+        const float4 of4 = *(const float4*)&off_lds[i0];
+        const float4 ks4 = *(const float4*)&ksc_lds[ga * KS + i0];
+        const float4 kz4 = *(const float4*)&kzr_lds[ga * KS + i0];
+        const float ofv[4] = {of4.x, of4.y, of4.z, of4.w};
+        const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w}, kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s], Bqa[qs][s], sc, 0, 0, 0);
+          float sv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float part = __builtin_fmaf(sc[e] - kqa[qs], ksv[e], kzv[e] * Qa[qs]);
+            part += dpp_f32<0xB1>(part);  // quad_perm [1,0,3,2]
+            part += dpp_f32<0x4E>(part);  // quad_perm [2,3,0,1]
+            sv[e] = part + ofv[e];
+            mxa[qs] = __builtin_fmaxf(mxa[qs], sv[e]);
+          }
+          if (ga == 0) *(float4*)&s_lds[4 * qs + gq][i0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        }
+      }
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        float m = __builtin_fmaxf(mxa[qs], __shfl_xor(mxa[qs], 16, 64));
+        m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
+        if (lane < 16 && ga == 0) mx_lds[w][4 * qs + gq] = m;
+      }
+    } else {
     for (int t0 = w; 16 * t0 < cnt; t0 += TWO ? 8 : 4) {
       const bool two = TWO && 16 * (t0 + 4) < cnt;  // uniform over the wave
       uint32_t W[2][SNW];
@@ -505,6 +632,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lane < NQ) mx_lds[w][lane] = mx;
+    }
     __syncthreads();
 
     // ---- p = exp2(s - max) and p * step_v (0 past the round's tokens); the
@@ -575,6 +703,13 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         for (int k = 0; k < NACC; ++k)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
+      if constexpr (AF) {
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          const float al = x == 0 ? alpha[4 * qs] : (x == 1 ? alpha[4 * qs + 1] : (x == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
+          zs[qs] *= al;
+        }
+      }
     }
     __syncthreads();
 
@@ -584,6 +719,8 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       const uint32_t* vp = (const uint32_t*)vc_lds;
       const uint16_t* pt = (const uint16_t*)kc_lds;
       constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : 0x00780078u;
+      uint32_t vhi = 0x3F003F00u;  // the operands' constant high bytes, held in a VGPR
+      asm volatile("" : "+v"(vhi));
       for (int n0 = 0; n0 < n16; n0 += 32) {
         const int nk = n0 + 8 * grp;  // this lane's 8 tokens: pairs nk / 2 .. nk / 2 + 3
         bf16x8 P[QS];
@@ -595,7 +732,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           u32x4 av;
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            av[t] = (__builtin_amdgcn_alignbit(wp[t], wp[t], vrot[mt]) & VMASK) | 0x3F003F00u;
+            av[t] = and_or_sv(__builtin_amdgcn_alignbit(wp[t], wp[t], vrot[mt]), VMASK, vhi);
           const bf16x8 A = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
           for (int qs = 0; qs < QS; ++qs)
@@ -612,6 +749,15 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         load_words<VNW>(&vc_lds[i * REC + voff], U[jj]);  // any bytes if absent (its weight is 0)
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) pa[jj][qs] = s_lds[4 * qs + x][i];
+        if constexpr (AF) {
+          // v^ = z + c s of wave w's group: weights p s for the codes, p z summed aside
+          const float vsg = vsc_lds[w * KS + i], vzg = vzr_lds[w * KS + i];
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs) {
+            zs[qs] = __builtin_fmaf(pa[jj][qs], vzg, zs[qs]);
+            pa[jj][qs] *= vsg;
+          }
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < PU; ++jj) {
@@ -658,6 +804,18 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         }
         acc[qs][k][e] = v;
       }
+  if constexpr (AF) {
+    // the 16 token blocks' zero sums (lanes x, x + 4, ..., x + 60), per query 4 qs + x
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      float v = zs[qs];
+      v = v + dpp_f32<0x124>(v);  // row_ror:4
+      v = v + dpp_f32<0x128>(v);  // row_ror:8
+      v = xor_sum(v, 16);
+      v = xor_sum(v, 32);
+      if (lane < 4) zsum_lds[w][4 * qs + lane] = v;
+    }
+  }
   __syncthreads();
   if constexpr (VT) {
     if (col < 4) {
@@ -686,8 +844,14 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         if (g < G) {
           const float vs = (sum_lds[0][g][1] + sum_lds[1][g][1]) + (sum_lds[2][g][1] + sum_lds[3][g][1]);
           float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + 4;
+          if constexpr (AF) {
+            const float zt = zsum_lds[w][g];
 #pragma unroll
-          for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = acc[qs][k][e] * inv - M * vs;
+            for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = __builtin_fmaf(acc[qs][k][e], inv, zt);
+          } else {
+#pragma unroll
+            for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = acc[qs][k][e] * inv - M * vs;
+          }
         }
       }
   }
@@ -752,8 +916,10 @@ __global__ void __launch_bounds__(128) combine_kernel(const AttnArgs a) {
 template <int BITS>
 hipError_t launch_attention_bits(const AttnArgs& a, int qs, hipStream_t st) {
   const dim3 grid((unsigned)(8 * (int64_t)a.n_splits8 * a.n_kv_heads * a.n_seqs));
-  return qs == 1 ? launch_kernel(attention_kernel<BITS, 1>, grid, dim3(256), st, a)
-                 : launch_kernel(attention_kernel<BITS, 2>, grid, dim3(256), st, a);
+  if (a.kz) return qs == 1 ? launch_kernel(attention_kernel<BITS, 1, true>, grid, dim3(256), st, a)
+                           : launch_kernel(attention_kernel<BITS, 2, true>, grid, dim3(256), st, a);
+  return qs == 1 ? launch_kernel(attention_kernel<BITS, 1, false>, grid, dim3(256), st, a)
+                 : launch_kernel(attention_kernel<BITS, 2, false>, grid, dim3(256), st, a);
 }
 
 }  // namespace

@@ -155,6 +155,8 @@ struct AttnArgs {
   const uint16_t* ks;
   const uint8_t* vc;
   const uint16_t* vs;
+  const uint16_t* kz;     // affine caches: [rows][Hkv][4] zeros beside [rows][Hkv][4] steps; NULL: symmetric
+  const uint16_t* vz;
   int64_t n_rows;
   const int64_t* row0;    // first cache row of each sequence
   const int32_t* len;     // tokens of each sequence

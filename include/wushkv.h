@@ -68,7 +68,7 @@ extern "C" {
 typedef enum {
   WUSHKV_OK = 0,
   WUSHKV_ERR_INVALID_ARG = 1,  /* NULL pointer, bad size, bad enum value        */
-  WUSHKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. affine caches in attention) */
+  WUSHKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. more than 8 query heads per KV head) */
   WUSHKV_ERR_ALIGNMENT = 3,    /* pointer or stride not aligned as required    */
   WUSHKV_ERR_NO_DEVICE = 4,    /* no HIP device visible                        */
   WUSHKV_ERR_HIP = 5,          /* a HIP runtime call failed                    */
@@ -233,8 +233,9 @@ wushkv_status wushkv_pair_queries(const void* Q, wushkv_dtype q_dtype, int64_t n
 wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n_kv_heads, int max_seq_len,
                                                 size_t* bytes);
 
-/* Decode attention of one query token per sequence over symmetric packed key
- * and value caches, without dequantizing the cache to memory.  Keys are scored
+/* Decode attention of one query token per sequence over packed key and value
+ * caches, symmetric or percentile-clipped affine, without dequantizing the cache
+ * to memory.  Keys are scored
  * in their transformed basis with the paired query; values are read as stored
  * (their transform is folded into the weights: ai4snews summary, deployment
  * paragraph).  For sequence b and query head hq (KV head hq / G, G =
@@ -243,9 +244,13 @@ wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n
  * over the cache rows seq_row0[b] + n, n < min(seq_len[b], max_seq_len); rows
  * outside [0, n_rows) are absent; a sequence with no row present gives 0.
  *   q_paired: device bf16 [n_seqs][n_q_heads][128] (wushkv_pair_queries).
- *   k_cache, v_cache: symmetric caches written by wushkv_quantize_keys /
- *      wushkv_quantize_values with the same bits and n_rows (their slots are
- *      not used here).
+ *   k_cache, v_cache: caches written by wushkv_quantize_keys /
+ *      wushkv_quantize_values with the same bits, quantizer and n_rows (their
+ *      slots are not used here).  Affine caches (zeros set) are read as
+ *      z_g + q s_g per 32-channel group (ai4snews summary, end-to-end
+ *      paragraph): the score product sums each group's codes in its own
+ *      column and the value product runs in fp32 with the weights times the
+ *      group's step, the weighted zeros summed beside it.
  *   seq_row0: device int64 [n_seqs]; seq_len: device int32 [n_seqs].
  *   workspace: device, 16-byte aligned, at least the bytes reported by
  *      wushkv_decode_attention_workspace; caller-owned scratch that the call
@@ -253,11 +258,10 @@ wushkv_status wushkv_decode_attention_workspace(int n_seqs, int n_q_heads, int n
  *   out: device fp32 [n_seqs][n_q_heads][128].
  * Precision: codes and steps exact; q' bf16; scores accumulated in fp32 on
  * MFMA; exp2 and the weighted sum of values in fp32 (no bf16 rounding of the
- * weights).  Affine caches return WUSHKV_ERR_UNSUPPORTED, and so do calls
- * with 8 * ceil(ceil(max_seq_len / 2048) / 8) * n_kv_heads * n_seqs at or
- * above 2^24 (one 256-thread block each; a dispatch holds fewer than 2^32
- * work-items), also from wushkv_decode_attention_workspace.  n_seqs == 0 is
- * a no-op. */
+ * weights).  Calls with 8 * ceil(ceil(max_seq_len / 2048) / 8) * n_kv_heads *
+ * n_seqs at or above 2^24 (one 256-thread block each; a dispatch holds fewer
+ * than 2^32 work-items) return WUSHKV_ERR_UNSUPPORTED, also from
+ * wushkv_decode_attention_workspace.  n_seqs == 0 is a no-op. */
 wushkv_status wushkv_decode_attention(const void* q_paired, int n_seqs, int n_q_heads,
                                       const wushkv_packed* k_cache, const wushkv_packed* v_cache,
                                       int n_kv_heads, int bits, const wushkv_quantizer* quantizer,

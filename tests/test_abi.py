@@ -133,7 +133,7 @@ def test_validation_without_device(lib):
         vp(16), n, 32, ctypes.byref(kc), ctypes.byref(p), 8, bits, ctypes.byref(qq), vp(16), vp(16), 4096,
         ctypes.c_float(sc), vp(16), ws, vp(16), None)
     assert att(2, bits=5) == _lib.ERR_INVALID_ARG
-    assert att(2, qq=_q(kind=1, group=32)) == _lib.ERR_UNSUPPORTED
+    assert att(2, qq=_q(kind=1, group=32)) == _lib.ERR_INVALID_ARG  # affine caches need zeros
     assert att(2, kc=_packed(rows=3)) == _lib.ERR_INVALID_ARG
     assert att(2, ws=100) == _lib.ERR_INVALID_ARG
     assert att(2, sc=float("inf")) == _lib.ERR_INVALID_ARG

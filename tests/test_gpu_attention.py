@@ -67,7 +67,9 @@ def random_cache(rng, rows, H, bits):
 
 def dev_cache(env, c):
     bk, torch = env["bk"], env["torch"]
-    return bk.PackedCache(to_dev(env, c["codes"]), to_dev(env, c["scales"]).view(torch.float16))
+    z = c.get("zeros")
+    return bk.PackedCache(to_dev(env, c["codes"]), to_dev(env, c["scales"]).view(torch.float16),
+                          None if z is None else to_dev(env, z).view(torch.float16))
 
 
 def value_max(v, bits, row0, lens, n_rows, H):
@@ -84,11 +86,35 @@ def value_max(v, bits, row0, lens, n_rows, H):
     return out
 
 
-def run_attention(env, qp_bits, k, v, Hkv, bits, row0, lens, scale, max_len=None, n_rows=None):
+def random_affine_cache(rng, rows, H, bits):
+    """Random codes with four fp16 steps and zeros per record (percentile-clipped affine)."""
+    codes = rng.integers(0, 256, (rows, H, 16 * bits), dtype=np.uint8)
+    steps = (np.abs(rng.standard_normal((rows, H, 4))) * 0.05 + 0.02).astype(np.float16).view(np.uint16)
+    zeros = (rng.standard_normal((rows, H, 4)) * 0.2).astype(np.float16).view(np.uint16)
+    return dict(codes=codes, scales=steps, zeros=zeros)
+
+
+def value_max_affine(v, bits, row0, lens, n_rows, H):
+    """max |z + q s| over each sequence's present rows, per (sequence, KV head)."""
+    L = 1 << bits
+    out = np.zeros((len(lens), H))
+    for b, (r0, n) in enumerate(zip(row0, lens)):
+        r = np.arange(r0, r0 + max(n, 0))
+        r = r[(r >= 0) & (r < n_rows)]
+        if r.size == 0:
+            continue
+        s = v["scales"][r].view(np.float16).astype(np.float64)  # [n][H][4]
+        z = v["zeros"][r].view(np.float16).astype(np.float64)
+        out[b] = np.maximum(np.abs(z), np.abs(z + (L - 1) * s)).max(axis=(0, 2))
+    return out
+
+
+def run_attention(env, qp_bits, k, v, Hkv, bits, row0, lens, scale, max_len=None, n_rows=None, quant=None):
     bk, torch = env["bk"], env["torch"]
     max_len = int(max(lens)) if max_len is None else max_len
     kc, vc = dev_cache(env, k), dev_cache(env, v)
-    out = bk.wushkv_decode_attention(to_dev(env, qp_bits), kc, vc, Hkv, bits, bk.sym(), to_dev(env, np.asarray(row0, np.int64)),
+    out = bk.wushkv_decode_attention(to_dev(env, qp_bits), kc, vc, Hkv, bits, quant or bk.sym(),
+                                     to_dev(env, np.asarray(row0, np.int64)),
                                      to_dev(env, np.asarray(lens, np.int32)), max_len, scale)
     torch.cuda.synchronize()
     return out.cpu().numpy()
@@ -242,3 +268,51 @@ def test_attention_decode_batch_full_size_sampled(env):
     pick = np.array([int(np.argmax(lens)), int(np.argmin(lens)), int(np.argsort(lens)[B // 2])])
     ref = oracle.decode_attention(qp[pick], k, v, bits, row0[pick], lens[pick], 1.0 / np.sqrt(D))
     check_attention(env, got[pick], ref, value_max(v, bits, row0[pick], lens[pick], rows, Hkv), G, "decode batch")
+
+
+# ---------------------------------------------------------------------------------- affine caches
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_affine_attention_matches_oracle(env, bits, G):
+    """Percentile-clipped affine caches (four steps and zeros per record): the
+    same sequences as the symmetric case, against the oracle's z + q s."""
+    oracle, bk = env["oracle"], env["bk"]
+    rng = np.random.default_rng(700 + 10 * bits + G)
+    Hkv = 2
+    Hq = G * Hkv
+    lens = np.array([0, 1, 17, 1024, 2500, 512, 40])
+    row0 = np.array([5, 9, 100, 200, 1300, 3900, -25])
+    rows = 4000
+    say(f"affine attention bits={bits} G={G}")
+    k, v = random_affine_cache(rng, rows, Hkv, bits), random_affine_cache(rng, rows, Hkv, bits)
+    qmag = np.array([0.5, 2.0, 8.0, 30.0, 4.0, 1.0, 3.0])[:, None, None]
+    qp = bf16_bits(rng.standard_normal((len(lens), Hq, D)) * qmag)
+    scale = 1.0 / np.sqrt(D)
+    got = run_attention(env, qp, k, v, Hkv, bits, row0, lens, scale, quant=bk.affine(1.0, 99.0))
+    ref = oracle.decode_attention(qp, k, v, bits, row0, lens, scale)
+    check_attention(env, got, ref, value_max_affine(v, bits, row0, lens, rows, Hkv), G, f"affine bits={bits} G={G}")
+
+
+def test_affine_attention_on_quantized_synthetic_cache(env):
+    """An affine cache that the oracle's own quantizer wrote from synthetic keys
+    (through RoPE and the workload's transform) and values, read with queries
+    paired through the inverse transform; also at general percentiles."""
+    s, oracle, bk = env["synth"], env["oracle"], env["bk"]
+    w = s.WORKLOADS["affine_pct"]
+    n, H, G = 3000, w.heads, 4
+    K, V = s.kv(w, 0, "K", 0, n), s.kv(w, 0, "V", 0, n)
+    pos = s.positions(w, 0, n)
+    T, Ti = s.transform(w, 0)
+    rng = np.random.default_rng(771)
+    Q = (rng.standard_normal((3, H * G, D)) * 0.3).astype(np.float32)
+    qp = oracle.pair_queries(Q, Ti)
+    row0, lens = np.array([0, 700, 2999]), np.array([3000, 1500, 1])
+    for plo, phi, bits in ((1.0, 99.0, 2), (5.0, 95.0, 4)):
+        say(f"affine synthetic cache {plo}/{phi} {bits}-bit")
+        q = oracle.affine(plo, phi)
+        k = oracle.quantize_keys(K, pos, T, w.theta, bits, q)
+        v = oracle.quantize_values(V, bits, q)
+        got = run_attention(env, qp, k, v, H, bits, row0, lens, 0.1, quant=bk.affine(plo, phi))
+        ref = oracle.decode_attention(qp, k, v, bits, row0, lens, 0.1)
+        check_attention(env, got, ref, value_max_affine(v, bits, row0, lens, n, H), G, f"affine synthetic {bits}-bit")
