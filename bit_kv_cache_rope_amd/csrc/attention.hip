@@ -17,11 +17,16 @@
 //     head, sequence), in rounds of 512 tokens (256 at 3 and 4 bits) whose
 //     key and value records are first copied to LDS with all loads in flight
 //     at once (at 2 and 4 bits, the next round's during this round's work).
-//       scores  S[n][g] = sum_j code-operand[n][j] * q'[g][j] on
-//               v_mfma_f32_16x16x32_bf16 (16 tokens x 16 columns, G used);
-//               the key codes enter as exact bf16 values 0.5 + c / SB built
-//               with one shift, mask and v_perm per pair of codes, and the
-//               constant part is subtracted after the product.
+//       scores  2 and 4 bits, symmetric keys: S[g][n] = sum_j q'[g][j] c[n][j]
+//               on v_mfma_f32_16x16x128_f8f6f4, all 128 channels in one
+//               product: the query in 20-bit fixed point as four base-32
+//               digits (fp8 integers in rows 4 g + i), the
+//               codes as fp4 (2 bits) or fp8 (4 bits) values made with one
+//               mask per word, one lane per (query, token) after the digits
+//               are combined.  3 bits and affine
+//               keys: v_mfma_f32_16x16x32_bf16 with the codes as exact bf16
+//               values 0.5 + c / SB (one shift, mask and v_perm per pair).
+//               The constant part is subtracted after the product.
 //       softmax p = exp2(s - max) over the split, then p * step_v.
 //       values  O[ch][g] += c[ch][n] * p[n][g] on v_mfma_f32_16x16x32_bf16
 //               (2 and 4 bits): rows = 16 channels, k = 32 tokens, columns =
@@ -228,6 +233,61 @@ __device__ __forceinline__ uint32_t and_or_sv(uint32_t x, uint32_t m, uint32_t c
   return r;
 }
 
+// ---- narrow-format score product (2 and 4 bits, symmetric keys) on
+// v_mfma_f32_16x16x128_f8f6f4: A = the paired query in fixed point as four
+// base-32 digits, each an fp8 (e4m3) integer; B = the key codes of 16 tokens,
+// k = the 128 channels.  A 2-bit code zero-extended to a nibble is the fp4
+// (e2m1) value c / 2, and a 4-bit code zero-extended to a byte is the fp8
+// (e4m3) value c * 2^-9, so the codes become operands with one mask (and one
+// shift) per word.  This product does not add its 128 terms as fp32 would:
+// measured, a sum is exact when every term's bits lie within 13 binary places
+// of the largest term's leading bit, and loses low bits beyond that.  A digit
+// row keeps every term on one grid (|digit| <= 16, code <= 15: 8 places), so
+// each row sums exactly, and the digits are combined afterwards in fp32.
+// Operand layout (measured): an 8-bit operand's lane (group g = lane / 16, row
+// or column lane % 16) holds k = 16 g + j in byte j < 16 and k = 64 + 16 g +
+// j - 16 in byte j >= 16; a 4-bit operand's lane holds k = 32 g + j in nibble
+// j.  Only the pairing of A's and B's elements matters, which the map below
+// fixes.
+
+// The fp8 (e4m3) pattern of an integer d in [-16, 16] (exact).
+__device__ __forceinline__ uint32_t e4m3_int(int d) {
+  const uint32_t m = (uint32_t)(d < 0 ? -d : d);
+  if (m == 0) return 0u;
+  const int e = 31 - __builtin_clz(m);  // 0..4
+  const uint32_t mant = (e <= 3 ? m << (3 - e) : m >> 1) & 7u;
+  return (d < 0 ? 0x80u : 0u) | ((uint32_t)(e + 7) << 3) | mant;
+}
+
+// Position 32 g + j (lane group g, byte j of A's 32) of channel ch in the
+// query operand, matched to where the code operand puts that channel's code.
+template <int BITS>
+__device__ __forceinline__ int qpart_pos(int ch) {
+  const int g = ch >> 5, c = ch & 31;
+  if constexpr (BITS == 2) {
+    // code operand: lane group g takes the record's bytes 8 g .. 8 g + 7 (words
+    // w0, w1) as the nibble words w0 & m, (w0 >> 2) & m, w1 & m, (w1 >> 2) & m
+    // (m = 0x33333333): nibble i of word d is channel 32 g + 16 (d / 2) + 2 i + d % 2
+    const int d = 2 * (c >> 4) + (c & 1), i = (c & 15) >> 1;
+    const int k = 32 * g + 8 * d + i;  // its k
+    return k < 64 ? 32 * (k >> 4) + (k & 15) : 32 * ((k - 64) >> 4) + 16 + ((k - 64) & 15);
+  } else {
+    // code operand: lane group g takes bytes 16 g .. 16 g + 15 (words W0..W3) as
+    // the byte words W0 & m, (W0 >> 4) & m, W1 & m, ... (m = 0x0F0F0F0F): byte
+    // i of word r is channel 32 g + 8 (r / 2) + 2 i + r % 2; both operands are
+    // 8-bit, so A's byte j pairs with B's byte j
+    const int r = 2 * (c >> 3) + (c & 1), i = (c & 7) >> 1;
+    return 32 * g + 4 * r + i;
+  }
+}
+
+// max(x, y) as one v_max_f32 (no quieting of signalling NaNs, which never occur here)
+__device__ __forceinline__ float vmax(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+
 // grid 8 * n_splits8 * Hkv * B blocks (see the block map below), 256 threads.
 // A block takes up to kChunk tokens of one sequence and KV head, in rounds of
 // KS tokens, with the running max, sums and value accumulators rescaled from
@@ -253,6 +313,8 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   // bf16 parts (columns g + 4 part); 3 bits and affine caches: fp32 4x4x1 MFMA,
   // where wave w owns channels 32 w .. 32 w + 31, one affine group.
   constexpr bool VT = BITS != 3 && !AF;
+  // scores on the narrow-format product (2 and 4 bits, symmetric keys)
+  constexpr bool F8S = BITS != 3 && !AF;
   constexpr int CPH = 16 / BITS;          // channels per halfword of a record (2 and 4 bits)
   constexpr int NHW = REC / 2;            // halfwords per record
   constexpr int VPROW = KS / 2 + 16;      // vp row (u32): one word per token pair, padded
@@ -271,6 +333,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   __shared__ float dv_lds[KS];                        // value step
   __shared__ float q_lds[NQ][kD + 1];
   __shared__ float k1_lds[NQ];
+  __shared__ float e_lds[NQ];  // narrow-format scores: 2^(shift - E) of each query
   __shared__ float mx_lds[4][NQ];
   __shared__ float sum_lds[4][NQ][2];
   // affine caches, per group g and token n at [g * KS + n]: the key step and zero
@@ -296,7 +359,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   const int n_lo = split * kChunk;
   if (n_lo >= len) return;  // uniform over the block
   const int cnt_all = min(len - n_lo, kChunk);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G, Hkv = a.n_kv_heads;
   if (a.n_rows <= 0) {
     // no row exists: the split contributes nothing (max -inf, sums and output 0)
@@ -326,13 +389,65 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   const int64_t row_base = a.row0[b] + n_lo;
   __syncthreads();
   if (tid < 32 * NQ) {
-    // sum_j q'_j (c_j - m) = raw - (SB / 2 + m) sum_j q'_j; the sum in fp64
+    // sum_j q'_j (c_j - m) = raw - k1 sum_j q'_j; the sum in fp64
     const int g = tid >> 5, part = tid & 31;
     double sq = ((double)q_lds[g][4 * part] + (double)q_lds[g][4 * part + 1]) +
                 ((double)q_lds[g][4 * part + 2] + (double)q_lds[g][4 * part + 3]);
+    float qm = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(q_lds[g][4 * part]), __builtin_fabsf(q_lds[g][4 * part + 1])),
+                               __builtin_fmaxf(__builtin_fabsf(q_lds[g][4 * part + 2]), __builtin_fabsf(q_lds[g][4 * part + 3])));
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o, 32);
-    if (part == 0) k1_lds[g] = (float)(sq * (double)(0.5f * SB + M));
+    for (int o = 1; o < 32; o <<= 1) {
+      sq += __shfl_xor(sq, o, 32);
+      qm = __builtin_fmaxf(qm, __shfl_xor(qm, o, 32));
+    }
+    if constexpr (F8S) {
+      // x = rint(q' 2^E) with max |q'| 2^E in [2^18, 2^19): exact for every
+      // element down to 2^-11 of the largest, and within 2^-19 of it below
+      // (less than one fp32 rounding of a sum over the same terms), as
+      // x = d0 2^15 + d1 2^10 + d2 2^5 + d3 with d1..d3 in [-16, 15] and
+      // |d0| <= 16, in rows 4 (g % 4) + i of query set g / 4's operand table
+      // (lane order, over the score array before its first use)
+      const int ex = (int)((__builtin_bit_cast(uint32_t, qm) >> 23) & 0xFFu) - 127;  // 0 or subnormal: -127
+      const int E = ex < -108 ? 126 : 18 - ex;                                      // -109 .. 126
+      const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
+      uint8_t* tab = (uint8_t*)&s_lds[0][0] + (g >> 2) * 2048 + 4 * (g & 3) * 32;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ch = 4 * part + e;
+        int r = (int)__builtin_rintf(q_lds[g][ch] * sc);
+        int d[4];
+#pragma unroll
+        for (int i = 3; i > 0; --i) {
+          d[i] = ((r + 16) & 31) - 16;
+          r = (r - d[i]) / 32;  // exact
+        }
+        d[0] = r;
+        const int pos = qpart_pos<BITS>(ch);
+        uint8_t* t = tab + (pos >> 5) * 512 + (pos & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[32 * i] = (uint8_t)e4m3_int(d[i]);
+      }
+      if (part == 0) {
+        // raw = S 2^(shift - E): shift 1 for the fp4 values c / 2, 9 for the fp8 c 2^-9
+        k1_lds[g] = (float)(sq * (double)M);
+        e_lds[g] = __builtin_bit_cast(float, (uint32_t)((BITS == 2 ? 128 : 136) - E) << 23);
+      }
+    } else {
+      if (part == 0) k1_lds[g] = (float)(sq * (double)(0.5f * SB + M));
+    }
+  }
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  i32x8 Aq[F8S ? QS : 1];
+  float eq[F8S ? QS : 1], k1q[F8S ? QS : 1];
+  if constexpr (F8S) {
+    __syncthreads();
+    // lane (group g, row r) of query set qs: its 32 bytes of the table
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      Aq[qs] = *(const i32x8*)((const uint8_t*)&s_lds[0][0] + qs * 2048 + 32 * (tid & 63));
+      eq[qs] = e_lds[4 * qs + ((tid & 63) >> 4)];
+      k1q[qs] = k1_lds[4 * qs + ((tid & 63) >> 4)];
+    }
   }
 
   // score operands of the paired queries: lane (column col, group grp)
@@ -598,6 +713,62 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         float m = __builtin_fmaxf(mxa[qs], __shfl_xor(mxa[qs], 16, 64));
         m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
         if (lane < 16 && ga == 0) mx_lds[w][4 * qs + gq] = m;
+      }
+    } else if constexpr (F8S) {
+      // lane (query 4 qs + grp, token 16 t + col): the digit sums a0..a3 give
+      // S = ((a0 32 + a1) 32 + a2) 32 + a3, raw = S 2^(shift - E)
+      float mxq[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) mxq[qs] = NINF;
+      // two tiles at a time; past the round's last tile the second repeats the
+      // first (same scores to the same places)
+      for (int t0 = w; 16 * t0 < cnt; t0 += 8) {
+        const int tt[2] = {t0, 16 * (t0 + 4) < cnt ? t0 + 4 : t0};
+        i32x8 B[2];
+        float dk[2], of[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = 16 * tt[j] + col;
+          if constexpr (BITS == 2) {
+            const uint2 wd = *(const uint2*)&kc_lds[n * REC + 8 * grp];  // any bytes if absent
+            constexpr uint32_t m = 0x33333333u;
+            B[j] = (i32x8){(int)(wd.x & m), (int)((wd.x >> 2) & m), (int)(wd.y & m), (int)((wd.y >> 2) & m), 0, 0, 0, 0};
+          } else {
+            const uint4 wd = *(const uint4*)&kc_lds[n * REC + 16 * grp];
+            constexpr uint32_t m = 0x0F0F0F0Fu;
+            B[j] = (i32x8){(int)(wd.x & m), (int)((wd.x >> 4) & m), (int)(wd.y & m), (int)((wd.y >> 4) & m),
+                           (int)(wd.z & m), (int)((wd.z >> 4) & m), (int)(wd.w & m), (int)((wd.w >> 4) & m)};
+          }
+          dk[j] = dk_lds[n];
+          of[j] = off_lds[n];
+        }
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          f32x4 sc[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            sc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[qs], B[j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0,
+                                                                     BITS == 2 ? 4 : 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float S = __builtin_fmaf(sc[j][0], 32.0f, sc[j][1]);
+            S = __builtin_fmaf(S, 32.0f, sc[j][2]);
+            S = __builtin_fmaf(S, 32.0f, sc[j][3]);
+            // (raw - k1) * step * scale * log2(e); -inf for an absent token
+            const float sv = __builtin_fmaf(__builtin_fmaf(S, eq[qs], -k1q[qs]), dk[j], of[j]);
+            mxq[qs] = vmax(mxq[qs], sv);
+            s_lds[4 * qs + grp][16 * tt[j] + col] = sv;
+          }
+        }
+      }
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        float m = mxq[qs];
+        m = vmax(m, dpp_f32<0xB1>(m));   // quad_perm [1,0,3,2]
+        m = vmax(m, dpp_f32<0x4E>(m));   // quad_perm [2,3,0,1]
+        m = vmax(m, dpp_f32<0x124>(m));  // row_ror:4
+        m = vmax(m, dpp_f32<0x128>(m));  // row_ror:8
+        if (col == 0) mx_lds[w][4 * qs + grp] = m;
       }
     } else {
     for (int t0 = w; 16 * t0 < cnt; t0 += TWO ? 8 : 4) {
