@@ -13,31 +13,30 @@
 // Work decomposition (one query token per sequence, grouped query heads):
 //   * pair_queries_kernel: q'_j = RN32(sum_r T~inv[r][j] q_r) in fp64 FMAs
 //     over ascending r (every product is exact), then bf16.
-//   * attention_kernel: one block of four waves per (2048-token split, KV
-//     head, sequence), in rounds of 512 tokens (256 at 3 and 4 bits) whose
-//     key and value records are first copied to LDS with all loads in flight
-//     at once (at 2 and 4 bits, the next round's during this round's work).
-//       scores  2 and 4 bits, symmetric keys: S[g][n] = sum_j q'[g][j] c[n][j]
-//               on v_mfma_f32_16x16x128_f8f6f4, all 128 channels in one
+//   * one block of four waves per (2048-token split, KV head, sequence); a
+//     split writes (max, sum, unnormalized output) per query head, and
+//     combine_kernel merges the splits of a sequence.
+//   * attention_wave_kernel (2- and 4-bit symmetric caches): each wave takes
+//     64-token rounds of the split on its own, loads its key codes straight
+//     into registers and keeps its own online softmax.
+//       scores  S[g][n] = sum_j q'[g][j] c[n][j] on
+//               v_mfma_f32_16x16x128_f8f6f4, all 128 channels in one
 //               product: the query in 20-bit fixed point as four base-32
-//               digits (fp8 integers in rows 4 g + i), the
-//               codes as fp4 (2 bits) or fp8 (4 bits) values made with one
-//               mask per word, one lane per (query, token) after the digits
-//               are combined.  3 bits and affine
-//               keys: v_mfma_f32_16x16x32_bf16 with the codes as exact bf16
-//               values 0.5 + c / SB (one shift, mask and v_perm per pair).
-//               The constant part is subtracted after the product.
-//       softmax p = exp2(s - max) over the split, then p * step_v.
-//       values  O[ch][g] += c[ch][n] * p[n][g] on v_mfma_f32_16x16x32_bf16
-//               (2 and 4 bits): rows = 16 channels, k = 32 tokens, columns =
-//               the query heads' weights p * step_v split into three bf16
-//               parts (exact to fp32).  The value records go to LDS as token
+//               digits (fp8 integers in rows 4 g + i), the codes as fp4
+//               (2 bits) or fp8 (4 bits) values made with one mask per word,
+//               one lane per (query, token) after the digits are combined.
+//       values  O[ch][g] += c[ch][n] * p[n][g] on v_mfma_f32_16x16x32_bf16:
+//               rows = 16 channels, k = 32 tokens, columns = the query heads'
+//               weights p * step_v split into three bf16 parts (exact to
+//               fp32).  The value records go to the wave's LDS as token
 //               pairs: halfword j of tokens 2i and 2i + 1 side by side in one
 //               word, so that a lane turns the word into its channel's two
-//               operands with one rotate and one mask.  3-bit codes straddle words: v_mfma_f32_4x4x1f32
-//               with fp32 weights (16 blocks = 16 tokens, rows = queries).
-//     A split writes (max, sum, unnormalized output) per query head.
-//   * combine_kernel merges the splits of a sequence.
+//               operands with one rotate and one mask.
+//   * attention_kernel (3-bit symmetric and affine caches of every width):
+//     rounds of 256 tokens staged in LDS by the whole block, scores on
+//     v_mfma_f32_16x16x32_bf16 with the codes as exact bf16 values 0.5 + c /
+//     SB, values on v_mfma_f32_4x4x1f32 with fp32 weights (3-bit codes
+//     straddle words; an affine record has a step and zero per 32 channels).
 #include "device_common.h"
 #include "internal.h"
 
@@ -48,7 +47,7 @@ namespace wushkv {
 namespace {
 
 constexpr int kChunk = 2048;     // tokens per split (one block)
-constexpr int kSub = 512;        // tokens staged in LDS per round
+constexpr int kSub = 256;        // tokens staged in LDS per round (attention_kernel)
 constexpr int kPartFloats = 132;  // per (sequence, query head, split): max, sum, 2 pad, o[128]
 constexpr int kPairVecs = 4;      // query vectors per pairing block
 
@@ -288,17 +287,18 @@ __device__ __forceinline__ float vmax(float x, float y) {
   return r;
 }
 
+// 3-bit symmetric caches and affine caches of every width.
 // grid 8 * n_splits8 * Hkv * B blocks (see the block map below), 256 threads.
 // A block takes up to kChunk tokens of one sequence and KV head, in rounds of
 // KS tokens, with the running max, sums and value accumulators rescaled from
-// round to round (online softmax).
+// round to round (online softmax).  Scores on v_mfma_f32_16x16x32_bf16 with
+// the codes as exact bf16 values 0.5 + c / SB; values on the fp32 4x4x1
+// product, where wave w owns channels 32 w .. 32 w + 31 (one affine group).
 template <int BITS, int QS, bool AF>
 __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const AttnArgs a) {
+  static_assert(BITS == 3 || AF, "2- and 4-bit symmetric caches run attention_wave_kernel");
   constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
-  // tokens per round: 512, or 256 for 3- and 4-bit records and affine caches
-  // (so that three blocks' LDS fits a CU and a 4-bit round's records fit one
-  // load round)
-  constexpr int KS = (BITS == 2 && !AF) ? kSub : kSub / 2;
+  constexpr int KS = kSub;  // tokens per round (three blocks' LDS fits a CU)
   constexpr int REC = 16 * BITS;
   constexpr int SNW = BITS;    // words of key codes per lane (32 channels)
   constexpr int VNW = BITS == 3 ? 3 : 2;  // words of value codes per lane
@@ -307,33 +307,15 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   constexpr int SROW = KS + 16;  // s_lds row (padded against bank conflicts)
   constexpr float NINF = -__builtin_inff();
   constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass (4x4x1 product)
-  constexpr bool TWO = BITS == 2 && !AF;  // score tiles two at a time
-  // 2 and 4 bits, symmetric: the value product runs on bf16 16x16x32 MFMA with
-  // the value records staged as token pairs and the weights split into three
-  // bf16 parts (columns g + 4 part); 3 bits and affine caches: fp32 4x4x1 MFMA,
-  // where wave w owns channels 32 w .. 32 w + 31, one affine group.
-  constexpr bool VT = BITS != 3 && !AF;
-  // scores on the narrow-format product (2 and 4 bits, symmetric keys)
-  constexpr bool F8S = BITS != 3 && !AF;
-  constexpr int CPH = 16 / BITS;          // channels per halfword of a record (2 and 4 bits)
-  constexpr int NHW = REC / 2;            // halfwords per record
-  constexpr int VPROW = KS / 2 + 16;      // vp row (u32): one word per token pair, padded
-                                          // so that a read's two to four rows hit other banks
-  constexpr int PROW = KS + 8;          // weight row (bf16), 16-byte pieces spread over the banks
-  constexpr int KBYTES = KS * REC > QS * 16 * PROW * 2 ? KS * REC : QS * 16 * PROW * 2;
 
-  // the round's key records; after the scores, the bf16 weights [QS][16][PROW]
-  __shared__ __align__(16) uint8_t kc_lds[KBYTES];
-  // value records: token-pair words vp[j][i] = halfword j of token 2i + 1 << 16 | that of
-  // token 2i (2 and 4 bits), or the records as stored (3 bits)
-  __shared__ __align__(16) uint8_t vc_lds[VT ? NHW * VPROW * 4 : KS * REC];
+  __shared__ __align__(16) uint8_t kc_lds[KS * REC];  // the round's key records
+  __shared__ __align__(16) uint8_t vc_lds[KS * REC];  // the round's value records
   __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p * step_v
   __shared__ __align__(16) float dk_lds[KS];          // key step * scale * log2(e); 0: token absent
   __shared__ __align__(16) float off_lds[KS];         // 0, or -inf for an absent token
   __shared__ float dv_lds[KS];                        // value step
   __shared__ float q_lds[NQ][kD + 1];
   __shared__ float k1_lds[NQ];
-  __shared__ float e_lds[NQ];  // narrow-format scores: 2^(shift - E) of each query
   __shared__ float mx_lds[4][NQ];
   __shared__ float sum_lds[4][NQ][2];
   // affine caches, per group g and token n at [g * KS + n]: the key step and zero
@@ -393,61 +375,9 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     const int g = tid >> 5, part = tid & 31;
     double sq = ((double)q_lds[g][4 * part] + (double)q_lds[g][4 * part + 1]) +
                 ((double)q_lds[g][4 * part + 2] + (double)q_lds[g][4 * part + 3]);
-    float qm = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(q_lds[g][4 * part]), __builtin_fabsf(q_lds[g][4 * part + 1])),
-                               __builtin_fmaxf(__builtin_fabsf(q_lds[g][4 * part + 2]), __builtin_fabsf(q_lds[g][4 * part + 3])));
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      sq += __shfl_xor(sq, o, 32);
-      qm = __builtin_fmaxf(qm, __shfl_xor(qm, o, 32));
-    }
-    if constexpr (F8S) {
-      // x = rint(q' 2^E) with max |q'| 2^E in [2^18, 2^19): exact for every
-      // element down to 2^-11 of the largest, and within 2^-19 of it below
-      // (less than one fp32 rounding of a sum over the same terms), as
-      // x = d0 2^15 + d1 2^10 + d2 2^5 + d3 with d1..d3 in [-16, 15] and
-      // |d0| <= 16, in rows 4 (g % 4) + i of query set g / 4's operand table
-      // (lane order, over the score array before its first use)
-      const int ex = (int)((__builtin_bit_cast(uint32_t, qm) >> 23) & 0xFFu) - 127;  // 0 or subnormal: -127
-      const int E = ex < -108 ? 126 : 18 - ex;                                      // -109 .. 126
-      const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
-      uint8_t* tab = (uint8_t*)&s_lds[0][0] + (g >> 2) * 2048 + 4 * (g & 3) * 32;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ch = 4 * part + e;
-        int r = (int)__builtin_rintf(q_lds[g][ch] * sc);
-        int d[4];
-#pragma unroll
-        for (int i = 3; i > 0; --i) {
-          d[i] = ((r + 16) & 31) - 16;
-          r = (r - d[i]) / 32;  // exact
-        }
-        d[0] = r;
-        const int pos = qpart_pos<BITS>(ch);
-        uint8_t* t = tab + (pos >> 5) * 512 + (pos & 31);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[32 * i] = (uint8_t)e4m3_int(d[i]);
-      }
-      if (part == 0) {
-        // raw = S 2^(shift - E): shift 1 for the fp4 values c / 2, 9 for the fp8 c 2^-9
-        k1_lds[g] = (float)(sq * (double)M);
-        e_lds[g] = __builtin_bit_cast(float, (uint32_t)((BITS == 2 ? 128 : 136) - E) << 23);
-      }
-    } else {
-      if (part == 0) k1_lds[g] = (float)(sq * (double)(0.5f * SB + M));
-    }
-  }
-  typedef int i32x8 __attribute__((ext_vector_type(8)));
-  i32x8 Aq[F8S ? QS : 1];
-  float eq[F8S ? QS : 1], k1q[F8S ? QS : 1];
-  if constexpr (F8S) {
-    __syncthreads();
-    // lane (group g, row r) of query set qs: its 32 bytes of the table
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      Aq[qs] = *(const i32x8*)((const uint8_t*)&s_lds[0][0] + qs * 2048 + 32 * (tid & 63));
-      eq[qs] = e_lds[4 * qs + ((tid & 63) >> 4)];
-      k1q[qs] = k1_lds[4 * qs + ((tid & 63) >> 4)];
-    }
+    for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o, 32);
+    if (part == 0) k1_lds[g] = (float)(sq * (double)(0.5f * SB + M));
   }
 
   // score operands of the paired queries: lane (column col, group grp)
@@ -502,8 +432,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
 
   const int tb = lane >> 2, x = lane & 3;  // 4x4x1 value product: token block, column
   const int voff = value_byte_offset<BITS>(w, x);
-  // 4x4x1: acc[qs][k]; 16x16x32: acc[qs][mt] (mt = 16-channel tile) in acc[qs][0..1]
-  constexpr int NACC = VT ? 2 : 8;
+  constexpr int NACC = 8;  // acc[qs][k]: product k of the lane's channels
   f32x4 acc[QS][NACC];
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs)
@@ -513,18 +442,6 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   float zs[QS];
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) zs[qs] = 0.0f;
-  // 16x16x32 value product: lane (row 16 mt + lane % 16 of the wave's 32
-  // channels, k group grp = 8 tokens); the row of its channel's halfword in
-  // vp and the rotation that takes the code from its place in each half to
-  // bit SH (5: 2 bits, 3: 4 bits)
-  const int vch = 32 * w + (lane & 15);  // + 16 mt
-  int vrow[2], vrot[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int ch = vch + 16 * mt;
-    vrow[mt] = (ch / CPH) * VPROW;
-    vrot[mt] = (BITS * (ch % CPH) - (BITS == 2 ? 5 : 3)) & 31;
-  }
   float m_run[NQ], lsum[NQ], vsum[NQ];  // running max (uniform); this thread's sums
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
@@ -534,26 +451,16 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   }
   float k1 = 0.0f;
 
-  // ---- records of a round: CPT 16-byte pieces per record, one load round
-  // (2 and 4 bits: the next round's records and steps are loaded into
-  // registers while this round is worked on, and go to LDS at its end).
+  // ---- records of a round: CPT 16-byte pieces per record, one load round.
   // Tokens [t0, t1) of a round have cache rows (rows r0 + t in [0, n_rows),
   // t < the round's count); the loads go through buffer resources over those
   // rows only, so that every other token reads zeros and moves no bytes.
   constexpr int CPT = REC / 16;
   constexpr int PR = KS * CPT / 256;  // pieces per thread and cache
   static_assert(PR * 256 == KS * CPT && PR <= 4, "one load round of at most four pieces");
-  constexpr bool PF = VT;  // prefetch the next round (3 bits: the registers are needed elsewhere)
-  // piece c of a round: 2 and 4 bits, pairs of tokens in neighbouring lanes
-  // (piece (2i + e, part) at c = 2 (CPT i + part) + e), so that a lane finds
-  // the same part of its pair partner's record in lane c ^ 1; 3 bits, c =
-  // CPT t + part
-  auto piece_tok = [&](int c) __attribute__((always_inline)) -> int {
-    return VT ? (((c >> 1) / CPT) << 1) | (c & 1) : c / CPT;
-  };
-  auto piece_part = [&](int c) __attribute__((always_inline)) -> int {
-    return VT ? (c >> 1) % CPT : c % CPT;
-  };
+  // piece c of a round: part c % CPT of token c / CPT
+  auto piece_tok = [&](int c) __attribute__((always_inline)) -> int { return c / CPT; };
+  auto piece_part = [&](int c) __attribute__((always_inline)) -> int { return c % CPT; };
   struct RoundSrc {
     int t0, t1;
     rsrc_t k, v, ks, vs, kz, vz;
@@ -617,21 +524,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     for (int j = 0; j < PR; ++j) {
       const int c = tid + 256 * j, tok = piece_tok(c), part = piece_part(c);
       *(u32x4*)&kc_lds[16 * (tok * CPT + part)] = pk[j];
-      if constexpr (VT) {
-        // halfwords of this token and its partner (lane c ^ 1): the even token
-        // writes the pair words of its words' low halfwords, the odd one those
-        // of the high halfwords
-        uint32_t* vp = (uint32_t*)vc_lds;
-        const uint32_t sel = (tok & 1) ? 0x03020706u : 0x05040100u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t own = pv[j][e];
-          const uint32_t oth = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-          vp[(2 * (4 * part + e) + (tok & 1)) * VPROW + (tok >> 1)] = __builtin_amdgcn_perm(oth, own, sel);
-        }
-      } else {
-        *(u32x4*)&vc_lds[16 * (tok * CPT + part)] = pv[j];
-      }
+      *(u32x4*)&vc_lds[16 * (tok * CPT + part)] = pv[j];
     }
 #pragma unroll
     for (int j = 0; j < KS / 256; ++j) {
@@ -656,21 +549,16 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       }
     }
   };
-  if constexpr (PF) load_round(0);
-
   for (int base = 0; base < cnt_all; base += KS) {
     const int cnt = min(cnt_all - base, KS);
-    if constexpr (!PF) load_round(base);
+    load_round(base);
     // every piece is written (tokens past the round's end read zeros), so that
     // the loads are waited for here and nowhere else
     stage_round(base);
     __syncthreads();
-    if constexpr (PF) {
-      if (base + KS < cnt_all) load_round(base + KS);
-    }
     if (base == 0) k1 = col < NQ ? k1_lds[col] : 0.0f;
 
-    // ---- scores: wave w takes 16-token tiles w, w + 4, ... (two at a time)
+    // ---- scores: wave w takes 16-token tiles w, w + 4, ...
     float mx = NINF;
     if constexpr (AF) {
       // per column (query gq, group ga): s_ga (raw - (SB / 2) Q) + z_ga Q, with the
@@ -714,91 +602,28 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
         if (lane < 16 && ga == 0) mx_lds[w][4 * qs + gq] = m;
       }
-    } else if constexpr (F8S) {
-      // lane (query 4 qs + grp, token 16 t + col): the digit sums a0..a3 give
-      // S = ((a0 32 + a1) 32 + a2) 32 + a3, raw = S 2^(shift - E)
-      float mxq[QS];
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) mxq[qs] = NINF;
-      // two tiles at a time; past the round's last tile the second repeats the
-      // first (same scores to the same places)
-      for (int t0 = w; 16 * t0 < cnt; t0 += 8) {
-        const int tt[2] = {t0, 16 * (t0 + 4) < cnt ? t0 + 4 : t0};
-        i32x8 B[2];
-        float dk[2], of[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = 16 * tt[j] + col;
-          if constexpr (BITS == 2) {
-            const uint2 wd = *(const uint2*)&kc_lds[n * REC + 8 * grp];  // any bytes if absent
-            constexpr uint32_t m = 0x33333333u;
-            B[j] = (i32x8){(int)(wd.x & m), (int)((wd.x >> 2) & m), (int)(wd.y & m), (int)((wd.y >> 2) & m), 0, 0, 0, 0};
-          } else {
-            const uint4 wd = *(const uint4*)&kc_lds[n * REC + 16 * grp];
-            constexpr uint32_t m = 0x0F0F0F0Fu;
-            B[j] = (i32x8){(int)(wd.x & m), (int)((wd.x >> 4) & m), (int)(wd.y & m), (int)((wd.y >> 4) & m),
-                           (int)(wd.z & m), (int)((wd.z >> 4) & m), (int)(wd.w & m), (int)((wd.w >> 4) & m)};
-          }
-          dk[j] = dk_lds[n];
-          of[j] = off_lds[n];
-        }
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-          f32x4 sc[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            sc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[qs], B[j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0,
-                                                                     BITS == 2 ? 4 : 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float S = __builtin_fmaf(sc[j][0], 32.0f, sc[j][1]);
-            S = __builtin_fmaf(S, 32.0f, sc[j][2]);
-            S = __builtin_fmaf(S, 32.0f, sc[j][3]);
-            // (raw - k1) * step * scale * log2(e); -inf for an absent token
-            const float sv = __builtin_fmaf(__builtin_fmaf(S, eq[qs], -k1q[qs]), dk[j], of[j]);
-            mxq[qs] = vmax(mxq[qs], sv);
-            s_lds[4 * qs + grp][16 * tt[j] + col] = sv;
-          }
-        }
-      }
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        float m = mxq[qs];
-        m = vmax(m, dpp_f32<0xB1>(m));   // quad_perm [1,0,3,2]
-        m = vmax(m, dpp_f32<0x4E>(m));   // quad_perm [2,3,0,1]
-        m = vmax(m, dpp_f32<0x124>(m));  // row_ror:4
-        m = vmax(m, dpp_f32<0x128>(m));  // row_ror:8
-        if (col == 0) mx_lds[w][4 * qs + grp] = m;
-      }
     } else {
-    for (int t0 = w; 16 * t0 < cnt; t0 += TWO ? 8 : 4) {
-      const bool two = TWO && 16 * (t0 + 4) < cnt;  // uniform over the wave
-      uint32_t W[2][SNW];
-      load_words<SNW>(&kc_lds[(16 * t0 + col) * REC + 4 * BITS * grp], W[0]);  // any bytes if absent
-      if (two) load_words<SNW>(&kc_lds[(16 * t0 + 64 + col) * REC + 4 * BITS * grp], W[1]);
+    for (int t = w; 16 * t < cnt; t += 4) {
+      uint32_t W[SNW];
+      load_words<SNW>(&kc_lds[(16 * t + col) * REC + 4 * BITS * grp], W);  // any bytes if absent
+      bf16x8 A[4];
+      score_operands<BITS>(W, A);
+      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j == 1 && !two) break;
-        const int t = t0 + 4 * j;
-        bf16x8 A[4];
-        score_operands<BITS>(W[j], A);
-        f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s], Bq[s], sc, 0, 0, 0);
+      // sc[e]: token 16 t + 4 grp + e, query head col
+      const int i0 = 16 * t + 4 * grp;
+      const float4 dk4 = *(const float4*)&dk_lds[i0];
+      const float4 of4 = *(const float4*)&off_lds[i0];
+      const float dkv[4] = {dk4.x, dk4.y, dk4.z, dk4.w}, ofv[4] = {of4.x, of4.y, of4.z, of4.w};
+      float sv[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s], Bq[s], sc, 0, 0, 0);
-        // sc[e]: token 16 t + 4 grp + e, query head col
-        const int i0 = 16 * t + 4 * grp;
-        const float4 dk4 = *(const float4*)&dk_lds[i0];
-        const float4 of4 = *(const float4*)&off_lds[i0];
-        const float dkv[4] = {dk4.x, dk4.y, dk4.z, dk4.w}, ofv[4] = {of4.x, of4.y, of4.z, of4.w};
-        float sv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (raw - k1) * step * scale * log2(e); -inf for an absent token
-          sv[e] = __builtin_fmaf(sc[e] - k1, dkv[e], ofv[e]);
-          mx = __builtin_fmaxf(mx, sv[e]);
-        }
-        if (col < NQ) *(float4*)&s_lds[col][i0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      for (int e = 0; e < 4; ++e) {
+        // (raw - k1) * step * scale * log2(e); -inf for an absent token
+        sv[e] = __builtin_fmaf(sc[e] - k1, dkv[e], ofv[e]);
+        mx = __builtin_fmaxf(mx, sv[e]);
       }
+      if (col < NQ) *(float4*)&s_lds[col][i0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
     }
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -820,7 +645,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       const float msub = mn == NINF ? 0.0f : mn;
       m_run[g] = mn;
       float ls = 0.0f, vs = 0.0f;
-      // two consecutive tokens per thread (paired bf16 writes)
+      // two consecutive tokens per thread
       for (int n = 2 * tid; n < KS; n += 512) {
         float pv[2];
 #pragma unroll
@@ -833,84 +658,29 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
             vs += pv[e];
           }
         }
-        if constexpr (VT) {
-          // pv = hi + mid + lo in bf16 (exact up to the last part's rounding)
-          uint32_t* pt = (uint32_t*)((uint16_t*)kc_lds + (g >> 2) * 16 * PROW + (g & 3) * PROW + n);
-          const uint32_t hb = pack_bf16x2(pv[0], pv[1]);
-          const float r10 = pv[0] - bf16lo_to_f32(hb), r11 = pv[1] - bf16hi_to_f32(hb);
-          const uint32_t mb = pack_bf16x2(r10, r11);
-          const float r20 = r10 - bf16lo_to_f32(mb), r21 = r11 - bf16hi_to_f32(mb);
-          pt[0] = hb;
-          pt[2 * PROW] = mb;
-          pt[4 * PROW] = pack_bf16x2(r20, r21);
-        } else {
-          s_lds[g][n] = pv[0];
-          s_lds[g][n + 1] = pv[1];
-        }
+        s_lds[g][n] = pv[0];
+        s_lds[g][n + 1] = pv[1];
       }
       lsum[g] = lsum[g] * alpha[g] + ls;
       vsum[g] = vsum[g] * alpha[g] + vs;
     }
-    if constexpr (VT) {
-      // weight columns 12..15 carry nothing (they overlay last round's key records)
-      for (int i = tid; i < QS * 4 * PROW / 8; i += 256) {
-        const int qs = i / (4 * PROW / 8), r = i - qs * (4 * PROW / 8);
-        *(u32x4*)((uint16_t*)kc_lds + qs * 16 * PROW + 12 * PROW + 8 * r) = (u32x4){0u, 0u, 0u, 0u};
-      }
-      // column col = g + 4 part of the weights: query 4 qs + col % 4
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int k = 0; k < NACC; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
+    if constexpr (AF) {
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
-        const int cg = col & 3;
-        const float al = cg == 0 ? alpha[4 * qs] : (cg == 1 ? alpha[4 * qs + 1] : (cg == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
-#pragma unroll
-        for (int k = 0; k < NACC; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[qs][k][e] *= al;
-      }
-    } else {
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-        for (int k = 0; k < NACC; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
-      if constexpr (AF) {
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-          const float al = x == 0 ? alpha[4 * qs] : (x == 1 ? alpha[4 * qs + 1] : (x == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
-          zs[qs] *= al;
-        }
+        const float al = x == 0 ? alpha[4 * qs] : (x == 1 ? alpha[4 * qs + 1] : (x == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
+        zs[qs] *= al;
       }
     }
     __syncthreads();
 
     // ---- values: wave w owns channels 32 w .. 32 w + 31 (the weights past
     // the round's tokens are 0)
-    if constexpr (VT) {
-      const uint32_t* vp = (const uint32_t*)vc_lds;
-      const uint16_t* pt = (const uint16_t*)kc_lds;
-      constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : 0x00780078u;
-      uint32_t vhi = 0x3F003F00u;  // the operands' constant high bytes, held in a VGPR
-      asm volatile("" : "+v"(vhi));
-      for (int n0 = 0; n0 < n16; n0 += 32) {
-        const int nk = n0 + 8 * grp;  // this lane's 8 tokens: pairs nk / 2 .. nk / 2 + 3
-        bf16x8 P[QS];
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) P[qs] = *(const bf16x8*)(pt + qs * 16 * PROW + col * PROW + nk);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const u32x4 wp = *(const u32x4*)(vp + vrow[mt] + (nk >> 1));
-          u32x4 av;
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            av[t] = and_or_sv(__builtin_amdgcn_alignbit(wp[t], wp[t], vrot[mt]), VMASK, vhi);
-          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-          for (int qs = 0; qs < QS; ++qs)
-            acc[qs][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P[qs], acc[qs][mt], 0, 0, 0);
-        }
-      }
-    } else
     for (int u = 0; u < n16; u += 16 * PU) {
       uint32_t U[PU][VNW];
       float pa[PU][QS];
@@ -964,15 +734,12 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     for (int k = 0; k < NACC; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // 16x16x32: the three weight parts (columns c, c + 4, c + 8; c + 12 is 0);
-        // 4x4x1: the 16 token blocks (lanes x, x + 4, ..., x + 60)
+        // the 16 token blocks (lanes x, x + 4, ..., x + 60)
         float v = acc[qs][k][e];
         v = v + dpp_f32<0x124>(v);  // row_ror:4
         v = v + dpp_f32<0x128>(v);  // row_ror:8
-        if constexpr (!VT) {
-          v = xor_sum(v, 16);
-          v = xor_sum(v, 32);
-        }
+        v = xor_sum(v, 16);
+        v = xor_sum(v, 32);
         acc[qs][k][e] = v;
       }
   if constexpr (AF) {
@@ -988,24 +755,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     }
   }
   __syncthreads();
-  if constexpr (VT) {
-    if (col < 4) {
-      // lane (column col, group grp): channels 32 w + 16 mt + 4 grp + e
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        const int g = 4 * qs + col;
-        if (g < G) {
-          const float vs = (sum_lds[0][g][1] + sum_lds[1][g][1]) + (sum_lds[2][g][1] + sum_lds[3][g][1]);
-          const float cst = (0.5f * SB + M) * vs;
-          float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + 4;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[32 * w + 16 * mt + 4 * grp + e] = SB * acc[qs][mt][e] - cst;
-        }
-      }
-    }
-  } else if (lane < 4) {
+  if (lane < 4) {
     const float inv = 1.0f / value_scale<BITS>(x);
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs)
@@ -1035,6 +785,393 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       if (gg == g) m = m_run[gg];
     o[0] = m;
     o[1] = (sum_lds[0][g][0] + sum_lds[1][g][0]) + (sum_lds[2][g][0] + sum_lds[3][g][0]);
+  }
+}
+
+// ---- decode attention for 2- and 4-bit symmetric caches.
+// Block map, split records and launch as attention_kernel; 256 threads.  Wave
+// w of a block takes the 64-token rounds w, w + 4, w + 8, ... of the block's
+// split on its own: the key codes go straight from memory into the score
+// product's operand layout (lane (k group g, token col) loads its 8 g .. or
+// 16 g .. bytes), the softmax runs in registers with the wave's own running
+// max, and the values pass through an LDS region of the wave's own (token-pair
+// words and bf16 weight parts).  No barrier inside the loop; the four waves'
+// (max, sum, output) merge once at the end.  The next round's loads are
+// issued at the start of a round, so that they are in flight during its
+// scores, softmax and value product.
+template <int BITS, int QS>
+__global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attention_wave_kernel(const AttnArgs a) {
+  constexpr int NW = 4;                     // waves per block
+  constexpr int NQ = 4 * QS;
+  constexpr int RT = 4;                    // 16-token tiles per round
+  constexpr int RTOK = 16 * RT;            // tokens per round
+  constexpr int REC = 16 * BITS;
+  constexpr int CPT = REC / 16;            // 16-byte pieces per record
+  constexpr float SB = BITS == 2 ? 8.0f : 32.0f;
+  constexpr float M = (float)((1 << BITS) - 1) * 0.5f;
+  constexpr int CPH = 16 / BITS;           // channels per halfword of a record
+  constexpr int NHW = REC / 2;             // halfwords per record
+  constexpr int VPR = RTOK / 2 + 4;        // pair words per halfword row (padded)
+  constexpr int WPR = RTOK + 8;            // bf16 weights per column row (padded)
+  constexpr int VPB = NHW * VPR * 4;       // bytes of pair words
+  constexpr int WTB = QS * 16 * WPR * 2;   // bytes of weight parts
+  constexpr int REDB = NQ * kD * 4;        // bytes of the merge
+  constexpr int WB = VPB + WTB > REDB ? VPB + WTB : REDB;
+  constexpr float NINF = -__builtin_inff();
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+  __shared__ __align__(16) uint8_t wbuf[NW][WB];  // per wave: pair words, weights; then its merge terms
+  __shared__ __align__(16) uint8_t qtab[QS * 2048];
+  __shared__ float q_lds[NQ][kD + 1];
+  __shared__ float k1_lds[NQ], e_lds[NQ];
+  __shared__ float mw_lds[NW][NQ], lw_lds[NW][NQ];
+
+  // block map: as attention_kernel
+  const int L = blockIdx.x, xcd = L & 7, q = L >> 3;
+  const int h = q % a.n_kv_heads, q2 = q / a.n_kv_heads;
+  const int b = q2 / a.n_splits8, s8 = q2 - b * a.n_splits8;
+  const int split = 8 * s8 + ((xcd - b) & 7);
+  if (split >= a.n_splits) return;
+  const int len = min(max(a.len[b], 0), a.max_len);
+  const int n_lo = split * kChunk;
+  if (n_lo >= len) return;  // uniform over the block
+  const int cnt_all = min(len - n_lo, kChunk);
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int G = a.G, Hkv = a.n_kv_heads;
+  if (a.n_rows <= 0) {
+    // no row exists: the split contributes nothing (max -inf, sums and output 0)
+    for (int i = tid; i < G * kPartFloats; i += 256) {
+      const int g = i / kPartFloats, e = i - g * kPartFloats;
+      a.part[(((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + e] =
+          e == 0 ? -__builtin_inff() : 0.0f;
+    }
+    return;
+  }
+
+  // ---- the paired queries as fixed-point digits: x =
+  // rint(q' 2^E) with max |q'| 2^E in [2^18, 2^19) (exact for every element
+  // down to 2^-11 of the largest, and within 2^-19 of it below: less than one
+  // fp32 rounding of a sum over the same terms), x = d0 2^15 + d1 2^10 + d2 2^5
+  // + d3 with d1..d3 in [-16, 15] and |d0| <= 16, in rows 4 (g % 4) + i of
+  // query set g / 4's operand table (lane order)
+  for (int i = tid; i < NQ * kD; i += 256) {
+    const int g = i / kD, c = i % kD;
+    q_lds[g][c] = g < G ? bf16lo_to_f32(a.qp[((int64_t)b * a.n_q_heads + h * G + g) * kD + c]) : 0.0f;
+  }
+  const int64_t row_base = a.row0[b] + n_lo;
+  __syncthreads();
+  if (tid < 32 * NQ) {
+    const int g = tid >> 5, part = tid & 31;
+    const float* qr = q_lds[g];
+    double sq = ((double)qr[4 * part] + (double)qr[4 * part + 1]) + ((double)qr[4 * part + 2] + (double)qr[4 * part + 3]);
+    float qm = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(qr[4 * part]), __builtin_fabsf(qr[4 * part + 1])),
+                               __builtin_fmaxf(__builtin_fabsf(qr[4 * part + 2]), __builtin_fabsf(qr[4 * part + 3])));
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      sq += __shfl_xor(sq, o, 32);
+      qm = __builtin_fmaxf(qm, __shfl_xor(qm, o, 32));
+    }
+    const int ex = (int)((__builtin_bit_cast(uint32_t, qm) >> 23) & 0xFFu) - 127;  // 0 or subnormal: -127
+    const int E = ex < -108 ? 126 : 18 - ex;                                      // -109 .. 126
+    const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
+    uint8_t* tab = qtab + (g >> 2) * 2048 + 4 * (g & 3) * 32;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = 4 * part + e;
+      int r = (int)__builtin_rintf(qr[ch] * sc);
+      int d[4];
+#pragma unroll
+      for (int i = 3; i > 0; --i) {
+        d[i] = ((r + 16) & 31) - 16;
+        r = (r - d[i]) / 32;  // exact
+      }
+      d[0] = r;
+      const int pos = qpart_pos<BITS>(ch);
+      uint8_t* t = tab + (pos >> 5) * 512 + (pos & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[32 * i] = (uint8_t)e4m3_int(d[i]);
+    }
+    if (part == 0) {
+      // sum_j q'_j (c_j - m) = raw - m sum_j q'_j (the sum in fp64); raw = S 2^(shift - E):
+      // shift 1 for the fp4 values c / 2, 9 for the fp8 c 2^-9
+      k1_lds[g] = (float)(sq * (double)M);
+      e_lds[g] = __builtin_bit_cast(float, (uint32_t)((BITS == 2 ? 128 : 136) - E) << 23);
+    }
+  }
+  __syncthreads();
+  i32x8 Aq[QS];
+  float eq[QS], k1q[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    Aq[qs] = *(const i32x8*)(qtab + qs * 2048 + 32 * lane);
+    eq[qs] = e_lds[4 * qs + grp];
+    k1q[qs] = k1_lds[4 * qs + grp];
+  }
+
+  uint32_t* vp = (uint32_t*)wbuf[w];              // pair words [NHW][VPR]
+  uint16_t* wt = (uint16_t*)(wbuf[w] + VPB);      // weight parts [QS][16][WPR]
+  // columns 12..15 of each set's weights carry nothing
+  for (int i = lane; i < QS * 4 * WPR / 8; i += 64) {
+    const int qs = i / (4 * WPR / 8), r = i - qs * (4 * WPR / 8);
+    *(u32x4*)(wt + qs * 16 * WPR + 12 * WPR + 8 * r) = (u32x4){0u, 0u, 0u, 0u};
+  }
+  // value operand of this lane: channel 16 mt + col, halfword row (16 mt + col) / CPH
+  const int vrow0 = (col / CPH) * VPR;
+  const int vrot = (BITS * (col % CPH) - (BITS == 2 ? 5 : 3)) & 31;
+  constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : 0x00780078u;
+
+  f32x4 acc[QS][8];
+  float m_run[QS], l_run[QS], vs_run[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[qs][mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[qs] = NINF;
+    l_run[qs] = 0.0f;
+    vs_run[qs] = 0.0f;
+  }
+
+  // ---- rounds
+  struct RoundSrc {
+    int t0, t1;
+    rsrc_t k, v, ks, vs;
+  };
+  const uint32_t row_stride = (uint32_t)Hkv * REC;
+  auto round_src = [&](int base) __attribute__((always_inline)) -> RoundSrc {
+    const int cnt = min(cnt_all - base, RTOK);
+    const int64_t r0 = row_base + base;
+    const int64_t lo = r0 < 0 ? -r0 : 0, hi = a.n_rows - r0;
+    RoundSrc R;
+    R.t0 = (int)(lo < RTOK ? lo : RTOK);
+    R.t1 = (int)(hi < cnt ? (hi > 0 ? hi : 0) : cnt);
+    R.t1 = R.t1 > R.t0 ? R.t1 : R.t0;
+    const uint32_t n = (uint32_t)(R.t1 - R.t0);
+    const int64_t row = n ? r0 + R.t0 : 0;
+    R.k = buffer_rsrc(a.kc + (row * Hkv + h) * REC, n * row_stride);
+    R.v = buffer_rsrc(a.vc + (row * Hkv + h) * REC, n * row_stride);
+    R.ks = buffer_rsrc(a.ks + row * Hkv + h, n * (uint32_t)Hkv * 2u);
+    R.vs = buffer_rsrc(a.vs + row * Hkv + h, n * (uint32_t)Hkv * 2u);
+    return R;
+  };
+  // piece c = lane + 64 j of a round's value records: pairs of tokens in
+  // neighbouring lanes (piece (2 i + e, part) at c = 2 (CPT i + part) + e)
+  auto piece_tok = [&](int c) __attribute__((always_inline)) -> int { return ((c >> 1) / CPT << 1) | (c & 1); };
+  auto piece_part = [&](int c) __attribute__((always_inline)) -> int { return (c >> 1) % CPT; };
+  u32x2 kw2[RT];
+  u32x4 kw4[RT];
+  u32x4 vw[CPT];
+  uint32_t ksw, vsw;  // the steps of token `lane` of the round
+  // the lanes' offsets from the round's first row; a round subtracts t0 rows
+  // (a scalar), so that a token below the first present row wraps to a huge
+  // offset (|n - t0| <= 64 and row_stride < 2^22)
+  const uint32_t kbase = (uint32_t)col * row_stride + 4u * BITS * grp;
+  const uint32_t sbase = (uint32_t)lane * 2u * (uint32_t)Hkv;
+  uint32_t vbase[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) vbase[j] = (uint32_t)piece_tok(lane + 64 * j) * row_stride + 16u * piece_part(lane + 64 * j);
+  auto load_round = [&](int base) __attribute__((always_inline)) {
+    const RoundSrc R = round_src(base);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const uint32_t off = kbase + (uint32_t)((16 * t - R.t0) * (int)row_stride);
+      if constexpr (BITS == 2) kw2[t] = __builtin_amdgcn_raw_buffer_load_b64(R.k, off, 0, 0);
+      else kw4[t] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
+    }
+    const uint32_t so = sbase - (uint32_t)R.t0 * 2u * (uint32_t)Hkv;
+    ksw = __builtin_amdgcn_raw_buffer_load_b16(R.ks, so, 0, 0);
+    vsw = __builtin_amdgcn_raw_buffer_load_b16(R.vs, so, 0, 0);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      vw[j] = __builtin_amdgcn_raw_buffer_load_b128(R.v, vbase[j] - (uint32_t)R.t0 * row_stride, 0, 0);
+  };
+
+  uint32_t vhi = 0x3F003F00u;  // the value operands' constant high bytes, held in a VGPR
+  asm volatile("" : "+v"(vhi));
+  int base = RTOK * w;
+  if (base < cnt_all) load_round(base);
+  for (; base < cnt_all; base += NW * RTOK) {
+    const RoundSrc R = round_src(base);
+    // value records -> token-pair words: halfword j of tokens 2 i and 2 i + 1
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = lane + 64 * j, tok = piece_tok(c), part = piece_part(c);
+      const uint32_t sel = (tok & 1) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t own = vw[j][e];
+        const uint32_t oth = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+        vp[(2 * (4 * part + e) + (tok & 1)) * VPR + (tok >> 1)] = __builtin_amdgcn_perm(oth, own, sel);
+      }
+    }
+    // key operands and steps of tokens 16 t + col (the steps from lane 16 t + col)
+    i32x8 B[RT];
+    float dk[RT], dv[RT], of[RT];
+    const float dkl = f16_bits_to_f32((uint16_t)ksw) * a.c0, dvl = f16_bits_to_f32((uint16_t)vsw);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      if constexpr (BITS == 2) {
+        constexpr uint32_t m = 0x33333333u;
+        const u32x2 wd = kw2[t];
+        B[t] = (i32x8){(int)(wd[0] & m), (int)((wd[0] >> 2) & m), (int)(wd[1] & m), (int)((wd[1] >> 2) & m), 0, 0, 0, 0};
+      } else {
+        constexpr uint32_t m = 0x0F0F0F0Fu;
+        const u32x4 wd = kw4[t];
+        B[t] = (i32x8){(int)(wd[0] & m), (int)((wd[0] >> 4) & m), (int)(wd[1] & m), (int)((wd[1] >> 4) & m),
+                       (int)(wd[2] & m), (int)((wd[2] >> 4) & m), (int)(wd[3] & m), (int)((wd[3] >> 4) & m)};
+      }
+      const int n = 16 * t + col;
+      const bool ok = n >= R.t0 && n < R.t1;
+      dk[t] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * n, __builtin_bit_cast(int, dkl)));
+      const float dvn = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * n, __builtin_bit_cast(int, dvl)));
+      dv[t] = ok ? dvn : 0.0f;
+      of[t] = ok ? 0.0f : NINF;
+    }
+    if (base + NW * RTOK < cnt_all) load_round(base + NW * RTOK);
+
+    // ---- scores, softmax and weights: lane (query 4 qs + grp, token 16 t + col)
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      float sv[RT];
+      float rm = NINF;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        // the digit sums a0..a3 give S = ((a0 32 + a1) 32 + a2) 32 + a3, raw = S 2^(shift - E)
+        const f32x4 sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[qs], B[t], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0,
+                                                                          BITS == 2 ? 4 : 0, 0, 0, 0, 0);
+        float S = __builtin_fmaf(sc[0], 32.0f, sc[1]);
+        S = __builtin_fmaf(S, 32.0f, sc[2]);
+        S = __builtin_fmaf(S, 32.0f, sc[3]);
+        // (raw - k1) * step * scale * log2(e); -inf for an absent token
+        sv[t] = __builtin_fmaf(__builtin_fmaf(S, eq[qs], -k1q[qs]), dk[t], of[t]);
+        rm = vmax(rm, sv[t]);
+      }
+      rm = vmax(rm, dpp_f32<0xB1>(rm));   // quad_perm [1,0,3,2]
+      rm = vmax(rm, dpp_f32<0x4E>(rm));   // quad_perm [2,3,0,1]
+      rm = vmax(rm, dpp_f32<0x124>(rm));  // row_ror:4
+      rm = vmax(rm, dpp_f32<0x128>(rm));  // row_ror:8
+      const float mn = vmax(m_run[qs], rm);
+      // nothing seen yet: keep scale 1 and subtract 0 (every p is then 0)
+      const float alpha = m_run[qs] == NINF ? 1.0f : __builtin_amdgcn_exp2f(m_run[qs] - mn);
+      const float msub = mn == NINF ? 0.0f : mn;
+      m_run[qs] = mn;
+      float ls = 0.0f, vsum = 0.0f, pv[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const float p = __builtin_amdgcn_exp2f(sv[t] - msub);
+        pv[t] = p * dv[t];
+        ls += p;
+        vsum += pv[t];
+      }
+      l_run[qs] = __builtin_fmaf(l_run[qs], alpha, ls);
+      vs_run[qs] = __builtin_fmaf(vs_run[qs], alpha, vsum);
+      // weight parts hi + mid + lo (bf16, exact up to the last part's rounding),
+      // column grp + 4 part of the set
+      uint16_t* wq = wt + qs * 16 * WPR + grp * WPR + col;
+#pragma unroll
+      for (int t = 0; t < RT; t += 2) {
+        const uint32_t hb = pack_bf16x2(pv[t], pv[t + 1]);
+        const float r0 = pv[t] - bf16lo_to_f32(hb), r1 = pv[t + 1] - bf16hi_to_f32(hb);
+        const uint32_t mb = pack_bf16x2(r0, r1);
+        const uint32_t lb = pack_bf16x2(r0 - bf16lo_to_f32(mb), r1 - bf16hi_to_f32(mb));
+        wq[16 * t] = (uint16_t)hb;
+        wq[16 * t + 16] = (uint16_t)(hb >> 16);
+        wq[4 * WPR + 16 * t] = (uint16_t)mb;
+        wq[4 * WPR + 16 * t + 16] = (uint16_t)(mb >> 16);
+        wq[8 * WPR + 16 * t] = (uint16_t)lb;
+        wq[8 * WPR + 16 * t + 16] = (uint16_t)(lb >> 16);
+      }
+      // the accumulators' column col is query col % 4 of the set: its scale
+      // from lane 16 (col % 4); skipped when no query's max moved
+      const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 0));
+      const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 16));
+      const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 32));
+      const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 48));
+      if (!(a0 == 1.0f && a1 == 1.0f && a2 == 1.0f && a3 == 1.0f)) {
+        const int cq = col & 3;
+        const float ac = cq == 0 ? a0 : (cq == 1 ? a1 : (cq == 2 ? a2 : a3));
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[qs][mt][e] *= ac;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- values: O[ch][col] += c[ch][n] w[n][col], 32 tokens per product
+#pragma unroll
+    for (int ch2 = 0; ch2 < RTOK / 32; ++ch2) {
+      bf16x8 P[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) P[qs] = *(const bf16x8*)(wt + qs * 16 * WPR + col * WPR + 32 * ch2 + 8 * grp);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const u32x4 wp = *(const u32x4*)(vp + vrow0 + mt * (16 / CPH) * VPR + 16 * ch2 + 4 * grp);
+        u32x4 av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = and_or_sv(__builtin_amdgcn_alignbit(wp[i], wp[i], vrot), VMASK, vhi);
+        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs)
+          acc[qs][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P[qs], acc[qs][mt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the four waves: the block max, each wave's terms scaled to it
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const float ls = dpp_sum16(l_run[qs]);
+    vs_run[qs] = dpp_sum16(vs_run[qs]);
+    if (col == 0) {
+      mw_lds[w][4 * qs + grp] = m_run[qs];
+      lw_lds[w][4 * qs + grp] = ls;
+    }
+  }
+  __syncthreads();
+  float* red = (float*)wbuf[w];  // [NQ][128]: this wave's scaled output terms
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    // the three weight parts: columns c, c + 4, c + 8 (c + 12 is 0)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = acc[qs][mt][e];
+        v = v + dpp_f32<0x124>(v);  // row_ror:4
+        v = v + dpp_f32<0x128>(v);  // row_ror:8
+        acc[qs][mt][e] = v;
+      }
+    // this wave's scale for query g: lane col < 4 holds query 4 qs + col
+    const int g = 4 * qs + (col & 3);
+    const float mb = vmax(vmax(mw_lds[0][g], mw_lds[1][g]), vmax(mw_lds[2][g], mw_lds[3][g]));
+    const float scl = mw_lds[w][g] == NINF ? 0.0f : __builtin_amdgcn_exp2f(mw_lds[w][g] - mb);
+    // vs of query g: in lanes 16 (g % 4) + any
+    const float vsg = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * 16 * (col & 3), __builtin_bit_cast(int, vs_run[qs])));
+    const float cst = (0.5f * SB + M) * vsg;
+    if (col < 4) {
+      // lane (column col, group grp): channels 16 mt + 4 grp + e
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[g * kD + 16 * mt + 4 * grp + e] = scl * (SB * acc[qs][mt][e] - cst);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * kD; i += 256) {
+    const int g = i >> 7, c = i & 127;
+    float* rec = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats;
+    rec[4 + c] = (((const float*)wbuf[0])[i] + ((const float*)wbuf[1])[i]) +
+                 (((const float*)wbuf[2])[i] + ((const float*)wbuf[3])[i]);
+    if (c == 0) {
+      const float mb = vmax(vmax(mw_lds[0][g], mw_lds[1][g]), vmax(mw_lds[2][g], mw_lds[3][g]));
+      float l = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l += mw_lds[k][g] == NINF ? 0.0f : __builtin_amdgcn_exp2f(mw_lds[k][g] - mb) * lw_lds[k][g];
+      rec[0] = mb;
+      rec[1] = l;
+    }
   }
 }
 
@@ -1089,8 +1226,13 @@ hipError_t launch_attention_bits(const AttnArgs& a, int qs, hipStream_t st) {
   const dim3 grid((unsigned)(8 * (int64_t)a.n_splits8 * a.n_kv_heads * a.n_seqs));
   if (a.kz) return qs == 1 ? launch_kernel(attention_kernel<BITS, 1, true>, grid, dim3(256), st, a)
                            : launch_kernel(attention_kernel<BITS, 2, true>, grid, dim3(256), st, a);
-  return qs == 1 ? launch_kernel(attention_kernel<BITS, 1, false>, grid, dim3(256), st, a)
-                 : launch_kernel(attention_kernel<BITS, 2, false>, grid, dim3(256), st, a);
+  if constexpr (BITS == 3) {
+    return qs == 1 ? launch_kernel(attention_kernel<3, 1, false>, grid, dim3(256), st, a)
+                   : launch_kernel(attention_kernel<3, 2, false>, grid, dim3(256), st, a);
+  } else {
+    return qs == 1 ? launch_kernel(attention_wave_kernel<BITS, 1>, grid, dim3(256), st, a)
+                   : launch_kernel(attention_wave_kernel<BITS, 2>, grid, dim3(256), st, a);
+  }
 }
 
 }  // namespace
