@@ -958,14 +958,18 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
   // neighbouring lanes (piece (2 i + e, part) at c = 2 (CPT i + part) + e)
   auto piece_tok = [&](int c) __attribute__((always_inline)) -> int { return ((c >> 1) / CPT << 1) | (c & 1); };
   auto piece_part = [&](int c) __attribute__((always_inline)) -> int { return (c >> 1) % CPT; };
-  u32x2 kw2[RT];
+  // key codes: 2 bits, per pair of tiles (2 p, 2 p + 1) lane (g, col) loads
+  // bytes 16 (g / 2) .. + 15 of token 16 (2 p + g % 2) + col, and a swap of
+  // 16-lane rows hands each lane its 8 bytes of both tiles; 4 bits, per tile
+  // lane (g, col) loads bytes 16 g .. + 15 of token 16 t + col
   u32x4 kw4[RT];
   u32x4 vw[CPT];
   uint32_t ksw, vsw;  // the steps of token `lane` of the round
   // the lanes' offsets from the round's first row; a round subtracts t0 rows
   // (a scalar), so that a token below the first present row wraps to a huge
   // offset (|n - t0| <= 64 and row_stride < 2^22)
-  const uint32_t kbase = (uint32_t)col * row_stride + 4u * BITS * grp;
+  const uint32_t kbase = BITS == 2 ? (uint32_t)(col + 16 * (grp & 1)) * row_stride + 16u * (grp >> 1)
+                                   : (uint32_t)col * row_stride + 16u * grp;
   const uint32_t sbase = (uint32_t)lane * 2u * (uint32_t)Hkv;
   uint32_t vbase[CPT];
 #pragma unroll
@@ -973,10 +977,9 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
   auto load_round = [&](int base) __attribute__((always_inline)) {
     const RoundSrc R = round_src(base);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const uint32_t off = kbase + (uint32_t)((16 * t - R.t0) * (int)row_stride);
-      if constexpr (BITS == 2) kw2[t] = __builtin_amdgcn_raw_buffer_load_b64(R.k, off, 0, 0);
-      else kw4[t] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
+    for (int t = 0; t < (BITS == 2 ? RT / 2 : RT); ++t) {
+      const uint32_t off = kbase + (uint32_t)(((BITS == 2 ? 32 : 16) * t - R.t0) * (int)row_stride);
+      kw4[t] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
     }
     const uint32_t so = sbase - (uint32_t)R.t0 * 2u * (uint32_t)Hkv;
     ksw = __builtin_amdgcn_raw_buffer_load_b16(R.ks, so, 0, 0);
@@ -1008,6 +1011,18 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
     i32x8 B[RT];
     float dk[RT], dv[RT], of[RT];
     const float dkl = f16_bits_to_f32((uint16_t)ksw) * a.c0, dvl = f16_bits_to_f32((uint16_t)vsw);
+    u32x2 kw2[RT];
+    if constexpr (BITS == 2) {
+#pragma unroll
+      for (int p = 0; p < RT / 2; ++p) {
+        // odd rows of words 0, 1 <-> even rows of words 2, 3: then words 0, 1 hold
+        // tile 2 p and words 2, 3 tile 2 p + 1
+        const auto x0 = __builtin_amdgcn_permlane16_swap(kw4[p][0], kw4[p][2], false, false);
+        const auto x1 = __builtin_amdgcn_permlane16_swap(kw4[p][1], kw4[p][3], false, false);
+        kw2[2 * p] = (u32x2){x0[0], x1[0]};
+        kw2[2 * p + 1] = (u32x2){x0[1], x1[1]};
+      }
+    }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       if constexpr (BITS == 2) {
