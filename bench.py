@@ -639,6 +639,27 @@ def main() -> int:
     aff_kernel_us = float(np.mean([e[0].elapsed_time(e[1]) for e in aff_ev])) * 1e3
     aff_bytes = int(att_len.sum()) * H * 2 * (16 * bits + 16) + dn * att_q * D * 2 + dn * 2 * 12
     del aff, att_aff
+    # the same batch over 3- and 4-bit symmetric caches (random codes and steps)
+    width = {}
+    for wb in (3, 4):
+        wc = [bk.PackedCache(torch.randint(0, 256, (rows_all, H, 16 * wb), dtype=torch.uint8, device=dev, generator=g),
+                             (torch.rand((rows_all, H), device=dev, generator=g) * 0.05 + 0.02).to(torch.float16))
+              for _ in range(2)]
+        att_w = bk.prepare_decode_attention(att_qp, wc[0], wc[1], H, wb, q, att_row0, att_lens, 32768,
+                                            1.0 / np.sqrt(D), att_ws, att_out, stream=stream)
+        with torch.cuda.stream(stream):
+            for _ in range(2 * rep):
+                att_w()
+        torch.cuda.synchronize()
+        w_ev = new_events(5 * rep, 2)
+        for e in w_ev:
+            bk.wushkv_debug_time_next_launch(e[0], e[1])
+            att_w()
+        torch.cuda.synchronize()
+        w_us = float(np.mean([e[0].elapsed_time(e[1]) for e in w_ev])) * 1e3
+        w_bytes = int(att_len.sum()) * H * 2 * (16 * wb + 2) + dn * att_q * D * 2 + dn * 2 * 12
+        width[wb] = (round(w_us, 2), w_bytes, round(w_bytes / (w_us * 1e-6) / 8e12, 4))
+        del wc, att_w
 
     # ---- the other workloads' kernels, each against the HBM roofline (kernel-recorded events,
     # one buffer set: every input is at least 256 MiB, beyond the MALL).
@@ -744,6 +765,8 @@ def main() -> int:
             "affine_algorithmic_bytes": aff_bytes,
             "affine_attention_hbm_frac": round(aff_bytes / (aff_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "affine_note": "the same batch and codes as affine caches (four fp16 steps and zeros per record)",
+            "symmetric_widths": {f"{wb}bit": {"attention_kernel_us": v[0], "algorithmic_bytes": v[1], "attention_hbm_frac": v[2]}
+                                 for wb, v in width.items()},
         },
         "other_workloads": other,
     }
