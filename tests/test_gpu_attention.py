@@ -193,6 +193,48 @@ def test_attention_odd_kv_heads_and_split_edges(env, bits):
     check_attention(env, got, ref, value_max(v, bits, row0, lens, rows, Hkv), G, f"odd heads bits={bits}")
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_attention_query_dynamic_range(env, bits):
+    """Paired queries whose elements span many binades, against the oracle's
+    exact scores: the 2- and 4-bit kernels hold the query in 20-bit fixed
+    point relative to its largest element (exact within 2^-11 of it, rounded to
+    2^-19 of it below), so small elements beside a large one, a query of
+    bf16-tiny values (the scale exponent at its clamp) and a large query (a
+    peaked softmax) are the cases where that representation shows."""
+    oracle = env["oracle"]
+    rng = np.random.default_rng(1300 + bits)
+    Hkv, G = 2, 4
+    lens = np.array([1500, 700, 2100, 64])
+    row0 = np.array([0, 1600, 2400, 4600])
+    rows = 4700
+    k, v = random_cache(rng, rows, Hkv, bits), random_cache(rng, rows, Hkv, bits)
+    B, Hq = len(lens), Hkv * G
+    q = np.zeros((B, Hq, D))
+    sign = lambda shape: np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    for b in range(B):
+        base = b % 2  # the two KV heads see the patterns in turn
+        pats = []
+        pats.append(rng.standard_normal(D) * 3.0)                                     # ordinary
+        x = sign(D) * 8.0 * 10.0 ** rng.uniform(-7, -1, D); x[rng.integers(D)] = 8.0   # one large, the rest small
+        pats.append(x)
+        x = sign(D) * 1e-5; x[rng.integers(D)] = -20.0                                 # one large, the rest tiny
+        pats.append(x)
+        pats.append(sign(D) * 2.0)                                                     # equal magnitudes
+        pats.append(sign(D) * 16.0 * 2.0 ** -rng.uniform(0, 30, D))                    # 30 binades
+        pats.append(rng.standard_normal(D) * 1e-35)                                    # bf16-tiny values
+        pats.append(rng.standard_normal(D) * 40.0)                                     # large: a peaked softmax
+        x = np.zeros(D); x[rng.integers(D, size=3)] = rng.standard_normal(3) * 5.0     # three nonzero entries
+        pats.append(x)
+        for hq in range(Hq):
+            q[b, hq] = pats[(hq + 4 * base) % len(pats)]
+    qp = bf16_bits(q)
+    say(f"attention query dynamic range bits={bits}")
+    scale = 1.0 / np.sqrt(D)
+    got = run_attention(env, qp, k, v, Hkv, bits, row0, lens, scale)
+    ref = oracle.decode_attention(qp, k, v, bits, row0, lens, scale)
+    check_attention(env, got, ref, value_max(v, bits, row0, lens, rows, Hkv), G, f"query dynamic range bits={bits}")
+
+
 def test_attention_edge_cases(env):
     oracle = env["oracle"]
     rng = np.random.default_rng(31)
