@@ -249,15 +249,6 @@ __device__ __forceinline__ uint32_t and_or_sv(uint32_t x, uint32_t m, uint32_t c
 // j.  Only the pairing of A's and B's elements matters, which the map below
 // fixes.
 
-// The fp8 (e4m3) pattern of an integer d in [-16, 16] (exact).
-__device__ __forceinline__ uint32_t e4m3_int(int d) {
-  const uint32_t m = (uint32_t)(d < 0 ? -d : d);
-  if (m == 0) return 0u;
-  const int e = 31 - __builtin_clz(m);  // 0..4
-  const uint32_t mant = (e <= 3 ? m << (3 - e) : m >> 1) & 7u;
-  return (d < 0 ? 0x80u : 0u) | ((uint32_t)(e + 7) << 3) | mant;
-}
-
 // Position 32 g + j (lane group g, byte j of A's 32) of channel ch in the
 // query operand, matched to where the code operand puts that channel's code.
 template <int BITS>
@@ -887,10 +878,13 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
         r = (r - d[i]) / 32;  // exact
       }
       d[0] = r;
+      // the four digits as fp8 (e4m3) bytes, exact: integers of at most 5 bits
+      uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)d[0], (float)d[1], 0, false);
+      pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)d[2], (float)d[3], (int)pk, true);
       const int pos = qpart_pos<BITS>(ch);
       uint8_t* t = tab + (pos >> 5) * 512 + (pos & 31);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t[32 * i] = (uint8_t)e4m3_int(d[i]);
+      for (int i = 0; i < 4; ++i) t[32 * i] = (uint8_t)(pk >> (8 * i));
     }
     if (part == 0) {
       // sum_j q'_j (c_j - m) = raw - m sum_j q'_j (the sum in fp64); raw = S 2^(shift - E):
