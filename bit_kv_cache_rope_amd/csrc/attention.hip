@@ -782,10 +782,11 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
 // ---- decode attention for 2- and 4-bit symmetric caches.
 // Block map, split records and launch as attention_kernel; 256 threads.  Wave
 // w of a block takes the 64-token rounds w, w + 4, w + 8, ... of the block's
-// split on its own: the key codes go straight from memory into the score
-// product's operand layout (lane (k group g, token col) loads its 8 g .. or
-// 16 g .. bytes), the softmax runs in registers with the wave's own running
-// max, and the values pass through an LDS region of the wave's own (token-pair
+// split on its own: the key codes go straight from memory into registers
+// and into the score product's operand layout (4 bits: lane (k group g, token
+// col) loads its bytes 16 g ..; 2 bits: one 16-byte load covers two tiles and
+// a swap of 16-lane rows hands each lane its 8 bytes of both), the softmax
+// runs in registers with the wave's own running max, and the values pass through an LDS region of the wave's own (token-pair
 // words and bf16 weight parts).  No barrier inside the loop; the four waves'
 // (max, sum, output) merge once at the end.  The next round's loads are
 // issued at the start of a round, so that they are in flight during its
