@@ -16,15 +16,17 @@
 //   * one block of four waves per (2048-token split, KV head, sequence); a
 //     split writes (max, sum, unnormalized output) per query head, and
 //     combine_kernel merges the splits of a sequence.
-//   * attention_wave_kernel (2- and 4-bit symmetric caches): each wave takes
-//     64-token rounds of the split on its own, loads its key codes straight
-//     into registers and keeps its own online softmax.
+//   * attention_wave_kernel (symmetric caches of every width): each wave
+//     takes 64-token rounds of the split on its own, loads its key codes
+//     straight into registers and keeps its own online softmax.  3-bit
+//     records are loaded as 12-byte pieces (32 channels) and widened in
+//     registers to the 4-bit layout, after which they take the 4-bit path.
 //       scores  S[g][n] = sum_j q'[g][j] c[n][j] on
 //               v_mfma_f32_16x16x128_f8f6f4, all 128 channels in one
 //               product: the query in 20-bit fixed point as four base-32
 //               digits (fp8 integers in rows 4 g + i), the codes as fp4
-//               (2 bits) or fp8 (4 bits) values made with one mask per word,
-//               one lane per (query, token) after the digits are combined.
+//               (2 bits) or fp8 (3 and 4 bits) values made with one mask per
+//               word, one lane per (query, token) after the digits are combined.
 //       values  O[ch][g] += c[ch][n] * p[n][g] on v_mfma_f32_16x16x32_bf16:
 //               rows = 16 channels, k = 32 tokens, columns = the query heads'
 //               weights p * step_v split into three bf16 parts (exact to
@@ -32,28 +34,30 @@
 //               pairs: halfword j of tokens 2i and 2i + 1 side by side in one
 //               word, so that a lane turns the word into its channel's two
 //               operands with one rotate and one mask.
-//   * attention_kernel (3-bit symmetric and affine caches of every width):
-//     rounds of 256 tokens staged in LDS by the whole block, scores on
-//     v_mfma_f32_16x16x32_bf16 with the codes as exact bf16 values 0.5 + c /
-//     SB, values on v_mfma_f32_4x4x1f32 with fp32 weights (3-bit codes
-//     straddle words; an affine record has a step and zero per 32 channels).
+//   * attention_affine_kernel (affine caches of every width): rounds of 256 tokens
+//     staged in LDS by the whole block, scores on v_mfma_f32_16x16x32_bf16
+//     with the codes as exact bf16 values 0.5 + c / SB, values on
+//     v_mfma_f32_4x4x1f32 with fp32 weights (an affine record has a step and
+//     zero per 32 channels).
 #include "device_common.h"
 #include "internal.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace wushkv {
 
 namespace {
 
 constexpr int kChunk = 2048;     // tokens per split (one block)
-constexpr int kSub = 256;        // tokens staged in LDS per round (attention_kernel)
+constexpr int kSub = 256;        // tokens staged in LDS per round (attention_affine_kernel)
 constexpr int kPartFloats = 132;  // per (sequence, query head, split): max, sum, 2 pad, o[128]
 constexpr int kPairVecs = 4;      // query vectors per pairing block
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past `bytes`
@@ -232,6 +236,28 @@ __device__ __forceinline__ uint32_t and_or_sv(uint32_t x, uint32_t m, uint32_t c
   return r;
 }
 
+// (a & m) | (b & ~m): one v_bfi_b32
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+// 32 consecutive 3-bit codes (12 bytes of a record, LSB first) widened to the
+// 4-bit record layout: nibble n of word r holds code 8 r + n in its low three
+// bits; the nibble's top bit is left undefined (the operands mask it off).
+// Each 24-bit run of eight codes spreads in three steps: the high six codes'
+// bits move up by 4 (runs of four codes in each halfword), then codes 2, 3 of
+// each halfword by 2, then the odd codes of each byte by 1.
+__device__ __forceinline__ u32x4 widen3(const u32x3 d) {
+  const uint32_t x[4] = {d[0], __builtin_amdgcn_alignbit(d[1], d[0], 24), __builtin_amdgcn_alignbit(d[2], d[1], 16),
+                         d[2] >> 8};
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t w = bfi(0x00000FFFu, x[k], x[k] << 4);
+    w = bfi(0x003F003Fu, w, w << 2);
+    r[k] = bfi(0x07070707u, w, w << 1);
+  }
+  return r;
+}
+
 // ---- narrow-format score product (2 and 4 bits, symmetric keys) on
 // v_mfma_f32_16x16x128_f8f6f4: A = the paired query in fixed point as four
 // base-32 digits, each an fp8 (e4m3) integer; B = the key codes of 16 tokens,
@@ -278,45 +304,40 @@ __device__ __forceinline__ float vmax(float x, float y) {
   return r;
 }
 
-// 3-bit symmetric caches and affine caches of every width.
+// Affine caches of every width (a step and a zero per 32-channel group).
 // grid 8 * n_splits8 * Hkv * B blocks (see the block map below), 256 threads.
 // A block takes up to kChunk tokens of one sequence and KV head, in rounds of
 // KS tokens, with the running max, sums and value accumulators rescaled from
 // round to round (online softmax).  Scores on v_mfma_f32_16x16x32_bf16 with
 // the codes as exact bf16 values 0.5 + c / SB; values on the fp32 4x4x1
 // product, where wave w owns channels 32 w .. 32 w + 31 (one affine group).
-template <int BITS, int QS, bool AF>
-__global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const AttnArgs a) {
-  static_assert(BITS == 3 || AF, "2- and 4-bit symmetric caches run attention_wave_kernel");
+template <int BITS, int QS>
+__global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_affine_kernel(const AttnArgs a) {
   constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
   constexpr int KS = kSub;  // tokens per round (three blocks' LDS fits a CU)
   constexpr int REC = 16 * BITS;
   constexpr int SNW = BITS;    // words of key codes per lane (32 channels)
   constexpr int VNW = BITS == 3 ? 3 : 2;  // words of value codes per lane
   constexpr float SB = BITS == 2 ? 8.0f : (BITS == 3 ? 16.0f : 32.0f);
-  constexpr float M = (float)((1 << BITS) - 1) * 0.5f;
   constexpr int SROW = KS + 16;  // s_lds row (padded against bank conflicts)
   constexpr float NINF = -__builtin_inff();
   constexpr int PU = BITS == 2 ? 4 : 2;   // value steps per pass (4x4x1 product)
 
   __shared__ __align__(16) uint8_t kc_lds[KS * REC];  // the round's key records
   __shared__ __align__(16) uint8_t vc_lds[KS * REC];  // the round's value records
-  __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p * step_v
-  __shared__ __align__(16) float dk_lds[KS];          // key step * scale * log2(e); 0: token absent
+  __shared__ __align__(16) float s_lds[NQ][SROW];       // scores (log2 units), then p
   __shared__ __align__(16) float off_lds[KS];         // 0, or -inf for an absent token
-  __shared__ float dv_lds[KS];                        // value step
+  __shared__ float pr_lds[KS];                        // 1, or 0 for an absent token
   __shared__ float q_lds[NQ][kD + 1];
-  __shared__ float k1_lds[NQ];
   __shared__ float mx_lds[4][NQ];
-  __shared__ float sum_lds[4][NQ][2];
-  // affine caches, per group g and token n at [g * KS + n]: the key step and zero
-  // times scale * log2(e), the value step and zero (0 for an absent token)
-  constexpr int NAF = AF ? 4 * KS : 4;
-  __shared__ __align__(16) float ksc_lds[NAF];
-  __shared__ __align__(16) float kzr_lds[NAF];
-  __shared__ __align__(16) float vsc_lds[NAF];
-  __shared__ __align__(16) float vzr_lds[NAF];
-  __shared__ float zsum_lds[4][NQ];  // affine: sum_n p_n z_n of wave w's group, per query
+  __shared__ float sum_lds[4][NQ];
+  // per group g and token n at [g * KS + n]: the key step and zero times
+  // scale * log2(e), the value step and zero (0 for an absent token)
+  __shared__ __align__(16) float ksc_lds[4 * KS];
+  __shared__ __align__(16) float kzr_lds[4 * KS];
+  __shared__ __align__(16) float vsc_lds[4 * KS];
+  __shared__ __align__(16) float vzr_lds[4 * KS];
+  __shared__ float zsum_lds[4][NQ];  // sum_n p_n z_n of wave w's group, per query
 
   // Block L runs on XCD L % 8 (blocks are dispatched to the XCDs round-robin).
   // The split s of sequence b goes to XCD (s + b) % 8, so that each XCD gets
@@ -361,42 +382,18 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   // waited for in every round: the compiler cannot tell it from the stores)
   const int64_t row_base = a.row0[b] + n_lo;
   __syncthreads();
-  if (tid < 32 * NQ) {
-    // sum_j q'_j (c_j - m) = raw - k1 sum_j q'_j; the sum in fp64
-    const int g = tid >> 5, part = tid & 31;
-    double sq = ((double)q_lds[g][4 * part] + (double)q_lds[g][4 * part + 1]) +
-                ((double)q_lds[g][4 * part + 2] + (double)q_lds[g][4 * part + 3]);
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o, 32);
-    if (part == 0) k1_lds[g] = (float)(sq * (double)(0.5f * SB + M));
-  }
 
-  // score operands of the paired queries: lane (column col, group grp)
-  const int col = lane & 15, grp = lane >> 4;
-  bf16x8 Bq[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 v;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float x0 = 0.0f, x1 = 0.0f;
-      if (col < NQ) {
-        x0 = q_lds[col][score_channel<BITS>(grp, s, 2 * t)] * SB;
-        x1 = q_lds[col][score_channel<BITS>(grp, s, 2 * t + 1)] * SB;
-      }
-      v[t] = pack_bf16x2(x0, x1);  // exact: bf16 values times a power of two
-    }
-    Bq[s] = __builtin_bit_cast(bf16x8, v);
-  }
-  // Affine keys: the score product's 16 columns are (query gq = col / 4, group
+  // score operands of the paired queries: lane (column col, group grp).  The
+  // score product's 16 columns are (query gq = col / 4, group
   // ga = col % 4) of each 4-query set qs: a lane's operand holds its query's
   // channels of group ga only where its k group grp is that group (lane group
   // grp holds channels 32 grp .. 32 grp + 31), so each column sums one group:
   // raw = sum_{j in ga} (0.5 + c_j / SB) q'_j SB = (SB / 2) Q + sum_{j in ga} c_j q'_j,
   // with Q = sum_{j in ga} q'_j (fp64, then fp32).
-  bf16x8 Bqa[AF ? QS : 1][4];
-  float kqa[AF ? QS : 1], Qa[AF ? QS : 1];
-  if constexpr (AF) {
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 Bqa[QS][4];
+  float kqa[QS], Qa[QS];
+  {
     const int gq = col >> 2, ga = col & 3;
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
@@ -414,7 +411,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
             x0 = q_lds[4 * qs + gq][score_channel<BITS>(grp, s, 2 * t)] * SB;
             x1 = q_lds[4 * qs + gq][score_channel<BITS>(grp, s, 2 * t + 1)] * SB;
           }
-          v[t] = pack_bf16x2(x0, x1);
+          v[t] = pack_bf16x2(x0, x1);  // exact: bf16 values times a power of two
         }
         Bqa[qs][s] = __builtin_bit_cast(bf16x8, v);
       }
@@ -429,18 +426,16 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
     for (int k = 0; k < NACC; ++k) acc[qs][k] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  // affine values: this lane's sum_n p_n z_n (wave w's group) for query 4 qs + x
+  // this lane's sum_n p_n z_n (wave w's group) for query 4 qs + x
   float zs[QS];
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) zs[qs] = 0.0f;
-  float m_run[NQ], lsum[NQ], vsum[NQ];  // running max (uniform); this thread's sums
+  float m_run[NQ], lsum[NQ];  // running max (uniform); this thread's sums
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
     m_run[g] = NINF;
     lsum[g] = 0.0f;
-    vsum[g] = 0.0f;
   }
-  float k1 = 0.0f;
 
   // ---- records of a round: CPT 16-byte pieces per record, one load round.
   // Tokens [t0, t1) of a round have cache rows (rows r0 + t in [0, n_rows),
@@ -456,7 +451,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     int t0, t1;
     rsrc_t k, v, ks, vs, kz, vz;
   };
-  constexpr uint32_t NSC = AF ? 4 : 1;  // fp16 steps (and zeros) per record
+  constexpr uint32_t NSC = 4;  // fp16 steps and zeros per record
   const uint32_t row_stride = (uint32_t)Hkv * REC;  // bytes between cache rows (< 2^22)
   auto round_src = [&](int base) __attribute__((always_inline)) -> RoundSrc {
     const int cnt = min(cnt_all - base, KS);
@@ -472,15 +467,12 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     R.v = buffer_rsrc(a.vc + (row * Hkv + h) * REC, n * row_stride);
     R.ks = buffer_rsrc(a.ks + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
     R.vs = buffer_rsrc(a.vs + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
-    if constexpr (AF) {
-      R.kz = buffer_rsrc(a.kz + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
-      R.vz = buffer_rsrc(a.vz + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
-    }
+    R.kz = buffer_rsrc(a.kz + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
+    R.vz = buffer_rsrc(a.vz + (row * Hkv + h) * NSC, n * (uint32_t)Hkv * 2u * NSC);
     return R;
   };
   u32x4 pk[PR], pv[PR];
-  uint32_t pks[KS / 256], pvs[KS / 256];
-  u32x2 aks[AF ? KS / 256 : 1], akz[AF ? KS / 256 : 1], avs[AF ? KS / 256 : 1], avz[AF ? KS / 256 : 1];
+  u32x2 aks[KS / 256], akz[KS / 256], avs[KS / 256], avz[KS / 256];
   auto load_round = [&](int base) __attribute__((always_inline)) {
     const RoundSrc R = round_src(base);
 #pragma unroll
@@ -494,21 +486,15 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     }
 #pragma unroll
     for (int j = 0; j < KS / 256; ++j) {
-      if constexpr (AF) {
-        const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 8 * Hkv);
-        aks[j] = __builtin_amdgcn_raw_buffer_load_b64(R.ks, off, 0, 0);
-        akz[j] = __builtin_amdgcn_raw_buffer_load_b64(R.kz, off, 0, 0);
-        avs[j] = __builtin_amdgcn_raw_buffer_load_b64(R.vs, off, 0, 0);
-        avz[j] = __builtin_amdgcn_raw_buffer_load_b64(R.vz, off, 0, 0);
-      } else {
-        const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 2 * Hkv);
-        pks[j] = __builtin_amdgcn_raw_buffer_load_b16(R.ks, off, 0, 0);
-        pvs[j] = __builtin_amdgcn_raw_buffer_load_b16(R.vs, off, 0, 0);
-      }
+      const uint32_t off = (uint32_t)__mul24(tid + 256 * j - R.t0, 8 * Hkv);
+      aks[j] = __builtin_amdgcn_raw_buffer_load_b64(R.ks, off, 0, 0);
+      akz[j] = __builtin_amdgcn_raw_buffer_load_b64(R.kz, off, 0, 0);
+      avs[j] = __builtin_amdgcn_raw_buffer_load_b64(R.vs, off, 0, 0);
+      avz[j] = __builtin_amdgcn_raw_buffer_load_b64(R.vz, off, 0, 0);
     }
   };
-  // the registers of load_round(base) -> LDS: records, and per token the key
-  // step * scale * log2(e), the -inf offset of an absent token and the value step
+  // the registers of load_round(base) -> LDS: records, and per token the -inf
+  // offset of an absent token and the groups' steps and zeros
   auto stage_round = [&](int base) __attribute__((always_inline)) {
     const RoundSrc R = round_src(base);
 #pragma unroll
@@ -522,21 +508,17 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       const int i = tid + 256 * j;
       const bool ok = i >= R.t0 && i < R.t1;
       off_lds[i] = ok ? 0.0f : NINF;
-      if constexpr (AF) {
-        // the weights p * 1; the group steps and zeros go to the value product
-        dv_lds[i] = ok ? 1.0f : 0.0f;
+      // the weights are p (0 for an absent token); the group steps and zeros
+      // go to the value product
+      pr_lds[i] = ok ? 1.0f : 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t sw = aks[j][g >> 1] >> (16 * (g & 1)), zw = akz[j][g >> 1] >> (16 * (g & 1));
-          const uint32_t vw = avs[j][g >> 1] >> (16 * (g & 1)), uw = avz[j][g >> 1] >> (16 * (g & 1));
-          ksc_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)sw) * a.c0 : 0.0f;
-          kzr_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)zw) * a.c0 : 0.0f;
-          vsc_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)vw) : 0.0f;
-          vzr_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)uw) : 0.0f;
-        }
-      } else {
-        dk_lds[i] = ok ? f16_bits_to_f32((uint16_t)pks[j]) * a.c0 : 0.0f;
-        dv_lds[i] = ok ? f16_bits_to_f32((uint16_t)pvs[j]) : 0.0f;
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t sw = aks[j][g >> 1] >> (16 * (g & 1)), zw = akz[j][g >> 1] >> (16 * (g & 1));
+        const uint32_t vw = avs[j][g >> 1] >> (16 * (g & 1)), uw = avz[j][g >> 1] >> (16 * (g & 1));
+        ksc_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)sw) * a.c0 : 0.0f;
+        kzr_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)zw) * a.c0 : 0.0f;
+        vsc_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)vw) : 0.0f;
+        vzr_lds[g * KS + i] = ok ? f16_bits_to_f32((uint16_t)uw) : 0.0f;
       }
     }
   };
@@ -547,11 +529,9 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     // the loads are waited for here and nowhere else
     stage_round(base);
     __syncthreads();
-    if (base == 0) k1 = col < NQ ? k1_lds[col] : 0.0f;
 
     // ---- scores: wave w takes 16-token tiles w, w + 4, ...
-    float mx = NINF;
-    if constexpr (AF) {
+    {
       // per column (query gq, group ga): s_ga (raw - (SB / 2) Q) + z_ga Q, with the
       // step and zero already times scale * log2(e); the quad of a query's four
       // groups then sums them (every lane of the quad holds the score)
@@ -593,37 +573,11 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
         if (lane < 16 && ga == 0) mx_lds[w][4 * qs + gq] = m;
       }
-    } else {
-    for (int t = w; 16 * t < cnt; t += 4) {
-      uint32_t W[SNW];
-      load_words<SNW>(&kc_lds[(16 * t + col) * REC + 4 * BITS * grp], W);  // any bytes if absent
-      bf16x8 A[4];
-      score_operands<BITS>(W, A);
-      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s], Bq[s], sc, 0, 0, 0);
-      // sc[e]: token 16 t + 4 grp + e, query head col
-      const int i0 = 16 * t + 4 * grp;
-      const float4 dk4 = *(const float4*)&dk_lds[i0];
-      const float4 of4 = *(const float4*)&off_lds[i0];
-      const float dkv[4] = {dk4.x, dk4.y, dk4.z, dk4.w}, ofv[4] = {of4.x, of4.y, of4.z, of4.w};
-      float sv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // (raw - k1) * step * scale * log2(e); -inf for an absent token
-        sv[e] = __builtin_fmaf(sc[e] - k1, dkv[e], ofv[e]);
-        mx = __builtin_fmaxf(mx, sv[e]);
-      }
-      if (col < NQ) *(float4*)&s_lds[col][i0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
-    }
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lane < NQ) mx_lds[w][lane] = mx;
     }
     __syncthreads();
 
-    // ---- p = exp2(s - max) and p * step_v (0 past the round's tokens); the
-    // sums and accumulators so far are rescaled to the new max
+    // ---- p = exp2(s - max) (0 past the round's tokens); the sums and
+    // accumulators so far are rescaled to the new max
     const int n16 = (cnt + 15) & ~15;
     float alpha[NQ];
 #pragma unroll
@@ -635,7 +589,7 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       alpha[g] = m_run[g] == NINF ? 1.0f : __builtin_amdgcn_exp2f(m_run[g] - mn);
       const float msub = mn == NINF ? 0.0f : mn;
       m_run[g] = mn;
-      float ls = 0.0f, vs = 0.0f;
+      float ls = 0.0f;
       // two consecutive tokens per thread
       for (int n = 2 * tid; n < KS; n += 512) {
         float pv[2];
@@ -644,16 +598,14 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
           pv[e] = 0.0f;
           if (n + e < n16) {
             const float p = __builtin_amdgcn_exp2f(s_lds[g][n + e] - msub);
-            pv[e] = p * dv_lds[n + e];
+            pv[e] = p * pr_lds[n + e];
             ls += p;
-            vs += pv[e];
           }
         }
         s_lds[g][n] = pv[0];
         s_lds[g][n + 1] = pv[1];
       }
       lsum[g] = lsum[g] * alpha[g] + ls;
-      vsum[g] = vsum[g] * alpha[g] + vs;
     }
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs)
@@ -661,12 +613,10 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       for (int k = 0; k < NACC; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[qs][k][e] *= alpha[4 * qs + e];
-    if constexpr (AF) {
 #pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        const float al = x == 0 ? alpha[4 * qs] : (x == 1 ? alpha[4 * qs + 1] : (x == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
-        zs[qs] *= al;
-      }
+    for (int qs = 0; qs < QS; ++qs) {
+      const float al = x == 0 ? alpha[4 * qs] : (x == 1 ? alpha[4 * qs + 1] : (x == 2 ? alpha[4 * qs + 2] : alpha[4 * qs + 3]));
+      zs[qs] *= al;
     }
     __syncthreads();
 
@@ -681,14 +631,12 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         load_words<VNW>(&vc_lds[i * REC + voff], U[jj]);  // any bytes if absent (its weight is 0)
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) pa[jj][qs] = s_lds[4 * qs + x][i];
-        if constexpr (AF) {
-          // v^ = z + c s of wave w's group: weights p s for the codes, p z summed aside
-          const float vsg = vsc_lds[w * KS + i], vzg = vzr_lds[w * KS + i];
+        // v^ = z + c s of wave w's group: weights p s for the codes, p z summed aside
+        const float vsg = vsc_lds[w * KS + i], vzg = vzr_lds[w * KS + i];
 #pragma unroll
-          for (int qs = 0; qs < QS; ++qs) {
-            zs[qs] = __builtin_fmaf(pa[jj][qs], vzg, zs[qs]);
-            pa[jj][qs] *= vsg;
-          }
+        for (int qs = 0; qs < QS; ++qs) {
+          zs[qs] = __builtin_fmaf(pa[jj][qs], vzg, zs[qs]);
+          pa[jj][qs] *= vsg;
         }
       }
 #pragma unroll
@@ -708,16 +656,10 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
   // ---- sums over the block; the 16 token blocks of the value product
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
-    float ls = lsum[g], vs = vsum[g];
+    float ls = lsum[g];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      ls = xor_sum(ls, o);
-      vs = xor_sum(vs, o);
-    }
-    if (lane == 0) {
-      sum_lds[w][g][0] = ls;
-      sum_lds[w][g][1] = vs;
-    }
+    for (int o = 1; o < 64; o <<= 1) ls = xor_sum(ls, o);
+    if (lane == 0) sum_lds[w][g] = ls;
   }
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs)
@@ -733,17 +675,15 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
         v = xor_sum(v, 32);
         acc[qs][k][e] = v;
       }
-  if constexpr (AF) {
-    // the 16 token blocks' zero sums (lanes x, x + 4, ..., x + 60), per query 4 qs + x
+  // the 16 token blocks' zero sums (lanes x, x + 4, ..., x + 60), per query 4 qs + x
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      float v = zs[qs];
-      v = v + dpp_f32<0x124>(v);  // row_ror:4
-      v = v + dpp_f32<0x128>(v);  // row_ror:8
-      v = xor_sum(v, 16);
-      v = xor_sum(v, 32);
-      if (lane < 4) zsum_lds[w][4 * qs + lane] = v;
-    }
+  for (int qs = 0; qs < QS; ++qs) {
+    float v = zs[qs];
+    v = v + dpp_f32<0x124>(v);  // row_ror:4
+    v = v + dpp_f32<0x128>(v);  // row_ror:8
+    v = xor_sum(v, 16);
+    v = xor_sum(v, 32);
+    if (lane < 4) zsum_lds[w][4 * qs + lane] = v;
   }
   __syncthreads();
   if (lane < 4) {
@@ -754,16 +694,10 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
       for (int e = 0; e < 4; ++e) {
         const int g = 4 * qs + e;
         if (g < G) {
-          const float vs = (sum_lds[0][g][1] + sum_lds[1][g][1]) + (sum_lds[2][g][1] + sum_lds[3][g][1]);
           float* o = a.part + (((int64_t)b * a.n_q_heads + h * G + g) * a.n_splits + split) * kPartFloats + 4;
-          if constexpr (AF) {
-            const float zt = zsum_lds[w][g];
+          const float zt = zsum_lds[w][g];
 #pragma unroll
-            for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = __builtin_fmaf(acc[qs][k][e], inv, zt);
-          } else {
-#pragma unroll
-            for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = acc[qs][k][e] * inv - M * vs;
-          }
+          for (int k = 0; k < NACC; ++k) o[value_channel<BITS>(w, x, k)] = __builtin_fmaf(acc[qs][k][e], inv, zt);
         }
       }
   }
@@ -775,12 +709,12 @@ __global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_kernel(const A
     for (int gg = 1; gg < NQ; ++gg)
       if (gg == g) m = m_run[gg];
     o[0] = m;
-    o[1] = (sum_lds[0][g][0] + sum_lds[1][g][0]) + (sum_lds[2][g][0] + sum_lds[3][g][0]);
+    o[1] = (sum_lds[0][g] + sum_lds[1][g]) + (sum_lds[2][g] + sum_lds[3][g]);
   }
 }
 
-// ---- decode attention for 2- and 4-bit symmetric caches.
-// Block map, split records and launch as attention_kernel; 256 threads.  Wave
+// ---- decode attention for symmetric caches (2, 3 and 4 bits).
+// Block map, split records and launch as attention_affine_kernel; 256 threads.  Wave
 // w of a block takes the 64-token rounds w, w + 4, w + 8, ... of the block's
 // split on its own: the key codes go straight from memory into registers
 // and into the score product's operand layout (4 bits: lane (k group g, token
@@ -797,12 +731,17 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
   constexpr int NQ = 4 * QS;
   constexpr int RT = 4;                    // 16-token tiles per round
   constexpr int RTOK = 16 * RT;            // tokens per round
-  constexpr int REC = 16 * BITS;
-  constexpr int CPT = REC / 16;            // 16-byte pieces per record
+  constexpr int REC = 16 * BITS;           // bytes per record in the cache
+  // 3-bit records are widened in registers to the 4-bit layout as they
+  // arrive (widen3), and everything after the loads runs as for 4 bits
+  constexpr int OB = BITS == 3 ? 4 : BITS;  // bits per code in the operand layout
+  constexpr int OREC = 16 * OB;            // bytes per record in that layout
+  constexpr int CPT = OREC / 16;           // 16-byte pieces per record (in that layout)
+  constexpr int PB = BITS == 3 ? 12 : 16;  // bytes of a piece in the cache
   constexpr float SB = BITS == 2 ? 8.0f : 32.0f;
   constexpr float M = (float)((1 << BITS) - 1) * 0.5f;
-  constexpr int CPH = 16 / BITS;           // channels per halfword of a record
-  constexpr int NHW = REC / 2;             // halfwords per record
+  constexpr int CPH = 16 / OB;             // channels per halfword of a record
+  constexpr int NHW = OREC / 2;            // halfwords per record
   constexpr int VPR = RTOK / 2 + 4;        // pair words per halfword row (padded)
   constexpr int WPR = RTOK + 8;            // bf16 weights per column row (padded)
   constexpr int VPB = NHW * VPR * 4;       // bytes of pair words
@@ -818,7 +757,7 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
   __shared__ float k1_lds[NQ], e_lds[NQ];
   __shared__ float mw_lds[NW][NQ], lw_lds[NW][NQ];
 
-  // block map: as attention_kernel
+  // block map: as attention_affine_kernel
   const int L = blockIdx.x, xcd = L & 7, q = L >> 3;
   const int h = q % a.n_kv_heads, q2 = q / a.n_kv_heads;
   const int b = q2 / a.n_splits8, s8 = q2 - b * a.n_splits8;
@@ -882,7 +821,7 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
       // the four digits as fp8 (e4m3) bytes, exact: integers of at most 5 bits
       uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)d[0], (float)d[1], 0, false);
       pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)d[2], (float)d[3], (int)pk, true);
-      const int pos = qpart_pos<BITS>(ch);
+      const int pos = qpart_pos<OB>(ch);
       uint8_t* t = tab + (pos >> 5) * 512 + (pos & 31);
 #pragma unroll
       for (int i = 0; i < 4; ++i) t[32 * i] = (uint8_t)(pk >> (8 * i));
@@ -913,8 +852,9 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
   }
   // value operand of this lane: channel 16 mt + col, halfword row (16 mt + col) / CPH
   const int vrow0 = (col / CPH) * VPR;
-  const int vrot = (BITS * (col % CPH) - (BITS == 2 ? 5 : 3)) & 31;
-  constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : 0x00780078u;
+  const int vrot = (OB * (col % CPH) - (BITS == 2 ? 5 : 3)) & 31;
+  // (3 bits: the widened nibble's undefined top bit falls outside the mask)
+  constexpr uint32_t VMASK = BITS == 2 ? 0x00600060u : (BITS == 3 ? 0x00380038u : 0x00780078u);
 
   f32x4 acc[QS][8];
   float m_run[QS], l_run[QS], vs_run[QS];
@@ -957,31 +897,49 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
   // bytes 16 (g / 2) .. + 15 of token 16 (2 p + g % 2) + col, and a swap of
   // 16-lane rows hands each lane its 8 bytes of both tiles; 4 bits, per tile
   // lane (g, col) loads bytes 16 g .. + 15 of token 16 t + col
-  u32x4 kw4[RT];
-  u32x4 vw[CPT];
+  typedef std::conditional_t<BITS == 3, u32x3, u32x4> Piece;  // a piece as loaded
+  Piece kw4[RT];
+  Piece vw[CPT];
   uint32_t ksw, vsw;  // the steps of token `lane` of the round
   // the lanes' offsets from the round's first row; a round subtracts t0 rows
   // (a scalar), so that a token below the first present row wraps to a huge
   // offset (|n - t0| <= 64 and row_stride < 2^22)
   const uint32_t kbase = BITS == 2 ? (uint32_t)(col + 16 * (grp & 1)) * row_stride + 16u * (grp >> 1)
-                                   : (uint32_t)col * row_stride + 16u * grp;
+                                   : (uint32_t)col * row_stride + (uint32_t)PB * grp;
   const uint32_t sbase = (uint32_t)lane * 2u * (uint32_t)Hkv;
   uint32_t vbase[CPT];
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) vbase[j] = (uint32_t)piece_tok(lane + 64 * j) * row_stride + 16u * piece_part(lane + 64 * j);
+  for (int j = 0; j < CPT; ++j)
+    vbase[j] = (uint32_t)piece_tok(lane + 64 * j) * row_stride + (uint32_t)PB * piece_part(lane + 64 * j);
+  // one piece of a record: 16 bytes, or (3 bits) 12 bytes, widened to 16 only
+  // where it is used (widening at the load would wait for it there)
+  auto load_piece = [&](rsrc_t rs, uint32_t off) __attribute__((always_inline)) -> Piece {
+    if constexpr (BITS == 3) {
+      return __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0);
+    } else {
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    }
+  };
+  auto wide = [&](const Piece& x) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (BITS == 3) {
+      return widen3(x);
+    } else {
+      return x;
+    }
+  };
   auto load_round = [&](int base) __attribute__((always_inline)) {
     const RoundSrc R = round_src(base);
 #pragma unroll
     for (int t = 0; t < (BITS == 2 ? RT / 2 : RT); ++t) {
       const uint32_t off = kbase + (uint32_t)(((BITS == 2 ? 32 : 16) * t - R.t0) * (int)row_stride);
-      kw4[t] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
+      kw4[t] = load_piece(R.k, off);
     }
     const uint32_t so = sbase - (uint32_t)R.t0 * 2u * (uint32_t)Hkv;
     ksw = __builtin_amdgcn_raw_buffer_load_b16(R.ks, so, 0, 0);
     vsw = __builtin_amdgcn_raw_buffer_load_b16(R.vs, so, 0, 0);
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
-      vw[j] = __builtin_amdgcn_raw_buffer_load_b128(R.v, vbase[j] - (uint32_t)R.t0 * row_stride, 0, 0);
+      vw[j] = load_piece(R.v, vbase[j] - (uint32_t)R.t0 * row_stride);
   };
 
   uint32_t vhi = 0x3F003F00u;  // the value operands' constant high bytes, held in a VGPR
@@ -995,9 +953,10 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
     for (int j = 0; j < CPT; ++j) {
       const int c = lane + 64 * j, tok = piece_tok(c), part = piece_part(c);
       const uint32_t sel = (tok & 1) ? 0x03020706u : 0x05040100u;
+      const u32x4 vwj = wide(vw[j]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t own = vw[j][e];
+        const uint32_t own = vwj[e];
         const uint32_t oth = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
         vp[(2 * (4 * part + e) + (tok & 1)) * VPR + (tok >> 1)] = __builtin_amdgcn_perm(oth, own, sel);
       }
@@ -1025,8 +984,8 @@ __global__ void __launch_bounds__(256, QS == 2 ? 2 : (BITS == 2 ? 4 : 3)) attent
         const u32x2 wd = kw2[t];
         B[t] = (i32x8){(int)(wd[0] & m), (int)((wd[0] >> 2) & m), (int)(wd[1] & m), (int)((wd[1] >> 2) & m), 0, 0, 0, 0};
       } else {
-        constexpr uint32_t m = 0x0F0F0F0Fu;
-        const u32x4 wd = kw4[t];
+        constexpr uint32_t m = BITS == 3 ? 0x07070707u : 0x0F0F0F0Fu;  // (3 bits: the widened codes)
+        const u32x4 wd = wide(kw4[t]);
         B[t] = (i32x8){(int)(wd[0] & m), (int)((wd[0] >> 4) & m), (int)(wd[1] & m), (int)((wd[1] >> 4) & m),
                        (int)(wd[2] & m), (int)((wd[2] >> 4) & m), (int)(wd[3] & m), (int)((wd[3] >> 4) & m)};
       }
@@ -1234,15 +1193,10 @@ __global__ void __launch_bounds__(128) combine_kernel(const AttnArgs a) {
 template <int BITS>
 hipError_t launch_attention_bits(const AttnArgs& a, int qs, hipStream_t st) {
   const dim3 grid((unsigned)(8 * (int64_t)a.n_splits8 * a.n_kv_heads * a.n_seqs));
-  if (a.kz) return qs == 1 ? launch_kernel(attention_kernel<BITS, 1, true>, grid, dim3(256), st, a)
-                           : launch_kernel(attention_kernel<BITS, 2, true>, grid, dim3(256), st, a);
-  if constexpr (BITS == 3) {
-    return qs == 1 ? launch_kernel(attention_kernel<3, 1, false>, grid, dim3(256), st, a)
-                   : launch_kernel(attention_kernel<3, 2, false>, grid, dim3(256), st, a);
-  } else {
-    return qs == 1 ? launch_kernel(attention_wave_kernel<BITS, 1>, grid, dim3(256), st, a)
-                   : launch_kernel(attention_wave_kernel<BITS, 2>, grid, dim3(256), st, a);
-  }
+  if (a.kz) return qs == 1 ? launch_kernel(attention_affine_kernel<BITS, 1>, grid, dim3(256), st, a)
+                           : launch_kernel(attention_affine_kernel<BITS, 2>, grid, dim3(256), st, a);
+  return qs == 1 ? launch_kernel(attention_wave_kernel<BITS, 1>, grid, dim3(256), st, a)
+                 : launch_kernel(attention_wave_kernel<BITS, 2>, grid, dim3(256), st, a);
 }
 
 }  // namespace

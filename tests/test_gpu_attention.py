@@ -172,7 +172,7 @@ def test_attention_matches_oracle(env, bits, G):
     check_attention(env, got, ref, value_max(v, bits, row0, lens, rows, Hkv), G, f"bits={bits} G={G}")
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_attention_odd_kv_heads_and_split_edges(env, bits):
     """Three KV heads (the block map spreads heads and splits over the XCDs
     modulo the head count) with two query heads each; lengths one past, at and
@@ -193,10 +193,10 @@ def test_attention_odd_kv_heads_and_split_edges(env, bits):
     check_attention(env, got, ref, value_max(v, bits, row0, lens, rows, Hkv), G, f"odd heads bits={bits}")
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_attention_query_dynamic_range(env, bits):
     """Paired queries whose elements span many binades, against the oracle's
-    exact scores: the 2- and 4-bit kernels hold the query in 20-bit fixed
+    exact scores: the symmetric-cache kernel holds the query in 20-bit fixed
     point relative to its largest element (exact within 2^-11 of it, rounded to
     2^-19 of it below), so small elements beside a large one, a query of
     bf16-tiny values (the scale exponent at its clamp) and a large query (a
