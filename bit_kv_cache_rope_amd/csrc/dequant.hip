@@ -21,18 +21,25 @@ constexpr int kTile = 32;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 8 codes of channels 8*k .. 8*k+7 from a record held as dwords.
+// 8 codes of channels 16 s + 8 lh .. + 7 from a record held as dwords.  The
+// dword indices depend on s only (a compile-time constant where it is called);
+// the lane half lh picks a shift or a register, so that the record stays in
+// registers (an index that varies by lane would put it in scratch memory).
 template <int BITS>
-__device__ __forceinline__ uint32_t codes8(const uint32_t* w, int k) {
+__device__ __forceinline__ uint32_t codes8(const uint32_t* w, int s, int lh) {
   if constexpr (BITS == 2) {
-    return (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    return (w[s] >> (16 * lh)) & 0xFFFFu;
   } else if constexpr (BITS == 4) {
-    return w[k];
+    return lh ? w[2 * s + 1] : w[2 * s];
   } else {
-    const int bit = 24 * k, d = bit >> 5, sh = bit & 31;
-    const uint64_t lo = w[d];
-    const uint64_t hi = (d + 1 < 12) ? (uint64_t)w[d + 1] : 0ull;
-    return (uint32_t)(((hi << 32) | lo) >> sh) & 0xFFFFFFu;
+    // bits o .. o + 23, o = 48 s + 24 lh: both candidates from constant dwords
+    // (a 64-bit value assembled from the array would be loaded from memory)
+    auto at = [&](int o) __attribute__((always_inline)) -> uint32_t {
+      const int d = o >> 5, sh = o & 31;
+      const uint32_t v = sh + 24 <= 32 ? w[d] >> sh : __builtin_amdgcn_alignbit(w[d + 1], w[d], sh);
+      return v & 0xFFFFFFu;
+    };
+    return lh ? at(48 * s + 24) : at(48 * s);
   }
 }
 
@@ -234,14 +241,13 @@ __global__ void __launch_bounds__(128 * HG) dequant_tinv_kernel(const DequantArg
   };
 
   auto compute = [&](int64_t tile, const TileIn& p) __attribute__((always_inline)) {
-    const int64_t t = tile * kTile + col;
     const bool valid = p.valid;
     const uint32_t* w = p.w;
     // B operand: channels 16s + 8lh + e
     bf16x8 B[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint32_t c = codes8<BITS>(w, 2 * s + lh);
+      const uint32_t c = codes8<BITS>(w, s, lh);
       u32x4 pk;
       if constexpr (BITS == 2) {
         const uint64_t lo = lut[c & 0xFF], hi = lut[(c >> 8) & 0xFF];

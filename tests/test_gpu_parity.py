@@ -834,16 +834,20 @@ def test_dequant_plain_bit_exact(env, kind, bits):
     assert np.array_equal(out16.view(np.uint32), o.round_bf16(ref).view(np.uint32))
 
 
+@pytest.mark.parametrize("n", [1025, 4100])
 @pytest.mark.parametrize("kind,bits", QUANTS)
-def test_dequant_inverse_transform(env, kind, bits):
+def test_dequant_inverse_transform(env, kind, bits, n):
+    """Keys read back through T_k^-1, fp32 and bf16 out.  8 heads x 1025
+    tokens launch one head per block; 4100 tokens (a ragged last tile) launch
+    the four-head blocks (or the two-head blocks of the variants that take
+    those)."""
     s, o, bk, torch = env["synth"], env["oracle"], env["bk"], env["torch"]
     w = s.WORKLOADS["affine_pct" if kind == "affine" else "qwen3_32b_full"]
-    n = 1025
     K = s.kv(w, 0, "K", 0, n)
     pos = s.positions(w, 0, n)
     T, Ti = s.transform(w, 0)
     q = _bkq(env, kind)
-    say(f"dequant through T^-1 {kind} {bits}")
+    say(f"dequant through T^-1 {kind} {bits} n={n}")
     h = o.quantize_keys(K, pos, T, w.theta, bits, oracle_q(env, q))
     p = dev_packed(env, h)
     ref = o.dequantize(h["codes"], h["scales"], h["zeros"], n, K.shape[1], bits, oracle_q(env, q), Tinv=Ti)
