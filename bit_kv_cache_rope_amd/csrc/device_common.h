@@ -121,23 +121,22 @@ __device__ __forceinline__ uint32_t sym_code(float y, float delta, float rdelta)
 }
 
 // 3/4-bit symmetric code, fast path.  The midpoints are the integer multiples
-// j * step, |j| < 2^(b-1), so away from them the code is 2^(b-1) +
-// floor(y / step), clamped.  v = y * rdelta (rdelta = v_rcp_f32(step), within
-// 1 ulp) is within |y / step| * 1.8e-7 of y / step; after clamping to
-// +-(2^(b-1) - 1/2) (the codes there are the extremes, and no midpoint lies
-// between the clamp and the grid's end) that is below 1.5e-6, so when v is
-// farther than kSymNear from every integer, floor(v) = floor(y / step) and y
-// is no tie.  Otherwise `near` is set and the caller recomputes the code with
-// sym_code.  A zero step (rdelta = 0) gives v = 0, code 2^(b-1); callers drop
-// `near` for it.
+// j * step, |j| < 2^(b-1), so away from them the code is floor(y / step +
+// 2^(b-1)), clamped to the grid.  w = fma(y, rdelta, 2^(b-1)) (rdelta =
+// v_rcp_f32(step), within 1 ulp) is within |y / step| * 1.8e-7 + 2^-21 of
+// y / step + 2^(b-1); clamped to [1/2, 2^b - 1/2] (the codes beyond are the
+// extremes, and no midpoint lies between the clamp and the grid's end) that
+// is below 2e-6, so when w is farther than kSymNear from every integer,
+// trunc(w) is the code and y is no tie.  Otherwise `near` is set and the
+// caller recomputes the code with sym_code.  A zero step (rdelta = 0) gives
+// w = 2^(b-1), code 2^(b-1); callers drop `near` for it.
 constexpr float kSymNear = 0x1p-17f;
 template <int BITS>
 __device__ __forceinline__ uint32_t sym_code_fast(float y, float rdelta, bool& near) {
   constexpr float H = (float)(1 << (BITS - 1));
-  const float v = __builtin_amdgcn_fmed3f(y * rdelta, -H + 0.5f, H - 0.5f);
-  const float fl = __builtin_floorf(v);
-  near |= __builtin_fabsf(v - __builtin_rintf(v)) < kSymNear;
-  return (uint32_t)(fl + H);
+  const float w = __builtin_amdgcn_fmed3f(__builtin_fmaf(y, rdelta, H), 0.5f, 2.0f * H - 0.5f);
+  near |= __builtin_fabsf(w - __builtin_rintf(w)) < kSymNear;
+  return (uint32_t)w;  // w > 0: truncation is floor
 }
 
 // Lane masks of the two bits of a 2-bit symmetric code from the midpoint
@@ -224,20 +223,21 @@ __device__ __forceinline__ uint32_t affine_code(float x, double z, double s) {
   return q;
 }
 
-// Affine code, fast path.  v = (x - zero) * rstep (rstep = v_rcp_f32(step),
+// Affine code, fast path.  (x - zero) * rstep (rstep = v_rcp_f32(step),
 // within 1 ulp; the difference rounded once) is within |v| * 2.4e-7 of the
-// exact (x - zero) / step; clamped to [0, 2^b - 1] that is below 3.6e-6.  The
-// midpoints sit at v = k + 1/2, so when v is farther than kAffNear from every
-// half-integer, rint(v) is the nearest level and no tie; otherwise `near` is
-// set and the caller recomputes the code with affine_code.  A zero step
-// (rstep = 0) gives code 0, as affine_code's callers do.
+// exact v = (x - zero) / step, and w = fma(x - zero, rstep, 1/2) within that
+// plus 2^-21 of v + 1/2; clamped to [1/2, 2^b - 1/2] the bound is below
+// 4.2e-6.  The midpoints sit at integer w, so when w is farther than kAffNear
+// from every integer, trunc(w) is the nearest level and no tie; otherwise
+// `near` is set and the caller recomputes the code with affine_code.  A zero
+// step (rstep = 0) gives w = 1/2, code 0, as affine_code's callers do.
 constexpr float kAffNear = 0x1p-16f;
 template <int BITS>
 __device__ __forceinline__ uint32_t affine_code_fast(float x, float zero, float rstep, bool& near) {
   constexpr float Lm1 = (float)((1 << BITS) - 1);
-  const float v = __builtin_amdgcn_fmed3f((x - zero) * rstep, 0.0f, Lm1);
-  near |= __builtin_fabsf(v - __builtin_floorf(v) - 0.5f) < kAffNear;
-  return (uint32_t)__builtin_rintf(v);
+  const float w = __builtin_amdgcn_fmed3f(__builtin_fmaf(x - zero, rstep, 0.5f), 0.5f, Lm1 + 0.5f);
+  near |= __builtin_fabsf(w - __builtin_rintf(w)) < kAffNear;
+  return (uint32_t)w;  // w > 0: truncation is floor
 }
 
 // ---------------------------------------------------------------------------------------------
