@@ -185,30 +185,32 @@ __global__ void __launch_bounds__(128 * HG) dequant_tinv_kernel(const DequantArg
         A[m][s] = Tp[(((int64_t)h * 4 + 2 * half + m) * 8 + s) * 64 + lane];
   }
 
-  // B-operand lookup: for 2-bit records, entry b holds the four bf16 operands
-  // of the codes in byte b; for 4-bit, the two of its codes (3-bit codes
-  // straddle bytes and are converted arithmetically).  Operand of code q:
-  // 2q - (2^b - 1) (symmetric) or q (affine), exact in bf16.
-  constexpr bool LUT = BITS != 3;
-  __shared__ __align__(16) uint64_t lut[LUT ? 256 : 1];
+  // B-operand lookup: for 2-bit records, entry b (words 2b, 2b + 1) holds the
+  // four bf16 operands of the codes in byte b; for 4-bit, entry b (word b) the
+  // two of its codes; for 3-bit, entry b < 64 (word b) the two of a 6-bit pair
+  // of codes, each entry in its own LDS bank.  Operand of code q: 2q - (2^b - 1)
+  // (symmetric) or q (affine), exact in bf16.
+  __shared__ __align__(16) uint32_t lut[512];
   // Output staging: each wave's 32 tokens x 64 rows, padded rows of OROW bytes.
   constexpr int OESZ = BF16OUT ? 2 : 4;
   constexpr int OROW = 64 * OESZ + 16;
   __shared__ __align__(16) uint8_t out_lds[2 * HG][kTile * OROW];
-  if constexpr (LUT) {
-    for (int b = tid; b < 256; b += 128 * HG) {
-      constexpr int PER = BITS == 2 ? 4 : 2;
-      uint16_t v[4] = {0, 0, 0, 0};
+  for (int b = tid; b < 256; b += 128 * HG) {
+    constexpr int PER = BITS == 2 ? 4 : 2;  // codes per index (8 bits; 3 bits: 6)
+    uint16_t v[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int q = (b >> (BITS * i)) & (L - 1);
-        const float f = QK == 0 ? (float)(2 * q - (L - 1)) : (float)q;
-        v[i] = (uint16_t)(__float_as_uint(f) >> 16);  // exact: a small integer
-      }
-      lut[b] = (uint64_t)v[0] | ((uint64_t)v[1] << 16) | ((uint64_t)v[2] << 32) | ((uint64_t)v[3] << 48);
+    for (int i = 0; i < PER; ++i) {
+      const int q = (b >> (BITS * i)) & (L - 1);
+      const float f = QK == 0 ? (float)(2 * q - (L - 1)) : (float)q;
+      v[i] = (uint16_t)(__float_as_uint(f) >> 16);  // exact: a small integer
     }
-    __syncthreads();
+    if constexpr (BITS != 2) {
+      if (BITS == 4 || b < 64) lut[b] = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+    } else {
+      *(uint2*)&lut[2 * b] = make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+    }
   }
+  __syncthreads();
 
   // A tile's inputs for this lane's token: its record, its scale(s) (invalid
   // or past the end: the zero record), loaded one tile ahead.
@@ -250,20 +252,12 @@ __global__ void __launch_bounds__(128 * HG) dequant_tinv_kernel(const DequantArg
       const uint32_t c = codes8<BITS>(w, s, lh);
       u32x4 pk;
       if constexpr (BITS == 2) {
-        const uint64_t lo = lut[c & 0xFF], hi = lut[(c >> 8) & 0xFF];
-        pk = (u32x4){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+        const uint2 lo = *(const uint2*)&lut[2 * (c & 0xFF)], hi = *(const uint2*)&lut[2 * ((c >> 8) & 0xFF)];
+        pk = (u32x4){lo.x, lo.y, hi.x, hi.y};
       } else if constexpr (BITS == 4) {
-        pk = (u32x4){(uint32_t)lut[c & 0xFF], (uint32_t)lut[(c >> 8) & 0xFF], (uint32_t)lut[(c >> 16) & 0xFF],
-                     (uint32_t)lut[c >> 24]};
+        pk = (u32x4){lut[c & 0xFF], lut[(c >> 8) & 0xFF], lut[(c >> 16) & 0xFF], lut[c >> 24]};
       } else {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = (c >> (BITS * e)) & (L - 1);
-          v[e] = QK == 0 ? (float)(2 * q - (L - 1)) : (float)q;
-        }
-        pk = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                     pack_bf16x2(v[6], v[7])};
+        pk = (u32x4){lut[c & 63], lut[(c >> 6) & 63], lut[(c >> 12) & 63], lut[c >> 18]};
       }
       B[s] = __builtin_bit_cast(bf16x8, pk);
     }
