@@ -240,3 +240,45 @@ def test_affine_and_symmetric_caches_do_not_mix(oracle_mod):
     v = random_cache(rng, 4, 1, 2)
     with pytest.raises(ValueError):
         oracle_mod.decode_attention(np.zeros((1, 1, D), np.uint16), k, v, 2, np.array([0]), np.array([4]), 1.0)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_paired_attention_gap_for_a_general_transform(oracle_mod, synth_mod, bits):
+    """A general T_k (the decode workload's: an orthogonal factor times a
+    log-normal diagonal) makes the bf16 rounding of the paired query (R34)
+    inexact.  Against fp64 attention of the query itself over the read path's
+    keys k^ = T~inv y^, the rounding of q' = T~inv^T q to fp32 and then bf16
+    (relative error at most 2^-9 + 2^-24 per element) moves each score by at
+    most B = scale * (2^-9 + 2^-24) * max_n sum_j |q'_j y^_nj|, so every
+    softmax weight by a factor within exp(+-2B) and the output by at most
+    (exp(2B) - 1) max|v^|.  The test checks the oracle's output against that
+    bound and reports the gap it finds."""
+    w = synth_mod.WORKLOADS["decode_append"]
+    _, Tinv = synth_mod.transform(w, 5)
+    Tb = bf16_value(bf16_bits_of(Tinv)).astype(np.float64)  # T~inv, the read path's operand
+    rng = np.random.default_rng(60 + bits)
+    Hkv, G, rows = 2, 4, 600
+    Hq = Hkv * G
+    k, v = random_cache(rng, rows, Hkv, bits), random_cache(rng, rows, Hkv, bits)
+    q = bf16_bits_of(rng.standard_normal((2, Hq, D)) * 3.0)
+    row0, lens, scale = np.array([0, 250]), np.array([250, 350]), 1.0 / np.sqrt(D)
+    out = oracle_mod.decode_attention(oracle_mod.pair_queries(q, Tinv[:Hkv]), k, v, bits, row0, lens, scale)
+    qv = bf16_value(q).astype(np.float64)
+    worst = 0.0
+    for b in range(2):
+        r = np.arange(row0[b], row0[b] + lens[b])
+        for hq in range(Hq):
+            h = hq // G
+            Y = np.stack([dequant(k["codes"][i, h], k["scales"][i, h], bits) for i in r])
+            V = np.stack([dequant(v["codes"][i, h], v["scales"][i, h], bits) for i in r])
+            qe = Tb[h].T @ qv[b, hq]              # the exact paired query
+            s = (Y @ qe) * scale                  # = q . (T~inv y^) * scale
+            p = np.exp(s - s.max())
+            ref = (p / p.sum()) @ V
+            B = scale * (2.0 ** -9 + 2.0 ** -24) * np.max(np.abs(Y) @ np.abs(qe))
+            gap = np.max(np.abs(out[b, hq].astype(np.float64) - ref))
+            vmax = np.max(np.abs(V))
+            assert gap <= np.expm1(2 * B) * vmax + 1e-6 * vmax, (b, hq, gap, B)
+            worst = max(worst, gap / vmax)
+    print(f"[case] paired-query rounding, general T_k, {bits}-bit: worst gap / max|v| = {worst:.2e}")
+    assert worst > 0.0  # the rounding is visible for this transform
