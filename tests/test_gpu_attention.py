@@ -292,24 +292,26 @@ def synth_queries(B, Hq):
     return rng.standard_normal((B, Hq, D)) * 3.0
 
 
-def test_attention_decode_batch_full_size_sampled(env):
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_attention_decode_batch_full_size_sampled(env, bits):
     """The benchmark's launch: 64 sequences with the decode workload's lengths
-    (position + 1, up to 32768), 32 query heads over 8 KV heads, 2-bit caches of
-    64 x 32768 rows; the oracle checks a sample of sequences."""
+    (position + 1, up to 32768), 32 query heads over 8 KV heads, caches of
+    64 x 32768 rows at 2, 3 and 4 bits; the oracle checks a sample of
+    sequences."""
     synth, oracle = env["synth"], env["oracle"]
     w = synth.WORKLOADS["decode_append"]
     lens = synth.positions(w).astype(np.int64) + 1
-    B, Hkv, G, bits = len(lens), w.heads, 4, 2
+    B, Hkv, G = len(lens), w.heads, 4
     rows = w.cache_rows
-    rng = np.random.default_rng(51)
+    rng = np.random.default_rng(51 + bits)
     k, v = random_cache(rng, rows, Hkv, bits), random_cache(rng, rows, Hkv, bits)
     row0 = np.arange(B, dtype=np.int64) * 32768
     qp = bf16_bits(rng.standard_normal((B, Hkv * G, D)) * 3.0)
-    say(f"decode batch B={B} max len={int(lens.max())}")
+    say(f"decode batch B={B} max len={int(lens.max())} bits={bits}")
     got = run_attention(env, qp, k, v, Hkv, bits, row0, lens, 1.0 / np.sqrt(D), max_len=32768)
     pick = np.array([int(np.argmax(lens)), int(np.argmin(lens)), int(np.argsort(lens)[B // 2])])
     ref = oracle.decode_attention(qp[pick], k, v, bits, row0[pick], lens[pick], 1.0 / np.sqrt(D))
-    check_attention(env, got[pick], ref, value_max(v, bits, row0[pick], lens[pick], rows, Hkv), G, "decode batch")
+    check_attention(env, got[pick], ref, value_max(v, bits, row0[pick], lens[pick], rows, Hkv), G, f"decode batch bits={bits}")
 
 
 # ---------------------------------------------------------------------------------- affine caches
