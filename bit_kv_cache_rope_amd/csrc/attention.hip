@@ -312,7 +312,7 @@ __device__ __forceinline__ float vmax(float x, float y) {
 // the codes as exact bf16 values 0.5 + c / SB; values on the fp32 4x4x1
 // product, where wave w owns channels 32 w .. 32 w + 31 (one affine group).
 template <int BITS, int QS>
-__global__ void __launch_bounds__(256, QS == 1 ? 3 : 2) attention_affine_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(256, (QS == 1 && BITS != 4) ? 3 : 2) attention_affine_kernel(const AttnArgs a) {
   constexpr int NQ = 4 * QS;   // query rows of the value product (G <= NQ)
   constexpr int KS = kSub;  // tokens per round (three blocks' LDS fits a CU)
   constexpr int REC = 16 * BITS;
