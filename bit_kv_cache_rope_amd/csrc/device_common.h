@@ -86,6 +86,35 @@ __device__ __forceinline__ float total_order_value(int32_t k) {
   return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 
+// Running two smallest (m1 <= m2) and two largest (x1 >= x2) of a stream of
+// floats, one v_med3_f32 each: the median of (m1, m2, v) is the new second
+// smallest, the median of (m1, v, -inf) the new smallest.  It orders -0 and
+// +0 as equal, which the percentile-clipped quantizer may use only where both
+// percentiles interpolate between order statistics (a zero of either sign
+// there gives the same interpolated value, see affine_runs).
+struct Extremes2 {
+  float m1, m2, x1, x2;
+};
+__device__ __forceinline__ Extremes2 extremes2_init() {
+  return {__builtin_inff(), __builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+}
+__device__ __forceinline__ void extremes2_add(Extremes2& e, float v) {
+  e.m2 = __builtin_amdgcn_fmed3f(e.m1, e.m2, v);
+  e.m1 = __builtin_amdgcn_fmed3f(e.m1, v, -__builtin_inff());
+  e.x2 = __builtin_amdgcn_fmed3f(e.x1, e.x2, v);
+  e.x1 = __builtin_amdgcn_fmed3f(e.x1, v, __builtin_inff());
+}
+// The union of two such sets.
+__device__ __forceinline__ Extremes2 extremes2_merge(const Extremes2& a, const Extremes2& b) {
+  const float ninf = -__builtin_inff(), pinf = __builtin_inff();
+  Extremes2 r;
+  r.m1 = __builtin_amdgcn_fmed3f(a.m1, b.m1, ninf);
+  r.m2 = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(a.m1, b.m1, pinf), __builtin_amdgcn_fmed3f(a.m2, b.m2, ninf), ninf);
+  r.x1 = __builtin_amdgcn_fmed3f(a.x1, b.x1, pinf);
+  r.x2 = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(a.x1, b.x1, ninf), __builtin_amdgcn_fmed3f(a.x2, b.x2, pinf), pinf);
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Code assignment: index of the nearest level in exact arithmetic, ties to the even code.
 //

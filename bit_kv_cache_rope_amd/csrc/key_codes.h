@@ -143,7 +143,25 @@ __device__ __forceinline__ void affine_runs(const f32x16& acc, const QuantArgs& 
     bitonic_merge<16>(a, b, srt);
     lo = percentile_sorted(srt, qa.lo_i, qa.g_lo, qa.lo_mode);
     hi = percentile_sorted(srt, qa.hi_i, qa.g_hi, qa.hi_mode);
+  } else if (qa.lo_mode == 0 && qa.hi_mode == 0) {
+    // Both percentiles interpolate (the 1st/99th): the extremes by float
+    // minimum, maximum and median.  Where -0 and +0 tie for an order statistic
+    // their order does not reach the result: fma(g, s1 - s0, s0) with s0, s1
+    // zeros of either signs is +0 in every order (and so for s30, s31).
+    Extremes2 e = extremes2_init();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) extremes2_add(e, acc[i]);
+    Extremes2 o;
+    {
+      const Halves m1 = halves(e.m1), m2 = halves(e.m2), x1 = halves(e.x1), x2 = halves(e.x2);
+      o = extremes2_merge({__uint_as_float(m1.lo), __uint_as_float(m2.lo), __uint_as_float(x1.lo), __uint_as_float(x2.lo)},
+                          {__uint_as_float(m1.hi), __uint_as_float(m2.hi), __uint_as_float(x1.hi), __uint_as_float(x2.hi)});
+    }
+    lo = __builtin_fmaf(qa.g_lo, o.m2 - o.m1, o.m1);
+    hi = __builtin_fmaf(qa.g_hi, o.x1 - o.x2, o.x2);
   } else {
+    // a percentile taken as an order statistic itself: IEEE totalOrder keys
+    // (-0 below +0), as the oracle sorts
     int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

@@ -162,7 +162,21 @@ __device__ __forceinline__ uint32_t value_codes_affine(const float* x, const Qua
     bitonic_merge<16>(m01, m23, srt);
     lo = percentile_sorted(srt, qa.lo_i, qa.g_lo, qa.lo_mode);
     hi = percentile_sorted(srt, qa.hi_i, qa.g_hi, qa.hi_mode);
+  } else if (qa.lo_mode == 0 && qa.hi_mode == 0) {
+    // Both percentiles interpolate (the 1st/99th): the extremes by float
+    // minimum, maximum and median, merged over the quad by DPP (a zero of
+    // either sign tied for an order statistic gives the same lo and hi, see
+    // affine_runs).
+    Extremes2 e = extremes2_init();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) extremes2_add(e, x[i]);
+    e = extremes2_merge(e, {dpp_f32<0xB1>(e.m1), dpp_f32<0xB1>(e.m2), dpp_f32<0xB1>(e.x1), dpp_f32<0xB1>(e.x2)});
+    e = extremes2_merge(e, {dpp_f32<0x4E>(e.m1), dpp_f32<0x4E>(e.m2), dpp_f32<0x4E>(e.x1), dpp_f32<0x4E>(e.x2)});
+    lo = __builtin_fmaf(qa.g_lo, e.m2 - e.m1, e.m1);
+    hi = __builtin_fmaf(qa.g_hi, e.x1 - e.x2, e.x2);
   } else {
+    // a percentile taken as an order statistic itself: IEEE totalOrder keys
+    // (-0 below +0), as the oracle sorts
     int32_t mn1 = INT_MAX, mn2 = INT_MAX, mx1 = INT_MIN, mx2 = INT_MIN;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

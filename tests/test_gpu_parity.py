@@ -575,6 +575,53 @@ def test_keys_identity_equals_values_of_rope(env):
         assert_same_packed(g, r, "identity keys")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("p", [(1.0, 99.0), (2.0, 98.0), (0.0, 100.0), (0.0, 99.0)])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_affine_values_signed_zero_order_statistics(env, dtype, p, bits):
+    """Percentile-clipped values whose smallest or largest order statistics tie
+    between -0 and +0 (the oracle sorts by IEEE totalOrder, -0 below +0):
+    groups of positive values with both zeros among the two smallest, negative
+    values with both among the two largest, only zeros of both signs, a lone
+    -0 below positives, zeros in the middle.  Interpolating percentiles
+    (1st/99th, 2nd/98th) take the kernels' float selection, percentiles taken
+    as an order statistic (0th/100th, 0th with the 99th) their totalOrder
+    selection; records, steps and zeros bit-exact against the oracle."""
+    o, bk = env["oracle"], env["bk"]
+    rng = np.random.default_rng(int(10 * p[0] + p[1]) + 7 * bits)
+    N, H = 41, 3
+    V = rng.standard_normal((N, H, 4, 32)).astype(np.float32)
+    for n in range(N):
+        for h in range(H):
+            for gi in range(4):
+                x = V[n, h, gi]
+                kind = (n * H * 4 + h * 4 + gi) % 6
+                i, j = rng.choice(32, 2, replace=False)
+                if kind == 0:
+                    x[:] = np.abs(x) + 0.5
+                    x[i], x[j] = -0.0, 0.0
+                elif kind == 1:
+                    x[:] = -np.abs(x) - 0.5
+                    x[i], x[j] = 0.0, -0.0
+                elif kind == 2:
+                    x[:] = np.where(rng.random(32) < 0.5, -0.0, 0.0)
+                elif kind == 3:
+                    x[:] = np.abs(x) + 0.25
+                    x[i] = -0.0
+                elif kind == 4:
+                    x[rng.choice(32, 6, replace=False)] = np.where(rng.random(6) < 0.5, -0.0, 0.0)
+                else:
+                    x[:] = np.abs(x)
+                    x[rng.choice(32, 3, replace=False)] = [-0.0, 0.0, -0.0]
+    V = V.reshape(N, H, 128)
+    Vd = (V.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else V  # bf16: truncation keeps the zeros' signs
+    q = bk.affine(*p)
+    say(f"affine values with signed zeros, p={p}, {bits}-bit, {dtype}")
+    got = packed_host(run_values(env, Vd, bits, q))
+    ref = o.quantize_values(Vd, bits, oracle_q(env, q))
+    assert_same_packed(got, ref, f"signed zeros p={p} {bits}-bit {dtype}")
+
+
 def test_keys_exact_zero_outputs(env):
     """Transformed keys that are exactly zero (cancellation and zero channels)
     must come out as +0 from the MFMA and take code L/2 like the oracle's: at
