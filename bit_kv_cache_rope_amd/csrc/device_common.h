@@ -168,59 +168,6 @@ __device__ __forceinline__ uint32_t sym_code_fast(float y, float rdelta, bool& n
   return (uint32_t)w;  // w > 0: truncation is floor
 }
 
-// Lane masks of the two bits of a 2-bit symmetric code from the midpoint
-// tests A = [x > -step], B = [x >= 0], C = [x > step]: bit1 = B and
-// bit0 = B ? C : A, i.e. one test of x against the threshold that B selects
-// (+step or -step).  A zero step uses thresholds that make every code 2.
-struct Sym2Masks {
-  uint64_t b1, b0;
-};
-
-// For a value tested as a raw 32-bit word (see bf16_gt_threshold): B is the
-// unsigned bound word <= tb (x >= 0 or x = -0), A and C compare the word as a
-// float with the bf16-rounded thresholds ta and tc.  Two vector compares and
-// one select per code, no scalar mask logic.
-__device__ __forceinline__ Sym2Masks sym2_masks_raw(uint32_t w, float ta, uint32_t tb, float tc) {
-  const bool B = w <= tb;
-  const float t = B ? tc : ta;
-  return {__builtin_amdgcn_ballot_w64(B), __builtin_amdgcn_ballot_w64(__uint_as_float(w) > t)};
-}
-
-// r = 2r + bit, once per lane mask, first mask first (so it ends up most
-// significant): one v_addc_co_u32 per bit with the mask as carry-in.  The
-// leading s_nop gives the two wait states a vector compare's mask needs
-// before an add-with-carry may read it.
-__device__ __forceinline__ uint32_t shift_in8(uint32_t r, const uint64_t* m) {
-  uint64_t co;
-  asm("s_nop 1\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %2\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %3\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %4\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %5\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %6\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %7\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %8\n\t"
-      "v_addc_co_u32_e64 %0, %1, %0, %0, %9"
-      : "+v"(r), "=&s"(co)
-      : "s"(m[0]), "s"(m[1]), "s"(m[2]), "s"(m[3]), "s"(m[4]), "s"(m[5]), "s"(m[6]), "s"(m[7]));
-  return r;
-}
-
-// Thresholds that decide "x > t" for a bf16 value x from the raw 32-bit word
-// whose high half holds x (the low half holding anything): with c the
-// smallest bf16 above t, x > t iff x >= c.  For c > 0 every word with high
-// half x >= c reads as a float >= c and every other one as < c, so the test
-// is word > prev_fp32(c), whose bits are bits(t) | 0xFFFF.  For t < 0 the
-// test is word > d with d the largest bf16 <= t (a word's float lies within
-// one bf16 step below its high half, towards -inf).  Both tests also decide
-// exact bf16 values (low half zero) correctly.  t = +-inf maps to itself.
-__device__ __forceinline__ float bf16_gt_threshold(float t) {
-  const uint32_t b = __float_as_uint(t);
-  if (__builtin_isinf(t)) return t;
-  if (t >= 0.0f) return __uint_as_float(b | 0xFFFFu);
-  return __uint_as_float((((b & 0x7FFFFFFFu) + 0xFFFFu) & 0xFFFF0000u) | 0x80000000u);
-}
-
 // Sum over aligned groups of 2, 4, 8 and 16 lanes by DPP moves: after step k a
 // lane holds the sum of its 2^k-lane block, each step adding the two halves'
 // sums (commutative, so both halves hold the same value).  Equal to xor

@@ -59,20 +59,6 @@ __device__ __forceinline__ float dpp_xor4(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(lo, x, 0x114, 0xF, 0xA, false));  // row_shr:4
 }
 
-// 2-bit symmetric codes of the lane's 8 values, LSB first in the low 16 bits:
-// the key kernel's rule (high bit: y >= 0, the sign inverted; low bit: the
-// sign of (step - |y|) * y + 0), for values that are never -0.
-__device__ __forceinline__ uint32_t sym2_bits8(const float* y, float delta) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int e = 7; e >= 0; --e) {
-    const float m = __builtin_fmaf(delta - __builtin_fabsf(y[e]), y[e], 0.0f);
-    w = __builtin_amdgcn_alignbit(w, __float_as_uint(y[e]), 31);
-    w = __builtin_amdgcn_alignbit(w, __float_as_uint(m), 31);
-  }
-  return delta == 0.0f ? 0xAAAAu : (w ^ 0xAAAAu);
-}
-
 template <int BITS, int QK, bool F32IN, bool YOUT>
 __global__ void __launch_bounds__(64 * kFWaves) __attribute__((amdgpu_waves_per_eu(QK == 2 ? 2 : ((F32IN || QK) ? 3 : 4))))
 keys_fwht_kernel(const KeysArgs a) {
@@ -234,7 +220,7 @@ keys_fwht_kernel(const KeysArgs a) {
             if constexpr (BITS == 2) {
               th_lds[w][lane] = make_float4(delta, 0.0f, 0.0f, 0.0f);
             } else {
-              th_lds[w][lane] = value_thresholds<BITS, true>(delta);
+              th_lds[w][lane] = value_thresholds<BITS>(delta);
             }
           }
         }
@@ -246,7 +232,7 @@ keys_fwht_kernel(const KeysArgs a) {
           if constexpr (QK == 0) {
             const float4 th = th_lds[w][4 * kk + sub];
             if constexpr (BITS == 2) {
-              packed = sym2_bits8(y[kk], th.x);  // th.x: the step (0: every code is 2)
+              packed = sym2_bits8(y[kk], th.x);  // th.x: the step (0: every code is 2); y is never -0 here
             } else {
               packed = value_codes_sym<BITS>(y[kk], th);
             }

@@ -134,9 +134,9 @@ __global__ void __launch_bounds__(kThreads) kv_append_kernel(const AppendArgs a)
       if constexpr (QK == 0) {
         // every lane of the vector holds the whole sum after the butterflies
         sh = sym_step_f16<L>(dpp_sum16(lane_sumsq8(x)), a.q.alpha);
-        const float4 th = value_thresholds<BITS, F32IN>(f16_bits_to_f32(sh));
+        const float4 th = value_thresholds<BITS>(f16_bits_to_f32(sh));
         if constexpr (BITS == 2) {
-          packed = value_codes2<F32IN>(vw, th);
+          packed = value_codes2<F32IN>(vw, th.x);
         } else {
           packed = value_codes_sym<BITS>(x, th);
         }

@@ -49,20 +49,15 @@ __device__ __forceinline__ float lane_sumsq8(const float* x) {
 }
 
 // Per-vector constants of the symmetric code step from the fp16 step delta.
-// 2 bits: midpoint tests A = [x > -step], B = [x >= 0], C = [x > step] (ties as
-// in the nearest-level rule).  bf16 input: A and C are decided on the raw word
-// (bf16_gt_threshold), B as an unsigned bound (x >= 0 or x = -0); a zero step
-// makes A and B always true and C never: code 2.  3/4 bits: the step (+inf for
+// 2 bits: the step itself (0: every code is 2).  3/4 bits: the step (+inf for
 // a zero step) and its reciprocal (0 for a zero step, giving code L/2).
-template <int BITS, bool F32IN>
+template <int BITS>
 __device__ __forceinline__ float4 value_thresholds(float delta) {
   const float tp = delta == 0.0f ? __builtin_inff() : delta;  // +inf for a zero step
   float4 th;
   if constexpr (BITS == 2) {
-    th.x = F32IN ? -tp : bf16_gt_threshold(-tp);
-    th.y = F32IN ? tp : bf16_gt_threshold(tp);
-    th.z = __uint_as_float(delta == 0.0f ? 0xFFFFFFFFu : (F32IN ? 0x80000000u : 0x8000FFFFu));
-    th.w = 0.0f;
+    th.x = delta;
+    th.y = th.z = th.w = 0.0f;
   } else {
     th.x = tp;
     th.y = delta == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(delta);
@@ -71,37 +66,35 @@ __device__ __forceinline__ float4 value_thresholds(float delta) {
   return th;
 }
 
-// 2-bit symmetric codes of the lane's 8 channels, LSB first (16 bits), from the
-// raw words.  The masks are wave-wide ballots: every lane of the wave must run it.
-template <bool F32IN>
-__device__ __forceinline__ uint32_t value_codes2(const vu32x4* p, float4 th) {
-  // the 8 words to test, channel order: bf16 -> low halves shifted up, high
-  // halves raw; fp32 -> the values' bits
-  uint32_t w[8];
-  if constexpr (F32IN) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[e] = p[0][e];
-      w[4 + e] = p[1][e];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[2 * e] = p[0][e] << 16;
-      w[2 * e + 1] = p[0][e];
-    }
-  }
-  const uint32_t tb = __float_as_uint(th.z);
-  const uint32_t tbl = F32IN ? tb : (tb & 0xFFFF0000u);  // low halves are exact
-  uint64_t m[16];
+// 2-bit symmetric codes of 8 values, LSB first in the low 16 bits: code =
+// [y > -step] + [y >= 0] + [y > step].  The high bit is [y >= 0], the sign bit
+// inverted; the low bit is [y > step] for y >= 0 and [y > -step] for y < 0,
+// the sign of m = (step - |y|) * y + 0 (one fma): for |y| != step the signs of
+// (step - |y|) and y decide it, and at a tie |y| = step (and at y = +0) the
+// exact product is a zero that the +0 makes +0 (bit clear: the even code).
+// The bits are shifted in from the last value down (alignbit: w = 2w + bit 31
+// of the operand).  y must not be -0; a zero step gives code 2 everywhere.
+__device__ __forceinline__ uint32_t sym2_bits8(const float* y, float delta) {
+  uint32_t w = 0;
 #pragma unroll
   for (int e = 7; e >= 0; --e) {
-    const Sym2Masks k = sym2_masks_raw(w[e], th.x, (e & 1) ? tb : tbl, th.y);
-    m[2 * (7 - e)] = k.b1;
-    m[2 * (7 - e) + 1] = k.b0;
+    const float m = __builtin_fmaf(delta - __builtin_fabsf(y[e]), y[e], 0.0f);
+    w = __builtin_amdgcn_alignbit(w, __float_as_uint(y[e]), 31);
+    w = __builtin_amdgcn_alignbit(w, __float_as_uint(m), 31);
   }
-  const uint32_t packed = shift_in8(0u, m);
-  return shift_in8(packed, m + 8);
+  return delta == 0.0f ? 0xAAAAu : (w ^ 0xAAAAu);
+}
+
+// 2-bit symmetric codes of the lane's 8 channels from its raw words (delta:
+// the step, th.x of value_thresholds<2>).  The values are unpacked exactly and
+// a -0 becomes +0 (x + 0), so that a zero of either sign takes the even code 2.
+template <bool F32IN>
+__device__ __forceinline__ uint32_t value_codes2(const vu32x4* p, float delta) {
+  float x[8];
+  unpack_vals<F32IN>(p, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = x[e] + 0.0f;
+  return sym2_bits8(x, delta);
 }
 
 // 3/4-bit symmetric codes of the lane's 8 channels, LSB first: fast path, and

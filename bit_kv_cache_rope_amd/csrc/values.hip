@@ -168,7 +168,7 @@ values_kernel(const ValuesArgs a) {
         const uint16_t sc = sym_step_f16<L>(P, a.q.alpha);
         const float delta = f16_bits_to_f32(sc);
         sc_lds[par][wave * kPerWave + lane] = sc;
-        const float4 th = value_thresholds<BITS, F32IN>(delta);
+        const float4 th = value_thresholds<BITS>(delta);
         th_lds[wave][lane] = th;
       }
       // (3) codes
@@ -176,7 +176,7 @@ values_kernel(const ValuesArgs a) {
       for (int u = 0; u < kU; ++u) {
         const float4 th = th_lds[wave][4 * u + sub];
         if constexpr (BITS == 2) {
-          store_codes(wave * kPerWave + 4 * u + sub, value_codes2<F32IN>(words(u), th));
+          store_codes(wave * kPerWave + 4 * u + sub, value_codes2<F32IN>(words(u), th.x));
         } else {
           float x[8];
           unpack(u, x);
