@@ -576,6 +576,36 @@ def test_keys_identity_equals_values_of_rope(env):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_symmetric_values_signed_zeros(env, dtype, bits):
+    """Symmetric values with zeros of both signs: a zero is a tie between the
+    two middle levels and takes the even code 2^(b-1) whatever its sign; whole
+    zero vectors (a zero step) too.  Records and steps bit-exact against the
+    oracle, in the value kernel and in the fused append."""
+    o, bk, torch = env["oracle"], env["bk"], env["torch"]
+    rng = np.random.default_rng(90 + bits)
+    N, H = 67, 3
+    V = rng.standard_normal((N, H, 128)).astype(np.float32)
+    z = rng.random((N, H, 128)) < 0.3
+    V[z] = np.where(rng.random(z.sum()) < 0.5, -0.0, 0.0)
+    V[5] = -0.0                      # zero vectors: step 0
+    V[6, 1] = 0.0
+    V[7, 2] = np.where(np.arange(128) % 2, -0.0, 0.0)
+    Vd = (V.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else V  # bf16 bits by truncation, zeros keep their signs
+    q = bk.sym(2.0)
+    say(f"symmetric values with signed zeros, {bits}-bit, {dtype}")
+    ref = o.quantize_values(Vd, bits, oracle_q(env, q))
+    assert_same_packed(packed_host(run_values(env, Vd, bits, q)), ref, f"signed zeros {bits}-bit {dtype} values")
+    # the fused append: keys of the same tokens (identity transform, position 0)
+    K = Vd.copy()
+    kc, vc = bk.alloc_packed(N, H, bits, q), bk.alloc_packed(N, H, bits, q)
+    bk.wushkv_quantize_kv(to_dev(env, K), to_dev(env, Vd), to_dev(env, np.zeros(N, np.int32)), bk.Rope(1e6, 1 << 10),
+                          bk.Transform(np.stack([np.eye(128, dtype=np.float32)] * H)), bits, q, kc, vc)
+    torch.cuda.synchronize()
+    assert_same_packed(packed_host(vc), ref, f"signed zeros {bits}-bit {dtype} fused append values")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("p", [(1.0, 99.0), (2.0, 98.0), (0.0, 100.0), (0.0, 99.0)])
 @pytest.mark.parametrize("bits", [2, 4])
 def test_affine_values_signed_zero_order_statistics(env, dtype, p, bits):
